@@ -1,0 +1,443 @@
+"""Float64 definitions of every step of the sparse-attention hot path.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain NumPy, float64,
+one function per step, in the order the method runs:
+
+  O0 dense            textbook softmax attention (the reference every sparse
+                      result reduces to when nothing is dropped)
+  O1 sketch           per-block mean of the keys (the compact key summary)
+  O2 block_scores     group-averaged query . sketch, times the softmax scale
+  O3 select_topk      forced sink + local blocks, then the best-scoring rest
+  O4 attend_blocks    exact attention restricted to the selected blocks
+  O5 threshold        tau from the exact scores; keep every key at or above it
+  O6 prefill_select   pooled-query-block . pooled-key-block ranking, causal
+  O7 prefill_attend   causal attention of each query row over its block list
+  O8 mass_oracle      exact per-block attention mass, for recall reporting
+     lse_merge        exact merge of attention partials over a split support
+
+Arrays: q [B, Hq, D]; Q [B, Hq, L, D]; K, V [B, Hkv, N, D]; query head h uses
+kv head h // g with g = Hq // Hkv.  bf16 inputs arrive as uint16 bit patterns
+and are widened exactly.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+# ------------------------------------------------------------------ inputs
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 copy of a stored array ("f32" floats or "bf16" bits)."""
+    if dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+        return bits.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def _default_scale(D: int, scale: Optional[float]) -> float:
+    return 1.0 / math.sqrt(D) if scale is None or scale <= 0 else float(scale)
+
+
+def _attend(s: np.ndarray, Vrows: np.ndarray) -> Tuple[np.ndarray, float]:
+    """Softmax of the scores s [n] applied to the rows Vrows [n, D].
+
+    Returns (o, lse).  An empty support gives o = 0 and lse = -inf.
+    """
+    if s.size == 0:
+        return np.zeros(Vrows.shape[-1]), NEG_INF
+    m = s.max()
+    p = np.exp(s - m)
+    l = p.sum()
+    return (p @ Vrows) / l, m + math.log(l)
+
+
+# ------------------------------------------------------------------ O0
+def dense(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+          scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """O0: full softmax attention of one decode query per head over all N keys.
+
+    The decode query sees every cached key, unmasked (its own key is already
+    in the cache).  The dense result is what the attention-mass oracle of
+    "How Much Dense Attention is Necessary?" (§2.1) starts from and what any
+    sparse support must reproduce when it keeps everything.
+    """
+    B, Hq, D = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    sc = _default_scale(D, scale)
+    O = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // g
+            s = (K[b, kh] @ q[b, h]) * sc
+            O[b, h], lse[b, h] = _attend(s, V[b, kh])
+    return O, lse
+
+
+def dense_causal_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                      rows: Sequence[Tuple[int, int, int]],
+                      scale: Optional[float] = None):
+    """O0 for prefill rows: row (b, h, t) attends to keys 0..t (causal)."""
+    D = Q.shape[-1]
+    g = Q.shape[1] // K.shape[1]
+    sc = _default_scale(D, scale)
+    O = np.zeros((len(rows), D))
+    lse = np.zeros(len(rows))
+    for r, (b, h, t) in enumerate(rows):
+        kh = h // g
+        s = (K[b, kh, :t + 1] @ Q[b, h, t]) * sc
+        O[r], lse[r] = _attend(s, V[b, kh, :t + 1])
+    return O, lse
+
+
+# ------------------------------------------------------------------ O1
+def sketch(X: np.ndarray, block: int, head_pool: int = 1) -> np.ndarray:
+    """O1: per-block mean sketch of X [B, H, N, D] -> [B, H/head_pool, nb, D].
+
+    Block j covers tokens [j*block, min((j+1)*block, N)); the last block may be
+    partial and is averaged over its valid tokens only.  With head_pool > 1 the
+    mean also runs over each group of head_pool consecutive heads (the pooled
+    query block of block-sparse prefill).  The mean is this build's reading of
+    the "compact summary of the keys" that is scanned before any full key is
+    fetched ("Faster Than Flash", Metodologia §1) -- a per-block centre, like
+    the cluster centres of the range-search index ("Sparse Attention as a Range
+    Searching Problem", Metodologia §2).
+    """
+    B, H, N, D = X.shape
+    if H % head_pool:
+        raise ValueError("H must be a multiple of head_pool")
+    nb = -(-N // block)
+    Xg = X.reshape(B, H // head_pool, head_pool, N, D)
+    out = np.zeros((B, H // head_pool, nb, D))
+    for j in range(nb):
+        lo, hi = j * block, min((j + 1) * block, N)
+        out[:, :, j] = Xg[:, :, :, lo:hi, :].sum(axis=(2, 3)) / (head_pool * (hi - lo))
+    return out
+
+
+# ------------------------------------------------------------------ O2
+def block_scores(q: np.ndarray, sk: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """O2: score[b, kh, j] = mean over the group's query heads of (q_h . s_j) * scale.
+
+    Averaging over the query heads of a KV group follows the head-averaged
+    token importance of "How Much Dense Attention is Necessary?" (§2.1).
+    """
+    B, Hq, D = q.shape
+    Hkv = sk.shape[1]
+    g = Hq // Hkv
+    sc = _default_scale(D, scale)
+    out = np.zeros((B, Hkv, sk.shape[2]))
+    for b in range(B):
+        for kh in range(Hkv):
+            per_head = np.stack([sk[b, kh] @ q[b, h] for h in range(kh * g, (kh + 1) * g)])
+            out[b, kh] = per_head.mean(axis=0) * sc
+    return out
+
+
+# ------------------------------------------------------------------ O3
+def _rank_key(scores: np.ndarray) -> np.ndarray:
+    """Scores as ranking keys: NaN counts as -inf (never preferred)."""
+    s = np.array(scores, dtype=np.float64)
+    s[np.isnan(s)] = NEG_INF
+    return s
+
+
+def select_topk(scores: np.ndarray, k: int, forced: Iterable[int] = None) -> np.ndarray:
+    """O3: the kept blocks of one (b, kv head), ascending.
+
+    Forced blocks (default: the sink block 0 and the local block nb-1) are
+    always kept and count toward k.  The other k - |forced| slots go to the
+    remaining blocks by score, higher first, ties to the lower block index.
+    k >= nb keeps everything.  The sink follows the fixed attention-sink prefix
+    of "Pulsar Attention" (Fase 1; 64 tokens = one 64-token block); sink and
+    local tokens dominating the distribution is the observation of "Faster
+    Than Flash" (Metodologia §2); per-page selection from the full cache is
+    Quest as described in "The Sparse Frontier" (Contributi §2).
+    """
+    s = _rank_key(scores)
+    nb = s.size
+    if forced is None:
+        forced = {0, nb - 1}
+    F = sorted({int(j) for j in forced if 0 <= j < nb})
+    if k >= nb:
+        return np.arange(nb)
+    if k < len(F):
+        raise ValueError("k smaller than the number of forced blocks")
+    cand = np.array([j for j in range(nb) if j not in set(F)], dtype=np.int64)
+    order = cand[np.lexsort((cand, -s[cand]))]   # score desc, then index asc
+    return np.sort(np.concatenate([np.array(F, dtype=np.int64), order[:k - len(F)]]))
+
+
+def select_topk_all(scores: np.ndarray, k: int) -> np.ndarray:
+    """O3 over every (b, kv head): scores [B, Hkv, nb] -> idx [B, Hkv, min(k, nb)]."""
+    B, Hkv, nb = scores.shape
+    kk = min(k, nb)
+    idx = np.zeros((B, Hkv, kk), dtype=np.int64)
+    for b in range(B):
+        for kh in range(Hkv):
+            idx[b, kh] = select_topk(scores[b, kh], k)
+    return idx
+
+
+# ------------------------------------------------------------------ O4
+def block_tokens(blocks: Iterable[int], block: int, N: int) -> np.ndarray:
+    """Token positions of the given blocks, in block order."""
+    parts = [np.arange(j * block, min((j + 1) * block, N)) for j in blocks]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def attend_blocks(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
+                  block: int, scale: Optional[float] = None,
+                  count: Optional[np.ndarray] = None):
+    """O4: exact attention of each query head over the tokens of its group's blocks.
+
+    idx [B, Hkv, k] lists blocks (ascending; entries past count[b, kh] are
+    ignored).  The recomputation uses the original q, K, V on the support
+    only, as the oracle of "How Much Dense Attention is Necessary?" (§2.1)
+    does after choosing its support.
+    """
+    B, Hq, D = q.shape
+    Hkv, N = K.shape[1], K.shape[2]
+    g = Hq // Hkv
+    sc = _default_scale(D, scale)
+    O = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        for kh in range(Hkv):
+            n = idx.shape[2] if count is None else int(count[b, kh])
+            toks = block_tokens(idx[b, kh, :n], block, N)
+            for h in range(kh * g, (kh + 1) * g):
+                s = (K[b, kh, toks] @ q[b, h]) * sc
+                O[b, h], lse[b, h] = _attend(s, V[b, kh, toks])
+    return O, lse
+
+
+def attend_tokens(q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                  lists: Sequence[Sequence[np.ndarray]],
+                  scale: Optional[float] = None):
+    """O4 over per-head token lists: lists[b][h] holds token positions."""
+    B, Hq, D = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    sc = _default_scale(D, scale)
+    O = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        for h in range(Hq):
+            toks = np.asarray(lists[b][h], dtype=np.int64)
+            s = (K[b, h // g, toks] @ q[b, h]) * sc
+            O[b, h], lse[b, h] = _attend(s, V[b, h // g, toks])
+    return O, lse
+
+
+def lse_merge(parts: Sequence[Tuple[np.ndarray, float]]) -> Tuple[np.ndarray, float]:
+    """Exact merge of attention partials (o_i normalised, lse_i) over disjoint supports.
+
+    With weights w_i = exp(lse_i - max lse), the union's output is
+    sum_i w_i o_i / sum_i w_i and its lse is max lse + log(sum_i w_i): the
+    online-softmax merge that "Pulsar Attention" (Fase 2) uses to recover exact
+    global attention from per-shard results.  Empty parts (lse = -inf) drop out.
+    """
+    live = [(o, l) for o, l in parts if l != NEG_INF]
+    if not live:
+        D = parts[0][0].shape[-1]
+        return np.zeros(D), NEG_INF
+    m = max(l for _, l in live)
+    w = np.array([math.exp(l - m) for _, l in live])
+    o = sum(wi * oi for wi, (oi, _) in zip(w, live)) / w.sum()
+    return o, m + math.log(w.sum())
+
+
+# ------------------------------------------------------------------ O5
+def exact_scores(q: np.ndarray, K: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """s[b, h, t] = q_h . k_t * scale for every cached token (float64)."""
+    B, Hq, D = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    sc = _default_scale(D, scale)
+    s = np.zeros((B, Hq, K.shape[2]))
+    for b in range(B):
+        for h in range(Hq):
+            s[b, h] = (K[b, h // g] @ q[b, h]) * sc
+    return s
+
+
+def threshold_tau(q: np.ndarray, K: np.ndarray, percentile: float = 99.0,
+                  scale: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """tau[b, h] = the given percentile of the exact scores of head (b, h).
+
+    NumPy's default (linear interpolation) percentile, in float64; also
+    returned rounded toward -inf to float32, which is what a float32 caller
+    passes (it can only add keys, never drop one).
+    """
+    s = exact_scores(q, K, scale)
+    tau64 = np.percentile(s, percentile, axis=-1)
+    tau32 = tau64.astype(np.float32)
+    over = tau32.astype(np.float64) > tau64
+    tau32[over] = np.nextafter(tau32[over], np.float32(-np.inf))
+    return tau64, tau32
+
+
+def select_threshold(q: np.ndarray, K: np.ndarray, tau: np.ndarray,
+                     scale: Optional[float] = None):
+    """O5: every token whose exact score is >= tau[b, h], ascending, with scores.
+
+    This is the half-space H(q, tau) of "Sparse Attention as a Range Searching
+    Problem" (Metodologia §1) on the scaled dot product; returning every key
+    inside it is what makes the selection free of false negatives.
+    Returns (lists[b][h] -> int64 array, scores[b][h] -> float64 array).
+    """
+    s = exact_scores(q, K, scale)
+    B, Hq, _ = s.shape
+    lists = [[None] * Hq for _ in range(B)]
+    vals = [[None] * Hq for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            t = np.nonzero(s[b, h] >= tau[b, h])[0]
+            lists[b][h] = t
+            vals[b][h] = s[b, h, t]
+    return lists, vals
+
+
+# ------------------------------------------------------------------ O6
+def prefill_pool_queries(Q: np.ndarray, block: int, g: int) -> np.ndarray:
+    """Pooled query blocks: mean of Q over each block's tokens and the group's heads."""
+    return sketch(Q, block, head_pool=g)
+
+
+def prefill_select(Qbar: np.ndarray, Kbar: np.ndarray, k: int,
+                   scale: Optional[float] = None, rows: Optional[Iterable[int]] = None):
+    """O6: per (b, kv head, query block i) the kept key blocks, ascending.
+
+    Block 0 (sink) and the diagonal block i are always kept; the remaining
+    min(k - 2, i - 1) slots go to the earlier blocks j in [1, i-1] ranked by
+    r_ij = Qbar_i . Kbar_j * scale (higher first, ties to the lower j).  One
+    list is shared by all queries of the block and all heads of the group --
+    the block-shared support granularity of "How Much Dense Attention is
+    Necessary?" (§2.1) and the block-by-block selection of Block-Sparse
+    prefill ("The Sparse Frontier", Contributi §2).
+    Returns idx [B, Hkv, M, k] (unused slots -1) and count [B, Hkv, M].
+    """
+    if k < 2:
+        raise ValueError("prefill keeps at least the sink and the diagonal block")
+    B, Hkv, M, D = Qbar.shape
+    sc = _default_scale(D, scale)
+    idx = -np.ones((B, Hkv, M, k), dtype=np.int64)
+    cnt = np.zeros((B, Hkv, M), dtype=np.int64)
+    rows = range(M) if rows is None else rows
+    for b in range(B):
+        for kh in range(Hkv):
+            for i in rows:
+                if i == 0:
+                    S = np.array([0])
+                else:
+                    cand = np.arange(1, i)
+                    r = _rank_key((Kbar[b, kh, 1:i] @ Qbar[b, kh, i]) * sc)
+                    top = cand[np.lexsort((cand, -r))][:min(k - 2, i - 1)]
+                    S = np.sort(np.concatenate([[0, i], top]))
+                idx[b, kh, i, :S.size] = S
+                cnt[b, kh, i] = S.size
+    return idx, cnt
+
+
+# ------------------------------------------------------------------ O7
+def prefill_attend_rows(Q: np.ndarray, K: np.ndarray, V: np.ndarray,
+                        idx: np.ndarray, count: np.ndarray, block: int,
+                        rows: Sequence[Tuple[int, int, int]],
+                        scale: Optional[float] = None):
+    """O7 for chosen rows (b, h, t): causal attention over the tokens of S(t // block).
+
+    Keys after position t are masked; every other token of the listed blocks
+    is used with the original Q, K, V.
+    """
+    D = Q.shape[-1]
+    L = K.shape[2]
+    g = Q.shape[1] // K.shape[1]
+    sc = _default_scale(D, scale)
+    O = np.zeros((len(rows), D))
+    lse = np.zeros(len(rows))
+    for r, (b, h, t) in enumerate(rows):
+        kh, i = h // g, t // block
+        blocks = idx[b, kh, i, :int(count[b, kh, i])]
+        toks = block_tokens(blocks, block, L)
+        toks = toks[toks <= t]
+        s = (K[b, kh, toks] @ Q[b, h, t]) * sc
+        O[r], lse[r] = _attend(s, V[b, kh, toks])
+    return O, lse
+
+
+def prefill_attend(Q, K, V, idx, count, block, scale=None):
+    """O7 for every row (small sizes only): O [B, Hq, L, D], lse [B, Hq, L]."""
+    B, Hq, L, D = Q.shape
+    rows = [(b, h, t) for b in range(B) for h in range(Hq) for t in range(L)]
+    O, lse = prefill_attend_rows(Q, K, V, idx, count, block, rows, scale)
+    return O.reshape(B, Hq, L, D), lse.reshape(B, Hq, L)
+
+
+# ------------------------------------------------------------------ O8
+def mass_oracle(Q: np.ndarray, K: np.ndarray, block: int, k_free: int = 8,
+                scale: Optional[float] = None,
+                qblocks: Optional[Iterable[int]] = None):
+    """O8: attention-mass block ranking (recall reference for prefill selection).
+
+    For query block i of kv head kh: run dense causal softmax for every row t of
+    the block and every head of the group, sum each row's probability over the
+    tokens of key block j, and average over the rows and heads.  The k_free
+    earlier blocks j in [1, i-1] with the largest mass (ties to lower j) form
+    S_mass(i).  This is the attention-mass top-k oracle of "How Much Dense
+    Attention is Necessary?" (§2.1) at block granularity, with the head average
+    of its token-importance distribution and a block-shared support.
+    Returns {(b, kh, i): (mass [nb], S_mass ascending)}.
+    Parity unpinned beyond its invariants (see the package docstring).
+    """
+    B, Hq, L, D = Q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    nb = -(-L // block)
+    sc = _default_scale(D, scale)
+    qblocks = range(nb) if qblocks is None else qblocks
+    out = {}
+    for b in range(B):
+        for kh in range(Hkv):
+            for i in qblocks:
+                lo, hi = i * block, min((i + 1) * block, L)
+                mass = np.zeros(nb)
+                nrows = 0
+                for h in range(kh * g, (kh + 1) * g):
+                    S = (Q[b, h, lo:hi] @ K[b, kh, :hi].T) * sc      # [rows, hi]
+                    t = np.arange(lo, hi)[:, None]
+                    u = np.arange(hi)[None, :]
+                    S = np.where(u <= t, S, NEG_INF)
+                    P = np.exp(S - S.max(axis=1, keepdims=True))
+                    P /= P.sum(axis=1, keepdims=True)
+                    for j in range(i + 1):
+                        mass[j] += P[:, j * block:min((j + 1) * block, hi)].sum()
+                    nrows += hi - lo
+                mass /= nrows
+                if i >= 2:
+                    cand = np.arange(1, i)
+                    top = cand[np.lexsort((cand, -mass[1:i]))][:min(k_free, i - 1)]
+                    sel = np.sort(top)
+                else:
+                    sel = np.zeros(0, dtype=np.int64)
+                out[(b, kh, i)] = (mass, sel)
+    return out
+
+
+# ------------------------------------------------------------------ whole step
+def decode_step(q, K, V, block: int, k: int, scale: Optional[float] = None,
+                sk: Optional[np.ndarray] = None):
+    """Sketch -> scores -> top-k -> attention, all float64.  Returns a dict."""
+    if sk is None:
+        sk = sketch(K, block)
+    sc = block_scores(q, sk, scale)
+    idx = select_topk_all(sc, k)
+    O, lse = attend_blocks(q, K, V, idx, block, scale)
+    return {"sketch": sk, "scores": sc, "idx": idx, "O": O, "lse": lse}

@@ -1,0 +1,379 @@
+"""Pins for the float64 CPU oracle (runs without a GPU).
+
+Each test ties an oracle function to something other than itself: a
+hand-derived worked example (tests/golden), a closed form, a library routine
+that computes the same mathematical object differently, or brute-force
+enumeration on tiny inputs.  The cases are chosen so that a dropped term, a
+wrong sign or index, or a transposed operand in the oracle fails one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+from scipy.special import logsumexp, softmax
+
+import oracle
+from oracle import attention as A
+from tests.conftest import read_golden
+from workloads import (bf16_bits_to_f32, f32_to_bf16_bits, get_workload,
+                       make_inputs)
+
+
+def rnd(*shape, seed=0):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ------------------------------------------------------------------ O0 / O4
+def test_golden_two_key_softmax():
+    g = dict((k, v) for k, v in read_golden("softmax_two_keys.txt") if k not in ("k", "v"))
+    rows = read_golden("softmax_two_keys.txt")
+    K = np.array([[float(x) for x in v] for k, v in rows if k == "k"])
+    V = np.array([[float(x) for x in v] for k, v in rows if k == "v"])
+    q = np.array([float(x) for x in g["q"]])
+    scale = float(g["scale"][0])
+    O, lse = oracle.dense(q[None, None], K[None, None], V[None, None], scale)
+    np.testing.assert_allclose(O[0, 0], [float(x) for x in g["o"]], rtol=0, atol=1e-14)
+    assert abs(lse[0, 0] - float(g["lse"][0])) < 1e-14
+    # the same support through the block path (one 2-token block)
+    O2, lse2 = oracle.attend_blocks(q[None, None], K[None, None], V[None, None],
+                                    np.array([[[0]]]), block=2, scale=scale)
+    np.testing.assert_allclose(O2, O, atol=1e-15)
+
+
+def test_dense_matches_scipy_softmax():
+    B, Hq, Hkv, N, D = 2, 4, 2, 37, 8
+    q, K, V = rnd(B, Hq, D, seed=1), rnd(B, Hkv, N, D, seed=2), rnd(B, Hkv, N, D, seed=3)
+    O, lse = oracle.dense(q, K, V)
+    for b in range(B):
+        for h in range(Hq):
+            s = K[b, h // 2] @ q[b, h] / math.sqrt(D)
+            np.testing.assert_allclose(O[b, h], softmax(s) @ V[b, h // 2], rtol=1e-12, atol=1e-13)
+            assert abs(lse[b, h] - logsumexp(s)) < 1e-12
+
+
+def test_dense_closed_forms():
+    B, Hq, Hkv, N, D = 1, 2, 1, 9, 4
+    q, K = rnd(B, Hq, D, seed=4), rnd(B, Hkv, N, D, seed=5)
+    c = np.array([1.5, -2.0, 0.25, 3.0])
+    Vc = np.broadcast_to(c, (B, Hkv, N, D)).copy()
+    O, _ = oracle.dense(q, K, Vc)
+    np.testing.assert_allclose(O[0, 0], c, atol=1e-14)           # constant V -> V
+    Ksame = np.broadcast_to(K[:, :, :1], K.shape).copy()
+    V = rnd(B, Hkv, N, D, seed=6)
+    O, lse = oracle.dense(q, Ksame, V)
+    np.testing.assert_allclose(O[0, 1], V[0, 0].mean(axis=0), atol=1e-14)   # equal keys -> mean
+    s0 = K[0, 0, 0] @ q[0, 1] / 2.0
+    assert abs(lse[0, 1] - (s0 + math.log(N))) < 1e-13
+    O1, lse1 = oracle.dense(q, K[:, :, :1], V[:, :, :1])
+    np.testing.assert_allclose(O1[0, 0], V[0, 0, 0], atol=0)      # one token -> its value
+    assert abs(lse1[0, 0] - K[0, 0, 0] @ q[0, 0] / 2.0) < 1e-15
+
+
+def test_attend_all_blocks_is_dense_and_split_merge_is_exact():
+    B, Hq, Hkv, N, D, blk = 2, 8, 2, 200, 16, 32      # last block partial (8 tokens)
+    q, K, V = rnd(B, Hq, D, seed=7), rnd(B, Hkv, N, D, seed=8), rnd(B, Hkv, N, D, seed=9)
+    nb = -(-N // blk)
+    idx = np.broadcast_to(np.arange(nb), (B, Hkv, nb)).copy()
+    O, lse = oracle.attend_blocks(q, K, V, idx, blk)
+    Od, lsed = oracle.dense(q, K, V)
+    np.testing.assert_allclose(O, Od, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, rtol=0, atol=1e-13)
+    # any partition of the support merges back to the unsplit result
+    parts = [[0, 3], [1], [2, 4, 5, 6]]
+    for b in range(B):
+        for h in range(Hq):
+            pp = []
+            for blocks in parts:
+                o, l = oracle.attend_blocks(q[b:b + 1, h:h + 1], K[b:b + 1, h // 4:h // 4 + 1],
+                                            V[b:b + 1, h // 4:h // 4 + 1],
+                                            np.array([[blocks]]), blk)
+                pp.append((o[0, 0], l[0, 0]))
+            om, lm = oracle.lse_merge(pp + [(np.zeros(D), -math.inf)])
+            np.testing.assert_allclose(om, Od[b, h], atol=1e-12)
+            assert abs(lm - lsed[b, h]) < 1e-12
+
+
+def test_attend_restricts_to_selected_tokens():
+    """Dropping a block must equal dense attention on the remaining keys."""
+    B, Hq, Hkv, N, D, blk = 1, 4, 1, 96, 8, 32
+    q, K, V = rnd(B, Hq, D, seed=10), rnd(B, Hkv, N, D, seed=11), rnd(B, Hkv, N, D, seed=12)
+    O, lse = oracle.attend_blocks(q, K, V, np.array([[[0, 2]]]), blk)
+    keep = np.r_[0:32, 64:96]
+    Od, lsed = oracle.dense(q, K[:, :, keep], V[:, :, keep])
+    np.testing.assert_allclose(O, Od, atol=1e-14)
+    np.testing.assert_allclose(lse, lsed, atol=1e-14)
+
+
+# ------------------------------------------------------------------ O1 / O2
+def test_sketch_closed_forms():
+    B, H, D, blk = 1, 2, 3, 4
+    N = 10                                   # blocks of 4, 4, 2 tokens
+    X = np.zeros((B, H, N, D))
+    for t in range(N):
+        X[0, 0, t] = [t, 2 * t, -t]          # arithmetic progression
+        X[0, 1, t] = [7.0, -1.0, 0.5]        # constant
+    s = oracle.sketch(X, blk)
+    assert s.shape == (1, 2, 3, 3)
+    np.testing.assert_allclose(s[0, 0, :, 0], [1.5, 5.5, 8.5])    # midpoints; last block 8,9
+    np.testing.assert_allclose(s[0, 0, :, 1], [3.0, 11.0, 17.0])
+    np.testing.assert_allclose(s[0, 1], np.tile([7.0, -1.0, 0.5], (3, 1)))
+    # head pooling: mean over both heads and the block's tokens
+    sp = oracle.sketch(X, blk, head_pool=2)
+    np.testing.assert_allclose(sp[0, 0, 2], ((X[0, 0, 8:10] + X[0, 1, 8:10]) / 2).mean(axis=0))
+    # full blocks equal numpy's mean of the reshaped array
+    Y = rnd(2, 3, 64, 5, seed=13)
+    np.testing.assert_allclose(oracle.sketch(Y, 16), Y.reshape(2, 3, 4, 16, 5).mean(axis=3), atol=1e-15)
+
+
+def test_block_scores_head_average_and_needle_boost():
+    wl = get_workload("tiny_decode_f32")
+    planted = make_inputs(wl)
+    clean = make_inputs(wl.scaled(needle_gain=0.0))      # same draws, no needles
+    q = A.widen(planted.Q, "f32")
+    s_p = oracle.block_scores(q, oracle.sketch(A.widen(planted.K, "f32"), wl.block))
+    s_c = oracle.block_scores(q, oracle.sketch(A.widen(clean.K, "f32"), wl.block))
+    qbar = q[0].mean(axis=0)
+    boost = 3.0 * np.linalg.norm(qbar) / math.sqrt(wl.D)
+    diff = s_p[0, 0] - s_c[0, 0]
+    needles = set(planted.needles[0, 0].tolist())
+    for j in range(wl.nb):
+        # keys are stored in fp32 after planting: allow that rounding only
+        expect = boost if j in needles else 0.0
+        assert abs(diff[j] - expect) < 2e-6, (j, diff[j], expect)
+    # head average equals the mean query's score, and g = 1 is a plain dot
+    sk = rnd(1, 1, 10, wl.D, seed=14)
+    np.testing.assert_allclose(oracle.block_scores(q, sk)[0, 0], sk[0, 0] @ qbar / 8.0, atol=1e-14)
+    np.testing.assert_allclose(oracle.block_scores(q[:, :1], sk)[0, 0], sk[0, 0] @ q[0, 0] / 8.0,
+                               atol=1e-14)
+
+
+# ------------------------------------------------------------------ O3
+def test_golden_topk_pipeline_with_tie():
+    g = {}
+    sel = {}
+    for k, v in read_golden("topk_tie_pipeline.txt"):
+        if k == "select":
+            sel[int(v[0])] = [int(x) for x in v[1:]]
+        else:
+            g[k] = v
+    keys = np.array([float(x) for x in g["keys"]]).reshape(1, 1, -1, 1)
+    blk = int(g["block"][0])
+    sk = oracle.sketch(keys, blk)
+    sc = oracle.block_scores(np.ones((1, 1, 1)), sk, scale=1.0)
+    np.testing.assert_allclose(sc[0, 0], [float(x) for x in g["scores"]], atol=1e-15)
+    assert sc[0, 0, 1] == sc[0, 0, 3]
+    for k, want in sel.items():
+        assert oracle.select_topk(sc[0, 0], k).tolist() == want
+
+
+def _brute_topk(s, k, forced):
+    """Maximum total score over all subsets of the free blocks, ties to the
+    lexicographically smallest ascending list."""
+    nb = len(s)
+    F = sorted(set(forced))
+    C = [j for j in range(nb) if j not in F]
+    # NaN ranks below every real score (finite stand-in keeps sums comparable)
+    finite = [x for x in s if not math.isnan(x)]
+    low = (min(finite) if finite else 0.0) - 1000.0
+    val = [low if math.isnan(x) else x for x in s]
+    best, best_sum = None, -math.inf
+    for sub in itertools.combinations(C, k - len(F)):
+        tot = sum(val[j] for j in sub)
+        cand = sorted(F + list(sub))
+        if tot > best_sum or (tot == best_sum and cand < best):
+            best, best_sum = cand, tot
+    return best
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topk_equals_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb = int(rng.integers(3, 12))
+    # small integers force many exact ties; a few NaNs test the NaN reading
+    s = rng.integers(-3, 4, size=nb).astype(float)
+    if seed % 3 == 0:
+        s[rng.integers(0, nb)] = np.nan
+    if seed % 4 == 0:
+        s[rng.integers(0, nb)] = -0.0
+    for k in range(2, nb + 1):
+        got = oracle.select_topk(s, k).tolist()
+        want = list(range(nb)) if k >= nb else _brute_topk(s, k, [0, nb - 1])
+        assert got == want, (s, k, got, want)
+
+
+def test_topk_edge_cases():
+    assert oracle.select_topk(np.array([5.0]), 1).tolist() == [0]          # nb = 1
+    assert oracle.select_topk(np.array([1.0, 9.0, 9.0, 0.0]), 2).tolist() == [0, 3]
+    assert oracle.select_topk(np.array([1.0, 2.0, 3.0]), 99).tolist() == [0, 1, 2]
+    with pytest.raises(ValueError):
+        oracle.select_topk(np.zeros(8), 1)
+    # +0 and -0 are the same score: the lower index wins
+    assert oracle.select_topk(np.array([0.0, 0.0, -0.0, 0.0, 1.0]), 3).tolist() == [0, 1, 4]
+
+
+# ------------------------------------------------------------------ O5
+def test_threshold_count_and_zero_false_negatives():
+    wl = get_workload("threshold_decode_bf16", B=1)
+    inp = make_inputs(wl)
+    q, K, V = (A.widen(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    q = q[:, :8]                                   # two kv heads' worth of queries
+    K, V = K[:, :2], V[:, :2]
+    tau64, tau32 = oracle.threshold_tau(q, K, 99.0)
+    assert np.all(tau32.astype(np.float64) <= tau64)
+    assert np.all(np.nextafter(tau32, np.float32(np.inf)).astype(np.float64) > tau64)
+    lists, vals = oracle.select_threshold(q, K, tau64)
+    s = A.exact_scores(q, K)
+    for h in range(8):
+        # the linear-interpolated 99th percentile sits strictly between the
+        # order statistics i0 = floor(0.99 (N - 1)) and i0 + 1 whenever those
+        # two differ, so exactly N - i0 - 1 = 328 scores reach it
+        srt = np.sort(s[0, h])
+        i0 = int(math.floor(0.99 * (wl.N - 1)))
+        assert srt[i0] < srt[i0 + 1]
+        assert srt[i0] < tau64[0, h] < srt[i0 + 1]
+        assert len(lists[0][h]) == wl.N - i0 - 1 == 328
+        # zero false negatives against a plain loop over every token
+        brute = [t for t in range(wl.N) if s[0, h, t] >= tau64[0, h]]
+        assert lists[0][h].tolist() == brute
+        np.testing.assert_array_equal(vals[0][h], s[0, h, brute])
+    # tau = -inf keeps everything and reproduces dense attention
+    allk, _ = oracle.select_threshold(q[:, :4, :], K[:, :1], np.full((1, 4), -np.inf))
+    O, lse = oracle.attend_tokens(q[:, :4], K[:, :1], V[:, :1], allk)
+    Od, lsed = oracle.dense(q[:, :4], K[:, :1], V[:, :1])
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+def test_threshold_brute_force_tiny():
+    q, K = rnd(1, 2, 4, seed=20), rnd(1, 1, 50, 4, seed=21)
+    tau = np.array([[0.3, -0.1]])
+    lists, _ = oracle.select_threshold(q, K, tau)
+    for h in range(2):
+        want = [t for t in range(50)
+                if sum(q[0, h, c] * K[0, 0, t, c] for c in range(4)) / 2.0 >= tau[0, h]]
+        assert lists[0][h].tolist() == want
+    # a key exactly on the boundary <q, k> * scale == tau is inside the half-space
+    q1 = np.array([[[1.0, 0.0, 0.0, 0.0]]])
+    K1 = np.zeros((1, 1, 3, 4))
+    K1[0, 0, :, 0] = [0.25, 0.5, 0.75]           # scores 0.125, 0.25, 0.375 exactly
+    lists, vals = oracle.select_threshold(q1, K1, np.array([[0.25]]))
+    assert lists[0][0].tolist() == [1, 2] and vals[0][0].tolist() == [0.25, 0.375]
+
+
+# ------------------------------------------------------------------ O6 / O7
+def test_prefill_select_sizes_and_brute_force():
+    rng = np.random.default_rng(30)
+    M, D = 512, 16
+    Qb, Kb = rng.standard_normal((1, 1, M, D)), rng.standard_normal((1, 1, M, D))
+    idx, cnt = oracle.prefill_select(Qb, Kb, 10)
+    assert cnt[0, 0].tolist() == [min(i + 1, 10) for i in range(M)]
+    assert int(cnt.sum()) == 5075
+    for i in (0, 1, 2, 5, 9, 10, 11, 100, 511):
+        S = idx[0, 0, i, :cnt[0, 0, i]].tolist()
+        assert S == sorted(S) and S[0] == 0 and S[-1] == i and len(set(S)) == len(S)
+        if i >= 2:
+            r = (Kb[0, 0, :i] @ Qb[0, 0, i]) / 4.0
+            if i <= 12:   # the free part by subset enumeration
+                want = _brute_topk(np.r_[r[:i], 0.0], min(10, i + 1), [0, i])
+            else:         # ... or by Python's stable sort on (-r, j)
+                free = sorted(range(1, i), key=lambda j: (-r[j], j))[:8]
+                want = sorted([0, i] + free)
+            assert S == want
+
+
+def test_prefill_attend_widened_is_dense_causal():
+    B, Hq, Hkv, L, D, blk = 1, 4, 2, 96, 8, 16
+    Q, K, V = rnd(B, Hq, L, D, seed=31), rnd(B, Hkv, L, D, seed=32), rnd(B, Hkv, L, D, seed=33)
+    M = L // blk
+    Qb, Kb = oracle.prefill_pool_queries(Q, blk, 2), oracle.sketch(K, blk)
+    idx, cnt = oracle.prefill_select(Qb, Kb, M + 1)      # every earlier block
+    O, lse = oracle.prefill_attend(Q, K, V, idx, cnt, blk)
+    rows = [(0, h, t) for h in range(Hq) for t in range(L)]
+    Od, lsed = oracle.dense_causal_rows(Q, K, V, rows)
+    np.testing.assert_allclose(O.reshape(-1, D), Od, atol=1e-13)
+    np.testing.assert_allclose(lse.reshape(-1), lsed, atol=1e-13)
+    np.testing.assert_array_equal(O[0, :, 0], V[0, [0, 0, 1, 1], 0])   # row 0 -> v_0
+    # with k = 3 the rows of block 3 see blocks {0, best of 1..2, 3} only
+    idx3, cnt3 = oracle.prefill_select(Qb, Kb, 3)
+    S = idx3[0, 0, 3, :3]
+    toks = np.concatenate([np.arange(j * blk, (j + 1) * blk) for j in S])
+    t = 3 * blk + 5
+    o, l = oracle.prefill_attend_rows(Q, K, V, idx3, cnt3, blk, [(0, 1, t)])
+    keep = toks[toks <= t]
+    Od2, lsed2 = oracle.dense(Q[:, 1:2, t], K[:, :1, keep], V[:, :1, keep])
+    np.testing.assert_allclose(o[0], Od2[0, 0], atol=1e-14)
+
+
+def test_prefill_pooling_head_group():
+    Q = rnd(1, 4, 8, 3, seed=34)
+    Qb = oracle.prefill_pool_queries(Q, 4, 2)
+    np.testing.assert_allclose(Qb[0, 1, 1], Q[0, 2:4, 4:8].mean(axis=(0, 1)), atol=1e-15)
+
+
+# ------------------------------------------------------------------ O8
+def test_mass_oracle_invariants_and_identical_keys():
+    B, Hq, Hkv, L, D, blk = 1, 2, 1, 64, 4, 8
+    Q, K = rnd(B, Hq, L, D, seed=40), rnd(B, Hkv, L, D, seed=41)
+    res = oracle.mass_oracle(Q, K, blk, k_free=3)
+    for (b, kh, i), (mass, sel) in res.items():
+        assert abs(mass[:i + 1].sum() - 1.0) < 1e-12 and np.all(mass[i + 1:] == 0)
+        assert len(sel) == min(3, max(i - 1, 0))
+    # identical keys: uniform causal attention, block j gets |j-block ∩ [0, t]| / (t+1)
+    Ks = np.broadcast_to(K[:, :, :1], K.shape).copy()
+    res = oracle.mass_oracle(Q, Ks, blk, k_free=3)
+    for i in range(L // blk):
+        rows = np.arange(i * blk, (i + 1) * blk)
+        want = [np.mean([max(0, min(t + 1, (j + 1) * blk) - j * blk) / (t + 1) for t in rows])
+                for j in range(i + 1)]
+        mass, sel = res[(0, 0, i)]
+        np.testing.assert_allclose(mass[:i + 1], want, atol=1e-13)
+        # earlier full blocks tie exactly in mass -> lowest indices win
+        assert sel.tolist() == list(range(1, 1 + min(3, max(i - 1, 0))))
+
+
+# ------------------------------------------------------------------ needles
+@pytest.mark.parametrize("name,over", [
+    ("tiny_decode_f32", {}),
+    ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2}),
+    ("long_decode_bf16", {"Hq": 16, "Hkv": 2, "N": 65536}),
+])
+def test_needle_recovery_decode(name, over):
+    wl = get_workload(name, **over)
+    inp = make_inputs(wl)
+    q, K = A.widen(inp.Q, wl.dtype), A.widen(inp.K, wl.dtype)
+    sc = oracle.block_scores(q, oracle.sketch(K, wl.block))
+    idx = oracle.select_topk_all(sc, wl.k)
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            assert set(inp.needles[b, kh].tolist()) <= set(idx[b, kh].tolist())
+            assert idx[b, kh, 0] == 0 and idx[b, kh, -1] == wl.nb - 1
+
+
+def test_needle_recovery_prefill():
+    wl = get_workload("sparse_prefill_bf16", Hq=8, Hkv=1, N=8192, needles=16)
+    inp = make_inputs(wl)
+    Q, K = A.widen(inp.Q, "bf16"), A.widen(inp.K, "bf16")
+    idx, cnt = oracle.prefill_select(oracle.prefill_pool_queries(Q, wl.block, wl.g),
+                                     oracle.sketch(K, wl.block), wl.k)
+    for j, i in zip(inp.needles[0, 0], inp.partners[0, 0]):
+        assert j in idx[0, 0, i, :cnt[0, 0, i]]
+
+
+# ------------------------------------------------------------------ inputs
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    x = np.random.default_rng(50).standard_normal(100000).astype(np.float32) * 10
+    x[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 0.0]    # exact ties
+    ours = f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+    np.testing.assert_array_equal(bf16_bits_to_f32(ours), A.widen(ours, "bf16").astype(np.float32))
+
+
+def test_inputs_are_seeded():
+    a = make_inputs("tiny_decode_f32")
+    b = make_inputs("tiny_decode_f32")
+    np.testing.assert_array_equal(a.K, b.K)
+    c = make_inputs("tiny_decode_f32", seed=7)
+    assert not np.array_equal(a.K, c.K)
