@@ -1,0 +1,260 @@
+/*
+ * sa.h -- C ABI of the MI355X (gfx950) top-k block-sparse attention library.
+ *
+ * The library computes query-aware sparse attention over a GQA KV cache:
+ *   1. compress the keys into per-block mean sketches        (sa_build_sketch)
+ *   2. score blocks against the query heads of each KV group
+ *      and keep the top-k, always including sink and local     (sa_select_topk)
+ *      -- or keep every key above a score threshold            (sa_select_threshold)
+ *   3. exact softmax attention over the kept keys only         (sa_sparse_decode,
+ *                                                               sa_sparse_prefill)
+ *
+ * Pages the operations follow (title, section):
+ *   [ORACLE]  "How Much Dense Attention is Necessary? Oracle-Guided Sparse
+ *             Prefill for Full/GQA Layers in Hybrid Long-Context Models",
+ *             technical summary §2.1: choose a top-k support from head-averaged
+ *             importance, then recompute attention on that support with the
+ *             original Q, K, V; supports may be shared by a block of queries.
+ *   [FRONTIER] "The Sparse Frontier: Sparse Attention Trade-offs in Transformer
+ *             LLMs", Metodologia §1 and Contributi §2: block/page units, full
+ *             cache retained and loaded selectively (Quest decode), block-by-block
+ *             selection in prefill (Block-Sparse).
+ *   [FFD]     "Faster Than Flash: Exploiting Attention Sparsity for Efficient
+ *             Long-Context Decoding", Metodologia §1-§3: scan a compact key
+ *             summary first, fetch exact data only for the chosen parts; sink and
+ *             local tokens dominate attention.
+ *   [PULSAR]  "Pulsar Attention", Fase 1 (64-token attention-sink prefix) and
+ *             Fase 2 (online-softmax merge of partial attention is exact).
+ *   [RANGE]   "Sparse Attention as a Range Searching Problem: Towards an
+ *             Inference-Efficient Index for KV Cache", Metodologia §1: return
+ *             every key in the half-space <q, k> >= tau (no false negatives).
+ *
+ * Conventions shared by every entry point
+ *   - Layouts are row-major with D innermost:
+ *       K, V  [B, Hkv, N, D]      Q  [B, Hq, D] (decode) or [B, Hq, L, D] (prefill)
+ *     Query head h reads kv head h / g, g = Hq / Hkv (Hq % Hkv == 0).
+ *   - Every pointer is DEVICE memory owned by the caller.  Inputs are const.
+ *     The library allocates nothing and keeps no state between calls apart
+ *     from a cached device-property query.
+ *   - `ws` is a caller-provided device workspace of at least
+ *     sa_workspace_bytes(...) bytes.  It must be zero-filled once when it is
+ *     allocated; every call leaves its counters at zero again.  Two calls that
+ *     run concurrently must not share a workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; nothing synchronises the host.
+ *   - dtype codes: SA_F32 (float) or SA_BF16 (raw bfloat16 bits, uint16).
+ *   - scale <= 0 means 1/sqrt(D).
+ *   - Pointers must be 16-byte aligned.  D must be 64 or 128.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     return SA_ERR_INVALID; shapes/dtypes with no compiled kernel return
+ *     SA_ERR_UNSUPPORTED; a too-small workspace returns SA_ERR_WORKSPACE; a
+ *     failed launch returns SA_ERR_HIP.  sa_last_error() describes the last
+ *     failure of the calling thread.
+ *   - Same inputs, same device, same build -> bitwise identical outputs (no
+ *     floating-point atomics; every reduction has a fixed order).
+ *   - Index lists are ascending; unused slots are written as -1.
+ */
+#ifndef SA_H
+#define SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID = 1,
+  SA_ERR_UNSUPPORTED = 2,
+  SA_ERR_WORKSPACE = 3,
+  SA_ERR_HIP = 4
+} sa_status;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* selection flags */
+enum {
+  SA_FORCE_SINK = 1u,  /* always keep block 0 (the attention-sink prefix, [PULSAR] Fase 1) */
+  SA_FORCE_LOCAL = 2u, /* always keep the newest block (decode) / the diagonal block (prefill) */
+  SA_CAUSAL = 4u       /* prefill: query block i ranks key blocks 1..i-1 only */
+};
+
+/* sparse_decode modes */
+enum { SA_IDX_BLOCKS = 0, SA_IDX_TOKENS = 1 };
+
+/* operations for sa_workspace_bytes */
+enum {
+  SA_OP_SELECT_TOPK = 0,
+  SA_OP_SELECT_THRESHOLD = 1,
+  SA_OP_SPARSE_DECODE = 2,
+  SA_OP_DECODE_STEP = 3
+};
+
+/*
+ * sa_build_sketch -- per-block mean sketch ([FFD] Metodologia §1: the compact
+ * key summary scanned before any full key is fetched; a per-block centre as in
+ * [RANGE] Metodologia §2).
+ *
+ *   X        [B, H, N, D] dtype           input rows (keys, or queries to pool)
+ *   block    tokens per block; nb = ceil(N / block); the last block may be
+ *            partial and is averaged over its valid rows only
+ *   head_pool  1 for keys; g to also average each group of g consecutive heads
+ *            (the pooled query block of block-sparse prefill); H % head_pool == 0
+ *   blk_begin, blk_end  block range to (re)write, 0 <= begin <= end <= nb; a
+ *            decode step rewrites only the newest block
+ *   sketch   [B, H / head_pool, nb, D] float32, output (only the range is written)
+ *
+ * Entry s[b, hh, j, :] = mean over heads hh*head_pool .. +head_pool-1 and
+ * tokens of block j of X[b, h, t, :], accumulated in float32.
+ */
+sa_status sa_build_sketch(const void* X, int dtype, int B, int H, int N, int D,
+                          int block, int head_pool, int blk_begin, int blk_end,
+                          float* sketch, void* stream);
+
+/*
+ * sa_select_topk -- block scores and top-k block selection ([ORACLE] §2.1,
+ * [FRONTIER] Contributi §2, [FFD] Metodologia §2).
+ *
+ * Decode (Lq == 1, q_block == 1, no SA_CAUSAL):
+ *   Q        [B, Hq, D] dtype
+ *   ksketch  [B, Hkv, nb, D] float32 (sa_build_sketch of K)
+ *   score[b, kh, j] = (mean over the g query heads of kv head kh of q_h) . s_j * scale
+ *   Forced blocks (SA_FORCE_SINK: block 0; SA_FORCE_LOCAL: block nb-1) are kept
+ *   and count toward k; the other slots go to the best remaining scores, ties
+ *   to the lower block index; NaN scores rank below every number.  k >= nb
+ *   keeps all blocks.
+ *   idx      [B, Hkv, k] int32 out (ascending; slots past count are -1)
+ *   count    [B, Hkv]    int32 out (= min(k, nb))
+ *
+ * Causal prefill (SA_CAUSAL, q_block == the key block size, Lq == N):
+ *   Q        [B, Hq, Lq, D] dtype; pooled per query block i over its q_block
+ *            tokens and the group's g heads into Qbar_i (float32)
+ *   ksketch  [B, Hkv, nb, D] float32 with nb >= M = ceil(Lq / q_block)
+ *   r_ij = Qbar_i . s_j * scale for j in 1..i-1; query block i keeps block 0
+ *   (SA_FORCE_SINK), block i (SA_FORCE_LOCAL) and the top k - 2 of 1..i-1.
+ *   One list per (b, kv head, query block), shared by its queries and heads
+ *   ([ORACLE] §2.1 block-shared support).
+ *   idx      [B, Hkv, M, k] int32 out;  count [B, Hkv, M] int32 out (min(i + 1, k))
+ *
+ *   score    optional float32 out (NULL to skip): [B, Hkv, nb] (decode) or
+ *            [B, Hkv, M, nb] (prefill; entries outside 1..i-1 are -inf)
+ *   ws       workspace of sa_workspace_bytes(SA_OP_SELECT_TOPK, B, Hq, Hkv, Lq, D, q_block, nb)
+ *
+ * Errors: SA_ERR_INVALID if k < number of forced blocks, k <= 0 or nb <= 0;
+ * SA_ERR_UNSUPPORTED if nb > 8192 (decode) or M > 8192 (prefill).
+ */
+sa_status sa_select_topk(const void* Q, int dtype, int B, int Hq, int Hkv,
+                         int Lq, int D, int q_block, const float* ksketch,
+                         int nb, int k, unsigned flags, float scale,
+                         int32_t* idx, int32_t* count, float* score, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * sa_select_threshold -- every key in the half-space ([RANGE] Metodologia §1):
+ * keep token t for query head (b, h) when q_h . k_t * scale >= tau[b, h].
+ *
+ *   Q [B, Hq, D], K [B, Hkv, N, D] dtype;  tau [B, Hq] float32 (-inf keeps all)
+ *   cap      capacity of each list
+ *   idx      [B, Hq, cap] int32 out, ascending token positions (unused: -1)
+ *   score    [B, Hq, cap] float32 out, the scaled scores of those tokens
+ *   count    [B, Hq] int32 out, the TRUE number of kept tokens; when it exceeds
+ *            cap only the first cap (lowest positions) are written -- the
+ *            caller checks count > cap (reported in band, so the call stays
+ *            asynchronous).
+ *
+ * No false negatives: scores are computed in float32 and a token is kept when
+ * its float32 score plus a rigorous bound on the float32 rounding error of
+ * that score reaches tau, so every key whose exact score reaches tau is kept;
+ * the only extra keys are those within that bound below tau.
+ * ws: sa_workspace_bytes(SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0, cap).
+ */
+sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B,
+                              int Hq, int Hkv, int N, int D, const float* tau,
+                              float scale, int cap, int32_t* idx, float* score,
+                              int32_t* count, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * sa_sparse_decode -- exact attention restricted to the selected keys, as
+ * split-K flash decoding with a log-sum-exp merge of the partials ([ORACLE]
+ * §2.1 recompute on the support; [PULSAR] Fase 2 online-softmax merge).
+ *
+ *   Q [B, Hq, D], K, V [B, Hkv, N, D] dtype
+ *   mode SA_IDX_BLOCKS:  idx [B, Hkv, idx_stride] ascending block ids of size
+ *            `block` (the last block of the cache may be partial), count
+ *            [B, Hkv] valid entries (NULL: all idx_stride); the g heads of a
+ *            group share the list.
+ *   mode SA_IDX_TOKENS:  idx [B, Hq, idx_stride] token positions, count [B, Hq]
+ *            (required; values above idx_stride are clamped to it), score
+ *            [B, Hq, idx_stride] the scaled scores of those tokens as written
+ *            by sa_select_threshold (NULL: recomputed from Q and K).
+ *   O        [B, Hq, D] out_dtype;  lse [B, Hq] float32 (NULL to skip)
+ *            O = sum_t softmax(s)_t v_t over the kept tokens, lse = log sum exp s;
+ *            an empty selection gives O = 0, lse = -inf.
+ * Accumulation is float32 throughout.
+ * ws: sa_workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, block, idx_stride)
+ *     (for SA_IDX_TOKENS pass block = 0).
+ */
+sa_status sa_sparse_decode(const void* Q, const void* K, const void* V,
+                           int dtype, int B, int Hq, int Hkv, int N, int D,
+                           float scale, int mode, int block,
+                           const int32_t* idx, const int32_t* count,
+                           int idx_stride, const float* score, void* O,
+                           int out_dtype, float* lse, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * sa_sparse_prefill -- block-sparse causal attention ([FRONTIER] Contributi §2
+ * Block-Sparse prefill; [ORACLE] §2.1 block-shared support).
+ *
+ *   Q [B, Hq, L, D], K, V [B, Hkv, L, D] dtype (SA_BF16 only; bf16 matrix cores;
+ *            D = 128)
+ *   block    query and key block size (128)
+ *   idx      [B, Hkv, M, kmax] int32 ascending key blocks per query block
+ *            (M = ceil(L / block)), count [B, Hkv, M]; entries must be <= i
+ *   Row t of query block i attends to every token of its listed blocks at
+ *   position <= t.
+ *   O        [B, Hq, L, D] out_dtype;  lse [B, Hq, L] float32 (NULL to skip)
+ */
+sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V,
+                            int dtype, int B, int Hq, int Hkv, int L, int D,
+                            float scale, int block, const int32_t* idx,
+                            const int32_t* count, int kmax, void* O,
+                            int out_dtype, float* lse, void* stream);
+
+/*
+ * sa_decode_step -- one whole decode step for one layer, fused where the
+ * hardware allows: rewrite the sketch of block `update_block` (pass -1 to
+ * skip), score and select the top-k blocks (forced sink + local), then the
+ * split-K sparse attention and merge.  Same result as calling
+ * sa_build_sketch, sa_select_topk (decode) and sa_sparse_decode (blocks) in
+ * sequence; idx/count/score (score may be NULL) receive the selection.
+ * ws: sa_workspace_bytes(SA_OP_DECODE_STEP, B, Hq, Hkv, N, D, block, k).
+ */
+sa_status sa_decode_step(const void* Q, const void* K, const void* V,
+                         int dtype, int B, int Hq, int Hkv, int N, int D,
+                         int block, float* ksketch, int update_block, int k,
+                         float scale, int32_t* idx, int32_t* count,
+                         float* score, void* O, int out_dtype, float* lse,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes needed by an operation (0 if none; SIZE_MAX on bad input). */
+size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D,
+                          int block, int k);
+
+/* Static description of a status code. */
+const char* sa_status_str(int status);
+
+/* Description of the calling thread's last failure ("" if none). */
+const char* sa_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H */

@@ -1,0 +1,181 @@
+"""C-ABI tests that need no GPU.
+
+The library must load, export every function include/sa.h declares, and reject
+bad arguments on the host with the documented status codes before any HIP call
+(so these calls are safe without a GPU).  Every call below violates at least
+one documented precondition, so none of them reaches a kernel launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+LIB = os.path.join(ROOT, "top_sparse_attention_mean_amd", "libsa.so")
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+SINK, LOCAL, CAUSAL = 1, 2, 4
+A = 0x10000          # an aligned stand-in address; never dereferenced here
+MIS = 0x10004        # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libsa.so not built (run __graft_entry__.build())")
+    L = ctypes.CDLL(LIB)
+    P, I, F, Z, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint
+    L.sa_build_sketch.argtypes = [P, I, I, I, I, I, I, I, I, I, P, P]
+    L.sa_select_topk.argtypes = [P, I, I, I, I, I, I, I, P, I, I, U, F, P, P, P, P, Z, P]
+    L.sa_select_threshold.argtypes = [P, P, I, I, I, I, I, I, P, F, I, P, P, P, P, Z, P]
+    L.sa_sparse_decode.argtypes = [P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P, P, I, P, P, Z, P]
+    L.sa_sparse_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, I, P, I, P, P]
+    L.sa_decode_step.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P, P, Z, P]
+    L.sa_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    L.sa_workspace_bytes.restype = Z
+    L.sa_status_str.restype = ctypes.c_char_p
+    L.sa_last_error.restype = ctypes.c_char_p
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sa_status|size_t|const char\*|int)\s+(sa_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
+              "sa_sparse_prefill", "sa_decode_step", "sa_workspace_bytes", "sa_status_str",
+              "sa_last_error", "sa_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
+
+
+def test_binding_names_match_header():
+    pytest.importorskip("torch")
+    if not os.path.exists(LIB):
+        pytest.skip("libsa.so not built")
+    import top_sparse_attention_mean_amd as sa
+    assert sorted(sa.EXPORTS) == declared_functions()
+    for n in declared_functions():
+        if n not in ("sa_workspace_bytes", "sa_status_str", "sa_last_error", "sa_version"):
+            assert callable(getattr(sa, n))
+
+
+def test_status_strings_and_version(lib):
+    assert lib.sa_status_str(0) == b"ok"
+    assert lib.sa_status_str(3) == b"workspace too small"
+    assert lib.sa_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    # decode select: one float score per block of every (b, kv head)
+    assert lib.sa_workspace_bytes(0, 1, 64, 8, 1, 128, 1, 4096) == 8 * 4096 * 4
+    # threshold staging grows with B * Hq * N
+    a = lib.sa_workspace_bytes(1, 8, 32, 8, 32768, 128, 0, 1024)
+    assert a >= 8 * 32 * 32768 * 8
+    # decode partials are at least one float per (b, head, split, column)
+    assert lib.sa_workspace_bytes(2, 1, 64, 8, 262144, 128, 64, 82) >= 64 * 82 * 128 * 4
+    assert lib.sa_workspace_bytes(2, 0, 64, 8, 262144, 128, 64, 82) == ctypes.c_size_t(-1).value
+    assert lib.sa_workspace_bytes(9, 1, 1, 1, 1, 64, 64, 1) == ctypes.c_size_t(-1).value
+
+
+def test_sketch_validation(lib):
+    # null input
+    assert lib.sa_build_sketch(None, 1, 1, 8, 4096, 128, 64, 1, 0, 64, A, None) == INVALID
+    # misaligned output
+    assert lib.sa_build_sketch(A, 1, 1, 8, 4096, 128, 64, 1, 0, 64, MIS, None) == INVALID
+    # unsupported D
+    assert lib.sa_build_sketch(A, 1, 1, 8, 4096, 96, 64, 1, 0, 64, A, None) == UNSUPPORTED
+    # head_pool must divide H
+    assert lib.sa_build_sketch(A, 1, 1, 8, 4096, 128, 64, 3, 0, 64, A, None) == INVALID
+    # block range beyond nb
+    assert lib.sa_build_sketch(A, 1, 1, 8, 4096, 128, 64, 1, 0, 65, A, None) == INVALID
+    assert b"outside" in lib.sa_last_error()
+    # unknown dtype
+    assert lib.sa_build_sketch(A, 7, 1, 8, 4096, 128, 64, 1, 0, 64, A, None) == INVALID
+
+
+def test_select_validation(lib):
+    args = dict(Q=A, dt=1, B=1, Hq=64, Hkv=8, Lq=1, D=128, qb=1, sk=A, nb=4096, k=82,
+                fl=SINK | LOCAL, sc=0.0, idx=A, cnt=A, score=None, ws=A, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.sa_select_topk(a["Q"], a["dt"], a["B"], a["Hq"], a["Hkv"], a["Lq"], a["D"],
+                                  a["qb"], a["sk"], a["nb"], a["k"], a["fl"], a["sc"], a["idx"],
+                                  a["cnt"], a["score"], a["ws"], a["wsb"], None)
+
+    assert call(Hq=60) == INVALID                 # Hq % Hkv != 0
+    assert call(k=1) == INVALID                   # k below the two forced blocks
+    assert call(k=0) == INVALID
+    assert call(nb=9000) == UNSUPPORTED           # too many blocks for one LDS row
+    assert call(wsb=100) == WORKSPACE             # no room for the scores
+    assert call(fl=8) == INVALID                  # unknown flag
+    assert call(Lq=128) == INVALID                # multi-row query needs SA_CAUSAL
+    assert call(idx=None) == INVALID
+    assert call(fl=SINK | LOCAL | CAUSAL, Lq=65536, qb=128, nb=256, ws=A) == INVALID  # nb < M
+    assert call(fl=SINK | LOCAL | CAUSAL, Lq=65536, qb=128, nb=512, wsb=16) == WORKSPACE
+
+
+def test_threshold_validation(lib):
+    f = lib.sa_select_threshold
+    assert f(A, A, 1, 8, 32, 8, 32768, 128, None, 0.0, 1024, A, A, A, A, 1 << 30, None) == INVALID
+    assert f(A, A, 1, 8, 32, 8, 32768, 128, A, 0.0, 0, A, A, A, A, 1 << 30, None) == INVALID
+    assert f(A, A, 1, 8, 48, 8, 32768, 128, A, 0.0, 1024, A, A, A, A, 1 << 30, None) == UNSUPPORTED
+    assert f(A, A, 1, 8, 32, 8, 32768, 128, A, 0.0, 1024, A, A, A, A, 1024, None) == WORKSPACE
+
+
+def test_decode_validation(lib):
+    f = lib.sa_sparse_decode
+    base = [A, A, A, 1, 1, 64, 8, 262144, 128, 0.0, 0, 64, A, A, 82, None, A, 1, A, A, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(0, None) == INVALID               # Q
+    assert call(11, 32) == UNSUPPORTED            # bf16 block mode needs 64/128
+    assert call(10, 5) == INVALID                 # unknown mode
+    assert call(20, 64) == WORKSPACE
+    assert call(5, 48) == UNSUPPORTED             # g = 6
+    a = list(base)
+    a[10], a[13] = 1, None                        # token mode without counts
+    assert f(*a) == INVALID
+
+
+def test_prefill_validation(lib):
+    f = lib.sa_sparse_prefill
+    base = [A, A, A, 1, 1, 32, 4, 65536, 128, 0.0, 128, A, A, 10, A, 1, A, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(3, 0) == UNSUPPORTED              # float32 prefill
+    assert call(10, 64) == UNSUPPORTED            # 64-token blocks
+    assert call(8, 64) == UNSUPPORTED             # D = 64
+    assert call(12, None) == INVALID              # count
+    assert call(13, 0) == INVALID                 # kmax
+
+
+def test_decode_step_validation(lib):
+    f = lib.sa_decode_step
+    base = [A, A, A, 1, 1, 64, 8, 262144, 128, 64, A, 4095, 82, 0.0, A, A, None, A, 1, A, A,
+            1 << 30, None]
+    a = list(base)
+    a[11] = 4096                                  # update_block past the last block
+    assert f(*a) == INVALID
+    a = list(base)
+    a[21] = 128                                   # workspace
+    assert f(*a) == WORKSPACE

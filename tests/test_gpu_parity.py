@@ -1,0 +1,305 @@
+"""GPU parity of every entry point against the float64 oracle.
+
+Sizes here finish on the CPU oracle in seconds and still span several tiles,
+splits and ragged tails; tests/test_gpu_fullsize.py covers the full workloads.
+Tolerances: selections as in tests/parity_util.py (1e-5 relative tie band);
+outputs max-abs 2e-3 for bf16 inputs and 1e-5 for float32 inputs, compared in
+the float32-output mode against the oracle evaluated on the GPU's own index
+lists; the bf16-output mode must equal the round-to-nearest-even bf16 of the
+float32-output mode bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.attention import block_tokens, exact_scores, widen
+from tests.parity_util import (bf16_rne_of_f32, check_topk_row, max_abs, to_dev)
+from workloads import get_workload, make_inputs
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+import top_sparse_attention_mean_amd as sa  # noqa: E402  (fails loudly if not built)
+
+OUT_TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    torch.cuda.set_device(0)
+    yield
+
+
+def _decode_case(name, over, seed=None):
+    wl = get_workload(name, **over)
+    inp = make_inputs(wl, seed=seed)
+    d = wl.dtype
+    return wl, inp, widen(inp.Q, d), widen(inp.K, d), widen(inp.V, d)
+
+
+DECODE_CASES = [
+    ("tiny_decode_f32", {}),
+    ("tiny_decode_f32", {"N": 4096 - 23}),                                   # ragged last block
+    ("tiny_decode_f32", {"k": 64}),                                          # k = nb -> dense
+    ("tiny_decode_f32", {"N": 50, "k": 8}),                                  # nb = 1
+    ("gqa_decode_bf16", {"B": 2}),
+    ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 5000}),             # ragged
+    ("gqa_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 2, "D": 64, "N": 3001}),    # g = 2, D = 64
+    ("gqa_decode_bf16", {"B": 1, "Hq": 2, "Hkv": 2, "N": 4100, "k": 9, "needles": 5}),   # g = 1
+    ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 9000, "block": 128, "k": 12,
+                         "needles": 8}),
+    ("long_decode_bf16", {"N": 65536 + 100}),                                # g = 8
+]
+
+
+@pytest.mark.parametrize("name,over", DECODE_CASES)
+def test_decode_pipeline_parity(name, over):
+    wl, inp, q, K, V = _decode_case(name, over)
+    dt = wl.dtype
+    Qd, Kd, Vd = to_dev(inp.Q, dt), to_dev(inp.K, dt), to_dev(inp.V, dt)
+    # a1 sketch
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    sk_ref = oracle.sketch(K, wl.block)
+    assert max_abs(sk.cpu().numpy(), sk_ref) <= 2e-6 * max(1.0, np.abs(sk_ref).max())
+    # a2 + a3 scores and selection
+    idx, cnt, score = sa.sa_select_topk(Qd, sk, wl.k, want_score=True)
+    sc_ref = oracle.block_scores(q, sk_ref)
+    assert max_abs(score.cpu().numpy(), sc_ref) <= 1e-5 * max(1e-3, np.abs(sc_ref).max())
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    nb = wl.nb
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            n = int(cnt_h[b, kh])
+            assert n == min(wl.k, nb)
+            assert np.all(idx_h[b, kh, n:] == -1)
+            if wl.k >= nb:
+                assert idx_h[b, kh, :n].tolist() == list(range(nb))
+                continue
+            check_topk_row(idx_h[b, kh, :n], sc_ref[b, kh], wl.k, [0, nb - 1],
+                           np.arange(1, nb - 1), where=f"b{b} kh{kh}")
+            assert set(inp.needles[b, kh].tolist()) <= set(idx_h[b, kh, :n].tolist())
+    # a5 + a6 attention on the GPU's own lists, float32 and bf16 outputs
+    O32, lse = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, block=wl.block, out_dtype=torch.float32)
+    O_ref, lse_ref = oracle.attend_blocks(q, K, V, idx_h, wl.block, count=cnt_h)
+    err = max_abs(O32.cpu().numpy(), O_ref)
+    assert err <= OUT_TOL[dt], err
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    O16, _ = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, block=wl.block, out_dtype=torch.bfloat16)
+    bits = O16.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, bf16_rne_of_f32(O32.cpu().numpy()))
+    if wl.k >= nb:  # keeping every block is dense attention
+        Od, lsed = oracle.dense(q, K, V)
+        assert max_abs(O32.cpu().numpy(), Od) <= OUT_TOL[dt]
+    print(f"{name} {over}: max-abs O error {err:.2e}")
+
+
+def test_decode_step_equals_separate_calls():
+    wl, inp, q, K, V = _decode_case("gqa_decode_bf16", {"B": 2, "N": 8192 + 40})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    sk_full = sa.sa_build_sketch(Kd, wl.block)
+    # stale sketch of the newest block, refreshed inside the step
+    sk = sk_full.clone()
+    sk[:, :, -1] = 0
+    O, lse, idx, cnt = sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block,
+                                         update_block=wl.nb - 1, out_dtype=torch.float32)
+    assert torch.equal(sk, sk_full)
+    idx2, cnt2, _ = sa.sa_select_topk(Qd, sk_full, wl.k)
+    O2, lse2 = sa.sa_sparse_decode(Qd, Kd, Vd, idx2, cnt2, block=wl.block, out_dtype=torch.float32)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    assert torch.equal(O, O2) and torch.equal(lse, lse2)
+
+
+def test_decode_split_invariance_and_determinism():
+    wl, inp, q, K, V = _decode_case("long_decode_bf16", {"N": 32768})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    idx, cnt, _ = sa.sa_select_topk(Qd, sk, wl.k)
+    O1, l1 = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, block=wl.block, out_dtype=torch.float32)
+    O1b, l1b = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, block=wl.block, out_dtype=torch.float32)
+    assert torch.equal(O1, O1b) and torch.equal(l1, l1b)          # bitwise repeatable
+    # a wider index buffer changes the number of splits; results agree to rounding
+    for stride in (wl.k * 3, 1000):
+        wide = torch.full((wl.B, wl.Hkv, stride), -1, dtype=torch.int32, device="cuda")
+        wide[:, :, :wl.k] = idx
+        O2, l2 = sa.sa_sparse_decode(Qd, Kd, Vd, wide, cnt, block=wl.block, out_dtype=torch.float32)
+        assert max_abs(O1.cpu().numpy(), O2.cpu().numpy()) <= 2e-6
+        assert max_abs(l1.cpu().numpy(), l2.cpu().numpy()) <= 2e-6
+    # an empty selection gives O = 0 and lse = -inf
+    zero = torch.zeros_like(cnt)
+    O3, l3 = sa.sa_sparse_decode(Qd, Kd, Vd, idx, zero, block=wl.block, out_dtype=torch.float32)
+    assert torch.all(O3 == 0) and torch.all(torch.isinf(l3)) and torch.all(l3 < 0)
+
+
+def test_sketch_block_range_update():
+    wl, inp, q, K, V = _decode_case("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 1000})
+    Kd = to_dev(inp.K, "bf16")
+    sk = torch.full((1, 2, wl.nb, wl.D), 7.0, device="cuda")
+    sa.sa_build_sketch(Kd, wl.block, blk_begin=3, blk_end=5, out=sk)
+    ref = oracle.sketch(K, wl.block)
+    got = sk.cpu().numpy()
+    assert np.all(got[:, :, :3] == 7.0) and np.all(got[:, :, 5:] == 7.0)
+    assert max_abs(got[:, :, 3:5], ref[:, :, 3:5]) <= 1e-6
+
+
+def test_select_nan_and_ties():
+    """NaN scores rank last; equal scores resolve to the lower block index."""
+    B, Hq, Hkv, D, nb = 1, 1, 1, 64, 40
+    sk = torch.zeros(B, Hkv, nb, D, device="cuda")
+    sk[0, 0, :, 0] = torch.tensor([float(j % 5) for j in range(nb)])
+    sk[0, 0, 7, 0] = float("nan")
+    sk[0, 0, 12, 0] = 100.0
+    q = torch.zeros(B, Hq, D, device="cuda")
+    q[0, 0, 0] = 1.0
+    idx, cnt, score = sa.sa_select_topk(q, sk, 10, want_score=True)
+    s = score.cpu().numpy()[0, 0].astype(np.float64)
+    check_topk_row(idx.cpu().numpy()[0, 0], s, 10, [0, nb - 1], np.arange(1, nb - 1))
+    got = idx.cpu().numpy()[0, 0].tolist()
+    assert 12 in got and 7 not in got
+    assert got == oracle.select_topk(s, 10).tolist()
+
+
+THRESH_CASES = [
+    ("threshold_decode_bf16", {"B": 2}),
+    ("threshold_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 5000}),
+    ("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 4, "D": 64, "N": 3000}),
+    ("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1, "D": 64, "N": 4096, "dtype": "f32",
+                               "outlier_channels": 0}),
+]
+
+
+def _eps_bound(q, K, wl):
+    """A loose float32 rounding bound of each score (for the false-positive band)."""
+    g = wl.Hq // wl.Hkv
+    sc = 1.0 / math.sqrt(wl.D)
+    A = np.stack([np.abs(K[:, h // g]) @ np.abs(q[:, h])[..., None] for h in range(wl.Hq)], 1)[..., 0]
+    return 4.0 * (wl.D + 1) * 2.0 ** -23 * A * sc + 2.0 ** -18 * (1 + np.abs(exact_scores(q, K)))
+
+
+@pytest.mark.parametrize("name,over", THRESH_CASES)
+def test_threshold_parity(name, over):
+    wl, inp, q, K, V = _decode_case(name, over)
+    dt = wl.dtype
+    Qd, Kd, Vd = to_dev(inp.Q, dt), to_dev(inp.K, dt), to_dev(inp.V, dt)
+    tau64, tau32 = oracle.threshold_tau(q, K, wl.percentile)
+    s = exact_scores(q, K)
+    eps = _eps_bound(q, K, wl)
+    cap = wl.cap
+    idx, score, cnt = sa.sa_select_threshold(Qd, Kd, torch.from_numpy(tau32).cuda(), cap)
+    idx_h, sc_h, cnt_h = idx.cpu().numpy(), score.cpu().numpy(), cnt.cpu().numpy()
+    lists = [[None] * wl.Hq for _ in range(wl.B)]
+    extra = 0
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            n = int(cnt_h[b, h])
+            assert n <= cap
+            got = idx_h[b, h, :n]
+            assert np.all(idx_h[b, h, n:] == -1)
+            assert np.all(np.diff(got) > 0)
+            exact = np.nonzero(s[b, h] >= tau64[b, h])[0]
+            missing = set(exact.tolist()) - set(got.tolist())
+            assert not missing, f"false negatives at b{b} h{h}: {sorted(missing)[:5]}"
+            ex = np.setdiff1d(got, exact)
+            assert np.all(s[b, h, ex] >= tau64[b, h] - 2 * eps[b, h, ex])
+            extra += ex.size
+            assert max_abs(sc_h[b, h, :n], s[b, h, got]) <= 1e-4
+            lists[b][h] = got
+    # token-mode attention on the GPU's lists, with and without the stored scores
+    O_ref, lse_ref = oracle.attend_tokens(q, K, V, lists)
+    for use_scores in (True, False):
+        O32, lse = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS,
+                                       score=score if use_scores else None,
+                                       out_dtype=torch.float32)
+        err = max_abs(O32.cpu().numpy(), O_ref)
+        assert err <= OUT_TOL[dt], err
+        assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    print(f"{name} {over}: extra keys {extra}, max-abs O error {err:.2e}")
+
+
+def test_threshold_capacity_and_minus_inf():
+    wl, inp, q, K, V = _decode_case("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1, "N": 3000})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    tau = torch.full((1, 4), -float("inf"), device="cuda")
+    idx, score, cnt = sa.sa_select_threshold(Qd, Kd, tau, 3000)
+    assert torch.all(cnt == 3000)
+    O32, _ = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS, score=score,
+                                 out_dtype=torch.float32)
+    Od, _ = oracle.dense(q, K, V)
+    assert max_abs(O32.cpu().numpy(), Od) <= 2e-3
+    # capacity overflow: true count reported, first `cap` positions written
+    tau64, tau32 = oracle.threshold_tau(q, K, 90.0)
+    idx, score, cnt = sa.sa_select_threshold(Qd, Kd, torch.from_numpy(tau32).cuda(), 50)
+    s = exact_scores(q, K)
+    for h in range(4):
+        n = int(cnt[0, h])
+        assert n >= int((s[0, h] >= tau64[0, h]).sum()) > 50
+        full, _, _ = sa.sa_select_threshold(Qd, Kd, torch.from_numpy(tau32).cuda(), 3000)
+        assert torch.equal(idx[0, h], full[0, h, :50])
+
+
+PREFILL_CASES = [
+    ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 2048, "needles": 4}),
+    ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 1, "N": 2048 + 77, "needles": 4}),   # ragged
+    ("sparse_prefill_bf16", {"Hq": 4, "Hkv": 4, "N": 1536, "needles": 2, "k": 4}),
+]
+
+
+@pytest.mark.parametrize("name,over", PREFILL_CASES)
+def test_prefill_parity(name, over):
+    wl = get_workload(name, **over)
+    inp = make_inputs(wl)
+    Q, K, V = (widen(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    M = wl.nb
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    flags = sa.SA_FORCE_SINK | sa.SA_FORCE_LOCAL | sa.SA_CAUSAL
+    idx, cnt, score = sa.sa_select_topk(Qd, sk, wl.k, flags=flags, q_block=wl.block, want_score=True)
+    Qb, Kb = oracle.prefill_pool_queries(Q, wl.block, wl.g), oracle.sketch(K, wl.block)
+    scale = 1.0 / math.sqrt(wl.D)
+    idx_h, cnt_h, sc_h = idx.cpu().numpy(), cnt.cpu().numpy(), score.cpu().numpy()
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            for i in range(M):
+                n = int(cnt_h[b, kh, i])
+                assert n == min(i + 1, wl.k)
+                assert np.all(idx_h[b, kh, i, n:] == -1)
+                r = np.full(M, -np.inf)
+                r[1:i] = (Kb[b, kh, 1:i] @ Qb[b, kh, i]) * scale
+                if i >= 2:
+                    assert max_abs(sc_h[b, kh, i, 1:i], r[1:i]) <= 1e-5 * max(1e-3, np.abs(r[1:i]).max())
+                forced = [0] if i == 0 else [0, i]
+                check_topk_row(idx_h[b, kh, i, :n], r, wl.k, forced, np.arange(1, max(i, 1)),
+                               where=f"kh{kh} i{i}")
+    for j, i in zip(inp.needles[0, 0], inp.partners[0, 0]):
+        assert j in idx_h[0, 0, i, :cnt_h[0, 0, i]]
+    O32, lse = sa.sa_sparse_prefill(Qd, Kd, Vd, idx, cnt, block=wl.block, out_dtype=torch.float32)
+    O_ref, lse_ref = oracle.prefill_attend(Q, K, V, idx_h, cnt_h, wl.block)
+    err = max_abs(O32.cpu().numpy(), O_ref)
+    assert err <= 2e-3, err
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    O16, _ = sa.sa_sparse_prefill(Qd, Kd, Vd, idx, cnt, block=wl.block, out_dtype=torch.bfloat16)
+    bits = O16.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(bits, bf16_rne_of_f32(O32.cpu().numpy()))
+    print(f"{name} {over}: max-abs O error {err:.2e}")
+
+
+def test_prefill_all_blocks_is_dense_causal():
+    wl = get_workload("sparse_prefill_bf16", Hq=4, Hkv=2, N=1024, needles=2)
+    inp = make_inputs(wl)
+    Q, K, V = (widen(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    M = wl.nb
+    idx = torch.full((1, 2, M, M), -1, dtype=torch.int32)
+    for i in range(M):
+        idx[0, :, i, :i + 1] = torch.arange(i + 1, dtype=torch.int32)
+    cnt = torch.arange(1, M + 1, dtype=torch.int32).repeat(1, 2, 1)
+    O32, lse = sa.sa_sparse_prefill(Qd, Kd, Vd, idx.cuda(), cnt.cuda().contiguous(), block=128,
+                                    out_dtype=torch.float32)
+    rows = [(0, h, t) for h in range(4) for t in range(0, wl.N, 7)]
+    Od, lsed = oracle.dense_causal_rows(Q, K, V, rows)
+    got = O32.cpu().numpy()
+    assert max_abs(np.stack([got[b, h, t] for b, h, t in rows]), Od) <= 2e-3
+    gl = lse.cpu().numpy()
+    assert max_abs(np.array([gl[b, h, t] for b, h, t in rows]), lsed) <= 1e-4

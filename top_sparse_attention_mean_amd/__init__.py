@@ -1,0 +1,289 @@
+"""Python binding of the gfx950 top-k block-sparse attention library (libsa.so).
+
+Argument marshalling only: every function takes torch tensors that live on the
+GPU, passes their device pointers and the current HIP stream to the C ABI in
+``include/sa.h`` and raises if the library reports an error.  All arithmetic
+runs in the library's HIP kernels; there is no CPU fallback, and importing this
+module fails loudly when ``libsa.so`` has not been built.
+
+bf16 tensors are passed as ``torch.bfloat16`` (raw 16-bit patterns); float32 as
+``torch.float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsa.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+        "or `python top_sparse_attention_mean_amd/build.py`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(5)
+SA_F32, SA_BF16 = 0, 1
+SA_FORCE_SINK, SA_FORCE_LOCAL, SA_CAUSAL = 1, 2, 4
+SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
+SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP = range(4)
+
+EXPORTS = ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
+           "sa_sparse_prefill", "sa_decode_step", "sa_workspace_bytes", "sa_status_str",
+           "sa_last_error", "sa_version"]
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+_U = ctypes.c_uint
+
+
+def _sig(name, restype, *args):
+    f = getattr(_lib, name)
+    f.restype = restype
+    f.argtypes = list(args)
+    return f
+
+
+_build_sketch = _sig("sa_build_sketch", _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P)
+_select_topk = _sig("sa_select_topk", _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _U, _F,
+                    _P, _P, _P, _P, _Z, _P)
+_select_threshold = _sig("sa_select_threshold", _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I,
+                         _P, _P, _P, _P, _Z, _P)
+_sparse_decode = _sig("sa_sparse_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
+                      _P, _P, _I, _P, _P, _I, _P, _P, _Z, _P)
+_sparse_prefill = _sig("sa_sparse_prefill", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P,
+                       _P, _I, _P, _I, _P, _P)
+_decode_step = _sig("sa_decode_step", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _F,
+                    _P, _P, _P, _P, _I, _P, _P, _Z, _P)
+_workspace_bytes = _sig("sa_workspace_bytes", _Z, _I, _I, _I, _I, _I, _I, _I, _I)
+_status_str = _sig("sa_status_str", ctypes.c_char_p, _I)
+_last_error = _sig("sa_last_error", ctypes.c_char_p)
+_version = _sig("sa_version", _I)
+
+
+class SAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _status_str(status).decode()
+        detail = _last_error().decode()
+        super().__init__(f"{where}: {msg}: {detail}")
+
+
+def _check(st: int, where: str) -> None:
+    if st != SA_OK:
+        raise SAError(st, where)
+
+
+def version() -> int:
+    return _version()
+
+
+def workspace_bytes(op: int, B: int, Hq: int, Hkv: int, N: int, D: int, block: int, k: int) -> int:
+    n = _workspace_bytes(op, B, Hq, Hkv, N, D, block, k)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("invalid workspace query")
+    return n
+
+
+# ------------------------------------------------------------------ helpers
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must live on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+_ws_cache = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    """A zero-filled device workspace of at least nbytes (cached per device)."""
+    key = torch.device(device)
+    ws = _ws_cache.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key)
+        _ws_cache[key] = ws
+    return ws
+
+
+# ------------------------------------------------------------------ entry points
+def sa_build_sketch(X: torch.Tensor, block: int, head_pool: int = 1, blk_begin: int = 0,
+                    blk_end: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Per-block mean sketch of X [B, H, N, D] -> float32 [B, H/head_pool, nb, D]."""
+    _dev(X, out)
+    B, H, N, D = X.shape
+    nb = -(-N // block)
+    if blk_end is None:
+        blk_end = nb
+    if out is None:
+        out = torch.empty(B, H // head_pool, nb, D, dtype=torch.float32, device=X.device)
+    _check(_build_sketch(_ptr(X), _dt(X), B, H, N, D, block, head_pool, blk_begin, blk_end,
+                         _ptr(out), _stream(stream)), "sa_build_sketch")
+    return out
+
+
+def sa_select_topk(Q: torch.Tensor, ksketch: torch.Tensor, k: int,
+                   flags: int = SA_FORCE_SINK | SA_FORCE_LOCAL, scale: float = 0.0,
+                   Hkv: Optional[int] = None, q_block: int = 1,
+                   idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                   score: Optional[torch.Tensor] = None, want_score: bool = False,
+                   ws: Optional[torch.Tensor] = None, stream=None):
+    """Top-k block selection.
+
+    Decode: Q [B, Hq, D] -> idx [B, Hkv, k], count [B, Hkv] (score [B, Hkv, nb]).
+    Causal prefill (flags & SA_CAUSAL): Q [B, Hq, L, D], q_block = key block ->
+    idx [B, Hkv, M, k], count [B, Hkv, M] (score [B, Hkv, M, nb]).
+    """
+    _dev(Q, ksketch, idx, count, score)
+    B, Hkv_, nb, D = ksketch.shape
+    Hkv = Hkv or Hkv_
+    Hq = Q.shape[1]
+    causal = bool(flags & SA_CAUSAL)
+    Lq = Q.shape[2] if causal else 1
+    M = -(-Lq // q_block)
+    rows = (B, Hkv, M) if causal else (B, Hkv)
+    if idx is None:
+        idx = torch.empty(*rows, k, dtype=torch.int32, device=Q.device)
+    if count is None:
+        count = torch.empty(*rows, dtype=torch.int32, device=Q.device)
+    if score is None and want_score:
+        score = torch.empty(*rows, nb, dtype=torch.float32, device=Q.device)
+    need = workspace_bytes(SA_OP_SELECT_TOPK, B, Hq, Hkv, Lq, D, q_block, nb)
+    if ws is None:
+        ws = workspace(need, Q.device)
+    _check(_select_topk(_ptr(Q), _dt(Q), B, Hq, Hkv, Lq, D, q_block, _ptr(ksketch), nb, k, flags,
+                        scale, _ptr(idx), _ptr(count), _ptr(score), _ptr(ws), ws.numel(),
+                        _stream(stream)), "sa_select_topk")
+    return idx, count, score
+
+
+def sa_select_threshold(Q: torch.Tensor, K: torch.Tensor, tau: torch.Tensor, cap: int,
+                        scale: float = 0.0, idx=None, score=None, count=None, ws=None,
+                        stream=None):
+    """Half-space selection: every token with q . k * scale >= tau[b, h].
+
+    Returns idx [B, Hq, cap] (ascending, -1 padded), score [B, Hq, cap] and
+    count [B, Hq] (the true count, which may exceed cap).
+    """
+    _dev(Q, K, tau, idx, score, count)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = K.shape
+    dev = Q.device
+    if idx is None:
+        idx = torch.empty(B, Hq, cap, dtype=torch.int32, device=dev)
+    if score is None:
+        score = torch.empty(B, Hq, cap, dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    need = workspace_bytes(SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0, cap)
+    if ws is None:
+        ws = workspace(need, dev)
+    _check(_select_threshold(_ptr(Q), _ptr(K), _dt(Q), B, Hq, Hkv, N, D, _ptr(tau), scale, cap,
+                             _ptr(idx), _ptr(score), _ptr(count), _ptr(ws), ws.numel(),
+                             _stream(stream)), "sa_select_threshold")
+    return idx, score, count
+
+
+def sa_sparse_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
+                     count: Optional[torch.Tensor] = None, mode: int = SA_IDX_BLOCKS,
+                     block: int = 64, score: Optional[torch.Tensor] = None, scale: float = 0.0,
+                     out_dtype: Optional[torch.dtype] = None, O: Optional[torch.Tensor] = None,
+                     lse: Optional[torch.Tensor] = None, want_lse: bool = True, ws=None,
+                     stream=None):
+    """Exact attention over the selected blocks/tokens: O [B, Hq, D], lse [B, Hq]."""
+    _dev(Q, K, V, idx, count, score, O, lse)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = K.shape
+    dev = Q.device
+    od = out_dtype or Q.dtype
+    if O is None:
+        O = torch.empty(B, Hq, D, dtype=od, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    stride = idx.shape[-1]
+    need = workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D,
+                           block if mode == SA_IDX_BLOCKS else 0, stride)
+    if ws is None:
+        ws = workspace(need, dev)
+    _check(_sparse_decode(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, scale, mode, block,
+                          _ptr(idx), _ptr(count), stride, _ptr(score), _ptr(O), _dt(O), _ptr(lse),
+                          _ptr(ws), ws.numel(), _stream(stream)), "sa_sparse_decode")
+    return O, lse
+
+
+def sa_sparse_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,
+                      count: torch.Tensor, block: int = 128, scale: float = 0.0,
+                      out_dtype: Optional[torch.dtype] = None, O=None, lse=None,
+                      want_lse: bool = True, stream=None):
+    """Block-sparse causal prefill: O [B, Hq, L, D], lse [B, Hq, L]."""
+    _dev(Q, K, V, idx, count, O, lse)
+    B, Hq, L, D = Q.shape
+    Hkv = K.shape[1]
+    dev = Q.device
+    od = out_dtype or Q.dtype
+    if O is None:
+        O = torch.empty(B, Hq, L, D, dtype=od, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, L, dtype=torch.float32, device=dev)
+    _check(_sparse_prefill(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, L, D, scale, block,
+                           _ptr(idx), _ptr(count), idx.shape[-1], _ptr(O), _dt(O), _ptr(lse),
+                           _stream(stream)), "sa_sparse_prefill")
+    return O, lse
+
+
+def sa_decode_step(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksketch: torch.Tensor,
+                   k: int, block: int = 64, update_block: int = -1, scale: float = 0.0,
+                   out_dtype=None, idx=None, count=None, score=None, O=None, lse=None,
+                   want_lse: bool = True, ws=None, stream=None):
+    """One decode step: optional sketch update of one block, top-k select, sparse attention."""
+    _dev(Q, K, V, ksketch, idx, count, score, O, lse)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = K.shape
+    dev = Q.device
+    if idx is None:
+        idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty(B, Hq, D, dtype=out_dtype or Q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    need = workspace_bytes(SA_OP_DECODE_STEP, B, Hq, Hkv, N, D, block, k)
+    if ws is None:
+        ws = workspace(need, dev)
+    _check(_decode_step(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, block,
+                        _ptr(ksketch), update_block, k, scale, _ptr(idx), _ptr(count),
+                        _ptr(score), _ptr(O), _dt(O), _ptr(lse), _ptr(ws), ws.numel(),
+                        _stream(stream)), "sa_decode_step")
+    return O, lse, idx, count
+
+
+__all__ = [n for n in dir() if n.startswith("sa_") or n.startswith("SA_")] + [
+    "workspace", "workspace_bytes", "version", "SAError", "LIB_PATH", "EXPORTS"]

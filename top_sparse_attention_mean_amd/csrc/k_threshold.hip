@@ -1,0 +1,244 @@
+// k_threshold.hip -- half-space (threshold) selection with no false negatives.
+//
+// Every key k_t with q_h . k_t * scale >= tau[b, h] is returned: the half-space
+// H(q, tau) of "Sparse Attention as a Range Searching Problem" (Metodologia §1),
+// whose defining property is that no key inside it is missed.  With no index
+// the exact check runs over every key (the index's second phase, §2, applied to
+// all keys), so the kernel is a full scan of K and HBM-bound.
+//
+// Rigorous float32 test.  A token is kept when fl32(s) + eps_t >= tau, where
+// eps_t bounds |fl32(s) - s_exact|:
+//   * the dot product is one chain of bf16 matrix-core products (each product of
+//     two bf16 values is exact in float32) accumulated in float32; for any
+//     summation order and any accumulator that loses at most one unit of 2^-23
+//     relative per addition, |err| <= gamma_D * sum_c |q_c k_c| with
+//     gamma_D = D u / (1 - D u), u = 2^-23;  float32 inputs add one rounding
+//     per product (gamma_{D+1});
+//   * sum_c |q_c k_c| is itself computed by a second matrix-core chain on |K|
+//     and |q| (a sign-bit mask), so it carries the same relative bound, which
+//     the host folds into gamma;
+//   * the final scaling, the comparison and tau's own float32 rounding are
+//     covered by 2^-20 (|s| + |tau|).
+// Hence every exactly-qualifying key is kept; extra keys lie within 2 eps_t
+// below tau.
+//
+// Output order is ascending token position: each wave owns a 128-token
+// segment, compacts its kept tokens per head with ballots (token order inside
+// a 16-token tile is 4*(lane/16) + r), and stages them; k_threshold_compact
+// then prefix-sums the per-segment counts of each (b, head) and copies the
+// staged pairs into the capped output lists.
+#include "sa_device.h"
+#include "sa_internal.h"
+
+namespace sa {
+
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_threshold_mfma(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int BH, int Hq, int Hkv,
+    int N, float scale, float gamma, const float* __restrict__ tau, int nseg,
+    int32_t* __restrict__ st_idx, float* __restrict__ st_val, int32_t* __restrict__ st_cnt) {
+  static_assert(G <= 16, "heads are the 16 columns of the score tile");
+  constexpr int NST = D / 32;
+  const int bh = blockIdx.x % BH, chunk = blockIdx.x / BH;
+  const int b = bh / Hkv, kh = bh % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gq = lane >> 4, nn = lane & 15;
+  const int seg = chunk * 4 + wave;
+  if (seg >= nseg) return;  // no barriers below
+
+  u32x4 qb[NST], qa[NST];
+  float th = __builtin_inff();
+  if (nn < G) {
+    const uint16_t* qp = Q + (size_t(b) * Hq + kh * G + nn) * D + 8 * gq;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      qb[st] = ld16(qp + 32 * st);
+      qa[st] = qb[st] & 0x7fff7fffu;
+    }
+    th = tau[size_t(b) * Hq + kh * G + nn];
+  } else {
+#pragma unroll
+    for (int st = 0; st < NST; ++st) { qb[st] = u32x4{0u, 0u, 0u, 0u}; qa[st] = qb[st]; }
+  }
+  const float gs = gamma * scale;
+  const float tabs = fabsf(th);
+  const uint16_t* Kb = K + size_t(bh) * N * D;
+  const size_t sbase = ((size_t(b) * Hq + kh * G + min(nn, G - 1)) * nseg + seg) * kThrSeg;
+  const uint64_t headmask = 0x0001000100010001ull << nn;
+  const uint64_t lower = headmask & ((1ull << (16 * gq)) - 1ull);
+  int run = 0;
+
+  for (int tile = 0; tile < kThrSeg / 16; ++tile) {
+    const int tok0 = seg * kThrSeg + tile * 16;
+    if (tok0 >= N) break;
+    u32x4 ka[NST], kb[NST];
+    const int kr = min(tok0 + nn, N - 1);
+    const uint16_t* kp = Kb + size_t(kr) * D + 8 * gq;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      ka[st] = ld16(kp + 32 * st);
+      kb[st] = ka[st] & 0x7fff7fffu;
+    }
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, ab = sc;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      sc = mfma16x16x32(ka[st], qb[st], sc);
+      ab = mfma16x16x32(kb[st], qa[st], ab);
+    }
+    bool keep[4];
+    float s32[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = tok0 + 4 * gq + r;
+      s32[r] = sc[r] * scale;
+      const float eps = gs * ab[r] + (fabsf(s32[r]) + tabs) * 9.5367431640625e-07f;  // 2^-20
+      keep[r] = nn < G && tok < N && (s32[r] + eps >= th);
+    }
+    uint64_t m[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) m[r] = __ballot(keep[r]);
+    int before = 0, total = 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      before += __popcll(m[r] & lower);
+      total += __popcll(m[r] & headmask);
+    }
+    int pos = run + before;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (keep[r]) {
+        st_idx[sbase + pos] = tok0 + 4 * gq + r;
+        st_val[sbase + pos] = s32[r];
+        ++pos;
+      }
+    }
+    run += total;
+  }
+  if (gq == 0 && nn < G) st_cnt[(size_t(b) * Hq + kh * G + nn) * nseg + seg] = run;
+}
+
+// float32 inputs: one token per lane, dot products on the vector ALUs.
+template <int D>
+__global__ __launch_bounds__(256) void k_threshold_valu(
+    const float* __restrict__ Q, const float* __restrict__ K, int BH, int Hq, int Hkv, int G,
+    int N, float scale, float gamma, const float* __restrict__ tau, int nseg,
+    int32_t* __restrict__ st_idx, float* __restrict__ st_val, int32_t* __restrict__ st_cnt) {
+  __shared__ float sq[16][D];
+  const int bh = blockIdx.x % BH, chunk = blockIdx.x / BH;
+  const int b = bh / Hkv, kh = bh % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = threadIdx.x; o < G * D; o += 256)
+    sq[o / D][o % D] = Q[(size_t(b) * Hq + kh * G + o / D) * D + o % D];
+  __syncthreads();
+  const int seg = chunk * 4 + wave;
+  if (seg >= nseg) return;
+  const float* Kb = K + size_t(bh) * N * D;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int h = 0; h < G; ++h) {
+    const float th = tau[size_t(b) * Hq + kh * G + h];
+    const size_t sbase = ((size_t(b) * Hq + kh * G + h) * nseg + seg) * kThrSeg;
+    int run = 0;
+    for (int part = 0; part < kThrSeg / 64; ++part) {
+      const int tok = seg * kThrSeg + part * 64 + lane;
+      float s = 0.f, a = 0.f;
+      if (tok < N) {
+        const float* kp = Kb + size_t(tok) * D;
+        for (int d = 0; d < D; d += 4) {
+          u32x4 w = ld16(kp + d);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float kv = __uint_as_float(w[c]);
+            s += sq[h][d + c] * kv;
+            a += fabsf(sq[h][d + c] * kv);
+          }
+        }
+      }
+      const float s32 = s * scale;
+      const float eps = gamma * scale * a + (fabsf(s32) + fabsf(th)) * 9.5367431640625e-07f;
+      const bool keep = tok < N && (s32 + eps >= th);
+      const uint64_t m = __ballot(keep);
+      if (keep) {
+        const int pos = run + __popcll(m & below);
+        st_idx[sbase + pos] = tok;
+        st_val[sbase + pos] = s32;
+      }
+      run += __popcll(m);
+    }
+    if (lane == 0) st_cnt[(size_t(b) * Hq + kh * G + h) * nseg + seg] = run;
+  }
+}
+
+// One 256-thread workgroup per (b, query head): ordered copy of the staged
+// segments into idx/score [cap] and the true count.
+__global__ __launch_bounds__(256) void k_threshold_compact(
+    const int32_t* __restrict__ st_idx, const float* __restrict__ st_val,
+    const int32_t* __restrict__ st_cnt, int nseg, int cap, int32_t* __restrict__ idx,
+    float* __restrict__ score, int32_t* __restrict__ count) {
+  __shared__ int scan[17];
+  const int bhq = blockIdx.x, tid = threadIdx.x;
+  const int per = (nseg + 255) / 256;
+  const int s0 = min(tid * per, nseg), s1 = min(s0 + per, nseg);
+  const int32_t* cnt = st_cnt + size_t(bhq) * nseg;
+  int mine = 0;
+  for (int s = s0; s < s1; ++s) mine += cnt[s];
+  int total;
+  int off = block_excl_scan<256>(mine, scan, &total);
+  int32_t* oi = idx + size_t(bhq) * cap;
+  float* ov = score + size_t(bhq) * cap;
+  for (int s = s0; s < s1; ++s) {
+    const size_t base = (size_t(bhq) * nseg + s) * kThrSeg;
+    const int c = cnt[s];
+    for (int e = 0; e < c && off + e < cap; ++e) {
+      oi[off + e] = st_idx[base + e];
+      ov[off + e] = st_val[base + e];
+    }
+    off += c;
+  }
+  for (int p = total + tid; p < cap; p += 256) {
+    oi[p] = -1;
+    ov[p] = -__builtin_inff();
+  }
+  if (tid == 0) count[bhq] = total;
+}
+
+hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
+                            int N, int D, const float* tau, float scale, int cap, int32_t* idx,
+                            float* score, int32_t* count, const ThrWs& w, void* ws,
+                            hipStream_t st) {
+  const int BH = B * Hkv, G = Hq / Hkv;
+  char* base = static_cast<char*>(ws);
+  int32_t* si = reinterpret_cast<int32_t*>(base + w.idx_off);
+  float* sv = reinterpret_cast<float*>(base + w.val_off);
+  int32_t* sc = reinterpret_cast<int32_t*>(base + w.cnt_off);
+  const int chunks = cdiv(w.nseg, 4);
+  dim3 g(unsigned(long(BH) * chunks));
+  const double u = 1.0 / 8388608.0;  // 2^-23
+  const int terms = dtype == SA_BF16 ? D : D + 1;
+  const double gam = terms * u / (1.0 - terms * u);
+  // the |q|.|k| sum carries its own relative error; fold it in, plus margin
+  const float gamma = float(gam * (1.0 + gam) * 1.001);
+  if (dtype == SA_BF16) {
+    auto q = static_cast<const uint16_t*>(Q);
+    auto k = static_cast<const uint16_t*>(K);
+#define SA_THR(DD, GG) k_threshold_mfma<DD, GG><<<g, 256, 0, st>>>(q, k, BH, Hq, Hkv, N, scale, gamma, tau, w.nseg, si, sv, sc)
+    if (D == 128) {
+      switch (G) { case 1: SA_THR(128, 1); break; case 2: SA_THR(128, 2); break;
+                   case 4: SA_THR(128, 4); break; default: SA_THR(128, 8); break; }
+    } else {
+      switch (G) { case 1: SA_THR(64, 1); break; case 2: SA_THR(64, 2); break;
+                   case 4: SA_THR(64, 4); break; default: SA_THR(64, 8); break; }
+    }
+#undef SA_THR
+  } else {
+    auto q = static_cast<const float*>(Q);
+    auto k = static_cast<const float*>(K);
+    if (D == 128) k_threshold_valu<128><<<g, 256, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, si, sv, sc);
+    else          k_threshold_valu<64><<<g, 256, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, si, sv, sc);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_threshold_compact<<<dim3(B * Hq), 256, 0, st>>>(si, sv, sc, w.nseg, cap, idx, score, count);
+  return hipGetLastError();
+}
+
+}  // namespace sa

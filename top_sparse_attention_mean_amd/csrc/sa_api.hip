@@ -1,0 +1,335 @@
+// sa_api.hip -- the extern "C" entry points declared in include/sa.h.
+//
+// Every argument check runs on the host before anything is enqueued and
+// before any HIP runtime call, so invalid calls fail the same way with or
+// without a GPU.  Launches are asynchronous on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sa_internal.h"
+
+using namespace sa;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sa_status fail(sa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return SA_OK;
+  return fail(SA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dtype_ok(int dt) { return dt == SA_F32 || dt == SA_BF16; }
+int elem_bytes(int dt) { return dt == SA_BF16 ? 2 : 4; }
+float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf(float(D)); }
+bool pow2_le8(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+#define REQ(cond, ...)                                   \
+  do {                                                   \
+    if (!(cond)) return fail(SA_ERR_INVALID, __VA_ARGS__); \
+  } while (0)
+#define SUP(cond, ...)                                       \
+  do {                                                       \
+    if (!(cond)) return fail(SA_ERR_UNSUPPORTED, __VA_ARGS__); \
+  } while (0)
+#define PTR(p) REQ((p) != nullptr && al16(p), #p " must be a non-null 16-byte aligned device pointer")
+
+sa_status check_heads(int B, int Hq, int Hkv) {
+  REQ(B >= 1 && Hq >= 1 && Hkv >= 1, "B, Hq, Hkv must be >= 1 (got %d, %d, %d)", B, Hq, Hkv);
+  REQ(Hq % Hkv == 0, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  return SA_OK;
+}
+
+// --------------------------------------------------------------- validation
+sa_status v_sketch(const void* X, int dtype, int B, int H, int N, int D, int block, int hp,
+                   int b0, int b1, const float* sk) {
+  PTR(X);
+  PTR(sk);
+  REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
+  REQ(B >= 1 && H >= 1 && N >= 1, "B, H, N must be >= 1");
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(block >= 1, "block must be >= 1");
+  REQ(hp >= 1 && H % hp == 0, "head_pool (%d) must divide H (%d)", hp, H);
+  const int nb = cdiv(N, block);
+  REQ(0 <= b0 && b0 <= b1 && b1 <= nb, "block range [%d, %d) outside [0, %d]", b0, b1, nb);
+  REQ(long(B) * (H / hp) * (b1 - b0) < (1L << 31), "too many output rows");
+  return SA_OK;
+}
+
+sa_status v_select(const void* Q, int dtype, int B, int Hq, int Hkv, int Lq, int D, int q_block,
+                   const float* ksk, int nb, int k, unsigned flags, int32_t* idx,
+                   int32_t* count, float* score, void* ws, size_t ws_bytes) {
+  PTR(Q);
+  PTR(ksk);
+  PTR(idx);
+  PTR(count);
+  if (score) PTR(score);
+  REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(nb >= 1 && k >= 1, "nb and k must be >= 1 (got %d, %d)", nb, k);
+  REQ((flags & ~7u) == 0, "unknown flag bits 0x%x", flags);
+  const int nF = int((flags & SA_FORCE_SINK) != 0) + int((flags & SA_FORCE_LOCAL) != 0);
+  if (flags & SA_CAUSAL) {
+    REQ(Lq >= 1 && q_block >= 1, "Lq and q_block must be >= 1");
+    const int M = cdiv(Lq, q_block);
+    REQ(nb >= M, "the key sketch has %d blocks but the queries need %d", nb, M);
+    SUP(M <= kMaxNbPrefill, "at most %d query blocks per selection row", kMaxNbPrefill);
+    REQ(k >= nF, "k (%d) smaller than the %d forced blocks", k, nF);
+    REQ(long(B) * Hkv * M < (1L << 31), "too many selection rows");
+  } else {
+    REQ(Lq == 1 && q_block == 1, "decode selection takes one query position (Lq = q_block = 1)");
+    SUP(nb <= kMaxNbDecode, "at most %d blocks per decode selection row", kMaxNbDecode);
+    REQ(nb == 1 || k >= nF, "k (%d) smaller than the %d forced blocks", k, nF);
+  }
+  const size_t need = select_ws_bytes(B, Hkv, (flags & SA_CAUSAL) ? Lq : 1, D, q_block, nb);
+  const bool uses_ws = (flags & SA_CAUSAL) || score == nullptr;
+  if (uses_ws) {
+    if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+    PTR(ws);
+  }
+  return SA_OK;
+}
+
+sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                   int Hkv, int N, int D, int mode, int block, const int32_t* idx,
+                   const int32_t* count, int idx_stride, const float* score, const void* O,
+                   int out_dtype, const float* lse, const void* ws, size_t ws_bytes) {
+  PTR(Q);
+  PTR(K);
+  PTR(V);
+  PTR(idx);
+  PTR(O);
+  if (count) PTR(count);
+  if (score) PTR(score);
+  if (lse) PTR(lse);
+  REQ(dtype_ok(dtype) && dtype_ok(out_dtype), "unknown dtype");
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(N >= 1 && idx_stride >= 1, "N and idx_stride must be >= 1");
+  const int G = Hq / Hkv;
+  if (mode == SA_IDX_BLOCKS) {
+    REQ(block >= 1, "block must be >= 1");
+    if (dtype == SA_BF16) {
+      SUP(block == 64 || block == 128, "bf16 block-mode decode needs block 64 or 128");
+      SUP(pow2_le8(G), "bf16 block-mode decode needs g in {1, 2, 4, 8} (got %d)", G);
+    } else {
+      SUP(block <= kValuTokensPerWG && kValuTokensPerWG % block == 0,
+          "float32 block-mode decode needs block dividing %d", kValuTokensPerWG);
+      SUP(G <= 8, "float32 decode needs g <= 8 (got %d)", G);
+    }
+  } else if (mode == SA_IDX_TOKENS) {
+    REQ(count != nullptr, "token mode needs count");
+  } else {
+    return fail(SA_ERR_INVALID, "unknown mode %d", mode);
+  }
+  const DecodeWs w = decode_ws(B, Hq, Hkv, D, mode, block, idx_stride);
+  REQ(long(B) * (mode == SA_IDX_BLOCKS ? Hkv : Hq) * w.S < (1L << 31), "grid too large");
+  if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);
+  PTR(ws);
+  return SA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_version(void) { return 100; }
+
+const char* sa_last_error(void) { return g_err; }
+
+const char* sa_status_str(int s) {
+  switch (s) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case SA_ERR_WORKSPACE: return "workspace too small";
+    case SA_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int block, int k) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || N < 1 || D < 1) return SIZE_MAX;
+  switch (op) {
+    case SA_OP_SELECT_TOPK:          // N = Lq, block = q_block, k = nb
+      if (k < 1 || block < 1) return SIZE_MAX;
+      return select_ws_bytes(B, Hkv, N, D, block, k);
+    case SA_OP_SELECT_THRESHOLD:
+      return threshold_ws(B, Hq, N).bytes;
+    case SA_OP_SPARSE_DECODE:        // k = idx_stride; block = 0 for token mode
+      if (k < 1) return SIZE_MAX;
+      return decode_ws(B, Hq, Hkv, D, block > 0 ? SA_IDX_BLOCKS : SA_IDX_TOKENS, block, k).bytes;
+    case SA_OP_DECODE_STEP: {
+      if (k < 1 || block < 1) return SIZE_MAX;
+      const int nb = cdiv(N, block);
+      return select_ws_bytes(B, Hkv, 1, D, 1, nb) +
+             decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k).bytes;
+    }
+    default:
+      return SIZE_MAX;
+  }
+}
+
+sa_status sa_build_sketch(const void* X, int dtype, int B, int H, int N, int D, int block,
+                          int head_pool, int blk_begin, int blk_end, float* sketch,
+                          void* stream) {
+  sa_status s = v_sketch(X, dtype, B, H, N, D, block, head_pool, blk_begin, blk_end, sketch);
+  if (s) return s;
+  return hip_status(launch_sketch(X, dtype, B, H, N, D, block, head_pool, blk_begin, blk_end,
+                                  sketch, static_cast<hipStream_t>(stream)),
+                    "sa_build_sketch");
+}
+
+sa_status sa_select_topk(const void* Q, int dtype, int B, int Hq, int Hkv, int Lq, int D,
+                         int q_block, const float* ksketch, int nb, int k, unsigned flags,
+                         float scale, int32_t* idx, int32_t* count, float* score, void* ws,
+                         size_t ws_bytes, void* stream) {
+  sa_status s = v_select(Q, dtype, B, Hq, Hkv, Lq, D, q_block, ksketch, nb, k, flags, idx, count,
+                         score, ws, ws_bytes);
+  if (s) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = eff_scale(scale, D);
+  if (flags & SA_CAUSAL) {
+    const int M = cdiv(Lq, q_block);
+    float* qbar = static_cast<float*>(ws);
+    hipError_t e = launch_sketch(Q, dtype, B, Hq, Lq, D, q_block, Hq / Hkv, 0, M, qbar, st);
+    if (e != hipSuccess) return hip_status(e, "sa_select_topk (pool)");
+    return hip_status(launch_prefill_select(qbar, ksketch, B * Hkv, M, nb, D, k, flags, sc, idx,
+                                            count, score, st),
+                      "sa_select_topk (prefill)");
+  }
+  float* scores = score ? score : static_cast<float*>(ws);
+  hipError_t e = launch_block_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, sc, scores, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_topk (score)");
+  return hip_status(launch_topk_decode(scores, B * Hkv, nb, k, flags, idx, count, st),
+                    "sa_select_topk (select)");
+}
+
+sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
+                              int N, int D, const float* tau, float scale, int cap, int32_t* idx,
+                              float* score, int32_t* count, void* ws, size_t ws_bytes,
+                              void* stream) {
+  PTR(Q);
+  PTR(K);
+  PTR(tau);
+  PTR(idx);
+  PTR(score);
+  PTR(count);
+  REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(N >= 1 && cap >= 1, "N and cap must be >= 1");
+  const int G = Hq / Hkv;
+  if (dtype == SA_BF16) SUP(pow2_le8(G), "bf16 threshold selection needs g in {1, 2, 4, 8}");
+  else SUP(G <= 8, "float32 threshold selection needs g <= 8");
+  const ThrWs w = threshold_ws(B, Hq, N);
+  REQ(long(B) * Hkv * cdiv(w.nseg, 4) < (1L << 31), "grid too large");
+  if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);
+  PTR(ws);
+  return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, tau, eff_scale(scale, D), cap,
+                                     idx, score, count, w, ws, static_cast<hipStream_t>(stream)),
+                    "sa_select_threshold");
+}
+
+sa_status sa_sparse_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                           int Hkv, int N, int D, float scale, int mode, int block,
+                           const int32_t* idx, const int32_t* count, int idx_stride,
+                           const float* score, void* O, int out_dtype, float* lse, void* ws,
+                           size_t ws_bytes, void* stream) {
+  sa_status s = v_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, mode, block, idx, count, idx_stride,
+                         score, O, out_dtype, lse, ws, ws_bytes);
+  if (s) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = eff_scale(scale, D);
+  const DecodeWs w = decode_ws(B, Hq, Hkv, D, mode, block, idx_stride);
+  hipError_t e = mode == SA_IDX_BLOCKS
+                     ? launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx,
+                                            count, idx_stride, w, ws, st)
+                     : launch_decode_tokens(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, idx, count,
+                                            idx_stride, score, w, ws, st);
+  if (e != hipSuccess) return hip_status(e, "sa_sparse_decode (partials)");
+  return hip_status(launch_merge(w, ws, B * Hq, D, O, out_dtype, lse, st),
+                    "sa_sparse_decode (merge)");
+}
+
+sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                            int Hkv, int L, int D, float scale, int block, const int32_t* idx,
+                            const int32_t* count, int kmax, void* O, int out_dtype, float* lse,
+                            void* stream) {
+  PTR(Q);
+  PTR(K);
+  PTR(V);
+  PTR(idx);
+  PTR(count);
+  PTR(O);
+  if (lse) PTR(lse);
+  REQ(dtype_ok(dtype) && dtype_ok(out_dtype), "unknown dtype");
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  REQ(L >= 1 && kmax >= 1 && block >= 1, "L, kmax and block must be >= 1");
+  SUP(dtype == SA_BF16, "prefill runs on bf16 matrix cores: dtype must be SA_BF16");
+  SUP(D == 128, "prefill supports D = 128");
+  SUP(block == 128, "prefill supports 128-token blocks");
+  const long units = long(B) * Hkv * cdiv(L, block);
+  REQ(cdiv(units, 8) * 8L * (Hq / Hkv) < (1L << 31), "grid too large");
+  return hip_status(launch_prefill(Q, K, V, B, Hq, Hkv, L, D, eff_scale(scale, D), block, idx,
+                                   count, kmax, O, out_dtype, lse,
+                                   static_cast<hipStream_t>(stream)),
+                    "sa_sparse_prefill");
+}
+
+sa_status sa_decode_step(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                         int Hkv, int N, int D, int block, float* ksketch, int update_block,
+                         int k, float scale, int32_t* idx, int32_t* count, float* score,
+                         void* O, int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                         void* stream) {
+  PTR(ksketch);
+  REQ(block >= 1, "block must be >= 1");
+  const int nb = cdiv(N, block);
+  REQ(update_block >= -1 && update_block < nb, "update_block %d outside [-1, %d)", update_block, nb);
+  const size_t sel = select_ws_bytes(B, Hkv, 1, D, 1, nb);
+  sa_status s = v_select(Q, dtype, B, Hq, Hkv, 1, D, 1, ksketch, nb, k,
+                         SA_FORCE_SINK | SA_FORCE_LOCAL, idx, count, score, ws, ws_bytes);
+  if (s) return s;
+  if (ws_bytes < sel) return fail(SA_ERR_WORKSPACE, "workspace too small");
+  void* dws = static_cast<char*>(ws) + sel;
+  s = v_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, SA_IDX_BLOCKS, block, idx, count, k, nullptr, O,
+               out_dtype, lse, dws, ws_bytes - sel);
+  if (s) return s;
+  if (update_block >= 0) {
+    s = v_sketch(K, dtype, B, Hkv, N, D, block, 1, update_block, update_block + 1, ksketch);
+    if (s) return s;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = eff_scale(scale, D);
+  hipError_t e = hipSuccess;
+  if (update_block >= 0) {
+    e = launch_sketch(K, dtype, B, Hkv, N, D, block, 1, update_block, update_block + 1, ksketch, st);
+    if (e != hipSuccess) return hip_status(e, "sa_decode_step (sketch)");
+  }
+  float* scores = score ? score : static_cast<float*>(ws);
+  e = launch_block_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, sc, scores, st);
+  if (e != hipSuccess) return hip_status(e, "sa_decode_step (score)");
+  e = launch_topk_decode(scores, B * Hkv, nb, k, SA_FORCE_SINK | SA_FORCE_LOCAL, idx, count, st);
+  if (e != hipSuccess) return hip_status(e, "sa_decode_step (select)");
+  const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
+  e = launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count, k, w, dws, st);
+  if (e != hipSuccess) return hip_status(e, "sa_decode_step (partials)");
+  return hip_status(launch_merge(w, dws, B * Hq, D, O, out_dtype, lse, st), "sa_decode_step (merge)");
+}
+
+}  // extern "C"

@@ -1,0 +1,123 @@
+// sa_device.h -- device helpers shared by the gfx950 kernels of this library.
+//
+// Wave64 only.  Values stored as bf16 travel as raw 16-bit patterns packed two
+// per 32-bit word (the even element in the low half).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------ bf16 <-> f32
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// float -> bf16 with IEEE round-to-nearest-even (gfx950 v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
+
+// ------------------------------------------------------------ math
+// 2^x on the hardware exponential unit; 2^-inf = 0.
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------ loads
+template <typename T>
+__device__ __forceinline__ u32x4 ld16(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+template <typename T>
+__device__ __forceinline__ u32x2 ld8(const T* p) {
+  return *reinterpret_cast<const u32x2*>(p);
+}
+
+// ------------------------------------------------------------ matrix cores
+// D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16).  Lane l supplies row l%16 of
+// A and column l%16 of B, 8 contraction elements each (the same contraction
+// slots in both operands); D row 4*(l/16)+r, column l%16 lands in element r.
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+// Same with a 16-element contraction (4 elements per lane).
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
+// Byte permute: result byte i = byte sel_i of the 8-byte value (hi:lo).
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// Low halves of two words -> one word (a.lo | b.lo << 16); high halves likewise.
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return perm(b, a, 0x07060302u); }
+
+// ------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a whole workgroup of NT threads (thread order).
+// `tmp` must hold NT/64 + 1 ints of LDS.  Returns the exclusive prefix and the
+// total through *total.  Contains barriers: every thread must call it.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  constexpr int NW = NT / 64;
+  int incl = wave_incl_scan(v, lane);
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < NW; ++i) { int t = tmp[i]; tmp[i] = run; run += t; }
+    tmp[NW] = run;
+  }
+  __syncthreads();
+  int res = tmp[w] + incl - v;
+  *total = tmp[NW];
+  __syncthreads();
+  return res;
+}
+
+// Order-preserving 32-bit key of a float score: larger score -> larger key.
+// -0 ranks as +0; NaN ranks as -inf.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  if (f != f) f = -__builtin_inff();
+  if (f == 0.0f) f = 0.0f;
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace sa

@@ -1,0 +1,124 @@
+// sa_internal.h -- host-side plumbing shared by the C ABI and the kernel
+// launchers: workspace layouts, split plans and launcher declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sa.h"
+
+namespace sa {
+
+constexpr int kTargetWGs = 1024;      // 256 CUs x 4: enough workgroups to fill the chip
+constexpr int kMaxNbDecode = 8192;    // LDS-resident keys of one decode selection row (32 KiB)
+constexpr int kMaxNbPrefill = 8192;   // LDS-resident keys of one prefill selection row
+constexpr int kValuTokensPerWG = 1024;
+constexpr int kThrSeg = 128;          // tokens per threshold staging segment
+
+inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Number of splits per (b, kv head) for the block-mode split-K decode.  The
+// kernel divides the actual selected-block count evenly over these splits.
+// (The float32 kernel keeps a split's tokens in LDS, so a split never spans
+// more than kValuTokensPerWG tokens; the same plan serves both dtypes.)
+inline int decode_block_splits(int BH, int idx_stride, int block) {
+  int S = cdiv(kTargetWGs, BH);
+  if (S > idx_stride) S = idx_stride;
+  const int need = cdiv(long(idx_stride) * block, kValuTokensPerWG);
+  if (S < need) S = need;
+  if (S < 1) S = 1;
+  return S;
+}
+// Splits per (b, query head) for token-mode decode.
+inline int decode_token_splits(int BHq, int idx_stride) {
+  int S = cdiv(kTargetWGs, BHq);
+  int smax = cdiv(idx_stride, 16);
+  if (S > smax) S = smax;
+  int need = cdiv(idx_stride, kValuTokensPerWG);
+  if (S < need) S = need;
+  if (S < 1) S = 1;
+  return S;
+}
+
+// Workspace of the split-K decode: partial accumulators and (m, l) pairs.
+struct DecodeWs {
+  size_t acc_off, ml_off, bytes;
+  int S;
+};
+inline DecodeWs decode_ws(int B, int Hq, int Hkv, int D, int mode, int block,
+                          int idx_stride) {
+  DecodeWs w{};
+  w.S = mode == SA_IDX_BLOCKS ? decode_block_splits(B * Hkv, idx_stride, block)
+                              : decode_token_splits(B * Hq, idx_stride);
+  size_t parts = size_t(B) * Hq * w.S;
+  w.acc_off = 0;
+  w.ml_off = align256(parts * D * sizeof(float));
+  w.bytes = w.ml_off + align256(parts * 2 * sizeof(float));
+  return w;
+}
+
+// Workspace of the top-k selection: block scores (decode) or pooled query
+// blocks (prefill).
+inline size_t select_ws_bytes(int B, int Hkv, int Lq, int D, int q_block, int nb) {
+  if (Lq <= 1) return align256(size_t(B) * Hkv * nb * sizeof(float));
+  int M = cdiv(Lq, q_block);
+  return align256(size_t(B) * Hkv * M * D * sizeof(float));
+}
+
+// Workspace of the threshold selection: per 128-token segment staging of the
+// kept (index, score) pairs and their counts.
+struct ThrWs {
+  size_t idx_off, val_off, cnt_off, bytes;
+  int nseg;
+};
+inline ThrWs threshold_ws(int B, int Hq, int N) {
+  ThrWs w{};
+  w.nseg = cdiv(N, kThrSeg);
+  size_t slots = size_t(B) * Hq * w.nseg * kThrSeg;
+  w.idx_off = 0;
+  w.val_off = align256(slots * sizeof(int32_t));
+  w.cnt_off = w.val_off + align256(slots * sizeof(float));
+  w.bytes = w.cnt_off + align256(size_t(B) * Hq * w.nseg * sizeof(int32_t));
+  return w;
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_sketch(const void* X, int dtype, int B, int H, int N, int D,
+                         int block, int head_pool, int blk_begin, int blk_end,
+                         float* out, hipStream_t st);
+hipError_t launch_block_score(const void* Q, int dtype, int B, int Hq, int Hkv,
+                              int D, const float* sk, int nb, float scale,
+                              float* scores, hipStream_t st);
+hipError_t launch_topk_decode(const float* scores, int rows, int nb, int k,
+                              unsigned flags, int32_t* idx, int32_t* count,
+                              hipStream_t st);
+hipError_t launch_prefill_select(const float* qbar, const float* ksk, int BH,
+                                 int M, int nb, int D, int k, unsigned flags,
+                                 float scale, int32_t* idx, int32_t* count,
+                                 float* score, hipStream_t st);
+hipError_t launch_decode_blocks(const void* Q, const void* K, const void* V,
+                                int dtype, int B, int Hq, int Hkv, int N, int D,
+                                float scale, int block, const int32_t* idx,
+                                const int32_t* count, int idx_stride,
+                                const DecodeWs& w, void* ws, hipStream_t st);
+hipError_t launch_decode_tokens(const void* Q, const void* K, const void* V,
+                                int dtype, int B, int Hq, int Hkv, int N, int D,
+                                float scale, const int32_t* idx,
+                                const int32_t* count, int idx_stride,
+                                const float* score, const DecodeWs& w, void* ws,
+                                hipStream_t st);
+hipError_t launch_merge(const DecodeWs& w, const void* ws, int BHq, int D,
+                        void* O, int out_dtype, float* lse, hipStream_t st);
+hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
+                            int Hq, int Hkv, int N, int D, const float* tau,
+                            float scale, int cap, int32_t* idx, float* score,
+                            int32_t* count, const ThrWs& w, void* ws,
+                            hipStream_t st);
+hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B,
+                          int Hq, int Hkv, int L, int D, float scale, int block,
+                          const int32_t* idx, const int32_t* count, int kmax,
+                          void* O, int out_dtype, float* lse, hipStream_t st);
+
+}  // namespace sa
