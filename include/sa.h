@@ -37,9 +37,12 @@
  *     The library allocates nothing and keeps no state between calls apart
  *     from a cached device-property query.
  *   - `ws` is a caller-provided device workspace of at least
- *     sa_workspace_bytes(...) bytes.  It must be zero-filled once when it is
- *     allocated; every call leaves its counters at zero again.  Two calls that
- *     run concurrently must not share a workspace.
+ *     sa_workspace_bytes(...) bytes.  It holds partial results plus arrival
+ *     counters and histograms that must read zero when a call starts: zero-fill
+ *     it once when it is allocated; every completed call leaves that state at
+ *     zero again, so the same workspace can serve later calls of the same
+ *     operation and shapes.  Calls of another operation or shape, or calls
+ *     that run concurrently, need their own workspace (or a re-zeroed one).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on it and returns; nothing synchronises the host.
  *   - dtype codes: SA_F32 (float) or SA_BF16 (raw bfloat16 bits, uint16).

@@ -303,3 +303,41 @@ def test_prefill_all_blocks_is_dense_causal():
     assert max_abs(np.stack([got[b, h, t] for b, h, t in rows]), Od) <= 2e-3
     gl = lse.cpu().numpy()
     assert max_abs(np.array([gl[b, h, t] for b, h, t in rows]), lsed) <= 1e-4
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """The fused step captured in a HIP graph gives the eager result on every
+    replay (its arrival counters and histograms reset themselves in-kernel)."""
+    wl, inp, q, K, V = _decode_case("long_decode_bf16", {"N": 32768 + 64})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    ws = torch.zeros(sa.workspace_bytes(sa.SA_OP_DECODE_STEP, wl.B, wl.Hq, wl.Hkv, wl.N, wl.D,
+                                        wl.block, wl.k), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(wl.B, wl.Hkv, wl.k, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(wl.B, wl.Hkv, dtype=torch.int32, device="cuda")
+    O = torch.empty(wl.B, wl.Hq, wl.D, dtype=torch.float32, device="cuda")
+    lse = torch.empty(wl.B, wl.Hq, dtype=torch.float32, device="cuda")
+
+    def step():
+        sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block, update_block=wl.nb - 1,
+                          idx=idx, count=cnt, O=O, lse=lse, ws=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.clone(), O.clone(), lse.clone())
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        idx.zero_()
+        O.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]) and torch.equal(O, ref[1]) and torch.equal(lse, ref[2]), rep
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(O, ref[1])

@@ -122,13 +122,19 @@ def _stream(stream=None) -> int:
 _ws_cache = {}
 
 
-def workspace(nbytes: int, device) -> torch.Tensor:
-    """A zero-filled device workspace of at least nbytes (cached per device)."""
-    key = torch.device(device)
-    ws = _ws_cache.get(key)
+def workspace(nbytes: int, device, key=()) -> torch.Tensor:
+    """A zero-filled device workspace of at least nbytes, one per (device, key).
+
+    The library keeps arrival counters and histograms in the workspace and
+    leaves them at zero after every call, so a workspace may be reused by
+    later calls of the same operation and shape (the key); a different layout
+    gets its own buffer.
+    """
+    k = (torch.device(device), tuple(key))
+    ws = _ws_cache.get(k)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=key)
-        _ws_cache[key] = ws
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=k[0])
+        _ws_cache[k] = ws
     return ws
 
 
@@ -177,7 +183,7 @@ def sa_select_topk(Q: torch.Tensor, ksketch: torch.Tensor, k: int,
         score = torch.empty(*rows, nb, dtype=torch.float32, device=Q.device)
     need = workspace_bytes(SA_OP_SELECT_TOPK, B, Hq, Hkv, Lq, D, q_block, nb)
     if ws is None:
-        ws = workspace(need, Q.device)
+        ws = workspace(need, Q.device, ("select", B, Hq, Hkv, Lq, D, q_block, nb))
     _check(_select_topk(_ptr(Q), _dt(Q), B, Hq, Hkv, Lq, D, q_block, _ptr(ksketch), nb, k, flags,
                         scale, _ptr(idx), _ptr(count), _ptr(score), _ptr(ws), ws.numel(),
                         _stream(stream)), "sa_select_topk")
@@ -204,7 +210,7 @@ def sa_select_threshold(Q: torch.Tensor, K: torch.Tensor, tau: torch.Tensor, cap
         count = torch.empty(B, Hq, dtype=torch.int32, device=dev)
     need = workspace_bytes(SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0, cap)
     if ws is None:
-        ws = workspace(need, dev)
+        ws = workspace(need, dev, ("threshold", B, Hq, Hkv, N, D, cap))
     _check(_select_threshold(_ptr(Q), _ptr(K), _dt(Q), B, Hq, Hkv, N, D, _ptr(tau), scale, cap,
                              _ptr(idx), _ptr(score), _ptr(count), _ptr(ws), ws.numel(),
                              _stream(stream)), "sa_select_threshold")
@@ -228,10 +234,10 @@ def sa_sparse_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: tor
     if lse is None and want_lse:
         lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     stride = idx.shape[-1]
-    need = workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D,
-                           block if mode == SA_IDX_BLOCKS else 0, stride)
+    blk = block if mode == SA_IDX_BLOCKS else 0
+    need = workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, blk, stride)
     if ws is None:
-        ws = workspace(need, dev)
+        ws = workspace(need, dev, ("decode", B, Hq, Hkv, N, D, blk, stride))
     _check(_sparse_decode(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, scale, mode, block,
                           _ptr(idx), _ptr(count), stride, _ptr(score), _ptr(O), _dt(O), _ptr(lse),
                           _ptr(ws), ws.numel(), _stream(stream)), "sa_sparse_decode")
@@ -277,7 +283,7 @@ def sa_decode_step(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksketch: t
         lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     need = workspace_bytes(SA_OP_DECODE_STEP, B, Hq, Hkv, N, D, block, k)
     if ws is None:
-        ws = workspace(need, dev)
+        ws = workspace(need, dev, ("step", B, Hq, Hkv, N, D, block, k))
     _check(_decode_step(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, block,
                         _ptr(ksketch), update_block, k, scale, _ptr(idx), _ptr(count),
                         _ptr(score), _ptr(O), _dt(O), _ptr(lse), _ptr(ws), ws.numel(),

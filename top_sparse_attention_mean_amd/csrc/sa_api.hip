@@ -30,7 +30,6 @@ sa_status hip_status(hipError_t e, const char* where) {
 
 bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dtype_ok(int dt) { return dt == SA_F32 || dt == SA_BF16; }
-int elem_bytes(int dt) { return dt == SA_BF16 ? 2 : 4; }
 float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf(float(D)); }
 bool pow2_le8(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
@@ -94,11 +93,10 @@ sa_status v_select(const void* Q, int dtype, int B, int Hq, int Hkv, int Lq, int
     REQ(nb == 1 || k >= nF, "k (%d) smaller than the %d forced blocks", k, nF);
   }
   const size_t need = select_ws_bytes(B, Hkv, (flags & SA_CAUSAL) ? Lq : 1, D, q_block, nb);
-  const bool uses_ws = (flags & SA_CAUSAL) || score == nullptr;
-  if (uses_ws) {
-    if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-    PTR(ws);
-  }
+  if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  PTR(ws);
+  const long grid = long(B) * Hkv * select_plan(B * Hkv, nb).C + long(B) * Hkv;
+  REQ(grid < (1L << 31), "too many scoring workgroups");
   return SA_OK;
 }
 
@@ -126,8 +124,6 @@ sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B
       SUP(block == 64 || block == 128, "bf16 block-mode decode needs block 64 or 128");
       SUP(pow2_le8(G), "bf16 block-mode decode needs g in {1, 2, 4, 8} (got %d)", G);
     } else {
-      SUP(block <= kValuTokensPerWG && kValuTokensPerWG % block == 0,
-          "float32 block-mode decode needs block dividing %d", kValuTokensPerWG);
       SUP(G <= 8, "float32 decode needs g <= 8 (got %d)", G);
     }
   } else if (mode == SA_IDX_TOKENS) {
@@ -211,10 +207,12 @@ sa_status sa_select_topk(const void* Q, int dtype, int B, int Hq, int Hkv, int L
                                             count, score, st),
                       "sa_select_topk (prefill)");
   }
-  float* scores = score ? score : static_cast<float*>(ws);
-  hipError_t e = launch_block_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, sc, scores, st);
+  const SelectWs w = select_ws(B, Hkv, 1, D, 1, nb);
+  float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + w.score_off);
+  hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, const_cast<float*>(ksketch), nb, nullptr,
+                              0, 1, -1, sc, scores, st);
   if (e != hipSuccess) return hip_status(e, "sa_select_topk (score)");
-  return hip_status(launch_topk_decode(scores, B * Hkv, nb, k, flags, idx, count, st),
+  return hip_status(launch_select_rows(scores, B * Hkv, nb, k, flags, idx, count, st),
                     "sa_select_topk (select)");
 }
 
@@ -258,12 +256,10 @@ sa_status sa_sparse_decode(const void* Q, const void* K, const void* V, int dtyp
   const DecodeWs w = decode_ws(B, Hq, Hkv, D, mode, block, idx_stride);
   hipError_t e = mode == SA_IDX_BLOCKS
                      ? launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx,
-                                            count, idx_stride, w, ws, st)
+                                            count, idx_stride, w, ws, O, out_dtype, lse, st)
                      : launch_decode_tokens(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, idx, count,
-                                            idx_stride, score, w, ws, st);
-  if (e != hipSuccess) return hip_status(e, "sa_sparse_decode (partials)");
-  return hip_status(launch_merge(w, ws, B * Hq, D, O, out_dtype, lse, st),
-                    "sa_sparse_decode (merge)");
+                                            idx_stride, score, w, ws, O, out_dtype, lse, st);
+  return hip_status(e, "sa_sparse_decode");
 }
 
 sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
@@ -316,20 +312,24 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V, int dtype,
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float sc = eff_scale(scale, D);
-  hipError_t e = hipSuccess;
-  if (update_block >= 0) {
-    e = launch_sketch(K, dtype, B, Hkv, N, D, block, 1, update_block, update_block + 1, ksketch, st);
-    if (e != hipSuccess) return hip_status(e, "sa_decode_step (sketch)");
-  }
-  float* scores = score ? score : static_cast<float*>(ws);
-  e = launch_block_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, sc, scores, st);
+  const SelectWs sw = select_ws(B, Hkv, 1, D, 1, nb);
+  float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + sw.score_off);
+  const unsigned flags = SA_FORCE_SINK | SA_FORCE_LOCAL;
+  hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, K, N, block, update_block, sc,
+                              scores, st);
   if (e != hipSuccess) return hip_status(e, "sa_decode_step (score)");
-  e = launch_topk_decode(scores, B * Hkv, nb, k, SA_FORCE_SINK | SA_FORCE_LOCAL, idx, count, st);
-  if (e != hipSuccess) return hip_status(e, "sa_decode_step (select)");
   const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
-  e = launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count, k, w, dws, st);
-  if (e != hipSuccess) return hip_status(e, "sa_decode_step (partials)");
-  return hip_status(launch_merge(w, dws, B * Hq, D, O, out_dtype, lse, st), "sa_decode_step (merge)");
+  if (dtype == SA_BF16 && D == 128 && k <= kMaxKFused) {
+    return hip_status(launch_decode_select_blocks(Q, K, V, B, Hq, Hkv, N, D, sc, block, scores, nb,
+                                                  k, flags, idx, count, w, dws, O, out_dtype, lse,
+                                                  st),
+                      "sa_decode_step (select + decode)");
+  }
+  e = launch_select_rows(scores, B * Hkv, nb, k, flags, idx, count, st);
+  if (e != hipSuccess) return hip_status(e, "sa_decode_step (select)");
+  return hip_status(launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count,
+                                         k, w, dws, O, out_dtype, lse, st),
+                    "sa_decode_step (decode)");
 }
 
 }  // extern "C"

@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/sa.h"
+#include "sa.h"
 
 namespace sa {
 
@@ -19,52 +19,72 @@ constexpr int kThrSeg = 128;          // tokens per threshold staging segment
 inline int cdiv(long a, long b) { return int((a + b - 1) / b); }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Number of splits per (b, kv head) for the block-mode split-K decode.  The
-// kernel divides the actual selected-block count evenly over these splits.
-// (The float32 kernel keeps a split's tokens in LDS, so a split never spans
-// more than kValuTokensPerWG tokens; the same plan serves both dtypes.)
-inline int decode_block_splits(int BH, int idx_stride, int block) {
-  int S = cdiv(kTargetWGs, BH);
+constexpr int kMaxSplits = 128;       // partials merged by one workgroup
+constexpr int kMaxKFused = 1024;      // k of the decode step that selects inside the decode kernel
+constexpr int kTokensPerSplit = 256;  // block-mode split target: 16 tiles of 16 tokens
+constexpr int kCounterStride = 64;    // arrival counters 256 B apart (own cache lines)
+constexpr int kScoreRows = 64;        // sketch rows per scoring workgroup
+
+// Number of splits per (b, kv head) for the block-mode split-K decode: about
+// 256 selected tokens per workgroup (4 waves x 4 tiles of 16 tokens, all loads
+// in flight at once).  The kernel divides the actual selected-block count
+// evenly over the splits; the last split to finish merges them.
+inline int decode_block_splits(int idx_stride, int block) {
+  int S = cdiv(long(idx_stride) * block, kTokensPerSplit);
   if (S > idx_stride) S = idx_stride;
-  const int need = cdiv(long(idx_stride) * block, kValuTokensPerWG);
-  if (S < need) S = need;
+  if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
   return S;
 }
 // Splits per (b, query head) for token-mode decode.
 inline int decode_token_splits(int BHq, int idx_stride) {
   int S = cdiv(kTargetWGs, BHq);
-  int smax = cdiv(idx_stride, 16);
+  const int smax = cdiv(idx_stride, 16);
   if (S > smax) S = smax;
-  int need = cdiv(idx_stride, kValuTokensPerWG);
-  if (S < need) S = need;
+  if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
   return S;
 }
 
-// Workspace of the split-K decode: partial accumulators and (m, l) pairs.
+// Workspace of the split-K decode: partial accumulators, (m, l) pairs and one
+// arrival counter per head group (zero between calls).
 struct DecodeWs {
-  size_t acc_off, ml_off, bytes;
+  size_t acc_off, ml_off, cnt_off, bytes;
   int S;
 };
 inline DecodeWs decode_ws(int B, int Hq, int Hkv, int D, int mode, int block,
                           int idx_stride) {
   DecodeWs w{};
-  w.S = mode == SA_IDX_BLOCKS ? decode_block_splits(B * Hkv, idx_stride, block)
+  w.S = mode == SA_IDX_BLOCKS ? decode_block_splits(idx_stride, block)
                               : decode_token_splits(B * Hq, idx_stride);
-  size_t parts = size_t(B) * Hq * w.S;
+  const size_t parts = size_t(B) * Hq * w.S;
   w.acc_off = 0;
   w.ml_off = align256(parts * D * sizeof(float));
-  w.bytes = w.ml_off + align256(parts * 2 * sizeof(float));
+  w.cnt_off = w.ml_off + align256(parts * 2 * sizeof(float));
+  w.bytes = w.cnt_off + align256(size_t(B) * Hq * kCounterStride * sizeof(uint32_t));
+  (void)Hkv;
   return w;
 }
 
-// Workspace of the top-k selection: block scores (decode) or pooled query
-// blocks (prefill).
+// Workspace of the top-k selection.  Decode: the block scores.
+// Prefill: the pooled query blocks.
+struct SelectWs {
+  size_t score_off, bytes;
+};
+inline SelectWs select_ws(int B, int Hkv, int Lq, int D, int q_block, int nb) {
+  SelectWs w{};
+  if (Lq <= 1) {
+    const size_t BH = size_t(B) * Hkv;
+    w.score_off = 0;
+    w.bytes = align256(BH * nb * sizeof(float));
+  } else {
+    const int M = cdiv(Lq, q_block);
+    w.bytes = align256(size_t(B) * Hkv * M * D * sizeof(float));
+  }
+  return w;
+}
 inline size_t select_ws_bytes(int B, int Hkv, int Lq, int D, int q_block, int nb) {
-  if (Lq <= 1) return align256(size_t(B) * Hkv * nb * sizeof(float));
-  int M = cdiv(Lq, q_block);
-  return align256(size_t(B) * Hkv * M * D * sizeof(float));
+  return select_ws(B, Hkv, Lq, D, q_block, nb).bytes;
 }
 
 // Workspace of the threshold selection: per 128-token segment staging of the
@@ -85,15 +105,28 @@ inline ThrWs threshold_ws(int B, int Hq, int N) {
 }
 
 // ---------------------------------------------------------------- launchers
+struct SelectPlan {
+  int C;    // scoring workgroups per (b, kv head)
+  int RPW;  // sketch rows per scoring workgroup
+};
+SelectPlan select_plan(int BH, int nb);
+
 hipError_t launch_sketch(const void* X, int dtype, int B, int H, int N, int D,
                          int block, int head_pool, int blk_begin, int blk_end,
                          float* out, hipStream_t st);
-hipError_t launch_block_score(const void* Q, int dtype, int B, int Hq, int Hkv,
-                              int D, const float* sk, int nb, float scale,
-                              float* scores, hipStream_t st);
-hipError_t launch_topk_decode(const float* scores, int rows, int nb, int k,
-                              unsigned flags, int32_t* idx, int32_t* count,
-                              hipStream_t st);
+// Decode block scores (upd >= 0 also rebuilds that block's sketch from K).
+hipError_t launch_score(const void* Q, int dtype, int B, int Hq, int Hkv, int D, float* sk,
+                        int nb, const void* K, int N, int block, int upd, float scale,
+                        float* scores, hipStream_t st);
+// Top-k per score row (decode rules: forced sink/local, ties to lower index).
+hipError_t launch_select_rows(const float* scores, int rows, int nb, int k, unsigned flags,
+                              int32_t* idx, int32_t* count, hipStream_t st);
+// bf16 split-K decode whose workgroups select their blocks from the scores.
+hipError_t launch_decode_select_blocks(const void* Q, const void* K, const void* V, int B, int Hq,
+                                       int Hkv, int N, int D, float scale, int block,
+                                       const float* scores, int nb, int k, unsigned flags,
+                                       int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
+                                       void* O, int out_dtype, float* lse, hipStream_t st);
 hipError_t launch_prefill_select(const float* qbar, const float* ksk, int BH,
                                  int M, int nb, int D, int k, unsigned flags,
                                  float scale, int32_t* idx, int32_t* count,
@@ -102,15 +135,14 @@ hipError_t launch_decode_blocks(const void* Q, const void* K, const void* V,
                                 int dtype, int B, int Hq, int Hkv, int N, int D,
                                 float scale, int block, const int32_t* idx,
                                 const int32_t* count, int idx_stride,
-                                const DecodeWs& w, void* ws, hipStream_t st);
+                                const DecodeWs& w, void* ws, void* O, int out_dtype,
+                                float* lse, hipStream_t st);
 hipError_t launch_decode_tokens(const void* Q, const void* K, const void* V,
                                 int dtype, int B, int Hq, int Hkv, int N, int D,
                                 float scale, const int32_t* idx,
                                 const int32_t* count, int idx_stride,
                                 const float* score, const DecodeWs& w, void* ws,
-                                hipStream_t st);
-hipError_t launch_merge(const DecodeWs& w, const void* ws, int BHq, int D,
-                        void* O, int out_dtype, float* lse, hipStream_t st);
+                                void* O, int out_dtype, float* lse, hipStream_t st);
 hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
                             int Hq, int Hkv, int N, int D, const float* tau,
                             float scale, int cap, int32_t* idx, float* score,
