@@ -82,61 +82,63 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* f
 // Merge the S partials of query heads h0 .. h0+nh-1 (rows of [B*Hq]):
 // M = max m_s, L = sum l_s 2^(m_s - M), O = sum acc_s 2^(m_s - M) / L,
 // lse = (M + log2 L) ln 2 (scores are kept in log2 units).
+// Thread t owns head t / (D/4) and 4 consecutive columns (nh * D / 4 <= 256).
+// Its first kMergeChunk partial loads are issued before the (m, l) pairs are
+// staged in LDS, so both round trips overlap; every thread then forms its
+// head's weights itself (no serial per-head stage, one barrier).
+constexpr int kMergeChunk = 16;
+
 template <int D>
-__device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv, float* hm,
-                           float* hl) {
+__device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv) {
+  constexpr int CH = kMergeChunk;
   const int S = a.S, tid = threadIdx.x;
-  for (int i = tid; i < nh * S; i += 256) {   // (m, l) of every partial -> LDS
+  const bool act = tid < nh * (D / 4);
+  const int h = act ? tid / (D / 4) : 0, d0 = (tid % (D / 4)) * 4;
+  const float* pa = a.pacc + size_t(h0 + h) * S * D + d0;
+  u32x4 v[CH];
+#pragma unroll
+  for (int u = 0; u < CH; ++u)
+    if (act && u < S) v[u] = ld16(pa + size_t(u) * D);
+  for (int i = tid; i < nh * S; i += 256) {
     const u32x2 ml = ld8(a.pml + 2 * (size_t(h0) * S + i));
     w[i] = __uint_as_float(ml[0]);
     lv[i] = __uint_as_float(ml[1]);
   }
   __syncthreads();
-  if (tid < nh) {
-    float M = -__builtin_inff();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, w[tid * S + s]);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float f = M == -__builtin_inff() ? 0.f : exp2_fast(w[tid * S + s] - M);
-      L += lv[tid * S + s] * f;
-      w[tid * S + s] = f;
-    }
-    hm[tid] = M;
-    hl[tid] = L;
-  }
-  __syncthreads();
-  // one head and 4 consecutive columns per thread; 8 splits in flight
-  for (int o4 = tid; o4 < nh * D / 4; o4 += 256) {
-    const int h = o4 / (D / 4), d0 = (o4 % (D / 4)) * 4;
-    const float* pa = a.pacc + size_t(h0 + h) * S * D + d0;
-    const float* wh = w + h * S;
-    f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < S; s0 += 8) {
-      u32x4 v[8];
+  if (!act) return;
+  const float* wh = w + h * S;
+  const float* lh = lv + h * S;
+  float M = -__builtin_inff();
+  for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
+  float L = 0.f;
+  f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (M != -__builtin_inff()) {
+    for (int s0 = 0; s0 < S; s0 += CH) {
+      if (s0 > 0) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < S) v[u] = ld16(pa + size_t(s0 + u) * D);
+        for (int u = 0; u < CH; ++u)
+          if (s0 + u < S) v[u] = ld16(pa + size_t(s0 + u) * D);
+      }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < CH; ++u) {
         if (s0 + u < S) {
-          const float f = wh[s0 + u];
+          const float f = exp2_fast(wh[s0 + u] - M);
+          L += lh[s0 + u] * f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) A[q] += __uint_as_float(v[u][q]) * f;
         }
       }
     }
-    const float L = hl[h];
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const size_t oi = size_t(h0 + h) * D + d0;
-    if (a.out_bf16) {
-      const u32x2 pk = u32x2{pack_bf16x2(A[0] * inv, A[1] * inv), pack_bf16x2(A[2] * inv, A[3] * inv)};
-      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.O) + oi) = pk;
-    } else {
-      *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + oi) = f32x4{A[0] * inv, A[1] * inv, A[2] * inv, A[3] * inv};
-    }
   }
-  if (a.lse && tid < nh)
-    a.lse[h0 + tid] = hl[tid] > 0.f ? (hm[tid] + __log2f(hl[tid])) * kLn2 : -__builtin_inff();
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const size_t oi = size_t(h0 + h) * D + d0;
+  if (a.out_bf16) {
+    const u32x2 pk = u32x2{pack_bf16x2(A[0] * inv, A[1] * inv), pack_bf16x2(A[2] * inv, A[3] * inv)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.O) + oi) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + oi) = f32x4{A[0] * inv, A[1] * inv, A[2] * inv, A[3] * inv};
+  }
+  if (a.lse && d0 == 0) a.lse[h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
 }
 
 // ---------------------------------------------------------------- bf16 MFMA
@@ -152,7 +154,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   __shared__ float s_acc[4][2 * G][D + 4];
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ float s_w[G * kMaxSplits], s_lv[G * kMaxSplits];
-  __shared__ float s_hm[G], s_hl[G];
   __shared__ int s_flag;
 
   const int BH = a.B * a.Hkv, N = a.N;
@@ -171,14 +172,13 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   const int32_t* ib;
   if constexpr (SEL) {
     // every split selects its kv head's blocks itself from the score row
-    extern __shared__ __attribute__((aligned(16))) int dyn_i[];   // tmp[k + 8], list[k]
-    __shared__ SelectLds S;
-    int* tmp = dyn_i;
-    int* list = dyn_i + ((a.k + 8 + 3) & ~3);
+    extern __shared__ __attribute__((aligned(16))) int dyn_i[];   // list[k]
     constexpr int KPT = SELKPT > 0 ? SELKPT : 1;
+    __shared__ SelectLdsT<256, KPT> S;
+    int* list = dyn_i;
     uint32_t kr[KPT];
     load_keys_reg<256, KPT>(a.sel_scores + size_t(bh) * a.nb, a.nb, kr);
-    cnt = select_decode_row<256, KPT>(kr, a.nb, a.k, a.flags, tmp, list, S);
+    cnt = select_decode_row<256, KPT>(kr, a.nb, a.k, a.flags, list, S);
     ib = list;
     if (s == 0) {
       int32_t* orow = a.sel_idx + size_t(bh) * a.k;
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
     if (d == 0) { a.pml[2 * pi] = M; a.pml[2 * pi + 1] = Ls; }
   }
   if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
-  merge_tail<D>(a, h0, G, s_w, s_lv, s_hm, s_hl);
+  merge_tail<D>(a, h0, G, s_w, s_lv);
 }
 
 // ---------------------------------------------------------------- float32 VALU
@@ -345,7 +345,6 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
   __shared__ int stok[CH];
   __shared__ float red[8][4];
   __shared__ float s_w[8 * kMaxSplits], s_lv[8 * kMaxSplits];
-  __shared__ float s_hm[8], s_hl[8];
   __shared__ int s_flag;
 
   const int BH = a.B * a.Hkv, G = a.G, N = a.N, block = a.block;
@@ -449,7 +448,7 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
     }
   }
   if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
-  merge_tail<D>(a, h0, G, s_w, s_lv, s_hm, s_hl);
+  merge_tail<D>(a, h0, G, s_w, s_lv);
 }
 
 // ---------------------------------------------------------------- token lists
@@ -463,7 +462,6 @@ __global__ __launch_bounds__(256) void k_decode_tokens(DecodeArgs a) {
   __shared__ float red[4];
   __shared__ float racc[16][D + 4];
   __shared__ float s_w[kMaxSplits], s_lv[kMaxSplits];
-  __shared__ float s_hm[1], s_hl[1];
   __shared__ int s_flag;
 
   const int BHq = a.B * a.Hq, N = a.N;
@@ -580,7 +578,7 @@ __global__ __launch_bounds__(256) void k_decode_tokens(DecodeArgs a) {
     if (d == 0) { a.pml[2 * pi] = m_run; a.pml[2 * pi + 1] = l_run; }
   }
   if (!arrive_last(&a.counter[bhq * kCounterStride], a.S, &s_flag)) return;
-  merge_tail<D>(a, bhq, 1, s_w, s_lv, s_hm, s_hl);
+  merge_tail<D>(a, bhq, 1, s_w, s_lv);
 }
 
 // ---------------------------------------------------------------- launchers
@@ -643,7 +641,7 @@ hipError_t launch_decode_select_blocks(const void* Q, const void* K, const void*
                            ws, O, out_dtype, lse);
   a.sel_scores = scores; a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
   const dim3 g(static_cast<unsigned>(long(B) * Hkv * w.S));
-  const size_t lds = (size_t((k + 8 + 3) & ~3) + size_t(k)) * sizeof(int);
+  const size_t lds = size_t(k) * sizeof(int);
   (void)D;   // the selecting variant is compiled for D = 128
   const bool small = nb <= 4096;
   if (block == 64) {

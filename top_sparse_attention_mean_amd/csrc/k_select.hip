@@ -27,6 +27,8 @@
 //                   scores pooled query block i against key blocks [1, i-1]
 //                   and selects with the same core (no cross-workgroup
 //                   dependency, so scoring and selection fuse).
+#include <type_traits>
+
 #include "sa_device.h"
 #include "sa_internal.h"
 #include "sa_select_core.h"
@@ -49,6 +51,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   constexpr int NT = 256;
   constexpr int LPR = D / 4, RPI = 64 / LPR;
   constexpr int CPT = 8, TPR = D / CPT, RPP = NT / TPR;
+  constexpr bool BF = sizeof(T) == 2;
   __shared__ float qbar[D];
   __shared__ float red[RPP][D + 4];
 
@@ -58,66 +61,126 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   const int bh = is_upd ? int(blockIdx.x) - nscore : int(blockIdx.x) % a.BH;
   const int c = is_upd ? 0 : int(blockIdx.x) / a.BH;
   const int b = bh / a.Hkv, kh = bh % a.Hkv;
-  const int nb = a.nb;
+  const int nb = a.nb, G = a.G;
+  const T* Qg = static_cast<const T*>(a.Q) + (size_t(b) * a.Hq + kh * G) * D;
+  float* srow = a.scores + size_t(bh) * nb;
 
-  // scoring workgroups issue their sketch loads before anything waits on Q
-  constexpr int RPWV = kScoreRows / 4;          // rows per wave
-  constexpr int NLD = RPWV / RPI;               // 16-byte loads per lane
-  const int sub = lane / LPR, lc = lane % LPR;
-  const int rw = c * kScoreRows + wave * RPWV;
-  u32x4 w[NLD];
   if (!is_upd) {
+    // Each lane forms the 4 group-mean query columns it multiplies itself.  Its
+    // query loads go out first and the sketch rows right after, so waiting for
+    // the query does not wait for the rows, and each row's dot product starts
+    // when that row arrives: no LDS and no barrier on this path.
+    constexpr int RPWV = kScoreRows / 4;        // rows per wave
+    constexpr int NLD = RPWV / RPI;             // 16-byte row loads per lane
+    const int sub = lane / LPR, lc = lane % LPR;
+    const int rw = c * kScoreRows + wave * RPWV;
+    using QV = typename std::conditional<BF, u32x2, u32x4>::type;
+    // loads are unconditional (clamped to head G-1) so none sits behind a branch
+    QV qv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const T* qp = Qg + size_t(min(u, G - 1)) * D + lc * 4;
+      if constexpr (BF) qv[u] = ld8(qp);
+      else qv[u] = ld16(qp);
+    }
+    __builtin_amdgcn_sched_barrier(0);          // keep the query loads ahead of the rows
+    u32x4 w[NLD];
     const float* base = a.sk + size_t(bh) * nb * D;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = min(rw + i * RPI + sub, nb - 1);
       w[i] = ld16(base + size_t(r) * D + lc * 4);
     }
-  }
-  if (tid < D) {
-    const T* Qp = static_cast<const T*>(a.Q);
-    float s = 0.f;
-    for (int h = 0; h < a.G; ++h) {
-      const size_t o = (size_t(b) * a.Hq + kh * a.G + h) * D + tid;
-      if constexpr (sizeof(T) == 2) s += bf16_to_f32(Qp[o]);
-      else s += Qp[o];
+    __builtin_amdgcn_sched_barrier(0);          // every load issued before the first wait
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (BF) {
+        q[0] += u < G ? bf16lo(qv[u][0]) : 0.f; q[1] += u < G ? bf16hi(qv[u][0]) : 0.f;
+        q[2] += u < G ? bf16lo(qv[u][1]) : 0.f; q[3] += u < G ? bf16hi(qv[u][1]) : 0.f;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] += u < G ? __uint_as_float(qv[u][e]) : 0.f;
+      }
     }
-    qbar[tid] = (s / float(a.G)) * a.scale;
-  }
-  __syncthreads();
-
-  float* srow = a.scores + size_t(bh) * nb;
-  if (!is_upd) {
-    const float q0 = qbar[lc * 4], q1 = qbar[lc * 4 + 1], q2 = qbar[lc * 4 + 2],
-                q3 = qbar[lc * 4 + 3];
+    for (int h = 8; h < G; ++h) {              // groups of more than 8 query heads
+      const T* qp = Qg + size_t(h) * D + lc * 4;
+      if constexpr (BF) {
+        const u32x2 v = ld8(qp);
+        q[0] += bf16lo(v[0]); q[1] += bf16hi(v[0]); q[2] += bf16lo(v[1]); q[3] += bf16hi(v[1]);
+      } else {
+        const u32x4 v = ld16(qp);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) q[e] += __uint_as_float(v[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) q[e] = (q[e] / float(G)) * a.scale;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = rw + i * RPI + sub;
-      float p = q0 * __uint_as_float(w[i][0]) + q1 * __uint_as_float(w[i][1]) +
-                q2 * __uint_as_float(w[i][2]) + q3 * __uint_as_float(w[i][3]);
+      float p = q[0] * __uint_as_float(w[i][0]) + q[1] * __uint_as_float(w[i][1]) +
+                q[2] * __uint_as_float(w[i][2]) + q[3] * __uint_as_float(w[i][3]);
 #pragma unroll
       for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
       if (r < nb && r != a.upd && lc == 0) srow[r] = p;
     }
     return;
   }
-  // rebuild the sketch of block upd from K, then score it
+  // Rebuild the sketch of block upd from K, then score it.  The query loads
+  // and every K row load of the block are in flight together.
   const int t0 = a.upd * a.block, nj = min(a.block, a.N - t0);
   const int tr = tid / TPR, tc = tid % TPR;
   float acc[CPT];
 #pragma unroll
   for (int q = 0; q < CPT; ++q) acc[q] = 0.f;
   const T* Kp = static_cast<const T*>(a.K) + (size_t(bh) * a.N + t0) * D + tc * CPT;
-  for (int r = tr; r < nj; r += RPP) {
-    if constexpr (sizeof(T) == 2) {
-      const u32x4 v = ld16(Kp + size_t(r) * D);
+  constexpr int NV = BF ? 1 : 2;               // 16-byte loads per row segment
+  constexpr int KB = BF ? 8 : 4;               // rows per thread in flight
+  auto k_batch = [&](int r0, bool with_q, T (&qs)[8]) {
+    u32x4 kv[KB][NV];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { acc[2 * q] += bf16lo(v[q]); acc[2 * q + 1] += bf16hi(v[q]); }
-    } else {
-      const u32x4 v0 = ld16(Kp + size_t(r) * D), v1 = ld16(Kp + size_t(r) * D + 4);
+    for (int u = 0; u < KB; ++u) {
+      const int r = min(r0 + u * RPP, nj - 1);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { acc[q] += __uint_as_float(v0[q]); acc[4 + q] += __uint_as_float(v1[q]); }
+      for (int v = 0; v < NV; ++v) kv[u][v] = ld16(Kp + size_t(r) * D + 4 * v);
     }
+    if (with_q) {
+      const int qd = tid < D ? tid : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qs[u] = Qg[size_t(min(u, G - 1)) * D + qd];
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (r0 + u * RPP < nj) {
+        if constexpr (BF) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { acc[2 * q] += bf16lo(kv[u][0][q]); acc[2 * q + 1] += bf16hi(kv[u][0][q]); }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { acc[q] += __uint_as_float(kv[u][0][q]); acc[4 + q] += __uint_as_float(kv[u][1][q]); }
+        }
+      }
+    }
+  };
+  T qs[8];
+  k_batch(tr, true, qs);                       // with the query loads
+  // blocks longer than KB * RPP rows take further batches
+  for (int r0 = tr + KB * RPP; r0 < nj; r0 += KB * RPP) k_batch(r0, false, qs);
+  if (tid < D) {
+    float sq = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float v;
+      if constexpr (BF) v = bf16_to_f32(qs[u]);
+      else v = qs[u];
+      sq += u < G ? v : 0.f;
+    }
+    for (int h = 8; h < G; ++h) {
+      if constexpr (BF) sq += bf16_to_f32(Qg[size_t(h) * D + tid]);
+      else sq += Qg[size_t(h) * D + tid];
+    }
+    qbar[tid] = (sq / float(G)) * a.scale;
   }
 #pragma unroll
   for (int q = 0; q < CPT; ++q) red[tr][tc * CPT + q] = acc[q];
@@ -175,25 +238,23 @@ __global__ __launch_bounds__(256) void k_select_rows(const float* __restrict__ s
                                                      int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ count) {
   constexpr int NT = 256;
-  extern __shared__ __attribute__((aligned(16))) int dyn_i[];   // tmp[k + 8]
-  __shared__ SelectLds S;
+  __shared__ SelectLdsT<NT, KPT> S;
   const int row = blockIdx.x;
   uint32_t kr[KPT];
   load_keys_reg<NT, KPT>(scores + size_t(row) * nb, nb, kr);
   int32_t* out = idx + size_t(row) * k;
-  const int n = select_decode_row<NT, KPT>(kr, nb, k, flags, dyn_i, out, S);
+  const int n = select_decode_row<NT, KPT>(kr, nb, k, flags, out, S);
   for (int j = n + threadIdx.x; j < k; j += NT) out[j] = -1;
   if (threadIdx.x == 0) count[row] = n;
 }
 
 hipError_t launch_select_rows(const float* scores, int rows, int nb, int k, unsigned flags,
                               int32_t* idx, int32_t* count, hipStream_t st) {
-  const size_t lds = (size_t(k) + 8) * sizeof(int);
   const dim3 g(static_cast<unsigned>(rows));
   switch (keys_per_thread_tier(nb)) {
-    case 2: k_select_rows<2><<<g, 256, lds, st>>>(scores, nb, k, flags, idx, count); break;
-    case 8: k_select_rows<8><<<g, 256, lds, st>>>(scores, nb, k, flags, idx, count); break;
-    default: k_select_rows<32><<<g, 256, lds, st>>>(scores, nb, k, flags, idx, count); break;
+    case 2: k_select_rows<2><<<g, 256, 0, st>>>(scores, nb, k, flags, idx, count); break;
+    case 8: k_select_rows<8><<<g, 256, 0, st>>>(scores, nb, k, flags, idx, count); break;
+    default: k_select_rows<32><<<g, 256, 0, st>>>(scores, nb, k, flags, idx, count); break;
   }
   return hipGetLastError();
 }
@@ -209,10 +270,8 @@ __global__ __launch_bounds__(256) void k_prefill_select(const float* __restrict_
                                                         float* __restrict__ score) {
   constexpr int NT = 256;
   constexpr int LPR = D / 4, RPI = 64 / LPR;
-  extern __shared__ __attribute__((aligned(16))) uint32_t dyn[];  // tmp[k + 8], keys[M]
-  __shared__ SelectLds S;
-  int* tmp = reinterpret_cast<int*>(dyn);
-  uint32_t* keys = dyn + ((k + 8 + 3) & ~3);
+  extern __shared__ __attribute__((aligned(16))) uint32_t keys[];   // keys[M]
+  __shared__ SelectLdsT<NT, KPT> S;
   const int i = blockIdx.x % M;
   const int bh = blockIdx.x / M;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -256,31 +315,35 @@ __global__ __launch_bounds__(256) void k_prefill_select(const float* __restrict_
       if (j < c0 || j >= c1) srow[j] = -__builtin_inff();
   }
   __syncthreads();
-  const int total = nF + nfree;
-  if (tid == 0) {
-    if (sink) out[0] = 0;
-    if (diag_forced) out[total - 1] = i;
-    count[size_t(bh) * M + i] = total;
-  }
-  for (int j = total + tid; j < k; j += NT) out[j] = -1;
-  int32_t* free_out = out + (sink ? 1 : 0);
-  if (nfree >= n) {
-    for (int j = tid; j < n; j += NT) free_out[j] = c0 + j;
-  } else if (nfree > 0) {
+  // kept set as a bitmap over blocks [0, i]: sink, diagonal, chosen candidates
+  const int W = (i + 32) >> 5;
+  sel_init(S, W);
+  if (nfree > 0 && nfree < n) {
     uint32_t kr[KPT];
 #pragma unroll
     for (int r = 0; r < KPT; ++r) {
       const int j = r * NT + tid;
       kr[r] = (j >= c0 && j < c1) ? keys[j] : 0u;
     }
-    select_core<NT, KPT>(kr, c0, c1, nfree, tmp, free_out, S);
+    sel_mark_top<NT, KPT>(kr, c0, c1, nfree, S);
+  } else {
+    __syncthreads();
+    if (nfree > 0)
+      for (int j = c0 + tid; j < c1; j += NT) sel_mark(S.bm, j);
   }
+  if (tid == 0) {
+    if (sink) sel_mark(S.bm, 0);
+    if (diag_forced) sel_mark(S.bm, i);
+  }
+  const int total = sel_bitmap_to_list(S, W, out, k);
+  for (int j = total + tid; j < k; j += NT) out[j] = -1;
+  if (tid == 0) count[size_t(bh) * M + i] = total;
 }
 
 hipError_t launch_prefill_select(const float* qbar, const float* ksk, int BH, int M, int nb,
                                  int D, int k, unsigned flags, float scale, int32_t* idx,
                                  int32_t* count, float* score, hipStream_t st) {
-  const size_t lds = (size_t((k + 8 + 3) & ~3) + size_t(max(M, 1))) * sizeof(uint32_t);
+  const size_t lds = size_t(max(M, 1)) * sizeof(uint32_t);
   const dim3 g(static_cast<unsigned>(long(BH) * M)), t(256);
 #define SA_PSEL(DD, KK) k_prefill_select<DD, KK><<<g, t, lds, st>>>(qbar, ksk, M, nb, k, flags, scale, idx, count, score)
   const int tier = keys_per_thread_tier(M);

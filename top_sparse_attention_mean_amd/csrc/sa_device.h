@@ -68,47 +68,74 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return perm(b, a, 0x07060302u); }
 
-// ------------------------------------------------------------ wave reductions
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// ------------------------------------------------------------ wave scans (DPP)
+// A 64-lane inclusive scan in six register-to-register steps, no LDS: row
+// shifts by 1, 2, 4 and 8 scan each 16-lane row, then row broadcasts add lane
+// 15 of rows 0 and 2 into rows 1 and 3, and lane 31 into rows 2 and 3 (GFX9
+// DPP row_shr / row_bcast controls).  A lane whose source falls outside its row
+// or whose row is masked off reads `id`, the identity of the operation.  The
+// whole wave must be converged.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t id, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(id), int(v), CTRL, ROWMASK, 0xf, false));
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t dpp_scan(uint32_t v, uint32_t id, Op op) {
+  v = op(v, dpp_u32<0x111>(id, v));
+  v = op(v, dpp_u32<0x112>(id, v));
+  v = op(v, dpp_u32<0x114>(id, v));
+  v = op(v, dpp_u32<0x118>(id, v));
+  v = op(v, dpp_u32<0x142, 0xa>(id, v));
+  v = op(v, dpp_u32<0x143, 0xc>(id, v));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+__device__ __forceinline__ uint32_t lane63(uint32_t v) {
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
 // Inclusive prefix sum over the 64 lanes (lane order).
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  return int(dpp_scan(uint32_t(v), 0u, [](uint32_t a, uint32_t b) { return a + b; }));
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) {
+  return lane63(dpp_scan(v, ~0u, [](uint32_t a, uint32_t b) { return a < b ? a : b; }));
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  return lane63(dpp_scan(v, 0u, [](uint32_t a, uint32_t b) { return a > b ? a : b; }));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  const uint32_t r = dpp_scan(__float_as_uint(v), __float_as_uint(-__builtin_inff()),
+                              [](uint32_t a, uint32_t b) {
+                                return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                              });
+  return __uint_as_float(lane63(r));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  const uint32_t r = dpp_scan(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  });
+  return __uint_as_float(lane63(r));
 }
 
 // Exclusive prefix sum over a whole workgroup of NT threads (thread order).
-// `tmp` must hold NT/64 + 1 ints of LDS.  Returns the exclusive prefix and the
+// `tmp` must hold NT/64 ints of LDS.  Returns the exclusive prefix and the
 // total through *total.  Contains barriers: every thread must call it.
 template <int NT>
 __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   constexpr int NW = NT / 64;
-  int incl = wave_incl_scan(v, lane);
+  const int incl = wave_incl_scan(v);
   if (lane == 63) tmp[w] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < NW; ++i) { int t = tmp[i]; tmp[i] = run; run += t; }
-    tmp[NW] = run;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const int t = tmp[i];
+    base += i < w ? t : 0;
+    tot += t;
   }
-  __syncthreads();
-  int res = tmp[w] + incl - v;
-  *total = tmp[NW];
-  __syncthreads();
-  return res;
+  *total = tot;
+  __syncthreads();   // tmp may be rewritten right after the call
+  return base + incl - v;
 }
 
 // Order-preserving 32-bit key of a float score: larger score -> larger key.

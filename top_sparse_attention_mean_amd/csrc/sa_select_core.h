@@ -7,15 +7,20 @@
 // aside, the best scores are kept, ties to the lower block index).
 //
 // Layout: thread tid holds the keys of indices j = r*NT + tid (r < KPT) in
-// registers, so every pass below is a register sweep plus LDS atomics -- no
-// dependent LDS reads.
-// Radix select with early exit: level 0 histograms the top 11 bits of every
-// candidate key in LDS and finds the bin holding the cut (one block-wide scan);
-// keys above that bin are appended to the result, and when the cut bin holds at
-// most kBoundCap keys they are ranked exactly by (key desc, index asc).
-// Otherwise the next 11 (then 10) bits of the cut bin's members are
-// histogrammed the same way.  The small rank and sort loops read their lists
-// with unrolled 16-byte LDS loads over sentinel-padded arrays.
+// registers, so every pass is a register sweep.
+//
+// 1. Range: wave min / max of the candidate keys (DPP), u = key - min.
+// 2. Radix cut: up to 11 bits of u at a time, from its top set bit down, are
+//    histogrammed in LDS for the keys sharing the current prefix; a block scan
+//    (DPP inside each wave) finds the digit holding the cut.  This repeats
+//    until the cut bin is taken whole or holds at most kBoundCap keys.  With
+//    the prefix P under the mask M, a key is above the cut when (u & M) > P
+//    and a boundary member when (u & M) == P.
+// 3. Boundary members are appended to LDS and ranked exactly by
+//    (key desc, index asc); if more than kBoundCap keys share all 32 bits,
+//    the lowest indices win by a prefix count over a member bitmap.
+// 4. Every kept index sets its bit in an LDS bitmap; one block scan of the
+//    word popcounts turns the bitmap into the ascending index list.
 #pragma once
 
 #include "sa_device.h"
@@ -24,131 +29,296 @@ namespace sa {
 
 constexpr int kSelBins = 2048;
 constexpr int kBoundCap = 512;
+constexpr int kSelWords = 256;    // bitmap words: rows of up to 8192 indices
+constexpr int kCandCap = 512;     // pre-filtered candidate list
 
-struct SelectLds {
-  uint32_t hist[kSelBins];
-  __attribute__((aligned(16))) uint32_t bkey[kBoundCap + 8];
-  __attribute__((aligned(16))) int bidx[kBoundCap + 8];
-  int scan[17];
+template <int NT, int KPT>
+struct SelectLdsT {
+  __attribute__((aligned(16))) uint32_t hist[kSelBins];
+  __attribute__((aligned(16))) uint32_t bm[kSelWords];
+  __attribute__((aligned(16))) uint32_t bkey[kBoundCap];
+  __attribute__((aligned(16))) int bidx[kBoundCap];
+  uint32_t ckey[kCandCap];
+  int cidx[kCandCap];
+  int wsum[8][NT / 64];
   int misc[8];
 };
 
-// Top `need` of the candidates c0 <= j < c1 (need < c1 - c0) among the keys
-// kr[r] of indices j = r*NT + tid.  Writes the chosen indices ascending to
-// out[0..need).  tmp must hold need + 8 ints of LDS (16-byte aligned).  All NT
-// threads call.
+// Sum of the wave totals of waves before `wave` and of all waves.
+template <int NW>
+__device__ __forceinline__ int wave_base(const int* wt, int wave, int* all) {
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = wt[w];
+    base += w < wave ? t : 0;
+    tot += t;
+  }
+  *all = tot;
+  return base;
+}
+
+// Clear the histogram, the bitmap words [0, W) and the member counter.  No
+// barrier: the first barrier of sel_mark_top (or the caller's) publishes it.
 template <int NT, int KPT>
-__device__ void select_core(const uint32_t (&kr)[KPT], int c0, int c1, int need, int* tmp,
-                            int* out, SelectLds& S) {
+__device__ __forceinline__ void sel_init(SelectLdsT<NT, KPT>& S, int W) {
+  static_assert(NT == 256, "the cut search assumes 8 histogram bins per thread");
   const int tid = threadIdx.x;
-  if (tid == 0) { S.misc[0] = 0; S.misc[4] = 0; }
-  uint32_t prefix = 0u, pmask = 0u;
-  int want = need;
-  for (int level = 0; level < 3; ++level) {
-    const int width = level < 2 ? 11 : 10;
-    const int shift = level == 0 ? 21 : (level == 1 ? 10 : 0);
-    const int nbins = 1 << width;
-    const uint32_t dmask = uint32_t(nbins - 1);
-    for (int i = tid; i < nbins; i += NT) S.hist[i] = 0u;
-    __syncthreads();
+  u32x4* h4 = reinterpret_cast<u32x4*>(S.hist);
+  h4[2 * tid] = u32x4{0u, 0u, 0u, 0u};
+  h4[2 * tid + 1] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < W) S.bm[tid] = 0u;
+  if (tid == 0) S.misc[6] = 0;
+}
+
+__device__ __forceinline__ void sel_mark(uint32_t* bm, int j) {
+  atomicOr(&bm[j >> 5], 1u << (j & 31));
+}
+
+// Mark in S.bm the top `need` of the ncand candidates held in registers:
+// key kr[r] of index ix[r] where cand[r] (0 < need < ncand, indices distinct
+// and below 32 * kSelWords).  The histogram must be zero and published by a
+// barrier before the first atomic (the barrier after the range reduction
+// below serves); all NT threads call.  Ends without a barrier after the last
+// marks.
+template <int NT, int KPT, int L>
+__device__ void sel_mark_top_kv(const uint32_t (&kr)[L], const int (&ix)[L], const bool (&cand)[L],
+                                int ncand, int need, SelectLdsT<NT, KPT>& S) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int j = r * NT + tid;
-      const uint32_t u = kr[r];
-      if (j >= c0 && j < c1 && (u & pmask) == prefix) atomicAdd(&S.hist[(u >> shift) & dmask], 1u);
-    }
-    __syncthreads();
-    // cut bin: thread t owns bins nbins-1-bpt*t .. (descending digits)
-    const int bpt = nbins / NT;
-    int tot = 0;
-    for (int q = 0; q < bpt; ++q) tot += int(S.hist[nbins - 1 - bpt * tid - q]);
-    int all;
-    int run = block_excl_scan<NT>(tot, S.scan, &all);
-    for (int q = 0; q < bpt; ++q) {
-      const int b = nbins - 1 - bpt * tid - q;
-      const int c = int(S.hist[b]);
-      if (run < want && want <= run + c) { S.misc[1] = b; S.misc[2] = run; S.misc[3] = c; }
-      run += c;
-    }
-    __syncthreads();
-    const uint32_t d = uint32_t(S.misc[1]);
-    const int above = S.misc[2], m = S.misc[3];
-    // keys of this prefix whose digit beats the cut bin are in
+  for (int r = 0; r < L; ++r)
+    if (cand[r]) { lo = min(lo, kr[r]); hi = max(hi, kr[r]); }
+  lo = wave_umin(lo);
+  hi = wave_umax(hi);
+  if (lane == 0) { S.wsum[0][wave] = int(lo); S.wsum[1][wave] = int(hi); }
+  __syncthreads();
 #pragma unroll
-    for (int r = 0; r < KPT; ++r) {
-      const int j = r * NT + tid;
-      const uint32_t u = kr[r];
-      if (j >= c0 && j < c1 && (u & pmask) == prefix && ((u >> shift) & dmask) > d)
-        tmp[atomicAdd(&S.misc[0], 1)] = j;
-    }
-    want -= above;
-    prefix |= d << shift;
-    pmask |= dmask << shift;
-    if (m <= kBoundCap) {
-      // rank the cut bin's members exactly by (key desc, index asc)
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, uint32_t(S.wsum[0][w]));
+    hi = max(hi, uint32_t(S.wsum[1][w]));
+  }
+  uint32_t u[L];
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) {
-        const int j = r * NT + tid;
-        const uint32_t u = kr[r];
-        if (j >= c0 && j < c1 && (u & pmask) == prefix) {
-          const int p = atomicAdd(&S.misc[4], 1);
-          S.bkey[p] = u;
-          S.bidx[p] = j;
-        }
-      }
-      if (tid < 8) { S.bkey[m + tid] = 0u; S.bidx[m + tid] = 0x7fffffff; }  // sentinels
+  for (int r = 0; r < L; ++r) u[r] = kr[r] - lo;
+  int bits = 32 - __clz(int(hi - lo));       // 0 when every candidate key is equal
+  uint32_t P = 0u, M = 0u;
+  int want = need, m = ncand, level = 0;
+  u32x4* h4 = reinterpret_cast<u32x4*>(S.hist);
+  while (bits > 0 && want < m) {
+    const int width = min(bits, 11), shift = bits - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    if (level > 0) {
+      h4[2 * tid] = u32x4{0u, 0u, 0u, 0u};
+      h4[2 * tid + 1] = u32x4{0u, 0u, 0u, 0u};
       __syncthreads();
-      for (int i = tid; i < m; i += NT) {
-        const uint32_t u = S.bkey[i];
-        const int ji = S.bidx[i];
-        int rk = 0;
-        for (int t = 0; t < m; t += 8) {
-          const u32x4 ka = *reinterpret_cast<const u32x4*>(&S.bkey[t]);
-          const u32x4 kb = *reinterpret_cast<const u32x4*>(&S.bkey[t + 4]);
-          const u32x4 ia = *reinterpret_cast<const u32x4*>(&S.bidx[t]);
-          const u32x4 ib = *reinterpret_cast<const u32x4*>(&S.bidx[t + 4]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            rk += (ka[q] > u) || (ka[q] == u && int(ia[q]) < ji);
-            rk += (kb[q] > u) || (kb[q] == u && int(ib[q]) < ji);
-          }
-        }
-        if (rk < want) tmp[atomicAdd(&S.misc[0], 1)] = ji;
-      }
-      break;
     }
-    if (level == 2) {
-      // more than kBoundCap identical keys: take the lowest indices, in index
-      // order, one NT-wide chunk (r) at a time
-      int taken = 0;
-      for (int r = 0; r < KPT && taken < want; ++r) {
-        const int j = r * NT + tid;
-        const int f = (j >= c0 && j < c1 && kr[r] == prefix) ? 1 : 0;
-        int tot2;
-        const int pre = block_excl_scan<NT>(f, S.scan, &tot2);
-        if (f && taken + pre < want) tmp[atomicAdd(&S.misc[0], 1)] = j;
-        taken += tot2;
+#pragma unroll
+    for (int r = 0; r < L; ++r)
+      if (cand[r] && (u[r] & M) == P) atomicAdd(&S.hist[(u[r] >> shift) & dmask], 1u);
+    __syncthreads();
+    // thread t owns bins [kSelBins - 8(t+1), kSelBins - 8t), scanned downward
+    const u32x4 ha = h4[kSelBins / 4 - 2 * tid - 2], hb = h4[kSelBins / 4 - 2 * tid - 1];
+    const int tot = int(ha[0] + ha[1] + ha[2] + ha[3] + hb[0] + hb[1] + hb[2] + hb[3]);
+    const int incl = wave_incl_scan(tot);
+    int* wt = S.wsum[3 + level];
+    if (lane == 63) wt[wave] = incl;
+    __syncthreads();
+    int all;
+    int run = incl - tot + wave_base<NW>(wt, wave, &all);
+    if (run < want && want <= run + tot) {
+      const uint32_t hv[8] = {hb[3], hb[2], hb[1], hb[0], ha[3], ha[2], ha[1], ha[0]};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = int(hv[q]);
+        if (run < want && want <= run + c) {
+          S.misc[0] = kSelBins - 1 - 8 * tid - q; S.misc[1] = run; S.misc[2] = c;
+        }
+        run += c;
       }
-      break;
     }
     __syncthreads();
+    want -= S.misc[1];
+    m = S.misc[2];
+    P |= uint32_t(S.misc[0]) << shift;
+    M |= dmask << shift;
+    bits = shift;
+    ++level;
+    if (m <= kBoundCap) break;
   }
-  __syncthreads();
-  if (tid < 8) tmp[need + tid] = 0x7fffffff;  // sentinels for the sort
-  __syncthreads();
-  // ascending order by index (indices are distinct)
-  for (int i = tid; i < need; i += NT) {
-    const int v = tmp[i];
-    int rk = 0;
-    for (int t = 0; t < need; t += 8) {
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(&tmp[t]);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(&tmp[t + 4]);
+  // above the cut: kept; boundary members: kept whole, ranked, or by index
+  const bool whole = want >= m;
+  const bool ranked = !whole && m <= kBoundCap;
+  uint32_t* mbm = S.hist;                    // member bitmap (identical keys only)
+  if (!whole && !ranked) {
+    if (tid < kSelWords) mbm[tid] = 0u;      // the histogram is no longer read
+    __syncthreads();
+  }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) rk += (int(a0[q]) < v) + (int(a1[q]) < v);
+  for (int r = 0; r < L; ++r) {
+    const int j = ix[r];
+    if (!cand[r]) continue;
+    const uint32_t um = u[r] & M;
+    if (um > P || (whole && um == P)) {
+      sel_mark(S.bm, j);
+    } else if (um == P) {
+      if (ranked) {
+        const int p = atomicAdd(&S.misc[6], 1);
+        if (p < kBoundCap) { S.bkey[p] = u[r]; S.bidx[p] = j; }
+      } else {
+        sel_mark(mbm, j);
+      }
     }
-    out[rk] = v;
   }
+  if (whole) return;
   __syncthreads();
+  if (ranked) {
+    for (int i = tid; i < m; i += NT) {
+      const uint32_t x = S.bkey[i];
+      const int xi = S.bidx[i];
+      int rk = 0;
+      for (int t = 0; t < m; t += 4) {
+        const u32x4 kk = *reinterpret_cast<const u32x4*>(&S.bkey[t]);
+        const u32x4 ii = *reinterpret_cast<const u32x4*>(&S.bidx[t]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          rk += (t + q < m) && ((kk[q] > x) || (kk[q] == x && int(ii[q]) < xi));
+      }
+      if (rk < want) sel_mark(S.bm, xi);
+    }
+    return;
+  }
+  // more than kBoundCap identical keys at the cut: the `want` lowest indices
+  const uint32_t wv = tid < kSelWords ? mbm[tid] : 0u;
+  const int c = __popc(wv);
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) S.wsum[6][wave] = incl;
+  __syncthreads();
+  int all;
+  int pos = incl - c + wave_base<NW>(S.wsum[6], wave, &all);
+  for (uint32_t x = wv; x != 0u && pos < want; x &= x - 1u, ++pos)
+    sel_mark(S.bm, tid * 32 + __ffs(int(x)) - 1);
+}
+
+
+// Mark in S.bm the top `need` of the candidates c0 <= j < c1 among the keys
+// kr[r] of indices j = r*NT + tid (0 < need < c1 - c0).  sel_init must have
+// run; all NT threads call.  Ends without a barrier after the last marks.
+//
+// Pre-filter: a histogram of the per-thread maxima (one LDS atomic per
+// thread) gives a lower bound T0 that at least `need` candidate keys reach, so
+// the exact top set lies in {key >= T0}.  Those keys are compacted into an LDS
+// list by a block scan and the radix select runs on the list (at most two
+// entries per thread) instead of on every key; LDS atomics serialize per lane,
+// so this is what keeps the histogram passes short.  When the bound is too
+// weak (list over kCandCap, need above 3NT/4) the keys are selected directly.
+template <int NT, int KPT>
+__device__ void sel_mark_top(const uint32_t (&kr)[KPT], int c0, int c1, int need,
+                             SelectLdsT<NT, KPT>& S) {
+  constexpr int NW = NT / 64;
+  static_assert(kCandCap == 2 * NT, "two list entries per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  bool cand[KPT];
+  int ix[KPT];
+  uint32_t tmax = 0u;                 // real keys are nonzero: 0 = no candidate
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    ix[r] = r * NT + tid;
+    cand[r] = ix[r] >= c0 && ix[r] < c1;
+    if (cand[r]) tmax = max(tmax, kr[r]);
+  }
+  if (KPT > 2 && need <= 3 * NT / 4) {
+    // range of the per-thread maxima, then their histogram
+    uint32_t lo = wave_umin(tmax != 0u ? tmax : 0xffffffffu), hi = wave_umax(tmax);
+    if (lane == 0) { S.wsum[0][wave] = int(lo); S.wsum[1][wave] = int(hi); }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      lo = min(lo, uint32_t(S.wsum[0][w]));
+      hi = max(hi, uint32_t(S.wsum[1][w]));
+    }
+    const int bits = 32 - __clz(int(hi - lo));
+    const int shift = bits > 11 ? bits - 11 : 0;
+    if (tmax != 0u) atomicAdd(&S.hist[(tmax - lo) >> shift], 1u);
+    __syncthreads();
+    u32x4* h4 = reinterpret_cast<u32x4*>(S.hist);
+    const u32x4 ha = h4[kSelBins / 4 - 2 * tid - 2], hb = h4[kSelBins / 4 - 2 * tid - 1];
+    const int tot = int(ha[0] + ha[1] + ha[2] + ha[3] + hb[0] + hb[1] + hb[2] + hb[3]);
+    const int incl = wave_incl_scan(tot);
+    if (lane == 63) S.wsum[2][wave] = incl;
+    __syncthreads();
+    int nmax;
+    int run = incl - tot + wave_base<NW>(S.wsum[2], wave, &nmax);
+    if (run < need && need <= run + tot) {
+      const uint32_t hv[8] = {hb[3], hb[2], hb[1], hb[0], ha[3], ha[2], ha[1], ha[0]};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int c = int(hv[q]);
+        if (run < need && need <= run + c) S.misc[3] = kSelBins - 1 - 8 * tid - q;
+        run += c;
+      }
+    }
+    // the histogram is read: clear it for the list's radix select
+    h4[2 * tid] = u32x4{0u, 0u, 0u, 0u};
+    h4[2 * tid + 1] = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+    if (nmax >= need) {
+      const uint32_t T0 = lo + (uint32_t(S.misc[3]) << shift);
+      int nc = 0;
+#pragma unroll
+      for (int r = 0; r < KPT; ++r) nc += (cand[r] && kr[r] >= T0) ? 1 : 0;
+      const int inc2 = wave_incl_scan(nc);
+      if (lane == 63) S.wsum[7][wave] = inc2;
+      __syncthreads();
+      int C;
+      int pos = inc2 - nc + wave_base<NW>(S.wsum[7], wave, &C);
+      if (C <= kCandCap) {
+#pragma unroll
+        for (int r = 0; r < KPT; ++r)
+          if (cand[r] && kr[r] >= T0) { S.ckey[pos] = kr[r]; S.cidx[pos] = ix[r]; ++pos; }
+        __syncthreads();
+        uint32_t ck[2];
+        int ci[2];
+        bool cc[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int i = q * NT + tid;
+          cc[q] = i < C;
+          ck[q] = cc[q] ? S.ckey[i] : 0u;
+          ci[q] = cc[q] ? S.cidx[i] : 0;
+        }
+        if (need < C) sel_mark_top_kv<NT, KPT, 2>(ck, ci, cc, C, need, S);
+        else {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+            if (cc[q]) sel_mark(S.bm, ci[q]);
+        }
+        return;
+      }
+    }
+  }
+  sel_mark_top_kv<NT, KPT, KPT>(kr, ix, cand, c1 - c0, need, S);
+}
+
+// Ascending list of the set bits of S.bm[0, W) into out[0, min(total, cap));
+// returns the total.  Starts and ends with a barrier; all NT threads call.
+template <int NT, int KPT>
+__device__ int sel_bitmap_to_list(SelectLdsT<NT, KPT>& S, int W, int* out, int cap) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __syncthreads();
+  const uint32_t wv = tid < W ? S.bm[tid] : 0u;
+  const int c = __popc(wv);
+  const int incl = wave_incl_scan(c);
+  if (lane == 63) S.wsum[4][wave] = incl;
+  __syncthreads();
+  int total;
+  int pos = incl - c + wave_base<NW>(S.wsum[4], wave, &total);
+  for (uint32_t x = wv; x != 0u; x &= x - 1u, ++pos)
+    if (unsigned(pos) < unsigned(cap)) out[pos] = tid * 32 + __ffs(int(x)) - 1;
+  __syncthreads();
+  return total;
 }
 
 // Keys of score row srow (length nb) into registers: kr[r] <- key of index
@@ -168,10 +338,11 @@ __device__ __forceinline__ void load_keys_reg(const float* srow, int nb, uint32_
 
 // Full decode selection of one row: forced sink (block 0) and local (block
 // nb-1) per flags, then the best k - forced of the rest.  Writes min(k, nb)
-// ascending block ids to out.  tmp holds k + 8 ints of LDS.  Returns the count.
+// ascending block ids to out (capacity k).  Returns the count.  All NT
+// threads call; nb <= 32 * kSelWords.
 template <int NT, int KPT>
 __device__ int select_decode_row(const uint32_t (&kr)[KPT], int nb, int k, unsigned flags,
-                                 int* tmp, int* out, SelectLds& S) {
+                                 int* out, SelectLdsT<NT, KPT>& S) {
   const int tid = threadIdx.x;
   if (k >= nb) {
     for (int j = tid; j < nb; j += NT) out[j] = j;
@@ -181,13 +352,15 @@ __device__ int select_decode_row(const uint32_t (&kr)[KPT], int nb, int k, unsig
   const bool sink = flags & SA_FORCE_SINK, local = flags & SA_FORCE_LOCAL;
   const int c0 = sink ? 1 : 0, c1 = local ? nb - 1 : nb;   // nb >= 2 here
   const int nfree = k - int(sink) - int(local);
+  const int W = (nb + 31) >> 5;
+  sel_init(S, W);
+  if (nfree > 0) sel_mark_top<NT, KPT>(kr, c0, c1, nfree, S);
+  else __syncthreads();
   if (tid == 0) {
-    if (sink) out[0] = 0;
-    if (local) out[k - 1] = nb - 1;
+    if (sink) sel_mark(S.bm, 0);
+    if (local) sel_mark(S.bm, nb - 1);
   }
-  if (nfree > 0) select_core<NT, KPT>(kr, c0, c1, nfree, tmp, out + (sink ? 1 : 0), S);
-  __syncthreads();
-  return k;
+  return sel_bitmap_to_list(S, W, out, k);
 }
 
 // Register tiers for KPT = ceil(nb / 256) rounded up: 2, 8 or 32 keys per thread.
