@@ -139,12 +139,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
 }
 
 // Order-preserving 32-bit key of a float score: larger score -> larger key.
-// -0 ranks as +0; NaN ranks as -inf.
+// -0 ranks as +0; NaN ranks as -inf.  max(f, -inf) maps NaN to -inf (IEEE
+// maxNum returns the non-NaN operand), adding +0 turns -0 into +0, and the
+// sign-driven xor flips negative patterns and sets the top bit of positive
+// ones: five plain VALU operations.
 __device__ __forceinline__ uint32_t score_key(float f) {
-  if (f != f) f = -__builtin_inff();
-  if (f == 0.0f) f = 0.0f;
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(fmaxf(f, -__builtin_inff()) + 0.0f);
+  return u ^ (uint32_t(int32_t(u) >> 31) | 0x80000000u);
 }
 
 }  // namespace sa

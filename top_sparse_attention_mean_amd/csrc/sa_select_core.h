@@ -7,8 +7,16 @@
 // aside, the best scores are kept, ties to the lower block index).
 //
 // Layout: thread tid holds the keys of indices j = r*NT + tid (r < KPT) in
-// registers, so every pass is a register sweep.
+// registers, so every pass over the keys is a register sweep.
 //
+// Usual path (several keys per thread, k small against the thread count):
+// 1. A histogram of the per-thread maxima (one LDS atomic per thread) gives a
+//    lower bound T0 that at least `need` keys reach, so the exact top set lies
+//    in {key >= T0}.
+// 2. Those keys are compacted by a block scan into an LDS list of unique
+//    64-bit composites (key << 32 | ~index) and each is ranked by counting
+//    the list entries above it.
+// Direct path (bound too weak, or one or two keys per thread):
 // 1. Range: wave min / max of the candidate keys (DPP), u = key - min.
 // 2. Radix cut: up to 11 bits of u at a time, from its top set bit down, are
 //    histogrammed in LDS for the keys sharing the current prefix; a block scan
@@ -19,8 +27,8 @@
 // 3. Boundary members are appended to LDS and ranked exactly by
 //    (key desc, index asc); if more than kBoundCap keys share all 32 bits,
 //    the lowest indices win by a prefix count over a member bitmap.
-// 4. Every kept index sets its bit in an LDS bitmap; one block scan of the
-//    word popcounts turns the bitmap into the ascending index list.
+// Both paths set one bit per kept index in an LDS bitmap; one block scan of
+// the word popcounts turns it into the ascending index list.
 #pragma once
 
 #include "sa_device.h"
@@ -38,8 +46,9 @@ struct SelectLdsT {
   __attribute__((aligned(16))) uint32_t bm[kSelWords];
   __attribute__((aligned(16))) uint32_t bkey[kBoundCap];
   __attribute__((aligned(16))) int bidx[kBoundCap];
-  uint32_t ckey[kCandCap];
-  int cidx[kCandCap];
+  // (key << 32) | ~index; zero padding at [C, C + 64), per-lane discard
+  // slots at [kCandCap + 64, kCandCap + 128)
+  __attribute__((aligned(16))) uint64_t cand[kCandCap + 128];
   int wsum[8][NT / 64];
   int misc[8];
 };
@@ -209,24 +218,28 @@ __device__ void sel_mark_top_kv(const uint32_t (&kr)[L], const int (&ix)[L], con
 // Pre-filter: a histogram of the per-thread maxima (one LDS atomic per
 // thread) gives a lower bound T0 that at least `need` candidate keys reach, so
 // the exact top set lies in {key >= T0}.  Those keys are compacted into an LDS
-// list by a block scan and the radix select runs on the list (at most two
-// entries per thread) instead of on every key; LDS atomics serialize per lane,
-// so this is what keeps the histogram passes short.  When the bound is too
-// weak (list over kCandCap, need above 3NT/4) the keys are selected directly.
+// list by a block scan and ranked there by direct counting (the list is short:
+// about 1.1-1.5 need on continuous scores); LDS atomics serialize per lane, so
+// this avoids a histogram over every key.  When the bound is too weak (list
+// over kCandCap, need above 3NT/4) the keys are selected directly.
 template <int NT, int KPT>
-__device__ void sel_mark_top(const uint32_t (&kr)[KPT], int c0, int c1, int need,
+__device__ void sel_mark_top(const uint32_t (&kin)[KPT], int c0, int c1, int need,
                              SelectLdsT<NT, KPT>& S) {
   constexpr int NW = NT / 64;
-  static_assert(kCandCap == 2 * NT, "two list entries per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // keys outside [c0, c1) become 0, which no score maps to: the passes below
+  // need no candidate masks, and their stores are unconditional (branches
+  // around predicated stores cost more than the stores)
+  uint32_t kr[KPT];
   bool cand[KPT];
   int ix[KPT];
-  uint32_t tmax = 0u;                 // real keys are nonzero: 0 = no candidate
+  uint32_t tmax = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
     ix[r] = r * NT + tid;
-    cand[r] = ix[r] >= c0 && ix[r] < c1;
-    if (cand[r]) tmax = max(tmax, kr[r]);
+    kr[r] = unsigned(ix[r] - c0) < unsigned(c1 - c0) ? kin[r] : 0u;
+    cand[r] = kr[r] != 0u;
+    tmax = max(tmax, kr[r]);
   }
   if (KPT > 2 && need <= 3 * NT / 4) {
     // range of the per-thread maxima, then their histogram
@@ -240,7 +253,7 @@ __device__ void sel_mark_top(const uint32_t (&kr)[KPT], int c0, int c1, int need
     }
     const int bits = 32 - __clz(int(hi - lo));
     const int shift = bits > 11 ? bits - 11 : 0;
-    if (tmax != 0u) atomicAdd(&S.hist[(tmax - lo) >> shift], 1u);
+    atomicAdd(&S.hist[tmax != 0u ? (tmax - lo) >> shift : 0], tmax != 0u ? 1u : 0u);
     __syncthreads();
     u32x4* h4 = reinterpret_cast<u32x4*>(S.hist);
     const u32x4 ha = h4[kSelBins / 4 - 2 * tid - 2], hb = h4[kSelBins / 4 - 2 * tid - 1];
@@ -259,7 +272,7 @@ __device__ void sel_mark_top(const uint32_t (&kr)[KPT], int c0, int c1, int need
         run += c;
       }
     }
-    // the histogram is read: clear it for the list's radix select
+    // the histogram is read: clear it for a possible direct selection
     h4[2 * tid] = u32x4{0u, 0u, 0u, 0u};
     h4[2 * tid + 1] = u32x4{0u, 0u, 0u, 0u};
     __syncthreads();
@@ -267,32 +280,52 @@ __device__ void sel_mark_top(const uint32_t (&kr)[KPT], int c0, int c1, int need
       const uint32_t T0 = lo + (uint32_t(S.misc[3]) << shift);
       int nc = 0;
 #pragma unroll
-      for (int r = 0; r < KPT; ++r) nc += (cand[r] && kr[r] >= T0) ? 1 : 0;
+      for (int r = 0; r < KPT; ++r) nc += kr[r] >= T0 ? 1 : 0;
       const int inc2 = wave_incl_scan(nc);
       if (lane == 63) S.wsum[7][wave] = inc2;
       __syncthreads();
       int C;
       int pos = inc2 - nc + wave_base<NW>(S.wsum[7], wave, &C);
       if (C <= kCandCap) {
+        // (key << 32) | ~index orders by key, then lower index first, and is
+        // unique; candidates are nonzero, so zero padding never outranks one.
+        // Keys below T0 go to this lane's discard slot.
+        const int trash = kCandCap + 64 + lane;
 #pragma unroll
-        for (int r = 0; r < KPT; ++r)
-          if (cand[r] && kr[r] >= T0) { S.ckey[pos] = kr[r]; S.cidx[pos] = ix[r]; ++pos; }
-        __syncthreads();
-        uint32_t ck[2];
-        int ci[2];
-        bool cc[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int i = q * NT + tid;
-          cc[q] = i < C;
-          ck[q] = cc[q] ? S.ckey[i] : 0u;
-          ci[q] = cc[q] ? S.cidx[i] : 0;
+        for (int r = 0; r < KPT; ++r) {
+          const bool in = kr[r] >= T0;
+          S.cand[in ? pos : trash] = (uint64_t(kr[r]) << 32) | uint32_t(~ix[r]);
+          pos += in ? 1 : 0;
         }
-        if (need < C) sel_mark_top_kv<NT, KPT, 2>(ck, ci, cc, C, need, S);
-        else {
+        // zero padding to whole shares: share = ceil(C / R) rounded up to 16
+        const int R = C <= NT / 4 ? 4 : (C <= NT / 2 ? 2 : 1);
+        const int share = (((C + R - 1) / R) + 15) & ~15;
+        if (tid < R * share - C) S.cand[C + tid] = 0ull;
+        __syncthreads();
+        if (need >= C) {
+          for (int i = tid; i < C; i += NT) sel_mark(S.bm, int(~uint32_t(S.cand[i])));
+          return;
+        }
+        // rank by counting: R threads (adjacent lanes) per candidate, each over
+        // its share of the list, 16 entries (8 reads) per step
+        for (int i0 = 0; i0 < C; i0 += NT / R) {
+          const int i = i0 + tid / R, h = tid % R;
+          const uint64_t x = i < C ? S.cand[i] : ~0ull;
+          const uint64_t* lp = S.cand + h * share;
+          int rk = 0;
+          for (int t = 0; t < share; t += 16) {
+            u32x4 pr[8];
 #pragma unroll
-          for (int q = 0; q < 2; ++q)
-            if (cc[q]) sel_mark(S.bm, ci[q]);
+            for (int q = 0; q < 8; ++q) pr[q] = *reinterpret_cast<const u32x4*>(lp + t + 2 * q);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              rk += ((uint64_t(pr[q][1]) << 32) | pr[q][0]) > x;
+              rk += ((uint64_t(pr[q][3]) << 32) | pr[q][2]) > x;
+            }
+          }
+          if (R >= 2) rk += __shfl_xor(rk, 1, 64);
+          if (R >= 4) rk += __shfl_xor(rk, 2, 64);
+          if (i < C && h == 0 && rk < need) sel_mark(S.bm, int(~uint32_t(x)));
         }
         return;
       }
@@ -322,16 +355,15 @@ __device__ int sel_bitmap_to_list(SelectLdsT<NT, KPT>& S, int W, int* out, int c
 }
 
 // Keys of score row srow (length nb) into registers: kr[r] <- key of index
-// r*NT + tid (missing entries get key 0, never a candidate).
+// r*NT + tid (missing entries get key 0, never a candidate).  Every load is
+// issued (clamped in bounds, no branch) before the first is waited on.
 template <int NT, int KPT>
 __device__ __forceinline__ void load_keys_reg(const float* srow, int nb, uint32_t (&kr)[KPT]) {
   const int tid = threadIdx.x;
   float v[KPT];
 #pragma unroll
-  for (int r = 0; r < KPT; ++r) {
-    const int j = r * NT + tid;
-    v[r] = j < nb ? srow[j] : 0.f;
-  }
+  for (int r = 0; r < KPT; ++r) v[r] = srow[min(r * NT + tid, nb - 1)];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int r = 0; r < KPT; ++r) kr[r] = r * NT + tid < nb ? score_key(v[r]) : 0u;
 }
