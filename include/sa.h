@@ -243,6 +243,33 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V,
                          float* score, void* O, int out_dtype, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * sa_select_decode -- the selection and attention half of a decode step, as
+ * one kernel: top-k blocks per (b, kv head) from given block scores (the
+ * selection rule of sa_select_topk, decode), then the split-K sparse attention
+ * over the selected blocks and the merge (the decode steps of "The Sparse
+ * Frontier", Contributi §2 Quest; split-K merge, "Pulsar Attention", Fase 2).
+ * Each attention workgroup repeats the selection of its kv head from the score
+ * row instead of waiting on another workgroup.
+ *
+ *   Q [B, Hq, D], K, V [B, Hkv, N, D] dtype
+ *   score    [B, Hkv, nb] float32 block scores (input; nb = ceil(N / block));
+ *            NaN ranks as -inf
+ *   k        blocks per (b, kv head), forced ones included; flags: any of
+ *            SA_FORCE_SINK | SA_FORCE_LOCAL
+ *   idx      [B, Hkv, k] int32 out, ascending, -1 padded; count [B, Hkv] out
+ *   O        [B, Hq, D] out_dtype;  lse [B, Hq] float32 (NULL to skip)
+ * Same result as sa_select_topk's selection followed by sa_sparse_decode
+ * (blocks).  nb <= 8192.
+ * ws: sa_workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, block, k).
+ */
+sa_status sa_select_decode(const void* Q, const void* K, const void* V,
+                           int dtype, int B, int Hq, int Hkv, int N, int D,
+                           int block, const float* score, int k,
+                           unsigned flags, float scale, int32_t* idx,
+                           int32_t* count, void* O, int out_dtype, float* lse,
+                           void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes needed by an operation (0 if none; SIZE_MAX on bad input). */
 size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D,
                           int block, int k);

@@ -33,6 +33,7 @@ def lib():
     L.sa_sparse_decode.argtypes = [P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P, P, I, P, P, Z, P]
     L.sa_sparse_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, I, P, I, P, P]
     L.sa_decode_step.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P, P, Z, P]
+    L.sa_select_decode.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, U, F, P, P, P, I, P, P, Z, P]
     L.sa_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     L.sa_workspace_bytes.restype = Z
     L.sa_status_str.restype = ctypes.c_char_p
@@ -49,7 +50,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
-              "sa_sparse_prefill", "sa_decode_step", "sa_workspace_bytes", "sa_status_str",
+              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
+              "sa_status_str",
               "sa_last_error", "sa_version"]:
         assert n in names
 
@@ -180,3 +182,32 @@ def test_decode_step_validation(lib):
     a = list(base)
     a[21] = 128                                   # workspace
     assert f(*a) == WORKSPACE
+
+
+def test_select_decode_validation(lib):
+    f = lib.sa_select_decode
+    base = [A, A, A, 1, 1, 64, 8, 262144, 128, 64, A, 82, SINK | LOCAL, 0.0, A, A, A, 1, A, A,
+            1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(10, None) == INVALID              # score
+    assert call(15, None) == INVALID              # count
+    assert call(12, CAUSAL) == INVALID            # prefill flag
+    assert call(11, 1) == INVALID                 # k below the two forced blocks
+    assert call(9, 16) == UNSUPPORTED             # 16384 blocks per row
+    assert call(9, 32) == UNSUPPORTED             # bf16 block mode needs 64/128
+    assert call(20, 64) == WORKSPACE
+
+
+def test_binding_binds_every_entry_point():
+    """Every exported entry point has a ctypes signature and a wrapper in the binding."""
+    sa = pytest.importorskip("top_sparse_attention_mean_amd")
+    for n in sa.EXPORTS:
+        assert hasattr(sa, "_" + n[len("sa_"):]), f"no ctypes signature for {n}"
+    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
+              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
+        assert callable(getattr(sa, n)), n

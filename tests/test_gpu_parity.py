@@ -112,6 +112,55 @@ def test_decode_step_equals_separate_calls():
     assert torch.equal(O, O2) and torch.equal(lse, lse2)
 
 
+def test_select_decode_matches_step_and_flags():
+    wl, inp, q, K, V = _decode_case("gqa_decode_bf16", {"B": 2, "N": 8192 + 40})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    _, _, score = sa.sa_select_topk(Qd, sk, wl.k, want_score=True)
+    O, lse, idx, cnt = sa.sa_select_decode(Qd, Kd, Vd, score, wl.k, block=wl.block,
+                                           out_dtype=torch.float32)
+    O2, lse2, idx2, cnt2 = sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block,
+                                             out_dtype=torch.float32)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    assert torch.equal(O, O2) and torch.equal(lse, lse2)
+    # other forced-block choices, against the oracle
+    sc_ref = oracle.block_scores(q, oracle.sketch(K, wl.block))
+    nb = wl.nb
+    for flags, forced in ((sa.SA_FORCE_SINK, [0]), (0, [])):
+        O, lse, idx, cnt = sa.sa_select_decode(Qd, Kd, Vd, score, wl.k, block=wl.block,
+                                               flags=flags, out_dtype=torch.float32)
+        idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+        cand = np.array([j for j in range(nb) if j not in forced])
+        for b in range(wl.B):
+            for kh in range(wl.Hkv):
+                n = int(cnt_h[b, kh])
+                assert n == wl.k and np.all(idx_h[b, kh, n:] == -1)
+                check_topk_row(idx_h[b, kh, :n], sc_ref[b, kh], wl.k, forced, cand,
+                               where=f"flags {flags} b{b} kh{kh}")
+        O_ref, lse_ref = oracle.attend_blocks(q, K, V, idx_h, wl.block, count=cnt_h)
+        assert max_abs(O.cpu().numpy(), O_ref) <= OUT_TOL["bf16"]
+        assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+
+
+def test_decode_step_long_rows():
+    # 4500 blocks per row: the 32-keys-per-thread selection tier (4096 < nb <= 8192)
+    wl, inp, q, K, V = _decode_case("long_decode_bf16", {"Hq": 8, "Hkv": 1, "N": 4500 * 64 - 7})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    O, lse, idx, cnt = sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block,
+                                         out_dtype=torch.float32)
+    sc_ref = oracle.block_scores(q, oracle.sketch(K, wl.block))
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    nb = wl.nb
+    assert int(cnt_h[0, 0]) == wl.k
+    check_topk_row(idx_h[0, 0], sc_ref[0, 0], wl.k, [0, nb - 1], np.arange(1, nb - 1),
+                   where="long row")
+    assert set(inp.needles[0, 0].tolist()) <= set(idx_h[0, 0].tolist())
+    O_ref, lse_ref = oracle.attend_blocks(q, K, V, idx_h, wl.block, count=cnt_h)
+    assert max_abs(O.cpu().numpy(), O_ref) <= OUT_TOL["bf16"]
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+
+
 def test_decode_split_invariance_and_determinism():
     wl, inp, q, K, V = _decode_case("long_decode_bf16", {"N": 32768})
     Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")

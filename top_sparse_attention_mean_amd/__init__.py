@@ -33,7 +33,8 @@ SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
 SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP = range(4)
 
 EXPORTS = ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
-           "sa_sparse_prefill", "sa_decode_step", "sa_workspace_bytes", "sa_status_str",
+           "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
+           "sa_status_str",
            "sa_last_error", "sa_version"]
 
 _P = ctypes.c_void_p
@@ -61,6 +62,8 @@ _sparse_prefill = _sig("sa_sparse_prefill", _I, _P, _P, _P, _I, _I, _I, _I, _I, 
                        _P, _I, _P, _I, _P, _P)
 _decode_step = _sig("sa_decode_step", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _F,
                     _P, _P, _P, _P, _I, _P, _P, _Z, _P)
+_select_decode = _sig("sa_select_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _U,
+                      _F, _P, _P, _P, _I, _P, _P, _Z, _P)
 _workspace_bytes = _sig("sa_workspace_bytes", _Z, _I, _I, _I, _I, _I, _I, _I, _I)
 _status_str = _sig("sa_status_str", ctypes.c_char_p, _I)
 _last_error = _sig("sa_last_error", ctypes.c_char_p)
@@ -288,6 +291,32 @@ def sa_decode_step(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksketch: t
                         _ptr(ksketch), update_block, k, scale, _ptr(idx), _ptr(count),
                         _ptr(score), _ptr(O), _dt(O), _ptr(lse), _ptr(ws), ws.numel(),
                         _stream(stream)), "sa_decode_step")
+    return O, lse, idx, count
+
+
+def sa_select_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, score: torch.Tensor,
+                     k: int, block: int = 64, flags: int = SA_FORCE_SINK | SA_FORCE_LOCAL,
+                     scale: float = 0.0, out_dtype=None, idx=None, count=None, O=None, lse=None,
+                     want_lse: bool = True, ws=None, stream=None):
+    """Top-k selection from block scores fused with the split-K sparse decode."""
+    _dev(Q, K, V, score, idx, count, O, lse)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = K.shape
+    dev = Q.device
+    if idx is None:
+        idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if O is None:
+        O = torch.empty(B, Hq, D, dtype=out_dtype or Q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    need = workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, block, k)
+    if ws is None:
+        ws = workspace(need, dev, ("select_decode", B, Hq, Hkv, N, D, block, k))
+    _check(_select_decode(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, block,
+                          _ptr(score), k, flags, scale, _ptr(idx), _ptr(count), _ptr(O), _dt(O),
+                          _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)), "sa_select_decode")
     return O, lse, idx, count
 
 

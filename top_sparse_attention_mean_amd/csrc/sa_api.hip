@@ -140,6 +140,28 @@ sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B
 
 }  // namespace
 
+// Selection from a score row fused with the split-K decode where a fused
+// kernel exists (bf16, D = 128, k <= kMaxKFused); otherwise the selection
+// kernel followed by the block decode.
+static sa_status run_select_decode(const void* Q, const void* K, const void* V, int dtype, int B,
+                                   int Hq, int Hkv, int N, int D, int block, const float* scores,
+                                   int nb, int k, unsigned flags, float sc, int32_t* idx,
+                                   int32_t* count, void* O, int out_dtype, float* lse, void* dws,
+                                   hipStream_t st, const char* what) {
+  const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
+  if (dtype == SA_BF16 && D == 128 && k <= kMaxKFused) {
+    return hip_status(launch_decode_select_blocks(Q, K, V, B, Hq, Hkv, N, D, sc, block, scores, nb,
+                                                  k, flags, idx, count, w, dws, O, out_dtype, lse,
+                                                  st),
+                      what);
+  }
+  const hipError_t e = launch_select_rows(scores, B * Hkv, nb, k, flags, idx, count, st);
+  if (e != hipSuccess) return hip_status(e, what);
+  return hip_status(launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count,
+                                         k, w, dws, O, out_dtype, lse, st),
+                    what);
+}
+
 extern "C" {
 
 int sa_version(void) { return 100; }
@@ -314,22 +336,34 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V, int dtype,
   const float sc = eff_scale(scale, D);
   const SelectWs sw = select_ws(B, Hkv, 1, D, 1, nb);
   float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + sw.score_off);
-  const unsigned flags = SA_FORCE_SINK | SA_FORCE_LOCAL;
   hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, K, N, block, update_block, sc,
                               scores, st);
   if (e != hipSuccess) return hip_status(e, "sa_decode_step (score)");
-  const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
-  if (dtype == SA_BF16 && D == 128 && k <= kMaxKFused) {
-    return hip_status(launch_decode_select_blocks(Q, K, V, B, Hq, Hkv, N, D, sc, block, scores, nb,
-                                                  k, flags, idx, count, w, dws, O, out_dtype, lse,
-                                                  st),
-                      "sa_decode_step (select + decode)");
-  }
-  e = launch_select_rows(scores, B * Hkv, nb, k, flags, idx, count, st);
-  if (e != hipSuccess) return hip_status(e, "sa_decode_step (select)");
-  return hip_status(launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count,
-                                         k, w, dws, O, out_dtype, lse, st),
-                    "sa_decode_step (decode)");
+  return run_select_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, block, scores, nb, k,
+                           SA_FORCE_SINK | SA_FORCE_LOCAL, sc, idx, count, O, out_dtype, lse, dws,
+                           st, "sa_decode_step (select + decode)");
+}
+
+sa_status sa_select_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                           int Hkv, int N, int D, int block, const float* score, int k,
+                           unsigned flags, float scale, int32_t* idx, int32_t* count, void* O,
+                           int out_dtype, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  PTR(score);
+  PTR(count);
+  REQ(block >= 1, "block must be >= 1");
+  REQ(N >= 1 && k >= 1, "N and k must be >= 1 (got %d, %d)", N, k);
+  REQ((flags & ~3u) == 0, "decode selection takes SA_FORCE_SINK / SA_FORCE_LOCAL only (0x%x)",
+      flags);
+  const int nb = cdiv(N, block);
+  const int nF = int((flags & SA_FORCE_SINK) != 0) + int((flags & SA_FORCE_LOCAL) != 0);
+  REQ(nb == 1 || k >= nF, "k (%d) smaller than the %d forced blocks", k, nF);
+  SUP(nb <= kMaxNbDecode, "at most %d blocks per decode selection row", kMaxNbDecode);
+  sa_status s = v_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, SA_IDX_BLOCKS, block, idx, count, k,
+                         nullptr, O, out_dtype, lse, ws, ws_bytes);
+  if (s) return s;
+  return run_select_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, block, score, nb, k, flags,
+                           eff_scale(scale, D), idx, count, O, out_dtype, lse, ws,
+                           static_cast<hipStream_t>(stream), "sa_select_decode");
 }
 
 }  // extern "C"
