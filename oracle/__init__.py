@@ -27,8 +27,8 @@ Pages cited (by title, section):
     H(q, tau) = {p : <q, p> >= tau}; every key inside it is returned, so the
     selection has no false negatives).
 
-Readings where the pages are silent are listed in the design doc (section
-"Readings of the pages"); each function below names the reading it uses.
+Where the pages are silent or ambiguous, each function's docstring states the
+reading it takes.
 
 Parity status: every function is pinned by tests/test_oracle.py except
 ``mass_oracle`` (O8), whose selection is "parity unpinned" beyond its

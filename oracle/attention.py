@@ -104,7 +104,7 @@ def sketch(X: np.ndarray, block: int, head_pool: int = 1) -> np.ndarray:
     Block j covers tokens [j*block, min((j+1)*block, N)); the last block may be
     partial and is averaged over its valid tokens only.  With head_pool > 1 the
     mean also runs over each group of head_pool consecutive heads (the pooled
-    query block of block-sparse prefill).  The mean is this build's reading of
+    query block of block-sparse prefill).  The mean is our reading of
     the "compact summary of the keys" that is scanned before any full key is
     fetched ("Faster Than Flash", Metodologia §1) -- a per-block centre, like
     the cluster centres of the range-search index ("Sparse Attention as a Range
