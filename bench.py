@@ -93,13 +93,18 @@ def graph_time(fn, R, n_replay, warmup=3):
     return start.elapsed_time(end) * 1e3 / (n_replay * R)
 
 
+def _blas_threads() -> int:
+    """Threads the oracle's BLAS uses: OMP_NUM_THREADS within this process's CPU set."""
+    n = len(os.sched_getaffinity(0))
+    return min(int(os.environ.get("OMP_NUM_THREADS", "0")) or n, n)
+
+
 def cpu_baseline(inp, wl, budget_s: float = 12.0) -> dict:
     """The float64 oracle timed on this host on a bounded sample of steps."""
     import numpy as np
     import oracle
     from oracle.attention import widen
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    threads = min(threads, len(os.sched_getaffinity(0)))
+    threads = _blas_threads()
     q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
     sk = oracle.sketch(K, wl.block)                      # amortised at prefill, not timed
     steps, t0 = 0, time.perf_counter()
@@ -269,6 +274,152 @@ def bench_decode(args) -> dict:
     return res
 
 
+def bench_threshold(args) -> dict:
+    """Threshold variant (row a4, then token-mode a5 + a6) at its full size:
+    exact scores of every key, keep s >= tau - eps (zero false negatives),
+    ordered compaction, attention over the kept tokens."""
+    import numpy as np
+    import torch
+    import oracle
+    import top_sparse_attention_mean_amd as sa
+    from oracle.attention import widen
+    from tests.parity_util import to_dev
+    from workloads import get_workload, make_inputs
+    wl = get_workload("threshold_decode_bf16")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl)
+    q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
+    _, tau32 = oracle.threshold_tau(q, K, wl.percentile)        # the workload's tau (input)
+    R = 2                                                        # 2 x 1 GiB of K/V > Infinity Cache
+    Qs = [to_dev(inp.Q, wl.dtype, dev) for _ in range(R)]
+    Kd = to_dev(inp.K, wl.dtype, dev)
+    Ks = [Kd] + [Kd.clone() for _ in range(R - 1)]
+    Vd = to_dev(inp.V, wl.dtype, dev)
+    Vs = [Vd] + [Vd.clone() for _ in range(R - 1)]
+    tau = torch.from_numpy(tau32).to(dev)
+    B, Hq, Hkv, D, N = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N
+    idx = torch.empty(B, Hq, wl.cap, dtype=torch.int32, device=dev)
+    sc = torch.empty(B, Hq, wl.cap, dtype=torch.float32, device=dev)
+    cnt = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    O = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    tws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0, wl.cap),
+                      dtype=torch.uint8, device=dev)
+    dws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, 0, wl.cap),
+                      dtype=torch.uint8, device=dev)
+
+    def sel(r):
+        sa.sa_select_threshold(Qs[r], Ks[r], tau, wl.cap, idx=idx, score=sc, count=cnt, ws=tws)
+
+    def dec(r):
+        sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], idx, cnt, mode=sa.SA_IDX_TOKENS, score=sc,
+                            O=O, lse=lse, ws=dws)
+
+    n = max(4, args.steps // 20)
+    t_pass = graph_time(lambda r: (sel(r), dec(r)), R, n)
+    t_sel = graph_time(sel, R, n)
+    e = 2
+    kept = int(cnt.sum().item())
+    scan_bytes = B * Hkv * N * D * e + B * Hq * D * e + B * Hq * 4
+    list_bytes = B * Hq * wl.cap * 8 + B * Hq * 4
+    v_bytes = kept * D * e
+    ach = (scan_bytes + kept * 8) / (t_sel * 1e-6) / 1e9
+    res = {
+        "workload": wl.name, "us_per_pass": round(t_pass, 2),
+        "pass": "threshold scan + compaction (sa_select_threshold) + token-mode decode",
+        "kernels_us": {"sa_select_threshold (k_threshold_mfma + k_threshold_compact)": round(t_sel, 2),
+                       "sa_sparse_decode tokens (k_decode_tokens)": round(max(t_pass - t_sel, 0), 2)},
+        "kept_tokens": kept, "algorithmic_bytes_per_pass": scan_bytes + list_bytes + v_bytes,
+        "roofline": {"bound": "hbm", "kernel": "k_threshold_mfma (full K scan; the call also runs "
+                     "the small compaction kernel)", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes": scan_bytes + kept * 8,
+                     "avg_us": round(t_sel, 2)},
+    }
+    if not args.no_cpu:
+        # the oracle on the same arrays: exact scores, threshold, attention
+        t0 = time.perf_counter()
+        lists, _ = oracle.select_threshold(q, K, tau32.astype(np.float64))
+        oracle.attend_tokens(q, K, V, lists)
+        t_cpu = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(t_cpu * 1e6, 1), "unit": "us/pass",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "sample": "one full pass (all 256 heads, float64)"}
+    return res
+
+
+def bench_prefill(args) -> dict:
+    """Block-sparse causal prefill (rows a1 pooling, a3, a7) at its full size."""
+    import numpy as np
+    import torch
+    import oracle
+    import top_sparse_attention_mean_amd as sa
+    from oracle.attention import widen
+    from tests.parity_util import to_dev
+    from workloads import get_workload, make_inputs
+    wl = get_workload("sparse_prefill_bf16")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl)
+    Qd, Kd, Vd = (to_dev(x, wl.dtype, dev) for x in (inp.Q, inp.K, inp.V))
+    B, Hq, Hkv, D, L, blk = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N, wl.block
+    M = wl.nb
+    flags = sa.SA_FORCE_SINK | sa.SA_FORCE_LOCAL | sa.SA_CAUSAL
+    sk = sa.sa_build_sketch(Kd, blk)
+    idx = torch.empty(B, Hkv, M, wl.k, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, Hkv, M, dtype=torch.int32, device=dev)
+    O = torch.empty(B, Hq, L, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, Hq, L, dtype=torch.float32, device=dev)
+    sws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_TOPK, B, Hq, Hkv, L, D, blk, M),
+                      dtype=torch.uint8, device=dev)
+
+    def sketch(r):
+        sa.sa_build_sketch(Kd, blk, out=sk)
+
+    def select(r):
+        sa.sa_select_topk(Qd, sk, wl.k, flags=flags, q_block=blk, idx=idx, count=cnt, ws=sws)
+
+    def attend(r):
+        sa.sa_sparse_prefill(Qd, Kd, Vd, idx, cnt, block=blk, O=O, lse=lse)
+
+    n = max(3, args.steps // 100)
+    t_sk = graph_time(sketch, 1, n)
+    t_sel = graph_time(select, 1, n)
+    t_att = graph_time(attend, 1, n)
+    tiles = int(cnt.sum().item()) * (Hq // Hkv)
+    flops = tiles * 4.0 * blk * blk * D                   # QK^T + PV per 128x128 tile
+    tflops = flops / (t_att * 1e-6) / 1e12
+    res = {
+        "workload": wl.name, "us_per_pass": round(t_sk + t_sel + t_att, 2),
+        "pass": "key sketch (blocks of 128) + pooled-query selection + MFMA sparse attention",
+        "kernels_us": {"sa_build_sketch (k_sketch)": round(t_sk, 2),
+                       "sa_select_topk causal (k_sketch pooling Q + k_prefill_select)": round(t_sel, 2),
+                       "sa_sparse_prefill (k_prefill_bf16)": round(t_att, 2)},
+        "tiles_per_head_group": int(cnt.sum().item()),
+        "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 (bf16 32x32x16 MFMA, fp32 accumulate)",
+                     "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "flops_per_launch": flops, "avg_us": round(t_att, 2)},
+    }
+    if not args.no_cpu:
+        # the oracle: selection for every row of every kv head, attention on a row sample
+        Q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
+        t0 = time.perf_counter()
+        Qb, Kb = oracle.prefill_pool_queries(Q, blk, wl.g), oracle.sketch(K, blk)
+        oi, oc = oracle.prefill_select(Qb, Kb, wl.k)
+        t_osel = time.perf_counter() - t0
+        rng = np.random.default_rng(0)
+        rows = [(0, int(h), int(t)) for h, t in zip(rng.integers(0, Hq, 512), rng.integers(0, L, 512))]
+        t0 = time.perf_counter()
+        oracle.prefill_attend_rows(Q, K, V, oi, oc, blk, rows)
+        t_row = (time.perf_counter() - t0) / len(rows)
+        res["cpu_baseline"] = {
+            "value": round((t_osel + t_row * B * Hq * L) * 1e6, 1), "unit": "us/pass",
+            "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"selection of every row timed whole ({t_osel:.1f} s); attention timed "
+                      f"on 512 random rows and scaled to all {B * Hq * L} rows"}
+    return res
+
+
 def pmc_run(args) -> dict:
     """Short run for rocprofv3 counter passes: a plain device copy of known size
     (the counters' calibration) and the dominant kernel on every layer copy."""
@@ -303,6 +454,8 @@ def main(argv=None) -> int:
     ap.add_argument("--layers", type=int, default=16)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the threshold and prefill variant measurements")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 counter passes (no timing output)")
     args = ap.parse_args(argv)
@@ -312,7 +465,19 @@ def main(argv=None) -> int:
         return 2
     if int(os.environ.get("RANK", "0")) != 0:
         return 0
-    res = pmc_run(args) if args.pmc_run else bench_decode(args)
+    if args.pmc_run:
+        res = pmc_run(args)
+    else:
+        res = bench_decode(args)
+        if not args.no_variants:
+            import gc
+            import torch
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["variants"] = {"threshold": bench_threshold(args)}
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["variants"]["prefill"] = bench_prefill(args)
     print(json.dumps(res), flush=True)
     return 0
 
