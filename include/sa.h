@@ -197,6 +197,8 @@ sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B,
  *            O = sum_t softmax(s)_t v_t over the kept tokens, lse = log sum exp s;
  *            an empty selection gives O = 0, lse = -inf.
  * Accumulation is float32 throughout.
+ * bf16 block mode reads each kv head through a 32-bit buffer range:
+ * N * D * 2 <= 0x7f000000 (else SA_ERR_UNSUPPORTED).
  * ws: sa_workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, block, idx_stride)
  *     (for SA_IDX_TOKENS pass block = 0).
  */

@@ -151,6 +151,7 @@ def test_decode_validation(lib):
     assert call(10, 5) == INVALID                 # unknown mode
     assert call(20, 64) == WORKSPACE
     assert call(5, 48) == UNSUPPORTED             # g = 6
+    assert call(7, 9 * 1024 * 1024) == UNSUPPORTED   # one kv head past the 32-bit buffer range
     a = list(base)
     a[10], a[13] = 1, None                        # token mode without counts
     assert f(*a) == INVALID

@@ -84,48 +84,96 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* f
 // lse = (M + log2 L) ln 2 (scores are kept in log2 units).
 // Thread t owns head t / (D/4) and 4 consecutive columns (nh * D / 4 <= 256).
 // Its first kMergeChunk partial loads are issued before the (m, l) pairs are
-// staged in LDS, so both round trips overlap; every thread then forms its
-// head's weights itself (no serial per-head stage, one barrier).
+// staged in LDS (one row of S4 = S rounded up to 4 per head, padded with
+// m = -inf, l = 0), so both round trips overlap.  Up to kMergeRegSplits splits
+// the pairs are read with 16-byte LDS loads into registers and every loop is
+// unrolled; more splits take a plain loop.
 constexpr int kMergeChunk = 16;
+constexpr int kMergeRegSplits = 32;
 
 template <int D>
 __device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv) {
-  constexpr int CH = kMergeChunk;
-  const int S = a.S, tid = threadIdx.x;
+  constexpr int CH = kMergeChunk, SR = kMergeRegSplits;
+  static_assert(SR % CH == 0 && CH % 4 == 0, "chunking");
+  const int S = a.S, S4 = (S + 3) & ~3, tid = threadIdx.x;
   const bool act = tid < nh * (D / 4);
   const int h = act ? tid / (D / 4) : 0, d0 = (tid % (D / 4)) * 4;
   const float* pa = a.pacc + size_t(h0 + h) * S * D + d0;
   u32x4 v[CH];
 #pragma unroll
-  for (int u = 0; u < CH; ++u)
-    if (act && u < S) v[u] = ld16(pa + size_t(u) * D);
+  for (int u = 0; u < CH; ++u) v[u] = ld16(pa + size_t(min(u, S - 1)) * D);
   for (int i = tid; i < nh * S; i += 256) {
+    const int hh = i / S, ss = i - hh * S;
     const u32x2 ml = ld8(a.pml + 2 * (size_t(h0) * S + i));
-    w[i] = __uint_as_float(ml[0]);
-    lv[i] = __uint_as_float(ml[1]);
+    w[hh * S4 + ss] = __uint_as_float(ml[0]);
+    lv[hh * S4 + ss] = __uint_as_float(ml[1]);
+  }
+  if (S4 > S) {
+    for (int i = tid; i < nh * (S4 - S); i += 256) {
+      const int hh = i / (S4 - S), ss = S + i % (S4 - S);
+      w[hh * S4 + ss] = -__builtin_inff();
+      lv[hh * S4 + ss] = 0.f;
+    }
   }
   __syncthreads();
   if (!act) return;
-  const float* wh = w + h * S;
-  const float* lh = lv + h * S;
+  const float* wh = w + h * S4;
+  const float* lh = lv + h * S4;
   float M = -__builtin_inff();
-  for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
   float L = 0.f;
   f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (M != -__builtin_inff()) {
-    for (int s0 = 0; s0 < S; s0 += CH) {
-      if (s0 > 0) {
+  if (S <= SR) {
+    float mv[SR], lw[SR];
 #pragma unroll
-        for (int u = 0; u < CH; ++u)
-          if (s0 + u < S) v[u] = ld16(pa + size_t(s0 + u) * D);
+    for (int q = 0; q < SR / 4; ++q) {
+      f32x4 m4 = f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
+      f32x4 l4 = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (4 * q < S4) {
+        m4 = *reinterpret_cast<const f32x4*>(wh + 4 * q);
+        l4 = *reinterpret_cast<const f32x4*>(lh + 4 * q);
       }
 #pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        if (s0 + u < S) {
-          const float f = exp2_fast(wh[s0 + u] - M);
-          L += lh[s0 + u] * f;
+      for (int e = 0; e < 4; ++e) { mv[4 * q + e] = m4[e]; lw[4 * q + e] = l4[e]; }
+    }
+#pragma unroll
+    for (int s = 0; s < SR; ++s) M = fmaxf(M, mv[s]);
+    if (M != -__builtin_inff()) {
+#pragma unroll
+      for (int s = 0; s < SR; ++s) {
+        mv[s] = exp2_fast(mv[s] - M);         // 0 for the -inf padding
+        L += lw[s] * mv[s];
+      }
+#pragma unroll
+      for (int c = 0; c < SR / CH; ++c) {
+        if (c * CH >= S) break;
+        if (c > 0) {
+#pragma unroll
+          for (int u = 0; u < CH; ++u) v[u] = ld16(pa + size_t(min(c * CH + u, S - 1)) * D);
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          const float f = c * CH + u < S ? mv[c * CH + u] : 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) A[q] += __uint_as_float(v[u][q]) * f;
+        }
+      }
+    }
+  } else {
+    for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
+    if (M != -__builtin_inff()) {
+      for (int s0 = 0; s0 < S; s0 += CH) {
+        if (s0 > 0) {
+#pragma unroll
+          for (int u = 0; u < CH; ++u) v[u] = ld16(pa + size_t(min(s0 + u, S - 1)) * D);
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+          if (s0 + u < S) {
+            const float f = exp2_fast(wh[s0 + u] - M);
+            L += lh[s0 + u] * f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) A[q] += __uint_as_float(v[u][q]) * f;
+          }
         }
       }
     }
@@ -153,7 +201,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   constexpr int TPB = BLOCK / 16;  // 16-token tiles per block
   __shared__ float s_acc[4][2 * G][D + 4];
   __shared__ float s_m[4][G], s_l[4][G];
-  __shared__ float s_w[G * kMaxSplits], s_lv[G * kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float s_w[G * kMaxSplits], s_lv[G * kMaxSplits];
   __shared__ int s_flag;
 
   const int BH = a.B * a.Hkv, N = a.N;
@@ -206,8 +254,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* Kb = static_cast<const uint16_t*>(a.K) + size_t(bh) * N * D;
-  const uint16_t* Vb = static_cast<const uint16_t*>(a.V) + size_t(bh) * N * D;
+  // per-(b, kv head) buffer resources: rows past N (and invalid tiles) read as
+  // zeros, so every load of a batch issues unconditionally
+  const __amdgpu_buffer_rsrc_t rK =
+      make_rsrc(static_cast<const uint16_t*>(a.K) + size_t(bh) * N * D, uint32_t(N) * D * 2);
+  const __amdgpu_buffer_rsrc_t rV =
+      make_rsrc(static_cast<const uint16_t*>(a.V) + size_t(bh) * N * D, uint32_t(N) * D * 2);
   const int nbk = (N + BLOCK - 1) / BLOCK;
   const float sl2 = a.sl2;
 
@@ -228,22 +280,18 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
         }
       }
       tok0s[u] = tok0;
-      if (tok0 >= 0) {
-        const int kr = min(tok0 + nn, N - 1);
-        const uint16_t* kp = Kb + size_t(kr) * D + 8 * gq;
+      const int koff = tok0 >= 0 ? ((tok0 + nn) * D + 8 * gq) * 2 : kBufOOB;
+      const int voff = tok0 >= 0 ? ((tok0 + 4 * gq) * D + EPL * nn) * 2 : kBufOOB;
 #pragma unroll
-        for (int st = 0; st < NST; ++st) ka[u][st] = ld16(kp + 32 * st);
+      for (int st = 0; st < NST; ++st) ka[u][st] = bld16(rK, koff + 64 * st);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int vr = min(tok0 + 4 * gq + j, N - 1);
-          const uint16_t* vp = Vb + size_t(vr) * D + EPL * nn;
-          if constexpr (EPL == 8) {
-            const u32x4 w = ld16(vp);
-            vw[u][j][0] = w[0]; vw[u][j][1] = w[1]; vw[u][j][2] = w[2]; vw[u][j][3] = w[3];
-          } else {
-            const u32x2 w = ld8(vp);
-            vw[u][j][0] = w[0]; vw[u][j][1] = w[1];
-          }
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (EPL == 8) {
+          const u32x4 w = bld16(rV, voff + j * D * 2);
+          vw[u][j][0] = w[0]; vw[u][j][1] = w[1]; vw[u][j][2] = w[2]; vw[u][j][3] = w[3];
+        } else {
+          const u32x2 w = bld8(rV, voff + j * D * 2);
+          vw[u][j][0] = w[0]; vw[u][j][1] = w[1];
         }
       }
     }
@@ -344,7 +392,7 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
   __shared__ float sp[8][CH];
   __shared__ int stok[CH];
   __shared__ float red[8][4];
-  __shared__ float s_w[8 * kMaxSplits], s_lv[8 * kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float s_w[8 * kMaxSplits], s_lv[8 * kMaxSplits];
   __shared__ int s_flag;
 
   const int BH = a.B * a.Hkv, G = a.G, N = a.N, block = a.block;
@@ -461,7 +509,7 @@ __global__ __launch_bounds__(256) void k_decode_tokens(DecodeArgs a) {
   __shared__ float sq[D];
   __shared__ float red[4];
   __shared__ float racc[16][D + 4];
-  __shared__ float s_w[kMaxSplits], s_lv[kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float s_w[kMaxSplits], s_lv[kMaxSplits];
   __shared__ int s_flag;
 
   const int BHq = a.B * a.Hq, N = a.N;

@@ -123,6 +123,8 @@ sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B
     if (dtype == SA_BF16) {
       SUP(block == 64 || block == 128, "bf16 block-mode decode needs block 64 or 128");
       SUP(pow2_le8(G), "bf16 block-mode decode needs g in {1, 2, 4, 8} (got %d)", G);
+      SUP(long(N) * D * 2 <= 0x7f000000L, "bf16 block-mode decode reads one kv head through a "
+          "buffer resource of at most 0x7f000000 bytes (N * D * 2 = %ld)", long(N) * D * 2);
     } else {
       SUP(G <= 8, "float32 decode needs g <= 8 (got %d)", G);
     }

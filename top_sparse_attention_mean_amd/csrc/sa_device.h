@@ -68,6 +68,23 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return perm(b, a, 0x05040100u); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return perm(b, a, 0x07060302u); }
 
+// ------------------------------------------------------------ buffer loads
+// A raw buffer resource over [base, base + bytes) (bytes <= 0x7f000000).  Loads
+// at byte offsets past `bytes` return zeros instead of touching memory, so a
+// tile that is invalid or runs past the end needs no branch: it gets the offset
+// kBufOOB.  Each load takes one 32-bit offset register; constant parts of the
+// offset go into the instruction's immediate field.
+constexpr int kBufOOB = 0x7fff0000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
 // ------------------------------------------------------------ wave scans (DPP)
 // A 64-lane inclusive scan in six register-to-register steps, no LDS: row
 // shifts by 1, 2, 4 and 8 scan each 16-lane row, then row broadcasts add lane
