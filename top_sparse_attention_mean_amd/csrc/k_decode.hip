@@ -88,8 +88,8 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* f
 // m = -inf, l = 0), so both round trips overlap.  Up to kMergeRegSplits splits
 // the pairs are read with 16-byte LDS loads into registers and every loop is
 // unrolled; more splits take a plain loop.
-constexpr int kMergeChunk = 16;
-constexpr int kMergeRegSplits = 32;
+constexpr int kMergeChunk = 24;
+constexpr int kMergeRegSplits = 24;
 
 template <int D>
 __device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv) {
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   constexpr int NST = D / 32;      // contraction steps of the score MFMA
   constexpr int EPL = D / 16;      // value columns per lane = PV MFMAs per tile
   constexpr int TPB = BLOCK / 16;  // 16-token tiles per block
-  __shared__ float s_acc[4][2 * G][D + 4];
+  __shared__ __attribute__((aligned(16))) float s_acc[4][2 * G][D + 4];
   __shared__ float s_m[4][G], s_l[4][G];
   __shared__ __attribute__((aligned(16))) float s_w[G * kMaxSplits], s_lv[G * kMaxSplits];
   __shared__ int s_flag;
@@ -347,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
     }
   }
 
-  // per-wave results -> LDS
+  // per-wave results -> LDS (16-byte stores)
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
   l_tot += __shfl_xor(l_tot, 32, 64);
   if (gq == 0 && nn < G) { s_m[wave][nn] = m_run; s_l[wave][nn] = l_tot; }
@@ -356,28 +356,37 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
     const int row = 4 * gq + r;
     if (row < 2 * G) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) s_acc[wave][row][EPL * nn + e] = acc[e][r];
+      for (int e0 = 0; e0 < EPL; e0 += 4)
+        *reinterpret_cast<f32x4*>(&s_acc[wave][row][EPL * nn + e0]) =
+            f32x4{acc[e0][r], acc[e0 + 1][r], acc[e0 + 2][r], acc[e0 + 3][r]};
     }
   }
   __syncthreads();
 
-  // combine the 4 waves and the hi/lo rows: one (head, column) per thread
+  // combine the 4 waves and the hi/lo rows: one head and 4 columns per thread
   const int h0 = b * a.Hq + kh * G;
-  for (int o = tid; o < G * D; o += 256) {
-    const int h = o / D, d = o % D;
-    const float M = fmaxf(fmaxf(s_m[0][h], s_m[1][h]), fmaxf(s_m[2][h], s_m[3][h]));
-    float Ls = 0.f, A = 0.f;
+  for (int o4 = tid; o4 < G * D / 4; o4 += 256) {
+    const int h = o4 / (D / 4), d0 = (o4 % (D / 4)) * 4;
+    float mw[4], lw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) { mw[w] = s_m[w][h]; lw[w] = s_l[w][h]; }
+    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
+    float Ls = 0.f;
+    f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
     if (M != -__builtin_inff()) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float f = exp2_fast(s_m[w][h] - M);
-        Ls += s_l[w][h] * f;
-        A += (s_acc[w][h][d] + s_acc[w][h + G][d]) * f;
+        const float f = exp2_fast(mw[w] - M);
+        Ls += lw[w] * f;
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(&s_acc[w][h][d0]);
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(&s_acc[w][h + G][d0]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) A[q] += (hi[q] + lo[q]) * f;
       }
     }
     const size_t pi = size_t(h0 + h) * a.S + s;
-    a.pacc[pi * D + d] = A;
-    if (d == 0) { a.pml[2 * pi] = M; a.pml[2 * pi + 1] = Ls; }
+    *reinterpret_cast<f32x4*>(&a.pacc[pi * D + d0]) = A;
+    if (d0 == 0) *reinterpret_cast<u32x2*>(&a.pml[2 * pi]) = u32x2{__float_as_uint(M), __float_as_uint(Ls)};
   }
   if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
   merge_tail<D>(a, h0, G, s_w, s_lv);
