@@ -14,9 +14,10 @@
 //                   workgroup per (b, kv head, 64 sketch rows); each wave issues
 //                   all of its row loads before the group's mean query (scale
 //                   folded in) is formed; every row dot product is reduced
-//                   across 32 (D=128) or 16 (D=64) lanes.  Workgroup id %
-//                   (B*Hkv) picks the (b, kv head), so with B*Hkv a multiple of
-//                   8 every (b, kv head) stays on one XCD.  Optional extra
+//                   across 32 (D=128) or 16 (D=64) lanes with DPP row shifts.
+//                   Workgroup id % (B*Hkv) picks the (b, kv head), so with
+//                   B*Hkv a multiple of 8 every (b, kv head) stays on one
+//                   XCD.  Optional extra
 //                   workgroups rebuild one block's sketch from K and score it.
 //   k_select_rows   one 256-thread workgroup per (b, kv head): the row's
 //                   scores become order-preserving keys in LDS and the exact
@@ -121,9 +122,8 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
       const int r = rw + i * RPI + sub;
       float p = q[0] * __uint_as_float(w[i][0]) + q[1] * __uint_as_float(w[i][1]) +
                 q[2] * __uint_as_float(w[i][2]) + q[3] * __uint_as_float(w[i][3]);
-#pragma unroll
-      for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
-      if (r < nb && r != a.upd && lc == 0) srow[r] = p;
+      p = group_sum_to_last<LPR>(p);
+      if (r < nb && r != a.upd && lc == LPR - 1) srow[r] = p;
     }
     return;
   }
@@ -302,9 +302,8 @@ __global__ __launch_bounds__(256) void k_prefill_select(const float* __restrict_
           __uint_as_float(qv[2]) * __uint_as_float(w[2]) +
           __uint_as_float(qv[3]) * __uint_as_float(w[3]);
     }
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, 64);
-    if (ok && lc == 0) {
+    p = group_sum_to_last<LPR>(p);
+    if (ok && lc == LPR - 1) {
       p *= scale;
       keys[j] = score_key(p);
       if (srow) srow[j] = p;

@@ -109,6 +109,22 @@ __device__ __forceinline__ uint32_t dpp_scan(uint32_t v, uint32_t id, Op op) {
 __device__ __forceinline__ uint32_t lane63(uint32_t v) {
   return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
 }
+// Sum over aligned groups of L consecutive lanes (L = 16 or 32) by DPP; the
+// group's total lands in its last lane (the other lanes hold partial sums).
+template <int L>
+__device__ __forceinline__ float group_sum_to_last(float v) {
+  static_assert(L == 16 || L == 32, "groups of 16 or 32 lanes");
+  auto add = [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  };
+  uint32_t x = __float_as_uint(v);
+  x = add(x, dpp_u32<0x111>(0u, x));
+  x = add(x, dpp_u32<0x112>(0u, x));
+  x = add(x, dpp_u32<0x114>(0u, x));
+  x = add(x, dpp_u32<0x118>(0u, x));
+  if constexpr (L == 32) x = add(x, dpp_u32<0x142, 0xa>(0u, x));
+  return __uint_as_float(x);
+}
 // Inclusive prefix sum over the 64 lanes (lane order).
 __device__ __forceinline__ int wave_incl_scan(int v) {
   return int(dpp_scan(uint32_t(v), 0u, [](uint32_t a, uint32_t b) { return a + b; }));
