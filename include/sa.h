@@ -235,7 +235,9 @@ sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V,
  * skip), score and select the top-k blocks (forced sink + local), then the
  * split-K sparse attention and merge.  Same result as calling
  * sa_build_sketch, sa_select_topk (decode) and sa_sparse_decode (blocks) in
- * sequence; idx/count/score (score may be NULL) receive the selection.
+ * sequence (the same selection; the attention output up to float32 rounding,
+ * since the fused kernel splits the blocks over workgroups differently);
+ * idx/count/score (score may be NULL) receive the selection.
  * ws: sa_workspace_bytes(SA_OP_DECODE_STEP, B, Hq, Hkv, N, D, block, k).
  */
 sa_status sa_decode_step(const void* Q, const void* K, const void* V,
@@ -251,8 +253,10 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V,
  * selection rule of sa_select_topk, decode), then the split-K sparse attention
  * over the selected blocks and the merge (the decode steps of "The Sparse
  * Frontier", Contributi §2 Quest; split-K merge, "Pulsar Attention", Fase 2).
- * Each attention workgroup repeats the selection of its kv head from the score
- * row instead of waiting on another workgroup.
+ * Each attention workgroup repeats the selection pre-filter of its kv head from
+ * the score row instead of waiting on another workgroup, then ranks only the
+ * candidates of its own slice of tiles and attends to the kept ones; the last
+ * workgroup of the head merges the partials and writes idx and count.
  *
  *   Q [B, Hq, D], K, V [B, Hkv, N, D] dtype
  *   score    [B, Hkv, nb] float32 block scores (input; nb = ceil(N / block));
@@ -261,8 +265,9 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V,
  *            SA_FORCE_SINK | SA_FORCE_LOCAL
  *   idx      [B, Hkv, k] int32 out, ascending, -1 padded; count [B, Hkv] out
  *   O        [B, Hq, D] out_dtype;  lse [B, Hq] float32 (NULL to skip)
- * Same result as sa_select_topk's selection followed by sa_sparse_decode
- * (blocks).  nb <= 8192.
+ * Same selection as sa_select_topk's; the attention equals that of
+ * sa_sparse_decode (blocks) on it up to float32 rounding, and repeated calls
+ * give bitwise the same output.  nb <= 8192.
  * ws: sa_workspace_bytes(SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, block, k).
  */
 sa_status sa_select_decode(const void* Q, const void* K, const void* V,

@@ -40,7 +40,12 @@ def test_full_decode(name):
     # same step through the fused entry point, updating the newest block's sketch
     O2, lse2, idx2, cnt2 = sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block,
                                              update_block=wl.nb - 1, out_dtype=torch.float32)
-    assert torch.equal(idx, idx2) and torch.equal(O32, O2)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    # the fused kernel splits the same blocks differently, which changes the
+    # running maxima the probabilities are scaled by and so their rounding (P
+    # keeps 16 significant bits as bf16 hi + lo): agreement to ~2^-16
+    assert max_abs(O32.cpu().numpy(), O2.cpu().numpy()) <= 1e-5
+    assert max_abs(lse.cpu().numpy(), lse2.cpu().numpy()) <= 1e-5
     sk_ref = oracle.sketch(K, wl.block)
     assert max_abs(sk.cpu().numpy(), sk_ref) <= 2e-6 * max(1.0, np.abs(sk_ref).max())
     sc_ref = oracle.block_scores(q, sk_ref)

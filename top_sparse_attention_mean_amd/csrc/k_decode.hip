@@ -58,23 +58,30 @@ struct DecodeArgs {
   unsigned flags;
   int32_t* sel_idx;
   int32_t* sel_count;
+  int32_t* sel_ent;   // [B*Hkv, kSelEntCap] kept block (or -1) per entry of a row
 };
+static_assert(kSelWords * 32 >= kMaxNbDecode, "one bitmap word per 32 blocks of a row");
+static_assert(2 + kCandCap <= kSelEntCap && kSelEntCap <= 3 * 256, "entries of a row: forced blocks and candidates");
 
 // ---------------------------------------------------------------- merge tail
+// Partials cross workgroups through the workspace with agent-coherent (sc1)
+// stores and loads -- the accesses the compiler emits for agent-scope atomic
+// stores and loads -- so no L2 writeback or invalidate is needed.
+//
 // Publish this workgroup's partial and count arrivals; true for the last one.
-// Every wave waits for its own stores to reach L2 (s_waitcnt), then one thread
-// issues the agent-scope release (an L2 writeback) and the arrival atomic: a
-// single writeback per workgroup instead of one per wave.
+// Every wave waits until its sc1 stores have completed (s_waitcnt), then one
+// thread increments the counter; an atomic is performed at the device's
+// coherent level, so when it returns total - 1 every other workgroup's stores
+// had completed before its increment, and the last one's sc1 loads, issued
+// after that, see them.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    *flag = atomicAdd(counter, 1u) == uint32_t(total - 1);
-  }
+  if (threadIdx.x == 0)
+    *flag = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            uint32_t(total - 1);
   __syncthreads();
   if (!*flag) return false;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   if (threadIdx.x == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
@@ -83,96 +90,109 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* f
 // M = max m_s, L = sum l_s 2^(m_s - M), O = sum acc_s 2^(m_s - M) / L,
 // lse = (M + log2 L) ln 2 (scores are kept in log2 units).
 // Thread t owns head t / (D/4) and 4 consecutive columns (nh * D / 4 <= 256).
-// Its first kMergeChunk partial loads are issued before the (m, l) pairs are
-// staged in LDS (one row of S4 = S rounded up to 4 per head, padded with
-// m = -inf, l = 0), so both round trips overlap.  Up to kMergeRegSplits splits
-// the pairs are read with 16-byte LDS loads into registers and every loop is
-// unrolled; more splits take a plain loop.
-constexpr int kMergeChunk = 24;
-constexpr int kMergeRegSplits = 24;
+// Its first kMergeChunk partial loads and the (m, l) pair loads are issued
+// first; mid() (all threads call it) runs while they are in flight.  The
+// pairs are staged in LDS, one row per head of stride Sp (S up to
+// kMergeRegSplits: Sp = kMergeRegSplits, so one unrolled branch-free pass of
+// 16-byte LDS reads serves every split; else S rounded up to 4), padded with
+// m = -inf, l = 0.  Beyond kMergeRegSplits the rest follow 8 at a time.
+constexpr int kMergeChunk = 32;
+constexpr int kMergeRegSplits = 32;
 
-template <int D>
-__device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv) {
+struct NoMid {
+  __device__ void operator()() const {}
+};
+
+template <int D, typename Mid = NoMid>
+__device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv,
+                           Mid mid = Mid()) {
   constexpr int CH = kMergeChunk, SR = kMergeRegSplits;
-  static_assert(SR % CH == 0 && CH % 4 == 0, "chunking");
-  const int S = a.S, S4 = (S + 3) & ~3, tid = threadIdx.x;
+  static_assert(SR == CH && CH % 4 == 0, "one chunk holds the register path");
+  const int S = a.S, Sp = S <= SR ? SR : (S + 3) & ~3, tid = threadIdx.x;
   const bool act = tid < nh * (D / 4);
   const int h = act ? tid / (D / 4) : 0, d0 = (tid % (D / 4)) * 4;
-  const float* pa = a.pacc + size_t(h0 + h) * S * D + d0;
+  // the head group's partials through one buffer resource: a lane offset plus
+  // a scalar offset per split
+  const __amdgpu_buffer_rsrc_t rP =
+      make_rsrc(a.pacc + size_t(h0) * S * D, uint32_t(nh) * S * D * sizeof(float));
+  const int voff = (h * S * D + d0) * int(sizeof(float));
   u32x4 v[CH];
 #pragma unroll
-  for (int u = 0; u < CH; ++u) v[u] = ld16(pa + size_t(min(u, S - 1)) * D);
-  for (int i = tid; i < nh * S; i += 256) {
-    const int hh = i / S, ss = i - hh * S;
-    const u32x2 ml = ld8(a.pml + 2 * (size_t(h0) * S + i));
-    w[hh * S4 + ss] = __uint_as_float(ml[0]);
-    lv[hh * S4 + ss] = __uint_as_float(ml[1]);
-  }
-  if (S4 > S) {
-    for (int i = tid; i < nh * (S4 - S); i += 256) {
-      const int hh = i / (S4 - S), ss = S + i % (S4 - S);
-      w[hh * S4 + ss] = -__builtin_inff();
-      lv[hh * S4 + ss] = 0.f;
+  for (int u = 0; u < CH; ++u) v[u] = bld16c(rP, voff, min(u, S - 1) * D * int(sizeof(float)));
+  // (m, l) pairs: nh * S <= 8 * kMaxSplits = 4 per thread
+  static_assert(8 * kMaxSplits <= 4 * 256, "pairs per thread");
+  const int np = nh * S;
+  const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.pml + 2 * size_t(h0) * S, uint32_t(np) * 8);
+  u32x2 ml[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ml[q] = bld8c(rM, min(tid + 256 * q, np - 1) * 8);
+  mid();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = tid + 256 * q;
+    if (i < np) {
+      const int hh = i / S, ss = i - hh * S;
+      w[hh * Sp + ss] = __uint_as_float(ml[q][0]);
+      lv[hh * Sp + ss] = __uint_as_float(ml[q][1]);
     }
+  }
+  for (int i = tid; i < nh * (Sp - S); i += 256) {
+    const int hh = i / (Sp - S), ss = S + i % (Sp - S);
+    w[hh * Sp + ss] = -__builtin_inff();
+    lv[hh * Sp + ss] = 0.f;
   }
   __syncthreads();
   if (!act) return;
-  const float* wh = w + h * S4;
-  const float* lh = lv + h * S4;
+  const float* wh = w + h * Sp;
+  const float* lh = lv + h * Sp;
   float M = -__builtin_inff();
   float L = 0.f;
   f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
   if (S <= SR) {
-    float mv[SR], lw[SR];
+    // every partial is already loaded: M from the staged m row, then one
+    // unrolled pass of (m, l) 16-byte LDS reads (the -inf padding weighs 0)
+    f32x4 m4[SR / 4];
 #pragma unroll
     for (int q = 0; q < SR / 4; ++q) {
-      f32x4 m4 = f32x4{-__builtin_inff(), -__builtin_inff(), -__builtin_inff(), -__builtin_inff()};
-      f32x4 l4 = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (4 * q < S4) {
-        m4 = *reinterpret_cast<const f32x4*>(wh + 4 * q);
-        l4 = *reinterpret_cast<const f32x4*>(lh + 4 * q);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { mv[4 * q + e] = m4[e]; lw[4 * q + e] = l4[e]; }
+      m4[q] = *reinterpret_cast<const f32x4*>(wh + 4 * q);
+      M = fmaxf(M, fmaxf(fmaxf(m4[q][0], m4[q][1]), fmaxf(m4[q][2], m4[q][3])));
     }
-#pragma unroll
-    for (int s = 0; s < SR; ++s) M = fmaxf(M, mv[s]);
     if (M != -__builtin_inff()) {
 #pragma unroll
-      for (int s = 0; s < SR; ++s) {
-        mv[s] = exp2_fast(mv[s] - M);         // 0 for the -inf padding
-        L += lw[s] * mv[s];
-      }
+      for (int q = 0; q < SR / 4; ++q) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lh + 4 * q);
 #pragma unroll
-      for (int c = 0; c < SR / CH; ++c) {
-        if (c * CH >= S) break;
-        if (c > 0) {
+        for (int e = 0; e < 4; ++e) {
+          const float f = exp2_fast(m4[q][e] - M);
+          L += l4[e] * f;
 #pragma unroll
-          for (int u = 0; u < CH; ++u) v[u] = ld16(pa + size_t(min(c * CH + u, S - 1)) * D);
-        }
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-          const float f = c * CH + u < S ? mv[c * CH + u] : 0.f;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) A[q] += __uint_as_float(v[u][q]) * f;
+          for (int c = 0; c < 4; ++c) A[c] += __uint_as_float(v[4 * q + e][c]) * f;
         }
       }
     }
   } else {
     for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
     if (M != -__builtin_inff()) {
-      for (int s0 = 0; s0 < S; s0 += CH) {
-        if (s0 > 0) {
+      // the first CH partials are loaded; the rest follow 8 at a time
 #pragma unroll
-          for (int u = 0; u < CH; ++u) v[u] = ld16(pa + size_t(min(s0 + u, S - 1)) * D);
-        }
+      for (int u = 0; u < CH; ++u) {
+        const float f = exp2_fast(wh[u] - M);
+        L += lh[u] * f;
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
+        for (int c = 0; c < 4; ++c) A[c] += __uint_as_float(v[u][c]) * f;
+      }
+      for (int s0 = CH; s0 < S; s0 += 8) {
+        u32x4 w8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          w8[u] = bld16c(rP, voff, min(s0 + u, S - 1) * D * int(sizeof(float)));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
           if (s0 + u < S) {
             const float f = exp2_fast(wh[s0 + u] - M);
             L += lh[s0 + u] * f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) A[q] += __uint_as_float(v[u][q]) * f;
+            for (int c = 0; c < 4; ++c) A[c] += __uint_as_float(w8[u][c]) * f;
           }
         }
       }
@@ -210,28 +230,105 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int gq = lane >> 4, nn = lane & 15;
 
-  // the split's slot range comes from idx_stride, so its index loads do not
-  // wait for count; slots at or past count are skipped
-  const int bps = (a.idx_stride + a.S - 1) / a.S;
-  const int blk0 = s * bps;
-  const int blk1 = min(blk0 + bps, a.idx_stride);
-  const int ntiles = max(blk1 - blk0, 0) * TPB;
-  int cnt;
-  const int32_t* ib;
+  // Work is split by 16-token tiles: split s takes tiles [g0, g0 + tps) of
+  // the head's slot list (slot = tile / TPB).  The range comes from
+  // idx_stride, so the index loads do not wait for count; slots at or past
+  // count are skipped.
+  const int tps = (a.idx_stride * TPB + a.S - 1) / a.S;
+  const int g0 = s * tps;
+  int ntiles = max(min(g0 + tps, a.idx_stride * TPB) - g0, 0);
+  int cnt = 0;
+  const int32_t* ib = nullptr;
+  constexpr int KPT = SEL ? SELKPT : 1;
+  SelectLdsT<256, KPT>* selp = nullptr;
+  // slice mode of the selecting kernel: the head's splits own tile slices of
+  // the candidate list instead of the ranked selection
+  bool cmode = false;
+  const int* wl = nullptr;   // this wave's kept tiles (token offsets), slice mode
+  const int* es = nullptr;   // kept block or -1 of the entries this split owns
+  int cm_E = 0, cm_ea = 0, cm_ne = 0, cm_u0 = 0;
   if constexpr (SEL) {
-    // every split selects its kv head's blocks itself from the score row
-    extern __shared__ __attribute__((aligned(16))) int dyn_i[];   // list[k]
-    constexpr int KPT = SELKPT > 0 ? SELKPT : 1;
+    // every split runs the selection pre-filter of its kv head from the score row
+    extern __shared__ __attribute__((aligned(16))) int dyn_i[];   // max(k, 320) ints
     __shared__ SelectLdsT<256, KPT> S;
+    selp = &S;
     int* list = dyn_i;
+    const int nb = a.nb, k = a.k;
+    const bool sink = a.flags & SA_FORCE_SINK, local = a.flags & SA_FORCE_LOCAL;
+    const int F = int(sink) + int(local), need = k - F, W = (nb + 31) >> 5;
     uint32_t kr[KPT];
-    load_keys_reg<256, KPT>(a.sel_scores + size_t(bh) * a.nb, a.nb, kr);
-    cnt = select_decode_row<256, KPT>(kr, a.nb, a.k, a.flags, list, S);
-    ib = list;
-    if (s == 0) {
-      int32_t* orow = a.sel_idx + size_t(bh) * a.k;
-      for (int j = tid; j < a.k; j += 256) orow[j] = j < cnt ? list[j] : -1;
-      if (tid == 0) a.sel_count[bh] = cnt;
+    load_keys_reg<256, KPT>(a.sel_scores + size_t(bh) * nb, nb, kr);
+    if (k >= nb) {
+      for (int j = tid; j < nb; j += 256) list[j] = j;
+      __syncthreads();
+      cnt = nb;
+    } else {
+      sel_init(S, W);
+      int ix[KPT];   // keys masked in place
+      int C = -1;
+      if (need > 0) {
+        const uint32_t tmax = sel_mask_keys<256, KPT>(kr, sink ? 1 : 0, local ? nb - 1 : nb, kr, ix);
+        C = sel_prefilter<256, KPT>(kr, ix, tmax, need, S);
+      }
+      // entries [forced blocks, candidates] of TPB tiles each: split s owns
+      // the tiles [s*cpu, s*cpu + cpu) of that sequence
+      const int E = F + C, U = E * TPB, cpu = (U + a.S - 1) / a.S;
+      cmode = C >= 0 && cpu <= 64;
+      if (cmode) {
+        // rank only the entries of the owned tiles (every wave does it, so no
+        // barrier; each keeps its own copy of the kept tiles, in tile order)
+        const int u0 = s * cpu, u1 = min(u0 + cpu, U);
+        const int ea = u0 / TPB, ne = u1 > u0 ? (u1 - 1) / TPB - ea + 1 : 0;
+        const int g = lane >> 3, h = lane & 7;
+        int* tl = list + wave * 64;
+        int* el = list + 256;   // written and read by wave 0 only
+        int nk = 0;
+        for (int j0 = 0; j0 < ne; j0 += 8) {
+          const int e = ea + j0 + g;
+          const bool in = j0 + g < ne, forced = e < F;
+          const uint64_t x = S.cand[min(max(e - F, 0), C - 1)];
+          const int rk = sel_rank_entry8<256, KPT>(x, C, S);
+          const int blk = forced ? (sink && e == 0 ? 0 : nb - 1) : int(~uint32_t(x));
+          const uint64_t km = __ballot(h == 7 && (forced || rk < need));
+          const bool keep = (km >> (8 * g + 7)) & 1ull;
+          // the split holding an entry's first tile reports it
+          if (wave == 0 && h == 7 && in && e * TPB >= u0) el[j0 + g] = keep ? blk : -1;
+          // lane h < TPB stands for tile h of entry e
+          const int u = e * TPB + h, tok0 = blk * BLOCK + h * 16;
+          const bool take = keep && in && h < TPB && u >= u0 && u < u1 && tok0 < N;
+          const uint64_t tm = __ballot(take);
+          if (take) tl[nk + __popcll(tm & ((1ull << lane) - 1ull))] = tok0;
+          nk += __popcll(tm);
+        }
+        wl = tl;
+        es = el;
+        ntiles = nk;
+        cm_E = E; cm_ea = ea; cm_ne = ne; cm_u0 = u0;
+      } else {
+        if (C >= 0) {
+          sel_rank_all<256, KPT>(C, need, S);
+        } else if (need > 0) {
+          bool cand[KPT];
+#pragma unroll
+          for (int r = 0; r < KPT; ++r) cand[r] = kr[r] != 0u;
+          sel_mark_top_kv<256, KPT, KPT>(kr, ix, cand, nb - F, need, S);
+        } else {
+          __syncthreads();   // publishes sel_init before the forced marks
+        }
+        if (tid == 0) {
+          if (sink) sel_mark(S.bm, 0);
+          if (local) sel_mark(S.bm, nb - 1);
+        }
+        cnt = sel_bitmap_to_list(S, W, list, k);
+      }
+    }
+    if (!cmode) {
+      ib = list;
+      if (s == 0) {
+        int32_t* orow = a.sel_idx + size_t(bh) * k;
+        for (int j = tid; j < k; j += 256) orow[j] = j < cnt ? list[j] : -1;
+        if (tid == 0) a.sel_count[bh] = cnt;
+      }
     }
   } else {
     cnt = a.count ? min(max(a.count[bh], 0), a.idx_stride) : a.idx_stride;
@@ -272,11 +369,15 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
     for (int u = 0; u < kTileBatch; ++u) {
       const int t = tb + 4 * u;
       int tok0 = -1;
-      if (t < ntiles && blk0 + t / TPB < cnt) {
-        const int blk = ib[blk0 + t / TPB];
-        if (blk >= 0 && blk < nbk) {
-          tok0 = blk * BLOCK + (t % TPB) * 16;
-          if (tok0 >= N) tok0 = -1;
+      if (t < ntiles) {
+        if (SEL && cmode) {
+          tok0 = wl[t];
+        } else if ((g0 + t) / TPB < cnt) {
+          const int blk = ib[(g0 + t) / TPB];
+          if (blk >= 0 && blk < nbk) {
+            tok0 = blk * BLOCK + ((g0 + t) % TPB) * 16;
+            if (tok0 >= N) tok0 = -1;
+          }
         }
       }
       tok0s[u] = tok0;
@@ -365,6 +466,9 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
 
   // combine the 4 waves and the hi/lo rows: one head and 4 columns per thread
   const int h0 = b * a.Hq + kh * G;
+  const __amdgpu_buffer_rsrc_t rPw =
+      make_rsrc(a.pacc + size_t(h0) * a.S * D, uint32_t(G) * a.S * D * sizeof(float));
+  const __amdgpu_buffer_rsrc_t rMw = make_rsrc(a.pml + 2 * size_t(h0) * a.S, uint32_t(G) * a.S * 8);
   for (int o4 = tid; o4 < G * D / 4; o4 += 256) {
     const int h = o4 / (D / 4), d0 = (o4 % (D / 4)) * 4;
     float mw[4], lw[4];
@@ -384,12 +488,47 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
         for (int q = 0; q < 4; ++q) A[q] += (hi[q] + lo[q]) * f;
       }
     }
-    const size_t pi = size_t(h0 + h) * a.S + s;
-    *reinterpret_cast<f32x4*>(&a.pacc[pi * D + d0]) = A;
-    if (d0 == 0) *reinterpret_cast<u32x2*>(&a.pml[2 * pi]) = u32x2{__float_as_uint(M), __float_as_uint(Ls)};
+    const int pi = h * a.S + s;   // partial within the head group
+    bst16c(rPw, (pi * D + d0) * int(sizeof(float)), __builtin_bit_cast(u32x4, A));
+    if (d0 == 0) bst8c(rMw, pi * 8, u32x2{__float_as_uint(M), __float_as_uint(Ls)});
+  }
+  int32_t* gent = nullptr;
+  if constexpr (SEL) {
+    gent = a.sel_ent + size_t(bh) * kSelEntCap;
+    if (cmode && wave == 0) {
+      for (int i = lane; i < cm_ne; i += 64)
+        if ((cm_ea + i) * TPB >= cm_u0)
+          __hip_atomic_store(gent + cm_ea + i, es[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
-  merge_tail<D>(a, h0, G, s_w, s_lv);
+  if constexpr (SEL) {
+    // slice mode: the ascending idx row from the entries' kept blocks, built
+    // while the partials load
+    int ev[3] = {-1, -1, -1};
+    if (cmode) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (tid + 256 * q < cm_E)
+          ev[q] = __hip_atomic_load(gent + tid + 256 * q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    auto write_idx = [&]() {
+      if (!cmode) return;
+      const int W = (a.nb + 31) >> 5;
+      if (tid < W) selp->bm[tid] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 3; ++q)
+        if (ev[q] >= 0) sel_mark(selp->bm, ev[q]);
+      int32_t* orow = a.sel_idx + size_t(bh) * a.k;
+      const int tot = sel_bitmap_to_list(*selp, W, orow, a.k);   // starts with a barrier
+      for (int j = tot + tid; j < a.k; j += 256) orow[j] = -1;
+      if (tid == 0) a.sel_count[bh] = tot;
+    };
+    merge_tail<D>(a, h0, G, s_w, s_lv, write_idx);
+  } else {
+    merge_tail<D>(a, h0, G, s_w, s_lv);
+  }
 }
 
 // ---------------------------------------------------------------- float32 VALU
@@ -500,8 +639,11 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
     if (o < G * D) {
       const int h = o / D, d = o % D;
       const size_t pi = size_t(h0 + h) * a.S + s;
-      a.pacc[pi * D + d] = acc[i];
-      if (d == 0) { a.pml[2 * pi] = m_run[h]; a.pml[2 * pi + 1] = l_run[h]; }
+      __hip_atomic_store(a.pacc + pi * D + d, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(a.pml + 2 * pi, m_run[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.pml + 2 * pi + 1, l_run[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
@@ -631,8 +773,11 @@ __global__ __launch_bounds__(256) void k_decode_tokens(DecodeArgs a) {
     float A = 0.f;
     for (int g = 0; g < 16; ++g) A += racc[g][d];
     const size_t pi = size_t(bhq) * a.S + s;
-    a.pacc[pi * D + d] = A;
-    if (d == 0) { a.pml[2 * pi] = m_run; a.pml[2 * pi + 1] = l_run; }
+    __hip_atomic_store(a.pacc + pi * D + d, A, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == 0) {
+      __hip_atomic_store(a.pml + 2 * pi, m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.pml + 2 * pi + 1, l_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   if (!arrive_last(&a.counter[bhq * kCounterStride], a.S, &s_flag)) return;
   merge_tail<D>(a, bhq, 1, s_w, s_lv);
@@ -656,6 +801,7 @@ static DecodeArgs make_args(const void* Q, const void* K, const void* V, int B, 
   a.O = O; a.out_bf16 = out_dtype == SA_BF16; a.lse = lse;
   a.sel_scores = nullptr; a.nb = 0; a.k = 0; a.flags = 0; a.sel_idx = nullptr;
   a.sel_count = nullptr;
+  a.sel_ent = reinterpret_cast<int32_t*>(base + w.ent_off);
   return a;
 }
 
@@ -698,7 +844,7 @@ hipError_t launch_decode_select_blocks(const void* Q, const void* K, const void*
                            ws, O, out_dtype, lse);
   a.sel_scores = scores; a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
   const dim3 g(static_cast<unsigned>(long(B) * Hkv * w.S));
-  const size_t lds = size_t(k) * sizeof(int);
+  const size_t lds = size_t(k > 320 ? k : 320) * sizeof(int);
   (void)D;   // the selecting variant is compiled for D = 128
   const bool small = nb <= 4096;
   if (block == 64) {

@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "sa_internal.h"
 
 using namespace sa;
@@ -134,7 +136,9 @@ sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B
     return fail(SA_ERR_INVALID, "unknown mode %d", mode);
   }
   const DecodeWs w = decode_ws(B, Hq, Hkv, D, mode, block, idx_stride);
-  REQ(long(B) * (mode == SA_IDX_BLOCKS ? Hkv : Hq) * w.S < (1L << 31), "grid too large");
+  const int Sg = mode == SA_IDX_BLOCKS ? std::max(w.S, decode_sel_splits(B * Hkv, idx_stride, block))
+                                       : w.S;
+  REQ(long(B) * (mode == SA_IDX_BLOCKS ? Hkv : Hq) * Sg < (1L << 31), "grid too large");
   if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);
   PTR(ws);
   return SA_OK;
@@ -150,13 +154,15 @@ static sa_status run_select_decode(const void* Q, const void* K, const void* V, 
                                    int nb, int k, unsigned flags, float sc, int32_t* idx,
                                    int32_t* count, void* O, int out_dtype, float* lse, void* dws,
                                    hipStream_t st, const char* what) {
-  const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
   if (dtype == SA_BF16 && D == 128 && k <= kMaxKFused) {
+    // same workspace size as the block decode; its own split count
+    const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k, true);
     return hip_status(launch_decode_select_blocks(Q, K, V, B, Hq, Hkv, N, D, sc, block, scores, nb,
                                                   k, flags, idx, count, w, dws, O, out_dtype, lse,
                                                   st),
                       what);
   }
+  const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
   const hipError_t e = launch_select_rows(scores, B * Hkv, nb, k, flags, idx, count, st);
   if (e != hipSuccess) return hip_status(e, what);
   return hip_status(launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count,

@@ -84,6 +84,30 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// Agent-coherent accesses (cache policy sc1, the policy the compiler gives
+// agent-scope atomic loads and stores): a completed sc1 store is visible to
+// sc1 loads from every compute unit of the device, whatever its L2 holds.
+// Loads take a wave-uniform part of the offset in a scalar register (soff),
+// so a run of loads shares one offset VGPR.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ u32x4 bld16c(__amdgpu_buffer_rsrc_t r, int off, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, kCoherent));
+}
+__device__ __forceinline__ u32x2 bld8c(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ uint32_t bld4c(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent);
+}
+__device__ __forceinline__ void bst16c(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherent);
+}
+__device__ __forceinline__ void bst8c(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCoherent);
+}
+__device__ __forceinline__ void bst4c(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kCoherent);
+}
 
 // ------------------------------------------------------------ wave scans (DPP)
 // A 64-lane inclusive scan in six register-to-register steps, no LDS: row
@@ -124,6 +148,15 @@ __device__ __forceinline__ float group_sum_to_last(float v) {
   x = add(x, dpp_u32<0x118>(0u, x));
   if constexpr (L == 32) x = add(x, dpp_u32<0x142, 0xa>(0u, x));
   return __uint_as_float(x);
+}
+// Integer sum over each group of 8 adjacent lanes, landing in the group's
+// last lane (the other lanes hold partial sums).
+__device__ __forceinline__ int group_isum8_to_last(int v) {
+  uint32_t x = uint32_t(v);
+  x += dpp_u32<0x111>(0u, x);
+  x += dpp_u32<0x112>(0u, x);
+  x += dpp_u32<0x114>(0u, x);
+  return int(x);
 }
 // Inclusive prefix sum over the 64 lanes (lane order).
 __device__ __forceinline__ int wave_incl_scan(int v) {

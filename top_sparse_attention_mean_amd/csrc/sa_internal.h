@@ -46,23 +46,51 @@ inline int decode_token_splits(int BHq, int idx_stride) {
   return S;
 }
 
-// Workspace of the split-K decode: partial accumulators, (m, l) pairs and one
-// arrival counter per head group (zero between calls).
+constexpr int kCUs = 256;             // compute units of the gfx950 part
+constexpr int kSelEntCap = 520;       // entries of a selecting-decode row: 2 forced + 512 candidates
+
+// Splits per (b, kv head) of the decode that selects its own blocks: one
+// workgroup per compute unit when the heads are few (the gather is then bound
+// by the busiest unit's bytes, so the work is spread as evenly as the heads
+// allow), capped where a split would get less than about half a batch of tiles.
+inline int decode_sel_splits(int BH, int k, int block) {
+  int S = cdiv(kCUs, BH);
+  const int cap = decode_block_splits(2 * k, block);
+  if (S > cap) S = cap;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  return S;
+}
+
+// Workspace of the split-K decode: partial accumulators, (m, l) pairs, one
+// arrival counter per head group (zero between calls) and, in block mode, the
+// per-entry kept blocks of the selecting decode ([B*Hkv, kSelEntCap] int32,
+// rewritten by every call).  Block mode sizes the partials for the larger
+// split count of the two block-mode kernels, so one workspace serves both;
+// `fused` picks the split count S of the selecting kernel.
 struct DecodeWs {
-  size_t acc_off, ml_off, cnt_off, bytes;
+  size_t acc_off, ml_off, cnt_off, ent_off, bytes;
   int S;
 };
 inline DecodeWs decode_ws(int B, int Hq, int Hkv, int D, int mode, int block,
-                          int idx_stride) {
+                          int idx_stride, bool fused = false) {
   DecodeWs w{};
-  w.S = mode == SA_IDX_BLOCKS ? decode_block_splits(idx_stride, block)
-                              : decode_token_splits(B * Hq, idx_stride);
-  const size_t parts = size_t(B) * Hq * w.S;
+  const bool blocks = mode == SA_IDX_BLOCKS;
+  int Ssz;
+  if (blocks) {
+    const int Sp = decode_block_splits(idx_stride, block);
+    const int Sf = decode_sel_splits(B * Hkv, idx_stride, block);
+    w.S = fused ? Sf : Sp;
+    Ssz = Sp > Sf ? Sp : Sf;
+  } else {
+    w.S = Ssz = decode_token_splits(B * Hq, idx_stride);
+  }
+  const size_t parts = size_t(B) * Hq * Ssz;
   w.acc_off = 0;
   w.ml_off = align256(parts * D * sizeof(float));
   w.cnt_off = w.ml_off + align256(parts * 2 * sizeof(float));
-  w.bytes = w.cnt_off + align256(size_t(B) * Hq * kCounterStride * sizeof(uint32_t));
-  (void)Hkv;
+  w.ent_off = w.cnt_off + align256(size_t(B) * Hq * kCounterStride * sizeof(uint32_t));
+  w.bytes = w.ent_off + (blocks ? align256(size_t(B) * Hkv * kSelEntCap * sizeof(int32_t)) : 0);
   return w;
 }
 

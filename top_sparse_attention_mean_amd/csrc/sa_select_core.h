@@ -211,126 +211,181 @@ __device__ void sel_mark_top_kv(const uint32_t (&kr)[L], const int (&ix)[L], con
 }
 
 
-// Mark in S.bm the top `need` of the candidates c0 <= j < c1 among the keys
-// kr[r] of indices j = r*NT + tid (0 < need < c1 - c0).  sel_init must have
-// run; all NT threads call.  Ends without a barrier after the last marks.
-//
-// Pre-filter: a histogram of the per-thread maxima (one LDS atomic per
-// thread) gives a lower bound T0 that at least `need` candidate keys reach, so
-// the exact top set lies in {key >= T0}.  Those keys are compacted into an LDS
-// list by a block scan and ranked there by direct counting (the list is short:
-// about 1.1-1.5 need on continuous scores); LDS atomics serialize per lane, so
-// this avoids a histogram over every key.  When the bound is too weak (list
-// over kCandCap, need above 3NT/4) the keys are selected directly.
+// Keys of the candidates c0 <= j < c1 among kin[r] (index j = r*NT + tid);
+// the others become 0, which no score maps to, so later passes need no masks
+// and their stores can be unconditional.  Returns the thread's largest key.
 template <int NT, int KPT>
-__device__ void sel_mark_top(const uint32_t (&kin)[KPT], int c0, int c1, int need,
-                             SelectLdsT<NT, KPT>& S) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // keys outside [c0, c1) become 0, which no score maps to: the passes below
-  // need no candidate masks, and their stores are unconditional (branches
-  // around predicated stores cost more than the stores)
-  uint32_t kr[KPT];
-  bool cand[KPT];
-  int ix[KPT];
+__device__ __forceinline__ uint32_t sel_mask_keys(const uint32_t (&kin)[KPT], int c0, int c1,
+                                                  uint32_t (&kr)[KPT], int (&ix)[KPT]) {
   uint32_t tmax = 0u;
 #pragma unroll
   for (int r = 0; r < KPT; ++r) {
-    ix[r] = r * NT + tid;
+    ix[r] = r * NT + threadIdx.x;
     kr[r] = unsigned(ix[r] - c0) < unsigned(c1 - c0) ? kin[r] : 0u;
-    cand[r] = kr[r] != 0u;
     tmax = max(tmax, kr[r]);
   }
-  if (KPT > 2 && need <= 3 * NT / 4) {
-    // range of the per-thread maxima, then their histogram
-    uint32_t lo = wave_umin(tmax != 0u ? tmax : 0xffffffffu), hi = wave_umax(tmax);
-    if (lane == 0) { S.wsum[0][wave] = int(lo); S.wsum[1][wave] = int(hi); }
-    __syncthreads();
+  return tmax;
+}
+
+// Pre-filter for the top `need` of the masked keys (sel_mask_keys; sel_init
+// must have run; all NT threads call).  A histogram of the per-thread maxima
+// (one LDS atomic per thread) gives a lower bound T0 that at least `need` keys
+// reach, so the exact top set lies in {key >= T0}.  Those C keys are compacted
+// by a block scan into S.cand[0, C) as (key << 32) | ~index -- unique, ordered
+// by key and then lower index first -- followed by zero padding up to the next
+// multiple of 128 and to the share layout of sel_rank_all.  Returns C after a
+// barrier, or -1 when the bound does not apply (one or two keys per thread,
+// need above 3NT/4, nmax below need or C above kCandCap); the histogram is
+// then zero again and published, ready for sel_mark_top_kv.
+template <int NT, int KPT>
+__device__ int sel_prefilter(const uint32_t (&kr)[KPT], const int (&ix)[KPT], uint32_t tmax,
+                             int need, SelectLdsT<NT, KPT>& S) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (!(KPT > 2 && need <= 3 * NT / 4)) return -1;
+  // range of the per-thread maxima, then their histogram
+  uint32_t lo = wave_umin(tmax != 0u ? tmax : 0xffffffffu), hi = wave_umax(tmax);
+  if (lane == 0) { S.wsum[0][wave] = int(lo); S.wsum[1][wave] = int(hi); }
+  __syncthreads();
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      lo = min(lo, uint32_t(S.wsum[0][w]));
-      hi = max(hi, uint32_t(S.wsum[1][w]));
-    }
-    const int bits = 32 - __clz(int(hi - lo));
-    const int shift = bits > 11 ? bits - 11 : 0;
-    atomicAdd(&S.hist[tmax != 0u ? (tmax - lo) >> shift : 0], tmax != 0u ? 1u : 0u);
-    __syncthreads();
-    u32x4* h4 = reinterpret_cast<u32x4*>(S.hist);
-    const u32x4 ha = h4[kSelBins / 4 - 2 * tid - 2], hb = h4[kSelBins / 4 - 2 * tid - 1];
-    const int tot = int(ha[0] + ha[1] + ha[2] + ha[3] + hb[0] + hb[1] + hb[2] + hb[3]);
-    const int incl = wave_incl_scan(tot);
-    if (lane == 63) S.wsum[2][wave] = incl;
-    __syncthreads();
-    int nmax;
-    int run = incl - tot + wave_base<NW>(S.wsum[2], wave, &nmax);
-    if (run < need && need <= run + tot) {
-      const uint32_t hv[8] = {hb[3], hb[2], hb[1], hb[0], ha[3], ha[2], ha[1], ha[0]};
+  for (int w = 0; w < NW; ++w) {
+    lo = min(lo, uint32_t(S.wsum[0][w]));
+    hi = max(hi, uint32_t(S.wsum[1][w]));
+  }
+  const int bits = 32 - __clz(int(hi - lo));
+  const int shift = bits > 11 ? bits - 11 : 0;
+  atomicAdd(&S.hist[tmax != 0u ? (tmax - lo) >> shift : 0], tmax != 0u ? 1u : 0u);
+  __syncthreads();
+  u32x4* h4 = reinterpret_cast<u32x4*>(S.hist);
+  const u32x4 ha = h4[kSelBins / 4 - 2 * tid - 2], hb = h4[kSelBins / 4 - 2 * tid - 1];
+  const int tot = int(ha[0] + ha[1] + ha[2] + ha[3] + hb[0] + hb[1] + hb[2] + hb[3]);
+  const int incl = wave_incl_scan(tot);
+  if (lane == 63) S.wsum[2][wave] = incl;
+  __syncthreads();
+  int nmax;
+  int run = incl - tot + wave_base<NW>(S.wsum[2], wave, &nmax);
+  if (run < need && need <= run + tot) {
+    const uint32_t hv[8] = {hb[3], hb[2], hb[1], hb[0], ha[3], ha[2], ha[1], ha[0]};
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int c = int(hv[q]);
-        if (run < need && need <= run + c) S.misc[3] = kSelBins - 1 - 8 * tid - q;
-        run += c;
-      }
-    }
-    // the histogram is read: clear it for a possible direct selection
-    h4[2 * tid] = u32x4{0u, 0u, 0u, 0u};
-    h4[2 * tid + 1] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
-    if (nmax >= need) {
-      const uint32_t T0 = lo + (uint32_t(S.misc[3]) << shift);
-      int nc = 0;
-#pragma unroll
-      for (int r = 0; r < KPT; ++r) nc += kr[r] >= T0 ? 1 : 0;
-      const int inc2 = wave_incl_scan(nc);
-      if (lane == 63) S.wsum[7][wave] = inc2;
-      __syncthreads();
-      int C;
-      int pos = inc2 - nc + wave_base<NW>(S.wsum[7], wave, &C);
-      if (C <= kCandCap) {
-        // (key << 32) | ~index orders by key, then lower index first, and is
-        // unique; candidates are nonzero, so zero padding never outranks one.
-        // Keys below T0 go to this lane's discard slot.
-        const int trash = kCandCap + 64 + lane;
-#pragma unroll
-        for (int r = 0; r < KPT; ++r) {
-          const bool in = kr[r] >= T0;
-          S.cand[in ? pos : trash] = (uint64_t(kr[r]) << 32) | uint32_t(~ix[r]);
-          pos += in ? 1 : 0;
-        }
-        // zero padding to whole shares: share = ceil(C / R) rounded up to 16
-        const int R = C <= NT / 4 ? 4 : (C <= NT / 2 ? 2 : 1);
-        const int share = (((C + R - 1) / R) + 15) & ~15;
-        if (tid < R * share - C) S.cand[C + tid] = 0ull;
-        __syncthreads();
-        if (need >= C) {
-          for (int i = tid; i < C; i += NT) sel_mark(S.bm, int(~uint32_t(S.cand[i])));
-          return;
-        }
-        // rank by counting: R threads (adjacent lanes) per candidate, each over
-        // its share of the list, 16 entries (8 reads) per step
-        for (int i0 = 0; i0 < C; i0 += NT / R) {
-          const int i = i0 + tid / R, h = tid % R;
-          const uint64_t x = i < C ? S.cand[i] : ~0ull;
-          const uint64_t* lp = S.cand + h * share;
-          int rk = 0;
-          for (int t = 0; t < share; t += 16) {
-            u32x4 pr[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) pr[q] = *reinterpret_cast<const u32x4*>(lp + t + 2 * q);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-              rk += ((uint64_t(pr[q][1]) << 32) | pr[q][0]) > x;
-              rk += ((uint64_t(pr[q][3]) << 32) | pr[q][2]) > x;
-            }
-          }
-          if (R >= 2) rk += __shfl_xor(rk, 1, 64);
-          if (R >= 4) rk += __shfl_xor(rk, 2, 64);
-          if (i < C && h == 0 && rk < need) sel_mark(S.bm, int(~uint32_t(x)));
-        }
-        return;
-      }
+    for (int q = 0; q < 8; ++q) {
+      const int c = int(hv[q]);
+      if (run < need && need <= run + c) S.misc[3] = kSelBins - 1 - 8 * tid - q;
+      run += c;
     }
   }
+  // the histogram is read: clear it for a possible direct selection
+  h4[2 * tid] = u32x4{0u, 0u, 0u, 0u};
+  h4[2 * tid + 1] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+  if (nmax < need) return -1;
+  const uint32_t T0 = lo + (uint32_t(S.misc[3]) << shift);
+  int nc = 0;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) nc += kr[r] >= T0 ? 1 : 0;
+  const int inc2 = wave_incl_scan(nc);
+  if (lane == 63) S.wsum[7][wave] = inc2;
+  __syncthreads();
+  int C;
+  int pos = inc2 - nc + wave_base<NW>(S.wsum[7], wave, &C);
+  if (C > kCandCap) return -1;
+  // keys below T0 go to this lane's discard slot
+  const int trash = kCandCap + 64 + lane;
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) {
+    const bool in = kr[r] >= T0;
+    S.cand[in ? pos : trash] = (uint64_t(kr[r]) << 32) | uint32_t(~ix[r]);
+    pos += in ? 1 : 0;
+  }
+  // zero padding (candidates are nonzero, so it never outranks one): to
+  // R * share for sel_rank_all and to a multiple of 128 for sel_rank_entry8;
+  // both ends stay below kCandCap + 64
+  const int R = C <= NT / 4 ? 4 : (C <= NT / 2 ? 2 : 1);
+  const int share = (((C + R - 1) / R) + 15) & ~15;
+  const int pad = max(R * share, (C + 127) & ~127) - C;
+  if (tid < pad) S.cand[C + tid] = 0ull;
+  __syncthreads();
+  return C;
+}
+
+// Mark in S.bm the top `need` of the C pre-filtered candidates (need <= C):
+// each is ranked by counting the list entries above it, R threads (adjacent
+// lanes) per candidate, each over its share of the list, 16 entries (8 reads)
+// per step.  Ends without a barrier after the last marks.
+template <int NT, int KPT>
+__device__ void sel_rank_all(int C, int need, SelectLdsT<NT, KPT>& S) {
+  const int tid = threadIdx.x;
+  if (need >= C) {
+    for (int i = tid; i < C; i += NT) sel_mark(S.bm, int(~uint32_t(S.cand[i])));
+    return;
+  }
+  const int R = C <= NT / 4 ? 4 : (C <= NT / 2 ? 2 : 1);
+  const int share = (((C + R - 1) / R) + 15) & ~15;
+  for (int i0 = 0; i0 < C; i0 += NT / R) {
+    const int i = i0 + tid / R, h = tid % R;
+    const uint64_t x = i < C ? S.cand[i] : ~0ull;
+    const uint64_t* lp = S.cand + h * share;
+    int rk = 0;
+    for (int t = 0; t < share; t += 16) {
+      u32x4 pr[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) pr[q] = *reinterpret_cast<const u32x4*>(lp + t + 2 * q);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        rk += ((uint64_t(pr[q][1]) << 32) | pr[q][0]) > x;
+        rk += ((uint64_t(pr[q][3]) << 32) | pr[q][2]) > x;
+      }
+    }
+    if (R >= 2) rk += __shfl_xor(rk, 1, 64);
+    if (R >= 4) rk += __shfl_xor(rk, 2, 64);
+    if (i < C && h == 0 && rk < need) sel_mark(S.bm, int(~uint32_t(x)));
+  }
+}
+
+// Rank of the list entry x = S.cand[i] (i < C) within groups of 8 adjacent
+// lanes that all pass the same x: the number of entries of S.cand[0, P) above
+// it, P = C rounded up to 128 (zero padded by sel_prefilter).  Lane h =
+// lane % 8 counts the h-th eighth of the list; the total lands in the
+// group's lane h = 7.
+template <int NT, int KPT>
+__device__ __forceinline__ int sel_rank_entry8(uint64_t x, int C, const SelectLdsT<NT, KPT>& S) {
+  const int h = threadIdx.x & 7;
+  const int e8 = ((C + 127) & ~127) >> 3;     // entries per lane: a multiple of 16
+  const uint64_t* lp = S.cand + h * e8;
+  int rk = 0;
+  for (int t = 0; t < e8; t += 16) {
+    u32x4 pr[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pr[q] = *reinterpret_cast<const u32x4*>(lp + t + 2 * q);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      rk += ((uint64_t(pr[q][1]) << 32) | pr[q][0]) > x;
+      rk += ((uint64_t(pr[q][3]) << 32) | pr[q][2]) > x;
+    }
+  }
+  return group_isum8_to_last(rk);
+}
+
+// Mark in S.bm the top `need` of the candidates c0 <= j < c1 among the keys
+// kin[r] of indices j = r*NT + tid (0 < need < c1 - c0).  sel_init must have
+// run; all NT threads call.  Ends without a barrier after the last marks.
+// The pre-filtered list is ranked by counting (it is short: about 1.1-1.5
+// need on continuous scores; LDS atomics serialize per lane, so this avoids a
+// histogram over every key); when the bound is too weak the keys are selected
+// directly.
+template <int NT, int KPT>
+__device__ void sel_mark_top(const uint32_t (&kin)[KPT], int c0, int c1, int need,
+                             SelectLdsT<NT, KPT>& S) {
+  uint32_t kr[KPT];
+  int ix[KPT];
+  const uint32_t tmax = sel_mask_keys<NT, KPT>(kin, c0, c1, kr, ix);
+  const int C = sel_prefilter<NT, KPT>(kr, ix, tmax, need, S);
+  if (C >= 0) {
+    sel_rank_all<NT, KPT>(C, need, S);
+    return;
+  }
+  bool cand[KPT];
+#pragma unroll
+  for (int r = 0; r < KPT; ++r) cand[r] = kr[r] != 0u;
   sel_mark_top_kv<NT, KPT, KPT>(kr, ix, cand, c1 - c0, need, S);
 }
 
