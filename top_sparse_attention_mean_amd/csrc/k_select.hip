@@ -57,10 +57,13 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
   __shared__ float red[RPP][D + 4];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nscore = a.BH * a.C;
-  const bool is_upd = int(blockIdx.x) >= nscore;
-  const int bh = is_upd ? int(blockIdx.x) - nscore : int(blockIdx.x) % a.BH;
-  const int c = is_upd ? 0 : int(blockIdx.x) / a.BH;
+  // the newest-block workgroups come first, so their K loads are not queued
+  // behind the sketch stream (they would finish last otherwise)
+  const int nupd = a.upd >= 0 ? a.BH : 0;
+  const bool is_upd = int(blockIdx.x) < nupd;
+  const int wid = int(blockIdx.x) - nupd;
+  const int bh = is_upd ? int(blockIdx.x) : wid % a.BH;
+  const int c = is_upd ? 0 : wid / a.BH;
   const int b = bh / a.Hkv, kh = bh % a.Hkv;
   const int nb = a.nb, G = a.G;
   const T* Qg = static_cast<const T*>(a.Q) + (size_t(b) * a.Hq + kh * G) * D;
