@@ -120,6 +120,39 @@ def test_decode_step_equals_separate_calls():
     assert torch.equal(O, O3) and torch.equal(lse, lse3)          # bitwise repeatable
 
 
+@pytest.mark.parametrize("D,upd", [(128, 5), (128, -1), (64, 7)])
+def test_decode_step_scores_and_paths(D, upd):
+    """The decode step's scores equal the standalone selection's bit for bit
+    (the refreshed block, anywhere in the row, to rounding); D = 128 runs the
+    selecting decode kernel after the score kernel, D = 64 the standalone
+    selection and the block decode."""
+    wl, inp, q, K, V = _decode_case("gqa_decode_bf16", {"B": 2, "Hq": 8, "Hkv": 2, "D": D,
+                                                        "N": 6000})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    sk_full = sa.sa_build_sketch(Kd, wl.block)
+    sk = sk_full.clone()
+    if upd >= 0:
+        sk[:, :, upd] = 0
+    score = torch.empty(wl.B, wl.Hkv, wl.nb, dtype=torch.float32, device="cuda")
+    O, lse, idx, cnt = sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block, update_block=upd,
+                                         score=score, out_dtype=torch.float32)
+    assert torch.equal(sk, sk_full)
+    idx2, cnt2, score2 = sa.sa_select_topk(Qd, sk_full, wl.k, want_score=True)
+    sc, sc2 = score.cpu().numpy(), score2.cpu().numpy()
+    if upd >= 0:
+        # the rebuilt block is scored right from its new sketch row, summed in
+        # another order than a sketch-row pass: equal up to float32 rounding
+        assert max_abs(sc[:, :, upd], sc2[:, :, upd]) <= 1e-6 * max(1.0, np.abs(sc2).max())
+        sc[:, :, upd] = sc2[:, :, upd] = 0
+    np.testing.assert_array_equal(sc, sc2)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    O2, lse2 = sa.sa_sparse_decode(Qd, Kd, Vd, idx2, cnt2, block=wl.block, out_dtype=torch.float32)
+    assert max_abs(O.cpu().numpy(), O2.cpu().numpy()) <= 1e-5
+    assert max_abs(lse.cpu().numpy(), lse2.cpu().numpy()) <= 1e-5
+    O_ref, lse_ref = oracle.attend_blocks(q, K, V, idx.cpu().numpy(), wl.block, count=cnt.cpu().numpy())
+    assert max_abs(O.cpu().numpy(), O_ref) <= OUT_TOL["bf16"]
+
+
 def _scores_for(mode, nb, rng):
     if mode == "ties":
         return (np.arange(nb) % 7).astype(np.float32)

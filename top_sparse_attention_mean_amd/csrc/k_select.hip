@@ -32,6 +32,7 @@
 
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "sa_score_core.h"
 #include "sa_select_core.h"
 
 namespace sa {
@@ -49,12 +50,8 @@ struct ScoreArgs {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
-  constexpr int NT = 256;
   constexpr int LPR = D / 4, RPI = 64 / LPR;
-  constexpr int CPT = 8, TPR = D / CPT, RPP = NT / TPR;
-  constexpr bool BF = sizeof(T) == 2;
-  __shared__ float qbar[D];
-  __shared__ float red[RPP][D + 4];
+  __shared__ ScoreUpdLds<D> L;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // the newest-block workgroups come first, so their K loads are not queued
@@ -78,15 +75,8 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
     constexpr int NLD = RPWV / RPI;             // 16-byte row loads per lane
     const int sub = lane / LPR, lc = lane % LPR;
     const int rw = c * kScoreRows + wave * RPWV;
-    using QV = typename std::conditional<BF, u32x2, u32x4>::type;
-    // loads are unconditional (clamped to head G-1) so none sits behind a branch
-    QV qv[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const T* qp = Qg + size_t(min(u, G - 1)) * D + lc * 4;
-      if constexpr (BF) qv[u] = ld8(qp);
-      else qv[u] = ld16(qp);
-    }
+    QCol<T> qv[8];
+    score_q_issue<T, D>(Qg, G, lc, qv);
     __builtin_amdgcn_sched_barrier(0);          // keep the query loads ahead of the rows
     u32x4 w[NLD];
     const float* base = a.sk + size_t(bh) * nb * D;
@@ -96,115 +86,21 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a) {
       w[i] = ld16(base + size_t(r) * D + lc * 4);
     }
     __builtin_amdgcn_sched_barrier(0);          // every load issued before the first wait
-    float q[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if constexpr (BF) {
-        q[0] += u < G ? bf16lo(qv[u][0]) : 0.f; q[1] += u < G ? bf16hi(qv[u][0]) : 0.f;
-        q[2] += u < G ? bf16lo(qv[u][1]) : 0.f; q[3] += u < G ? bf16hi(qv[u][1]) : 0.f;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] += u < G ? __uint_as_float(qv[u][e]) : 0.f;
-      }
-    }
-    for (int h = 8; h < G; ++h) {              // groups of more than 8 query heads
-      const T* qp = Qg + size_t(h) * D + lc * 4;
-      if constexpr (BF) {
-        const u32x2 v = ld8(qp);
-        q[0] += bf16lo(v[0]); q[1] += bf16hi(v[0]); q[2] += bf16lo(v[1]); q[3] += bf16hi(v[1]);
-      } else {
-        const u32x4 v = ld16(qp);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] += __uint_as_float(v[e]);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) q[e] = (q[e] / float(G)) * a.scale;
+    float q[4];
+    score_q_finish<T, D>(Qg, G, lc, a.scale, qv, q);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = rw + i * RPI + sub;
-      float p = q[0] * __uint_as_float(w[i][0]) + q[1] * __uint_as_float(w[i][1]) +
-                q[2] * __uint_as_float(w[i][2]) + q[3] * __uint_as_float(w[i][3]);
-      p = group_sum_to_last<LPR>(p);
+      const float p = score_row<D>(q, w[i]);
       if (r < nb && r != a.upd && lc == LPR - 1) srow[r] = p;
     }
     return;
   }
-  // Rebuild the sketch of block upd from K, then score it.  The query loads
-  // and every K row load of the block are in flight together.
+  // rebuild the sketch of block upd from K, then score it
   const int t0 = a.upd * a.block, nj = min(a.block, a.N - t0);
-  const int tr = tid / TPR, tc = tid % TPR;
-  float acc[CPT];
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) acc[q] = 0.f;
-  const T* Kp = static_cast<const T*>(a.K) + (size_t(bh) * a.N + t0) * D + tc * CPT;
-  constexpr int NV = BF ? 1 : 2;               // 16-byte loads per row segment
-  constexpr int KB = BF ? 8 : 4;               // rows per thread in flight
-  auto k_batch = [&](int r0, bool with_q, T (&qs)[8]) {
-    u32x4 kv[KB][NV];
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int r = min(r0 + u * RPP, nj - 1);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) kv[u][v] = ld16(Kp + size_t(r) * D + 4 * v);
-    }
-    if (with_q) {
-      const int qd = tid < D ? tid : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) qs[u] = Qg[size_t(min(u, G - 1)) * D + qd];
-    }
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      if (r0 + u * RPP < nj) {
-        if constexpr (BF) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { acc[2 * q] += bf16lo(kv[u][0][q]); acc[2 * q + 1] += bf16hi(kv[u][0][q]); }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { acc[q] += __uint_as_float(kv[u][0][q]); acc[4 + q] += __uint_as_float(kv[u][1][q]); }
-        }
-      }
-    }
-  };
-  T qs[8];
-  k_batch(tr, true, qs);                       // with the query loads
-  // blocks longer than KB * RPP rows take further batches
-  for (int r0 = tr + KB * RPP; r0 < nj; r0 += KB * RPP) k_batch(r0, false, qs);
-  if (tid < D) {
-    float sq = 0.f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      float v;
-      if constexpr (BF) v = bf16_to_f32(qs[u]);
-      else v = qs[u];
-      sq += u < G ? v : 0.f;
-    }
-    for (int h = 8; h < G; ++h) {
-      if constexpr (BF) sq += bf16_to_f32(Qg[size_t(h) * D + tid]);
-      else sq += Qg[size_t(h) * D + tid];
-    }
-    qbar[tid] = (sq / float(G)) * a.scale;
-  }
-#pragma unroll
-  for (int q = 0; q < CPT; ++q) red[tr][tc * CPT + q] = acc[q];
-  __syncthreads();
-  float part = 0.f;
-  if (tid < D) {
-    float sum = 0.f;
-    for (int g = 0; g < RPP; ++g) sum += red[g][tid];
-    const float v = sum / float(nj);
-    a.sk[(size_t(bh) * nb + a.upd) * D + tid] = v;
-    part = v * qbar[tid];
-  }
-  part = wave_sum(part);
-  __syncthreads();
-  if (lane == 0) red[0][wave] = part;
-  __syncthreads();
-  if (tid == 0) {
-    float p = 0.f;
-    for (int ww = 0; ww < D / 64; ++ww) p += red[0][ww];
-    srow[a.upd] = p;
-  }
+  const float p = score_update_block<T, D>(static_cast<const T*>(a.K) + (size_t(bh) * a.N + t0) * D,
+                                           nj, Qg, G, a.scale, a.sk + (size_t(bh) * nb + a.upd) * D, L);
+  if (tid == 0) srow[a.upd] = p;
 }
 
 SelectPlan select_plan(int BH, int nb) {
