@@ -68,51 +68,58 @@ __global__ __launch_bounds__(256) void k_threshold_mfma(
   const uint64_t lower = headmask & ((1ull << (16 * gq)) - 1ull);
   int run = 0;
 
-  for (int tile = 0; tile < kThrSeg / 16; ++tile) {
-    const int tok0 = seg * kThrSeg + tile * 16;
-    if (tok0 >= N) break;
-    u32x4 ka[NST], kb[NST];
-    const int kr = min(tok0 + nn, N - 1);
-    const uint16_t* kp = Kb + size_t(kr) * D + 8 * gq;
+  // a whole segment's K loads (8 tiles, 32 KiB per wave) are issued before the
+  // first is used: measured 129 -> 122 us at 32K tokens x 64 heads (4 tiles: 123)
+  constexpr int kTB = 8;
+  for (int t0 = 0; t0 < kThrSeg / 16; t0 += kTB) {
+    if (seg * kThrSeg + t0 * 16 >= N) break;
+    u32x4 ka[kTB][NST];
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      ka[st] = ld16(kp + 32 * st);
-      kb[st] = ka[st] & 0x7fff7fffu;
+    for (int u = 0; u < kTB; ++u) {
+      const int kr = min(seg * kThrSeg + (t0 + u) * 16 + nn, N - 1);
+      const uint16_t* kp = Kb + size_t(kr) * D + 8 * gq;
+#pragma unroll
+      for (int st = 0; st < NST; ++st) ka[u][st] = ld16(kp + 32 * st);
     }
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, ab = sc;
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      sc = mfma16x16x32(ka[st], qb[st], sc);
-      ab = mfma16x16x32(kb[st], qa[st], ab);
-    }
-    bool keep[4];
-    float s32[4];
+    for (int u = 0; u < kTB; ++u) {
+      const int tok0 = seg * kThrSeg + (t0 + u) * 16;
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, ab = sc;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int tok = tok0 + 4 * gq + r;
-      s32[r] = sc[r] * scale;
-      const float eps = gs * ab[r] + (fabsf(s32[r]) + tabs) * 9.5367431640625e-07f;  // 2^-20
-      keep[r] = nn < G && tok < N && (s32[r] + eps >= th);
-    }
-    uint64_t m[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) m[r] = __ballot(keep[r]);
-    int before = 0, total = 0;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      before += __popcll(m[r] & lower);
-      total += __popcll(m[r] & headmask);
-    }
-    int pos = run + before;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      if (keep[r]) {
-        st_idx[sbase + pos] = tok0 + 4 * gq + r;
-        st_val[sbase + pos] = s32[r];
-        ++pos;
+      for (int st = 0; st < NST; ++st) {
+        sc = mfma16x16x32(ka[u][st], qb[st], sc);
+        ab = mfma16x16x32(ka[u][st] & 0x7fff7fffu, qa[st], ab);
       }
+      bool keep[4];
+      float s32[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = tok0 + 4 * gq + r;
+        s32[r] = sc[r] * scale;
+        const float eps = gs * ab[r] + (fabsf(s32[r]) + tabs) * 9.5367431640625e-07f;  // 2^-20
+        keep[r] = nn < G && tok < N && (s32[r] + eps >= th);
+      }
+      uint64_t m[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m[r] = __ballot(keep[r]);
+      int before = 0, total = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        before += __popcll(m[r] & lower);
+        total += __popcll(m[r] & headmask);
+      }
+      int pos = run + before;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (keep[r]) {
+          st_idx[sbase + pos] = tok0 + 4 * gq + r;
+          st_val[sbase + pos] = s32[r];
+          ++pos;
+        }
+      }
+      run += total;
     }
-    run += total;
   }
   if (gq == 0 && nn < G) st_cnt[(size_t(b) * Hq + kh * G + nn) * nseg + seg] = run;
 }
