@@ -102,6 +102,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
   }
 
   const size_t kvbase = (size_t(b) * Hkv + kh) * size_t(L) * PF_D;
+  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kvbase, uint32_t(L) * PF_D * 2);
+  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kvbase, uint32_t(L) * PF_D * 2);
   const int32_t* lst = idx + (size_t(bkh) * M + i) * kmax;
   const int cnt = min(max(count[size_t(bkh) * M + i], 0), kmax);
 
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const int kr = min(key0 + ldr + 16 * (p0 + p), L - 1);
-        w[p] = ld16(K + kvbase + size_t(kr) * PF_D + 8 * ldc);
+        w[p] = bld16(rK, (kr * PF_D + 8 * ldc) * 2);
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p)
@@ -139,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vr = min(key0 + k0 + j, L - 1);
-        w[j] = ld16(V + kvbase + size_t(vr) * PF_D + 8 * ldc);
+        w[j] = bld16(rV, (vr * PF_D + 8 * ldc) * 2);
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -160,16 +162,16 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       f32x16 sfr[2];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sfr[kk][r] = 0.f;
         const uint16_t* kr = kt_lds + ((2 * sb + kk) * 32 + col) * PF_KS + 8 * half;
+        sfr[kk] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr), qf[0], f32x16{});
 #pragma unroll
-        for (int st = 0; st < PF_D / 16; ++st) {
+        for (int st = 1; st < PF_D / 16; ++st) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(kr + 16 * st);
           sfr[kk] = mfma32x32x16(a, qf[st], sfr[kk]);
         }
       }
-      float mloc = -__builtin_inff();
+      // the row maximum of the raw scores (the scale sl2 > 0 keeps the order)
+      float mraw = -__builtin_inff();
       if (diag || tail) {  // uniform: mask keys past this row or past L
         // key offset (2 sb + kk) 32 + 8 (r/4) + (r%4) is kept when <= lim
         const int lim = min(qrow, L - 1) - key0 - 4 * half;
@@ -178,42 +180,40 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int ko = (2 * sb + kk) * 32 + 8 * (r >> 2) + (r & 3);
-            const float sv = ko <= lim ? sfr[kk][r] * sl2 : -__builtin_inff();
-            sfr[kk][r] = sv;
-            mloc = fmaxf(mloc, sv);
+            sfr[kk][r] = ko <= lim ? sfr[kk][r] : -__builtin_inff();
+            mraw = fmaxf(mraw, sfr[kk][r]);
           }
         }
       } else {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float sv = sfr[kk][r] * sl2;
-            sfr[kk][r] = sv;
-            mloc = fmaxf(mloc, sv);
-          }
-        }
+          for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sfr[kk][r]);
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-      const float m_new = fmaxf(m, mloc);
-      const bool live = m_new != -__builtin_inff();
-      const float alpha = live ? exp2_fast(m - m_new) : 1.f;
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+      const float m_new = fmaxf(m, mraw * sl2);
+      // with no key seen yet (m_new = -inf) every p and alpha below is 0
+      const float m_use = m_new != -__builtin_inff() ? m_new : 0.f;
+      const float alpha = exp2_fast(m - m_use);
       float ls = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = live ? exp2_fast(sfr[kk][r] - m_new) : 0.f;
+          const float p = exp2_fast(__builtin_fmaf(sfr[kk][r], sl2, -m_use));
           sfr[kk][r] = p;
           ls += p;
         }
       }
       l = l * alpha + ls;
       m = m_new;
+      // the accumulators change only where a row's maximum moved
+      if (__ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
       if (i == 0) pv_tiles<true>(vt_lds, sfr, 2 * sb, acc, lane);
       else        pv_tiles<false>(vt_lds, sfr, 2 * sb, acc, lane);
     }
