@@ -7,12 +7,17 @@
 // Frontier", Contributi §2).  Each split produces an online-softmax partial
 // (m, l, sum p v) and the partials are merged exactly ("Pulsar Attention",
 // Fase 2: online-softmax merge of per-shard attention).  The merge runs in the
-// same launch: the last split workgroup of a head group to finish (arrival
-// counter, release/acquire fences at agent scope) combines all partials.
+// same launch: the last split workgroup of a head group to finish (an arrival
+// counter; partials written and read with agent-coherent accesses) combines
+// all partials.
 //
 // k_decode_blocks_mfma (bf16): one 256-thread workgroup per (b, kv head,
-//   split).  A 16-token tile is one wave's unit of work; each wave issues the
-//   loads of up to four tiles before computing any of them.  Scores of the g
+//   split); a split takes an equal share of the head's 16-token tiles.  A
+//   tile is one wave's unit of work; each wave issues the loads of up to four
+//   tiles before computing any of them.  The selecting variant first runs the
+//   selection pre-filter of its head from the score row, then takes its tiles
+//   from its own slice of the candidate list (ranking only those candidates)
+//   or, when the list does not suit slices, from the fully ranked selection.  Scores of the g
 //   heads for 16 tokens are one chain of v_mfma_f32_16x16x32_bf16 with the key
 //   rows as the A operand and the group's queries as the B operand -- both
 //   read in their natural row-major layout (contraction over d), so keys go

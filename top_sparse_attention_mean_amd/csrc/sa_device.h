@@ -96,17 +96,11 @@ __device__ __forceinline__ u32x4 bld16c(__amdgpu_buffer_rsrc_t r, int off, int s
 __device__ __forceinline__ u32x2 bld8c(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCoherent));
 }
-__device__ __forceinline__ uint32_t bld4c(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent);
-}
 __device__ __forceinline__ void bst16c(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kCoherent);
 }
 __device__ __forceinline__ void bst8c(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCoherent);
-}
-__device__ __forceinline__ void bst4c(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
-  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kCoherent);
 }
 
 // ------------------------------------------------------------ wave scans (DPP)
