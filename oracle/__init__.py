@@ -19,7 +19,8 @@ Pages cited (by title, section):
   * "Faster Than Flash: Exploiting Attention Sparsity for Efficient
     Long-Context Decoding" -- Metodologia §1 (scan a compact key summary, then
     fetch exact data for the chosen parts) and §2 (sink and local tokens
-    dominate the attention distribution).
+    dominate the attention distribution, so a pseudo-maximum from them sets
+    the top-delta threshold m~ - delta).
   * "Pulsar Attention" -- Fase 1 (64-token attention-sink prefix) and Fase 2
     (online-softmax merge of per-shard partial attention is exact).
   * "Sparse Attention as a Range Searching Problem: Towards an
@@ -39,6 +40,7 @@ from .attention import (
     select_topk_all, attend_blocks, attend_tokens, lse_merge,
     threshold_tau, select_threshold, prefill_pool_queries, prefill_select,
     prefill_attend_rows, prefill_attend, mass_oracle, decode_step,
+    window_tokens, pseudo_max, select_topdelta,
 )
 
 __all__ = [
@@ -46,5 +48,5 @@ __all__ = [
     "select_topk", "select_topk_all", "attend_blocks", "attend_tokens",
     "lse_merge", "threshold_tau", "select_threshold", "prefill_pool_queries",
     "prefill_select", "prefill_attend_rows", "prefill_attend", "mass_oracle",
-    "decode_step",
+    "decode_step", "window_tokens", "pseudo_max", "select_topdelta",
 ]

@@ -13,6 +13,7 @@ one function per step, in the order the method runs:
   O6 prefill_select   pooled-query-block . pooled-key-block ranking, causal
   O7 prefill_attend   causal attention of each query row over its block list
   O8 mass_oracle      exact per-block attention mass, for recall reporting
+  O9 select_topdelta  pseudo-max over sink + local tokens; keep s >= m~ - delta
      lse_merge        exact merge of attention partials over a split support
 
 Arrays: q [B, Hq, D]; Q [B, Hq, L, D]; K, V [B, Hkv, N, D]; query head h uses
@@ -441,3 +442,51 @@ def decode_step(q, K, V, block: int, k: int, scale: Optional[float] = None,
     idx = select_topk_all(sc, k)
     O, lse = attend_blocks(q, K, V, idx, block, scale)
     return {"sketch": sk, "scores": sc, "idx": idx, "O": O, "lse": lse}
+
+
+# ------------------------------------------------------------------ O9
+def window_tokens(N: int, sink: int, local: int) -> np.ndarray:
+    """Ascending positions of the sink prefix [0, sink) and the local window
+    [N - local, N), both clipped to the cache (their union when they meet)."""
+    head = np.arange(min(max(sink, 0), N))
+    tail = np.arange(max(N - max(local, 0), 0), N)
+    return np.union1d(head, tail).astype(np.int64)
+
+
+def pseudo_max(q: np.ndarray, K: np.ndarray, sink: int, local: int,
+               scale: Optional[float] = None) -> np.ndarray:
+    """O9a: m~[b, h], the largest exact score over the sink and local tokens.
+
+    "Faster Than Flash" (Metodologia §2) estimates the row maximum of the
+    scores from the initial (sink) tokens and the recent local context only,
+    so no reduction over the whole cache is needed.  Reading taken: the
+    estimate is the plain maximum of the exact scaled scores of those tokens.
+    An empty window (sink = local = 0) has no estimate and is rejected.
+    """
+    N = K.shape[2]
+    win = window_tokens(N, sink, local)
+    if win.size == 0:
+        raise ValueError("the sink and local windows are both empty")
+    s = exact_scores(q, K, scale)
+    return s[:, :, win].max(axis=-1)
+
+
+def select_topdelta(q: np.ndarray, K: np.ndarray, sink: int, local: int, delta: float,
+                    scale: Optional[float] = None):
+    """O9: top-delta selection: keep token j when s_j >= m~ - delta.
+
+    The criterion of "Faster Than Flash" (Metodologia §2): a token stays when
+    its score is within delta of the pseudo-maximum m~ (O9a), i.e. when its
+    unnormalised softmax weight exp(s_j) is at least exp(-delta) times that of
+    the estimated peak.  delta >= 0 (the pages use 5 and 7); +inf keeps every
+    token.  Reading taken: only this criterion decides; the sink and local
+    tokens are not forced in beyond it (the token that attains m~ always
+    passes, so the list is never empty).
+    Returns (lists, vals, tau) with tau[b, h] = m~ - delta and lists/vals as
+    select_threshold (O5) returns them.
+    """
+    if not delta >= 0:
+        raise ValueError("delta must be >= 0")
+    tau = pseudo_max(q, K, sink, local, scale) - float(delta)
+    lists, vals = select_threshold(q, K, tau, scale)
+    return lists, vals, tau

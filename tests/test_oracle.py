@@ -377,3 +377,128 @@ def test_inputs_are_seeded():
     np.testing.assert_array_equal(a.K, b.K)
     c = make_inputs("tiny_decode_f32", seed=7)
     assert not np.array_equal(a.K, c.K)
+
+
+# ------------------------------------------------------------------ O9
+def _golden_topdelta():
+    keys, cases = None, []
+    for k, v in read_golden("topdelta_window.txt"):
+        if k == "keys":
+            keys = np.array([float(x) for x in v])
+        elif k == "case":
+            sink, local, delta, _, tau, _, *kept = v
+            cases.append((int(sink), int(local), float(delta), float(tau),
+                          [int(x) for x in kept]))
+    return keys, cases
+
+
+def test_golden_topdelta_window():
+    keys, cases = _golden_topdelta()
+    assert len(cases) == 6
+    q = np.ones((1, 1, 1))
+    K = keys.reshape(1, 1, -1, 1)
+    for sink, local, delta, tau, kept in cases:
+        lists, vals, t = oracle.select_topdelta(q, K, sink, local, delta, scale=1.0)
+        assert t[0, 0] == tau, (sink, local, delta)
+        assert lists[0][0].tolist() == kept, (sink, local, delta)
+        np.testing.assert_array_equal(vals[0][0], keys[kept])
+
+
+def test_window_tokens_cases():
+    assert A.window_tokens(10, 2, 3).tolist() == [0, 1, 7, 8, 9]
+    assert A.window_tokens(10, 0, 1).tolist() == [9]
+    assert A.window_tokens(10, 6, 6).tolist() == list(range(10))     # windows meet
+    assert A.window_tokens(3, 64, 64).tolist() == [0, 1, 2]          # clipped
+    assert A.window_tokens(10, 0, 0).size == 0
+    with pytest.raises(ValueError):
+        oracle.pseudo_max(np.ones((1, 1, 2)), np.ones((1, 1, 5, 2)), 0, 0)
+    with pytest.raises(ValueError):
+        oracle.select_topdelta(np.ones((1, 1, 2)), np.ones((1, 1, 5, 2)), 1, 1, -1.0)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_topdelta_is_the_relative_weight_rule(seed):
+    """Keep j iff its softmax weight is at least e^-delta times the largest
+    weight in the sink/local window: the same rule stated on probabilities
+    (scipy softmax), with the window maximum found by a plain loop."""
+    rng = np.random.default_rng(300 + seed)
+    B, Hq, Hkv, N, D = 2, 4, 2, 90, 8
+    q = rng.standard_normal((B, Hq, D)) * 1.5
+    K = rng.standard_normal((B, Hkv, N, D))
+    sink, local, delta = [(4, 8, 5.0), (0, 16, 2.0), (16, 0, 3.5), (1, 1, 0.5)][seed]
+    lists, _, tau = oracle.select_topdelta(q, K, sink, local, delta)
+    win = [t for t in range(N) if t < sink or t >= N - local]
+    for b in range(B):
+        for h in range(Hq):
+            s = np.array([sum(q[b, h, c] * K[b, h // 2, t, c] for c in range(D)) for t in range(N)])
+            s /= math.sqrt(D)
+            p = softmax(s)
+            pw = max(p[t] for t in win)
+            r = p / pw
+            want = [t for t in range(N) if r[t] >= math.exp(-delta)]
+            # no score sits within rounding of the boundary on these draws
+            assert np.all(np.abs(np.log(r) + delta) > 1e-9)
+            assert lists[b][h].tolist() == want
+            assert abs(tau[b, h] - (max(s[t] for t in win) - delta)) < 1e-12
+
+
+def test_topdelta_special_cases():
+    rng = np.random.default_rng(310)
+    B, Hq, Hkv, N, D = 1, 4, 1, 70, 8
+    q = rng.standard_normal((B, Hq, D))
+    K = rng.standard_normal((B, Hkv, N, D))
+    V = rng.standard_normal((B, Hkv, N, D))
+    s = np.einsum("hd,nd->hn", q[0], K[0, 0]) / math.sqrt(D)
+    # window = whole cache: the pseudo-max is the true max; delta = 0 keeps
+    # exactly the arg-max
+    lists, _, tau = oracle.select_topdelta(q, K, N, 0, 0.0)
+    for h in range(Hq):
+        assert lists[0][h].tolist() == [int(np.argmax(s[h]))]
+        assert abs(tau[0, h] - s[h].max()) < 1e-12
+    # delta = +inf keeps every token: attention over the list is dense attention
+    lists, _, _ = oracle.select_topdelta(q, K, 1, 1, math.inf)
+    assert all(len(lists[0][h]) == N for h in range(Hq))
+    O, lse = oracle.attend_tokens(q, K, V, lists)
+    Od, lsed = oracle.dense(q, K, V)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+@pytest.mark.parametrize("delta", [2.0, 5.0, 7.0])
+def test_topdelta_dropped_mass_bound(delta):
+    """Each dropped token weighs under e^-delta of the window peak, which is
+    kept, so the dropped share of the softmax mass is below n_drop e^-delta and
+    the attention output moves by at most twice that times max |v|."""
+    rng = np.random.default_rng(320 + int(delta))
+    B, Hq, Hkv, N, D = 1, 8, 2, 400, 16
+    q = rng.standard_normal((B, Hq, D)) * 2.0
+    K = rng.standard_normal((B, Hkv, N, D))
+    V = rng.standard_normal((B, Hkv, N, D))
+    lists, _, _ = oracle.select_topdelta(q, K, 8, 8, delta)
+    O, _ = oracle.attend_tokens(q, K, V, lists)
+    Od, _ = oracle.dense(q, K, V)
+    for h in range(Hq):
+        s = K[0, h // 4] @ q[0, h] / math.sqrt(D)
+        p = softmax(s)
+        n_drop = N - len(lists[0][h])
+        f = 1.0 - p[lists[0][h]].sum()
+        bound = n_drop * math.exp(-delta)
+        assert f <= bound + 1e-15
+        assert np.abs(O[0, h] - Od[0, h]).max() <= 2 * f * np.abs(V[0, h // 4]).max() + 1e-12
+    assert any(len(lists[0][h]) < N for h in range(Hq))          # something was dropped
+
+
+def test_topdelta_workload_concentrates_on_anchors():
+    """The top-delta workload plants sink/local anchors and needles: on its
+    draws the selection keeps a few percent of the cache, almost all of it
+    planted tokens."""
+    wl = get_workload("topdelta_decode_bf16", B=1, Hq=8, Hkv=2, N=8192, needles=4)
+    inp = make_inputs(wl)
+    q, K = A.widen(inp.Q, "bf16"), A.widen(inp.K, "bf16")
+    lists, _, _ = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
+    win = A.window_tokens(wl.N, wl.sink, wl.local)
+    fr = [len(lists[0][h]) / wl.N for h in range(wl.Hq)]
+    assert max(fr) < 0.08 and np.mean(fr) < 0.04
+    for h in range(wl.Hq):
+        need = np.concatenate([np.arange(j * 64, (j + 1) * 64) for j in inp.needles[0, h // wl.g]])
+        assert np.isin(lists[0][h], np.union1d(win, need)).mean() > 0.95

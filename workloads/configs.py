@@ -1,4 +1,4 @@
-"""The five workloads of the hot path, by name and shape.
+"""The workloads of the hot path, by name and shape.
 
 Every workload is a single-layer attention problem over a GQA KV cache laid out
 as K, V = [B, Hkv, N, D] and Q = [B, Hq, D] (decode) or [B, Hq, L, D]
@@ -17,7 +17,7 @@ from typing import Optional
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                 # "decode_topk" | "decode_threshold" | "prefill"
+    kind: str                 # "decode_topk" | "decode_threshold" | "decode_topdelta" | "prefill"
     B: int
     Hq: int
     Hkv: int
@@ -34,7 +34,11 @@ class Workload:
     drift_rho: float = 0.0    # AR(1) coefficient of the drift across blocks
     needle_gain: float = 3.0  # planted keys get + needle_gain * unit query
     percentile: float = 99.0  # threshold workload: per-head score percentile
-    cap: int = 1024           # threshold workload: list capacity per head
+    cap: int = 1024           # threshold workloads: list capacity per head
+    sink: int = 0             # top-delta: leading tokens of the pseudo-max window
+    local: int = 0            # top-delta: trailing tokens of the pseudo-max window
+    delta: float = 0.0        # top-delta: keep s >= pseudo-max - delta
+    anchor_gain: float = 0.0  # sink and local keys get + anchor_gain * unit query
     extra: dict = field(default_factory=dict)
 
     @property
@@ -74,6 +78,16 @@ WORKLOADS = {
         Hkv=8, D=128, N=32768, block=64, k=0, dtype="bf16", seed=2,
         needles=16, outlier_channels=4, outlier_scale=8.0, percentile=99.0,
         cap=1024),
+    # The GQA decode shapes and draws with attention concentrated on the sink
+    # and local tokens, as "Faster Than Flash" (Metodologia §2) reports of real
+    # models: the first 64 and last 64 keys of every kv head, and the needle
+    # blocks, get + 16 * q_hat.  Keep every token within delta = 5 of the
+    # pseudo-max over those 128 tokens (about 2 % of the cache on these draws).
+    "topdelta_decode_bf16": Workload(
+        name="topdelta_decode_bf16", kind="decode_topdelta", B=8, Hq=32,
+        Hkv=8, D=128, N=32768, block=64, k=0, dtype="bf16", seed=2,
+        needles=16, outlier_channels=4, outlier_scale=8.0, needle_gain=16.0,
+        cap=4096, sink=64, local=64, delta=5.0, anchor_gain=16.0),
     # B=1, Hq=32, Hkv=4, d=128, L=64K, 128-token query and key blocks; each
     # query block keeps block 0, its diagonal block and the top-8 earlier blocks.
     "sparse_prefill_bf16": Workload(

@@ -14,6 +14,9 @@ Recipe (identical for every workload, so a reader can regenerate any array):
    * decode: for each (b, kv head), ``needles`` distinct blocks from
      [1, nb-2]; every key of such a block gets + gain * q_hat, q_hat being the
      unit-length mean of the group's query heads;
+   * decode with anchor_gain > 0 (top-delta workloads): then the first
+     ``sink`` and the last ``local`` keys of every (b, kv head) also get
+     + anchor_gain * q_hat (no draws, so the other arrays are unchanged);
    * prefill: for each (b, kv head), ``needles`` distinct key blocks j from
      [1, nb-2], then for each a partner query block i drawn uniformly from
      [j+1, nb-1]; every key of block j gets + gain * q_hat_i, q_hat_i being the
@@ -111,7 +114,7 @@ def _drift(rng: np.random.Generator, X: np.ndarray, wl: Workload) -> None:
 
 
 def make_decode_inputs(wl: Workload, seed: Optional[int] = None) -> DecodeInputs:
-    if wl.kind not in ("decode_topk", "decode_threshold"):
+    if wl.kind not in ("decode_topk", "decode_threshold", "decode_topdelta"):
         raise ValueError(f"{wl.name} is not a decode workload")
     rng = np.random.Generator(np.random.PCG64(wl.seed if seed is None else seed))
     B, Hq, Hkv, D, N = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N
@@ -146,6 +149,10 @@ def make_decode_inputs(wl: Workload, seed: Optional[int] = None) -> DecodeInputs
             qhat = (qm / np.linalg.norm(qm)).astype(np.float32)
             for j in needles[b, kh]:
                 K[b, kh, j * wl.block:min((j + 1) * wl.block, N)] += gain * qhat
+            if wl.anchor_gain > 0:
+                a = np.float32(wl.anchor_gain) * qhat
+                K[b, kh, :min(wl.sink, N)] += a
+                K[b, kh, max(N - wl.local, 0):] += a
 
     return DecodeInputs(wl, _store(Q, wl.dtype), _store(K, wl.dtype),
                         _store(V, wl.dtype), needles, outl)
