@@ -274,10 +274,15 @@ def bench_decode(args) -> dict:
     return res
 
 
-def bench_threshold(args) -> dict:
-    """Threshold variant (row a4, then token-mode a5 + a6) at its full size:
-    exact scores of every key, keep s >= tau - eps (zero false negatives),
-    ordered compaction, attention over the kept tokens."""
+def bench_threshold(args, which: str = "threshold") -> dict:
+    """Threshold variants at full size, then token-mode a5 + a6.
+
+    which = "threshold": row a4 with the workload's tau (exact scores of every
+    key, keep s >= tau - eps, ordered compaction).
+    which = "topdelta": the threshold comes from the pseudo-maximum over the
+    sink and local tokens (tau = m~ - delta), computed on the GPU in the same
+    call, then the same scan and compaction.
+    """
     import numpy as np
     import torch
     import oracle
@@ -285,31 +290,44 @@ def bench_threshold(args) -> dict:
     from oracle.attention import widen
     from tests.parity_util import to_dev
     from workloads import get_workload, make_inputs
-    wl = get_workload("threshold_decode_bf16")
+    wl = get_workload("threshold_decode_bf16" if which == "threshold" else "topdelta_decode_bf16")
     dev = torch.device("cuda:0")
     inp = make_inputs(wl)
     q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
-    _, tau32 = oracle.threshold_tau(q, K, wl.percentile)        # the workload's tau (input)
     R = 2                                                        # 2 x 1 GiB of K/V > Infinity Cache
     Qs = [to_dev(inp.Q, wl.dtype, dev) for _ in range(R)]
     Kd = to_dev(inp.K, wl.dtype, dev)
     Ks = [Kd] + [Kd.clone() for _ in range(R - 1)]
     Vd = to_dev(inp.V, wl.dtype, dev)
     Vs = [Vd] + [Vd.clone() for _ in range(R - 1)]
-    tau = torch.from_numpy(tau32).to(dev)
     B, Hq, Hkv, D, N = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N
     idx = torch.empty(B, Hq, wl.cap, dtype=torch.int32, device=dev)
     sc = torch.empty(B, Hq, wl.cap, dtype=torch.float32, device=dev)
     cnt = torch.empty(B, Hq, dtype=torch.int32, device=dev)
     O = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    tws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0, wl.cap),
-                      dtype=torch.uint8, device=dev)
+    tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
     dws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, 0, wl.cap),
                       dtype=torch.uint8, device=dev)
+    if which == "threshold":
+        _, tau32 = oracle.threshold_tau(q, K, wl.percentile)    # the workload's tau (input)
+        tau.copy_(torch.from_numpy(tau32))
+        tws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0,
+                                             wl.cap), dtype=torch.uint8, device=dev)
 
-    def sel(r):
-        sa.sa_select_threshold(Qs[r], Ks[r], tau, wl.cap, idx=idx, score=sc, count=cnt, ws=tws)
+        def sel(r):
+            sa.sa_select_threshold(Qs[r], Ks[r], tau, wl.cap, idx=idx, score=sc, count=cnt,
+                                   ws=tws)
+        call = "sa_select_threshold (k_threshold_mfma + k_threshold_compact)"
+    else:
+        tws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_TOPDELTA, B, Hq, Hkv, N, D, 0,
+                                             wl.cap), dtype=torch.uint8, device=dev)
+
+        def sel(r):
+            sa.sa_select_topdelta(Qs[r], Ks[r], wl.sink, wl.local, wl.delta, wl.cap, idx=idx,
+                                  score=sc, count=cnt, tau=tau, ws=tws)
+        call = ("sa_select_topdelta (k_pseudo_max_mfma + k_threshold_mfma + "
+                "k_threshold_compact)")
 
     def dec(r):
         sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], idx, cnt, mode=sa.SA_IDX_TOKENS, score=sc,
@@ -320,26 +338,38 @@ def bench_threshold(args) -> dict:
     t_sel = graph_time(sel, R, n)
     e = 2
     kept = int(cnt.sum().item())
+    assert int(cnt.max().item()) <= wl.cap, "list capacity exceeded"
+    win = 0 if which == "threshold" else B * Hkv * len(oracle.window_tokens(N, wl.sink, wl.local)) * D * e
     scan_bytes = B * Hkv * N * D * e + B * Hq * D * e + B * Hq * 4
     list_bytes = B * Hq * wl.cap * 8 + B * Hq * 4
     v_bytes = kept * D * e
-    ach = (scan_bytes + kept * 8) / (t_sel * 1e-6) / 1e9
+    ach = (scan_bytes + win + kept * 8) / (t_sel * 1e-6) / 1e9
     res = {
         "workload": wl.name, "us_per_pass": round(t_pass, 2),
-        "pass": "threshold scan + compaction (sa_select_threshold) + token-mode decode",
-        "kernels_us": {"sa_select_threshold (k_threshold_mfma + k_threshold_compact)": round(t_sel, 2),
+        "pass": (("threshold scan + compaction" if which == "threshold" else
+                  "pseudo-max + threshold scan + compaction") + f" ({call.split(' ')[0]}) "
+                 "+ token-mode decode"),
+        "kernels_us": {call: round(t_sel, 2),
                        "sa_sparse_decode tokens (k_decode_tokens)": round(max(t_pass - t_sel, 0), 2)},
-        "kept_tokens": kept, "algorithmic_bytes_per_pass": scan_bytes + list_bytes + v_bytes,
+        "kept_tokens": kept, "kept_fraction": round(kept / (B * Hq * N), 5),
+        "algorithmic_bytes_per_pass": scan_bytes + win + list_bytes + v_bytes,
         "roofline": {"bound": "hbm", "kernel": "k_threshold_mfma (full K scan; the call also runs "
-                     "the small compaction kernel)", "achieved": round(ach, 1),
+                     "the small compaction kernel" + (")" if which == "threshold" else
+                                                      " and the pseudo-max kernel)"),
+                     "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "algorithmic_bytes": scan_bytes + kept * 8,
+                     "traffic": None, "algorithmic_bytes": scan_bytes + win + kept * 8,
                      "avg_us": round(t_sel, 2)},
     }
+    if which == "topdelta":
+        res["delta"], res["sink"], res["local"] = wl.delta, wl.sink, wl.local
     if not args.no_cpu:
-        # the oracle on the same arrays: exact scores, threshold, attention
+        # the oracle on the same arrays: selection, then attention
         t0 = time.perf_counter()
-        lists, _ = oracle.select_threshold(q, K, tau32.astype(np.float64))
+        if which == "threshold":
+            lists, _ = oracle.select_threshold(q, K, tau32.astype(np.float64))
+        else:
+            lists, _, _ = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
         oracle.attend_tokens(q, K, V, lists)
         t_cpu = time.perf_counter() - t0
         res["cpu_baseline"] = {"value": round(t_cpu * 1e6, 1), "unit": "us/pass",
@@ -455,7 +485,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the threshold and prefill variant measurements")
+                    help="skip the threshold, top-delta and prefill variant measurements")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 counter passes (no timing output)")
     args = ap.parse_args(argv)
@@ -475,6 +505,9 @@ def main(argv=None) -> int:
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"] = {"threshold": bench_threshold(args)}
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["variants"]["topdelta"] = bench_threshold(args, "topdelta")
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"]["prefill"] = bench_prefill(args)

@@ -92,7 +92,8 @@ enum {
   SA_OP_SELECT_TOPK = 0,
   SA_OP_SELECT_THRESHOLD = 1,
   SA_OP_SPARSE_DECODE = 2,
-  SA_OP_DECODE_STEP = 3
+  SA_OP_DECODE_STEP = 3,
+  SA_OP_SELECT_TOPDELTA = 4
 };
 
 /*
@@ -178,6 +179,38 @@ sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B,
                               float scale, int cap, int32_t* idx, float* score,
                               int32_t* count, void* ws, size_t ws_bytes,
                               void* stream);
+
+/*
+ * sa_select_topdelta -- top-delta selection with a pseudo-maximum ([FFD]
+ * Metodologia §2): keep token t of query head (b, h) when
+ *     s_t >= m~ - delta,   s_t = q_h . k_t * scale,
+ * where m~ is the largest score over the sink prefix [0, sink) and the local
+ * window [N - local, N) (both clipped to the cache).  The estimate reads only
+ * those tokens, so the threshold needs no reduction over the whole cache;
+ * the scan, compaction and outputs are those of sa_select_threshold with
+ * tau = m~ - delta.  Follow with sa_sparse_decode in SA_IDX_TOKENS mode.
+ *
+ *   Q [B, Hq, D], K [B, Hkv, N, D] dtype
+ *   sink, local  window sizes in tokens, >= 0, not both 0
+ *   delta        >= 0 (the pages use 5 and 7); +inf keeps every token
+ *   cap, idx, score, count   as sa_select_threshold (count > cap is reported
+ *            in band; the first cap positions are written)
+ *   tau      [B, Hq] float32 out: the threshold used (NULL: kept in ws)
+ *
+ * No false negatives against the exact rule: tau is computed from lower
+ * bounds fl32(s) - eps of the window scores, so it never exceeds
+ * m~_exact - delta beyond its own float32 rounding, and the scan keeps every
+ * key whose exact score reaches it (see sa_select_threshold).  The extra keys
+ * lie within a few float32 rounding bounds below the exact threshold.  The
+ * token attaining m~ always passes, so no list is empty.  NaN window scores
+ * are ignored by the maximum.
+ * ws: sa_workspace_bytes(SA_OP_SELECT_TOPDELTA, B, Hq, Hkv, N, D, 0, cap).
+ */
+sa_status sa_select_topdelta(const void* Q, const void* K, int dtype, int B,
+                             int Hq, int Hkv, int N, int D, int sink, int local,
+                             float delta, float scale, int cap, int32_t* idx,
+                             float* score, int32_t* count, float* tau, void* ws,
+                             size_t ws_bytes, void* stream);
 
 /*
  * sa_sparse_decode -- exact attention restricted to the selected keys, as

@@ -30,6 +30,7 @@ def lib():
     L.sa_build_sketch.argtypes = [P, I, I, I, I, I, I, I, I, I, P, P]
     L.sa_select_topk.argtypes = [P, I, I, I, I, I, I, I, P, I, I, U, F, P, P, P, P, Z, P]
     L.sa_select_threshold.argtypes = [P, P, I, I, I, I, I, I, P, F, I, P, P, P, P, Z, P]
+    L.sa_select_topdelta.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, I, P, P, P, P, P, Z, P]
     L.sa_sparse_decode.argtypes = [P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P, P, I, P, P, Z, P]
     L.sa_sparse_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, I, P, I, P, P]
     L.sa_decode_step.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P, P, Z, P]
@@ -49,8 +50,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
-              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
+    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
+              "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step",
+              "sa_workspace_bytes",
               "sa_status_str",
               "sa_last_error", "sa_version"]:
         assert n in names
@@ -89,6 +91,8 @@ def test_workspace_sizes(lib):
     assert lib.sa_workspace_bytes(2, 1, 64, 8, 262144, 128, 64, 82) >= 64 * 21 * 130 * 4
     assert lib.sa_workspace_bytes(2, 0, 64, 8, 262144, 128, 64, 82) == ctypes.c_size_t(-1).value
     assert lib.sa_workspace_bytes(9, 1, 1, 1, 1, 64, 64, 1) == ctypes.c_size_t(-1).value
+    # top-delta: the threshold staging plus one float threshold per (b, head)
+    assert lib.sa_workspace_bytes(4, 8, 32, 8, 32768, 128, 0, 1024) >= a + 8 * 32 * 4
 
 
 def test_sketch_validation(lib):
@@ -135,6 +139,30 @@ def test_threshold_validation(lib):
     assert f(A, A, 1, 8, 32, 8, 32768, 128, A, 0.0, 0, A, A, A, A, 1 << 30, None) == INVALID
     assert f(A, A, 1, 8, 48, 8, 32768, 128, A, 0.0, 1024, A, A, A, A, 1 << 30, None) == UNSUPPORTED
     assert f(A, A, 1, 8, 32, 8, 32768, 128, A, 0.0, 1024, A, A, A, A, 1024, None) == WORKSPACE
+
+
+def test_topdelta_validation(lib):
+    f = lib.sa_select_topdelta
+    base = [A, A, 1, 8, 32, 8, 32768, 128, 64, 64, 5.0, 0.0, 1024, A, A, A, None, A, 1 << 30, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(8, -1) == INVALID                 # negative sink
+    assert call(9, -5) == INVALID                 # negative local
+    a = list(base)
+    a[8], a[9] = 0, 0                             # empty window
+    assert f(*a) == INVALID
+    assert b"empty" in lib.sa_last_error()
+    assert call(10, -1.0) == INVALID              # delta < 0
+    assert call(10, float("nan")) == INVALID
+    assert call(12, 0) == INVALID                 # cap
+    assert call(16, MIS) == INVALID               # misaligned tau
+    assert call(4, 48) == UNSUPPORTED             # bf16 g = 6
+    assert call(18, 1024) == WORKSPACE
+    assert call(1, None) == INVALID               # K
 
 
 def test_decode_validation(lib):
@@ -209,6 +237,6 @@ def test_binding_binds_every_entry_point():
     sa = pytest.importorskip("top_sparse_attention_mean_amd")
     for n in sa.EXPORTS:
         assert hasattr(sa, "_" + n[len("sa_"):]), f"no ctypes signature for {n}"
-    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
-              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
+    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
+              "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
         assert callable(getattr(sa, n)), n

@@ -391,6 +391,116 @@ def test_threshold_capacity_and_minus_inf():
         assert torch.equal(idx[0, h], full[0, h, :50])
 
 
+TOPDELTA_CASES = [
+    ("topdelta_decode_bf16", {"B": 2, "N": 8192, "needles": 4}),                  # g = 4
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 1, "N": 5000, "needles": 3,  # g = 8, ragged
+                              "delta": 7.0, "cap": 5000}),
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 4, "D": 64, "N": 3001, "needles": 2,
+                              "sink": 16, "local": 100}),                          # g = 1, D = 64
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 2, "N": 2048, "needles": 2,  # g = 2
+                              "sink": 0, "local": 1, "delta": 2.0, "cap": 2048}),
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1, "D": 64, "N": 4096 - 13, "dtype": "f32",
+                              "outlier_channels": 0, "needles": 2, "cap": 4096}),
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 6, "Hkv": 1, "D": 128, "N": 3000, "dtype": "f32",
+                              "needles": 2, "sink": 5, "local": 37, "cap": 3000}),  # f32 g = 6
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 100, "needles": 0,   # window = cache
+                              "delta": 0.0, "cap": 100}),
+    ("topdelta_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 7, "needles": 0,     # N < one tile
+                              "sink": 2, "local": 2, "delta": 1.0, "cap": 16}),
+]
+
+
+def _check_topdelta(wl, q, K, idx_h, sc_h, cnt_h, tau_h, where=""):
+    """Selection checks of one top-delta call against the oracle; returns the
+    GPU lists and the number of extra (boundary) keys."""
+    s = exact_scores(q, K)
+    eps = _eps_bound(q, K, wl)
+    _, _, tau_x = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
+    win = oracle.window_tokens(wl.N, wl.sink, wl.local)
+    lists = [[None] * wl.Hq for _ in range(wl.B)]
+    extra = 0
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            # the threshold: never above the exact one beyond its own rounding,
+            # below it by at most the window scores' error bounds
+            t = float(tau_h[b, h])
+            assert t <= tau_x[b, h] + 2.0 ** -21 * abs(tau_x[b, h]), (where, b, h)
+            assert t >= tau_x[b, h] - 2 * eps[b, h, win].max() - 1e-6, (where, b, h)
+            n = int(cnt_h[b, h])
+            cap = idx_h.shape[-1]
+            got = idx_h[b, h, :min(n, cap)]
+            assert n <= cap, (where, b, h, n)
+            assert np.all(idx_h[b, h, n:] == -1)
+            assert np.all(np.diff(got) > 0)
+            exact = np.nonzero(s[b, h] >= tau_x[b, h])[0]
+            missing = set(exact.tolist()) - set(got.tolist())
+            assert not missing, f"{where} false negatives at b{b} h{h}: {sorted(missing)[:5]}"
+            ex = np.setdiff1d(got, exact)
+            assert np.all(s[b, h, ex] >= t - 2 * eps[b, h, ex]), (where, b, h)
+            extra += ex.size
+            assert max_abs(sc_h[b, h, :n], s[b, h, got]) <= 1e-4 * max(1.0, np.abs(s[b, h]).max())
+            lists[b][h] = got
+    return lists, extra
+
+
+@pytest.mark.parametrize("name,over", TOPDELTA_CASES)
+def test_topdelta_parity(name, over):
+    wl, inp, q, K, V = _decode_case(name, over)
+    dt = wl.dtype
+    Qd, Kd, Vd = to_dev(inp.Q, dt), to_dev(inp.K, dt), to_dev(inp.V, dt)
+    idx, score, cnt, tau = sa.sa_select_topdelta(Qd, Kd, wl.sink, wl.local, wl.delta, wl.cap)
+    lists, extra = _check_topdelta(wl, q, K, idx.cpu().numpy(), score.cpu().numpy(),
+                                   cnt.cpu().numpy(), tau.cpu().numpy(), f"{name} {over}")
+    # token-mode attention over the GPU's lists, with and without the stored scores
+    O_ref, lse_ref = oracle.attend_tokens(q, K, V, lists)
+    for use_scores in (True, False):
+        O32, lse = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS,
+                                       score=score if use_scores else None,
+                                       out_dtype=torch.float32)
+        err = max_abs(O32.cpu().numpy(), O_ref)
+        assert err <= OUT_TOL[dt], err
+        assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    if extra == 0:
+        # the same lists as the oracle's rule: the oracle's top-delta attention
+        ol, _, _ = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
+        O_x, _ = oracle.attend_tokens(q, K, V, ol)
+        assert max_abs(O32.cpu().numpy(), O_x) <= OUT_TOL[dt]
+    # bitwise repeatable
+    idx2, score2, cnt2, tau2 = sa.sa_select_topdelta(Qd, Kd, wl.sink, wl.local, wl.delta, wl.cap)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2) and torch.equal(tau, tau2)
+    kept = int(cnt.sum())
+    print(f"{name} {over}: kept {kept} ({kept / (wl.B * wl.Hq * wl.N):.3%}), extra keys {extra}, "
+          f"max-abs O error {err:.2e}")
+
+
+def test_topdelta_infinite_delta_is_dense_and_capacity():
+    wl, inp, q, K, V = _decode_case("topdelta_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1,
+                                                             "N": 3000, "needles": 2})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    idx, score, cnt, tau = sa.sa_select_topdelta(Qd, Kd, 64, 64, math.inf, 3000)
+    assert torch.all(cnt == 3000) and torch.all(torch.isinf(tau) & (tau < 0))
+    O32, _ = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS, score=score,
+                                 out_dtype=torch.float32)
+    Od, _ = oracle.dense(q, K, V)
+    assert max_abs(O32.cpu().numpy(), Od) <= 2e-3
+    # capacity overflow: the true count is reported, the first `cap` written
+    full, _, cfull, _ = sa.sa_select_topdelta(Qd, Kd, 64, 64, 7.0, 3000)
+    small, _, csmall, _ = sa.sa_select_topdelta(Qd, Kd, 64, 64, 7.0, 40)
+    assert torch.equal(cfull, csmall) and int(cfull.min()) > 40
+    assert torch.equal(small, full[..., :40])
+    # the caller's threshold output may be omitted (kept in the workspace)
+    ws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_TOPDELTA, 1, 4, 1, 3000, 128, 0, 3000),
+                     dtype=torch.uint8, device="cuda")
+    i3 = torch.empty_like(full)
+    s3 = torch.empty(1, 4, 3000, dtype=torch.float32, device="cuda")
+    c3 = torch.empty_like(cfull)
+    st = sa._select_topdelta(sa._ptr(Qd), sa._ptr(Kd), sa.SA_BF16, 1, 4, 1, 3000, 128, 64, 64, 7.0,
+                             0.0, 3000, sa._ptr(i3), sa._ptr(s3), sa._ptr(c3), None, sa._ptr(ws),
+                             ws.numel(), sa._stream())
+    assert st == 0
+    assert torch.equal(i3, full) and torch.equal(c3, cfull)
+
+
 PREFILL_CASES = [
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 2048, "needles": 4}),
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 1, "N": 2048 + 77, "needles": 4}),   # ragged

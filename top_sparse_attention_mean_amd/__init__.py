@@ -30,9 +30,11 @@ SA_OK, SA_ERR_INVALID, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(
 SA_F32, SA_BF16 = 0, 1
 SA_FORCE_SINK, SA_FORCE_LOCAL, SA_CAUSAL = 1, 2, 4
 SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
-SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP = range(4)
+(SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP,
+ SA_OP_SELECT_TOPDELTA) = range(5)
 
-EXPORTS = ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_sparse_decode",
+EXPORTS = ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
+           "sa_sparse_decode",
            "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
            "sa_status_str",
            "sa_last_error", "sa_version"]
@@ -56,6 +58,8 @@ _select_topk = _sig("sa_select_topk", _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I
                     _P, _P, _P, _P, _Z, _P)
 _select_threshold = _sig("sa_select_threshold", _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I,
                          _P, _P, _P, _P, _Z, _P)
+_select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+                        _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _sparse_decode = _sig("sa_sparse_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
                       _P, _P, _I, _P, _P, _I, _P, _P, _Z, _P)
 _sparse_prefill = _sig("sa_sparse_prefill", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P,
@@ -218,6 +222,37 @@ def sa_select_threshold(Q: torch.Tensor, K: torch.Tensor, tau: torch.Tensor, cap
                              _ptr(idx), _ptr(score), _ptr(count), _ptr(ws), ws.numel(),
                              _stream(stream)), "sa_select_threshold")
     return idx, score, count
+
+
+def sa_select_topdelta(Q: torch.Tensor, K: torch.Tensor, sink: int, local: int, delta: float,
+                       cap: int, scale: float = 0.0, idx=None, score=None, count=None, tau=None,
+                       ws=None, stream=None):
+    """Top-delta selection: keep tokens with q . k * scale >= m~ - delta, m~ the
+    largest score over the first `sink` and the last `local` tokens.
+
+    Returns idx [B, Hq, cap] (ascending, -1 padded), score [B, Hq, cap],
+    count [B, Hq] (the true count, which may exceed cap) and tau [B, Hq], the
+    threshold the scan used.
+    """
+    _dev(Q, K, idx, score, count, tau)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = K.shape
+    dev = Q.device
+    if idx is None:
+        idx = torch.empty(B, Hq, cap, dtype=torch.int32, device=dev)
+    if score is None:
+        score = torch.empty(B, Hq, cap, dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    if tau is None:
+        tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    need = workspace_bytes(SA_OP_SELECT_TOPDELTA, B, Hq, Hkv, N, D, 0, cap)
+    if ws is None:
+        ws = workspace(need, dev, ("topdelta", B, Hq, Hkv, N, D, cap))
+    _check(_select_topdelta(_ptr(Q), _ptr(K), _dt(Q), B, Hq, Hkv, N, D, sink, local, delta, scale,
+                            cap, _ptr(idx), _ptr(score), _ptr(count), _ptr(tau), _ptr(ws),
+                            ws.numel(), _stream(stream)), "sa_select_topdelta")
+    return idx, score, count, tau
 
 
 def sa_sparse_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor,

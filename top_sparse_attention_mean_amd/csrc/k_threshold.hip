@@ -175,6 +175,127 @@ __global__ __launch_bounds__(256) void k_threshold_valu(
   }
 }
 
+// ---------------------------------------------------------------- top-delta
+// Threshold from a pseudo-maximum ("Faster Than Flash", Metodologia §2): per
+// query head, m~ = the largest score over the sink prefix [0, sink) and the
+// local window [N - local, N), and tau = m~ - delta.  One 256-thread workgroup
+// per (b, kv head) scores those <= sink + local tokens for the g heads of the
+// group; nothing else of the cache is read, so no reduction over the whole
+// cache is needed before the scan.
+//
+// tau stays on the safe side of the exact value: the workgroup takes the
+// maximum of fl32(s) - eps_t, a lower bound of every exact score (eps_t as in
+// the scan, without the tau term), so tau <= m~_exact - delta up to its own
+// float32 rounding, which the scan's comparison already covers.  Keys whose
+// exact score reaches m~_exact - delta are therefore all kept.
+struct PmWindow {
+  int ns, t0, W;  // sink tokens [0, ns), local tokens [t0, N), W = ns + N - t0
+  __device__ int token(int v) const { return v < ns ? v : t0 + (v - ns); }
+};
+
+__device__ __forceinline__ PmWindow pm_window(int N, int sink, int local) {
+  PmWindow w;
+  w.ns = min(sink, N);
+  w.t0 = max(N - min(local, N), w.ns);
+  w.W = w.ns + (N - w.t0);
+  return w;
+}
+
+// bf16: 16-token tiles on the same matrix-core chains as the scan.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_pseudo_max_mfma(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int Hq, int Hkv, int N,
+    int sink, int local, float delta, float scale, float gamma, float* __restrict__ tau) {
+  static_assert(G <= 16, "heads are the 16 columns of the score tile");
+  constexpr int NST = D / 32;
+  __shared__ float red[4][16];
+  const int bh = blockIdx.x, b = bh / Hkv, kh = bh % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gq = lane >> 4, nn = lane & 15;
+  const PmWindow win = pm_window(N, sink, local);
+  u32x4 qb[NST], qa[NST];
+  const uint16_t* qp = Q + (size_t(b) * Hq + kh * G + min(nn, G - 1)) * D + 8 * gq;
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    qb[st] = nn < G ? ld16(qp + 32 * st) : u32x4{0u, 0u, 0u, 0u};
+    qa[st] = qb[st] & 0x7fff7fffu;
+  }
+  const float gs = gamma * scale;
+  const uint16_t* Kb = K + size_t(bh) * N * D;
+  float lo = -__builtin_inff();
+  for (int v0 = wave * 16; v0 < win.W; v0 += 64) {
+    const int kr = win.token(min(v0 + nn, win.W - 1));
+    const uint16_t* kp = Kb + size_t(kr) * D + 8 * gq;
+    u32x4 ka[NST];
+#pragma unroll
+    for (int st = 0; st < NST; ++st) ka[st] = ld16(kp + 32 * st);
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f}, ab = sc;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      sc = mfma16x16x32(ka[st], qb[st], sc);
+      ab = mfma16x16x32(ka[st] & 0x7fff7fffu, qa[st], ab);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float s32 = sc[r] * scale;
+      const float eps = gs * ab[r] + fabsf(s32) * 9.5367431640625e-07f;  // 2^-20
+      if (v0 + 4 * gq + r < win.W) lo = fmaxf(lo, s32 - eps);
+    }
+  }
+  // lanes nn, nn + 16, nn + 32, nn + 48 hold head nn's rows
+  lo = fmaxf(lo, __shfl_xor(lo, 16));
+  lo = fmaxf(lo, __shfl_xor(lo, 32));
+  if (gq == 0) red[wave][nn] = lo;
+  __syncthreads();
+  if (wave == 0 && gq == 0 && nn < G) {
+    const float m = fmaxf(fmaxf(red[0][nn], red[1][nn]), fmaxf(red[2][nn], red[3][nn]));
+    tau[size_t(b) * Hq + kh * G + nn] = m - delta;
+  }
+}
+
+// float32: one (token, head) pair per thread, dot products on the vector ALUs.
+template <int D>
+__global__ __launch_bounds__(256) void k_pseudo_max_valu(
+    const float* __restrict__ Q, const float* __restrict__ K, int Hq, int Hkv, int G, int N,
+    int sink, int local, float delta, float scale, float gamma, float* __restrict__ tau) {
+  __shared__ float sq[8][D];
+  __shared__ float red[8][4];
+  const int bh = blockIdx.x, b = bh / Hkv, kh = bh % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = threadIdx.x; o < G * D; o += 256)
+    sq[o / D][o % D] = Q[(size_t(b) * Hq + kh * G + o / D) * D + o % D];
+  __syncthreads();
+  const PmWindow win = pm_window(N, sink, local);
+  const float* Kb = K + size_t(bh) * N * D;
+  for (int h = 0; h < G; ++h) {
+    float lo = -__builtin_inff();
+    for (int v = threadIdx.x; v < win.W; v += 256) {
+      const float* kp = Kb + size_t(win.token(v)) * D;
+      float s = 0.f, a = 0.f;
+      for (int d = 0; d < D; d += 4) {
+        const u32x4 w = ld16(kp + d);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float kv = __uint_as_float(w[c]);
+          s += sq[h][d + c] * kv;
+          a += fabsf(sq[h][d + c] * kv);
+        }
+      }
+      const float s32 = s * scale;
+      lo = fmaxf(lo, s32 - (gamma * scale * a + fabsf(s32) * 9.5367431640625e-07f));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lo = fmaxf(lo, __shfl_xor(lo, o));
+    if (lane == 0) red[h][wave] = lo;
+  }
+  __syncthreads();
+  if (threadIdx.x < G) {
+    const int h = threadIdx.x;
+    const float m = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
+    tau[size_t(b) * Hq + kh * G + h] = m - delta;
+  }
+}
+
 // One 256-thread workgroup per (b, query head): ordered copy of the staged
 // segments into idx/score [cap] and the true count.
 __global__ __launch_bounds__(256) void k_threshold_compact(
@@ -208,6 +329,42 @@ __global__ __launch_bounds__(256) void k_threshold_compact(
   if (tid == 0) count[bhq] = total;
 }
 
+// gamma of the float32 score bound: D bf16 products (exact) or D + 1 roundings
+// per float32 term, and the |q|.|k| sum's own relative error, plus margin.
+static float score_gamma(int dtype, int D) {
+  const double u = 1.0 / 8388608.0;  // 2^-23
+  const int terms = dtype == SA_BF16 ? D : D + 1;
+  const double gam = terms * u / (1.0 - terms * u);
+  return float(gam * (1.0 + gam) * 1.001);
+}
+
+hipError_t launch_pseudo_max(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
+                             int N, int D, int sink, int local, float delta, float scale,
+                             float* tau, hipStream_t st) {
+  const int G = Hq / Hkv;
+  const dim3 g(unsigned(B * Hkv));
+  const float gamma = score_gamma(dtype, D);
+  if (dtype == SA_BF16) {
+    auto q = static_cast<const uint16_t*>(Q);
+    auto k = static_cast<const uint16_t*>(K);
+#define SA_PM(DD, GG) k_pseudo_max_mfma<DD, GG><<<g, 256, 0, st>>>(q, k, Hq, Hkv, N, sink, local, delta, scale, gamma, tau)
+    if (D == 128) {
+      switch (G) { case 1: SA_PM(128, 1); break; case 2: SA_PM(128, 2); break;
+                   case 4: SA_PM(128, 4); break; default: SA_PM(128, 8); break; }
+    } else {
+      switch (G) { case 1: SA_PM(64, 1); break; case 2: SA_PM(64, 2); break;
+                   case 4: SA_PM(64, 4); break; default: SA_PM(64, 8); break; }
+    }
+#undef SA_PM
+  } else {
+    auto q = static_cast<const float*>(Q);
+    auto k = static_cast<const float*>(K);
+    if (D == 128) k_pseudo_max_valu<128><<<g, 256, 0, st>>>(q, k, Hq, Hkv, G, N, sink, local, delta, scale, gamma, tau);
+    else          k_pseudo_max_valu<64><<<g, 256, 0, st>>>(q, k, Hq, Hkv, G, N, sink, local, delta, scale, gamma, tau);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
                             int N, int D, const float* tau, float scale, int cap, int32_t* idx,
                             float* score, int32_t* count, const ThrWs& w, void* ws,
@@ -219,11 +376,7 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int 
   int32_t* sc = reinterpret_cast<int32_t*>(base + w.cnt_off);
   const int chunks = cdiv(w.nseg, 4);
   dim3 g(unsigned(long(BH) * chunks));
-  const double u = 1.0 / 8388608.0;  // 2^-23
-  const int terms = dtype == SA_BF16 ? D : D + 1;
-  const double gam = terms * u / (1.0 - terms * u);
-  // the |q|.|k| sum carries its own relative error; fold it in, plus margin
-  const float gamma = float(gam * (1.0 + gam) * 1.001);
+  const float gamma = score_gamma(dtype, D);
   if (dtype == SA_BF16) {
     auto q = static_cast<const uint16_t*>(Q);
     auto k = static_cast<const uint16_t*>(K);

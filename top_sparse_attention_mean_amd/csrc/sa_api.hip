@@ -195,6 +195,8 @@ size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int bloc
       return select_ws_bytes(B, Hkv, N, D, block, k);
     case SA_OP_SELECT_THRESHOLD:
       return threshold_ws(B, Hq, N).bytes;
+    case SA_OP_SELECT_TOPDELTA:
+      return topdelta_ws_bytes(B, Hq, N);
     case SA_OP_SPARSE_DECODE:        // k = idx_stride; block = 0 for token mode
       if (k < 1) return SIZE_MAX;
       return decode_ws(B, Hq, Hkv, D, block > 0 ? SA_IDX_BLOCKS : SA_IDX_TOKENS, block, k).bytes;
@@ -246,13 +248,10 @@ sa_status sa_select_topk(const void* Q, int dtype, int B, int Hq, int Hkv, int L
                     "sa_select_topk (select)");
 }
 
-sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
-                              int N, int D, const float* tau, float scale, int cap, int32_t* idx,
-                              float* score, int32_t* count, void* ws, size_t ws_bytes,
-                              void* stream) {
+static sa_status v_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
+                             int N, int D, int cap, int32_t* idx, float* score, int32_t* count) {
   PTR(Q);
   PTR(K);
-  PTR(tau);
   PTR(idx);
   PTR(score);
   PTR(count);
@@ -266,11 +265,46 @@ sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B, in
   else SUP(G <= 8, "float32 threshold selection needs g <= 8");
   const ThrWs w = threshold_ws(B, Hq, N);
   REQ(long(B) * Hkv * cdiv(w.nseg, 4) < (1L << 31), "grid too large");
+  return SA_OK;
+}
+
+sa_status sa_select_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
+                              int N, int D, const float* tau, float scale, int cap, int32_t* idx,
+                              float* score, int32_t* count, void* ws, size_t ws_bytes,
+                              void* stream) {
+  sa_status s = v_threshold(Q, K, dtype, B, Hq, Hkv, N, D, cap, idx, score, count);
+  if (s) return s;
+  PTR(tau);
+  const ThrWs w = threshold_ws(B, Hq, N);
   if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);
   PTR(ws);
   return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, tau, eff_scale(scale, D), cap,
                                      idx, score, count, w, ws, static_cast<hipStream_t>(stream)),
                     "sa_select_threshold");
+}
+
+sa_status sa_select_topdelta(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
+                             int N, int D, int sink, int local, float delta, float scale,
+                             int cap, int32_t* idx, float* score, int32_t* count, float* tau,
+                             void* ws, size_t ws_bytes, void* stream) {
+  sa_status s = v_threshold(Q, K, dtype, B, Hq, Hkv, N, D, cap, idx, score, count);
+  if (s) return s;
+  REQ(sink >= 0 && local >= 0, "sink and local must be >= 0 (got %d, %d)", sink, local);
+  REQ(sink > 0 || local > 0, "the sink and local windows are both empty");
+  REQ(delta >= 0.f, "delta must be >= 0 (got %g)", double(delta));   // NaN fails too
+  if (tau) PTR(tau);
+  const ThrWs w = threshold_ws(B, Hq, N);
+  const size_t need = topdelta_ws_bytes(B, Hq, N);
+  if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  PTR(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = eff_scale(scale, D);
+  float* t = tau ? tau : reinterpret_cast<float*>(static_cast<char*>(ws) + w.bytes);
+  hipError_t e = launch_pseudo_max(Q, K, dtype, B, Hq, Hkv, N, D, sink, local, delta, sc, t, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta (pseudo-max)");
+  return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, t, sc, cap, idx, score, count,
+                                     w, ws, st),
+                    "sa_select_topdelta (scan)");
 }
 
 sa_status sa_sparse_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,

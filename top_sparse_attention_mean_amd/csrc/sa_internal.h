@@ -131,6 +131,10 @@ inline ThrWs threshold_ws(int B, int Hq, int N) {
   w.bytes = w.cnt_off + align256(size_t(B) * Hq * w.nseg * sizeof(int32_t));
   return w;
 }
+// Top-delta adds the per-head thresholds [B, Hq] after the threshold workspace.
+inline size_t topdelta_ws_bytes(int B, int Hq, int N) {
+  return threshold_ws(B, Hq, N).bytes + align256(size_t(B) * Hq * sizeof(float));
+}
 
 // ---------------------------------------------------------------- launchers
 struct SelectPlan {
@@ -171,6 +175,9 @@ hipError_t launch_decode_tokens(const void* Q, const void* K, const void* V,
                                 const int32_t* count, int idx_stride,
                                 const float* score, const DecodeWs& w, void* ws,
                                 void* O, int out_dtype, float* lse, hipStream_t st);
+hipError_t launch_pseudo_max(const void* Q, const void* K, int dtype, int B,
+                             int Hq, int Hkv, int N, int D, int sink, int local,
+                             float delta, float scale, float* tau, hipStream_t st);
 hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
                             int Hq, int Hkv, int N, int D, const float* tau,
                             float scale, int cap, int32_t* idx, float* score,
