@@ -124,13 +124,18 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0) -> dict:
                       f"BLAS threads={threads}); sketch build excluded (amortised at prefill)"}
 
 
+# The sources the counted kernels (the selecting decode and the scoring scan)
+# and their launch configuration are built from.
+COUNTED_SOURCES = ["k_decode.hip", "k_select.hip", "sa_device.h", "sa_internal.h",
+                   "sa_score_core.h", "sa_select_core.h"]
+
+
 def kernel_source_hash() -> str:
-    """SHA-256 over the HIP sources and the C header (counter data goes stale with them)."""
+    """SHA-256 over the sources of the counted kernels (counter data goes stale with them)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "top_sparse_attention_mean_amd", "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
-    for path in files + [os.path.join(ROOT, "include", "sa.h")]:
+    for path in [os.path.join(csrc, f) for f in COUNTED_SOURCES]:
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
@@ -486,6 +491,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the threshold, top-delta and prefill variant measurements")
+    ap.add_argument("--variant", choices=["threshold", "topdelta", "prefill"],
+                    help="run only this variant measurement and print its JSON")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 counter passes (no timing output)")
     args = ap.parse_args(argv)
@@ -497,6 +504,9 @@ def main(argv=None) -> int:
         return 0
     if args.pmc_run:
         res = pmc_run(args)
+    elif args.variant:
+        res = (bench_prefill(args) if args.variant == "prefill" else
+               bench_threshold(args, args.variant))
     else:
         res = bench_decode(args)
         if not args.no_variants:

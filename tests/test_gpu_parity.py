@@ -319,6 +319,12 @@ THRESH_CASES = [
     ("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 4, "D": 64, "N": 3000}),
     ("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1, "D": 64, "N": 4096, "dtype": "f32",
                                "outlier_channels": 0}),
+    # long caches: several staging segments per compaction thread, then more
+    # segments than the compaction keeps in LDS
+    ("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1, "D": 64, "N": 300000, "needles": 8,
+                               "percentile": 99.8}),
+    ("threshold_decode_bf16", {"B": 1, "Hq": 4, "Hkv": 1, "D": 64, "N": 4099 * 128 - 51,
+                               "needles": 8, "percentile": 99.9}),
 ]
 
 

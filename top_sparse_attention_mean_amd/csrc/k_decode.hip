@@ -745,27 +745,64 @@ __global__ __launch_bounds__(256) void k_decode_tokens(DecodeArgs a) {
     m_run = mnew;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] *= alpha;
-    for (int i = rg; i < n; i += 16) {
-      const int tok = stok[i];
-      if (tok < 0) continue;
-      const float pv = sp[i];
-      const T* vp = Vb + size_t(tok) * D + lc * CPL;
+    // value pass: each 16-lane row group takes every 16th token; the V rows
+    // of UV of its tokens are loaded before any is used, so a row group has
+    // UV loads in flight instead of one (same summation order as one at a
+    // time; a missing token adds an exact zero whatever row 0 holds)
+    constexpr int UV = 8;
+    for (int i0 = rg; i0 < n; i0 += 16 * UV) {
+      float pv[UV];
+      bool ok[UV];
+      const T* vp[UV];
+#pragma unroll
+      for (int u = 0; u < UV; ++u) {
+        const int i = i0 + 16 * u;
+        const int tok = i < n ? stok[i] : -1;
+        ok[u] = tok >= 0;
+        pv[u] = ok[u] ? sp[i] : 0.f;
+        vp[u] = Vb + size_t(ok[u] ? tok : 0) * D + lc * CPL;
+      }
       if constexpr (sizeof(T) == 2) {
         if constexpr (CPL == 8) {
-          const u32x4 w = ld16(vp);
+          u32x4 w[UV];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) { acc[2 * q] += pv * bf16lo(w[q]); acc[2 * q + 1] += pv * bf16hi(w[q]); }
+          for (int u = 0; u < UV; ++u) w[u] = ld16(vp[u]);
+#pragma unroll
+          for (int u = 0; u < UV; ++u) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[2 * q] += ok[u] ? pv[u] * bf16lo(w[u][q]) : 0.f;
+              acc[2 * q + 1] += ok[u] ? pv[u] * bf16hi(w[u][q]) : 0.f;
+            }
+          }
         } else {
-          const u32x2 w = ld8(vp);
+          u32x2 w[UV];
 #pragma unroll
-          for (int q = 0; q < 2; ++q) { acc[2 * q] += pv * bf16lo(w[q]); acc[2 * q + 1] += pv * bf16hi(w[q]); }
+          for (int u = 0; u < UV; ++u) w[u] = ld8(vp[u]);
+#pragma unroll
+          for (int u = 0; u < UV; ++u) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+              acc[2 * q] += ok[u] ? pv[u] * bf16lo(w[u][q]) : 0.f;
+              acc[2 * q + 1] += ok[u] ? pv[u] * bf16hi(w[u][q]) : 0.f;
+            }
+          }
         }
       } else {
+        constexpr int NV = CPL / 4;
+        u32x4 w[UV][NV];
 #pragma unroll
-        for (int c = 0; c < CPL; c += 4) {
-          const u32x4 w = ld16(vp + c);
+        for (int u = 0; u < UV; ++u) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[c + q] += pv * __uint_as_float(w[q]);
+          for (int c = 0; c < NV; ++c) w[u][c] = ld16(vp[u] + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < UV; ++u) {
+#pragma unroll
+          for (int c = 0; c < NV; ++c) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[4 * c + q] += ok[u] ? pv[u] * __uint_as_float(w[u][c][q]) : 0.f;
+          }
         }
       }
     }

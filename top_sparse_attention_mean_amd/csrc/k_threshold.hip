@@ -297,30 +297,74 @@ __global__ __launch_bounds__(256) void k_pseudo_max_valu(
 }
 
 // One 256-thread workgroup per (b, query head): ordered copy of the staged
-// segments into idx/score [cap] and the true count.
+// segments into idx/score [cap] and the true count.  Thread t sums the counts
+// of its run of `per` consecutive segments; a block scan gives each run's
+// output offset.  The copy then goes by output position: position p finds its
+// run by binary search over the 256 run offsets and its segment by walking at
+// most `per` counts, so every position is copied independently.  With up to
+// kCompactLds segments (N <= 512K) the counts sit in LDS, and each thread
+// issues the loads of 4 positions before their stores: the only global reads
+// on a position's path are its staged pair.
+constexpr int kCompactLds = 4096;
+
+template <bool LDS>
 __global__ __launch_bounds__(256) void k_threshold_compact(
     const int32_t* __restrict__ st_idx, const float* __restrict__ st_val,
     const int32_t* __restrict__ st_cnt, int nseg, int cap, int32_t* __restrict__ idx,
     float* __restrict__ score, int32_t* __restrict__ count) {
   __shared__ int scan[17];
+  __shared__ int toff[256];
+  __shared__ int cl[LDS ? kCompactLds : 1];
   const int bhq = blockIdx.x, tid = threadIdx.x;
   const int per = (nseg + 255) / 256;
   const int s0 = min(tid * per, nseg), s1 = min(s0 + per, nseg);
   const int32_t* cnt = st_cnt + size_t(bhq) * nseg;
+  if constexpr (LDS) {
+    for (int s = tid; s < nseg; s += 256) cl[s] = cnt[s];
+    __syncthreads();
+  }
+  auto count_of = [&](int s) { if constexpr (LDS) return cl[s]; else return cnt[s]; };
   int mine = 0;
-  for (int s = s0; s < s1; ++s) mine += cnt[s];
+  for (int s = s0; s < s1; ++s) mine += count_of(s);
   int total;
-  int off = block_excl_scan<256>(mine, scan, &total);
+  toff[tid] = block_excl_scan<256>(mine, scan, &total);
+  __syncthreads();
   int32_t* oi = idx + size_t(bhq) * cap;
   float* ov = score + size_t(bhq) * cap;
-  for (int s = s0; s < s1; ++s) {
-    const size_t base = (size_t(bhq) * nseg + s) * kThrSeg;
-    const int c = cnt[s];
-    for (int e = 0; e < c && off + e < cap; ++e) {
-      oi[off + e] = st_idx[base + e];
-      ov[off + e] = st_val[base + e];
+  const size_t sb = size_t(bhq) * nseg;
+  const int lim = min(total, cap);
+  auto source = [&](int p) -> size_t {
+    int lo = 0, hi = 255;           // the last run whose offset is <= p
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (toff[mid] <= p) lo = mid;
+      else hi = mid - 1;
     }
-    off += c;
+    int s = lo * per, q = p - toff[lo];
+    for (int c = count_of(s); q >= c; c = count_of(s)) { q -= c; ++s; }
+    return (sb + s) * kThrSeg + q;
+  };
+  constexpr int U = 4;
+  for (int p0 = tid; p0 < lim; p0 += 256 * U) {
+    int32_t vi[U];
+    float vv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 256 * u;
+      if (p < lim) {
+        const size_t src = source(p);
+        vi[u] = st_idx[src];
+        vv[u] = st_val[src];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + 256 * u;
+      if (p < lim) {
+        oi[p] = vi[u];
+        ov[p] = vv[u];
+      }
+    }
   }
   for (int p = total + tid; p < cap; p += 256) {
     oi[p] = -1;
@@ -397,7 +441,10 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  k_threshold_compact<<<dim3(B * Hq), 256, 0, st>>>(si, sv, sc, w.nseg, cap, idx, score, count);
+  if (w.nseg <= kCompactLds)
+    k_threshold_compact<true><<<dim3(B * Hq), 256, 0, st>>>(si, sv, sc, w.nseg, cap, idx, score, count);
+  else
+    k_threshold_compact<false><<<dim3(B * Hq), 256, 0, st>>>(si, sv, sc, w.nseg, cap, idx, score, count);
   return hipGetLastError();
 }
 
