@@ -26,7 +26,9 @@ Pages cited (by title, section):
   * "Sparse Attention as a Range Searching Problem: Towards an
     Inference-Efficient Index for KV Cache" -- Metodologia §1 (the half-space
     H(q, tau) = {p : <q, p> >= tau}; every key inside it is returned, so the
-    selection has no false negatives).
+    selection has no false negatives) and §2 (subspace decomposition, bounding
+    spheres of clusters, the two-phase filter: prune by sphere, then check
+    the survivors exactly).
 
 Where the pages are silent or ambiguous, each function's docstring states the
 reading it takes.
@@ -40,7 +42,8 @@ from .attention import (
     select_topk_all, attend_blocks, attend_tokens, lse_merge,
     threshold_tau, select_threshold, prefill_pool_queries, prefill_select,
     prefill_attend_rows, prefill_attend, mass_oracle, decode_step,
-    window_tokens, pseudo_max, select_topdelta,
+    window_tokens, pseudo_max, select_topdelta, subspaces, subspace_radius,
+    block_upper_bound, select_threshold_pruned,
 )
 
 __all__ = [
@@ -48,5 +51,6 @@ __all__ = [
     "select_topk", "select_topk_all", "attend_blocks", "attend_tokens",
     "lse_merge", "threshold_tau", "select_threshold", "prefill_pool_queries",
     "prefill_select", "prefill_attend_rows", "prefill_attend", "mass_oracle",
-    "decode_step", "window_tokens", "pseudo_max", "select_topdelta",
+    "decode_step", "window_tokens", "pseudo_max", "select_topdelta", "subspaces",
+    "subspace_radius", "block_upper_bound", "select_threshold_pruned",
 ]

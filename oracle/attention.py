@@ -14,6 +14,7 @@ one function per step, in the order the method runs:
   O7 prefill_attend   causal attention of each query row over its block list
   O8 mass_oracle      exact per-block attention mass, for recall reporting
   O9 select_topdelta  pseudo-max over sink + local tokens; keep s >= m~ - delta
+  O10 select_threshold_pruned  block spheres per subspace prune, exact check after
      lse_merge        exact merge of attention partials over a split support
 
 Arrays: q [B, Hq, D]; Q [B, Hq, L, D]; K, V [B, Hkv, N, D]; query head h uses
@@ -490,3 +491,89 @@ def select_topdelta(q: np.ndarray, K: np.ndarray, sink: int, local: int, delta: 
     tau = pseudo_max(q, K, sink, local, scale) - float(delta)
     lists, vals = select_threshold(q, K, tau, scale)
     return lists, vals, tau
+
+
+# ------------------------------------------------------------------ O10
+def subspaces(D: int, S: int):
+    """Channel ranges of the S contiguous subspaces of a D-dim key space."""
+    if S < 1 or D % S:
+        raise ValueError("S must divide D")
+    w = D // S
+    return [(s * w, (s + 1) * w) for s in range(S)]
+
+
+def subspace_radius(K: np.ndarray, sk: np.ndarray, block: int, S: int) -> np.ndarray:
+    """O10a: rho[b, h, j, s] = max over the tokens t of block j of ||k_t,s - c_j,s||.
+
+    The bounding sphere of a cluster in one subspace ("Sparse Attention as a
+    Range Searching Problem", Metodologia §2: centre and radius per cluster,
+    one index per contiguous subspace).  Reading taken: the clusters are the
+    contiguous token blocks and the centre is the block's sketch row c_j (O1);
+    the radius is the exact largest distance of the block's keys from it.
+    """
+    B, H, N, D = K.shape
+    nb = -(-N // block)
+    out = np.zeros((B, H, nb, S))
+    for j in range(nb):
+        lo, hi = j * block, min((j + 1) * block, N)
+        dev = K[:, :, lo:hi, :] - sk[:, :, j][:, :, None, :]
+        for s, (c0, c1) in enumerate(subspaces(D, S)):
+            out[:, :, j, s] = np.sqrt((dev[..., c0:c1] ** 2).sum(axis=-1)).max(axis=-1)
+    return out
+
+
+def block_upper_bound(q: np.ndarray, sk: np.ndarray, rad: np.ndarray,
+                      scale: Optional[float] = None) -> np.ndarray:
+    """O10b: ub[b, h, j] = scale * sum_s (q_s . c_j,s + ||q_s|| rho_j,s).
+
+    For every key k in the block, q . k = sum_s q_s . c_s + q_s . (k_s - c_s),
+    and Cauchy-Schwarz bounds each q_s . (k_s - c_s) by ||q_s|| rho_s, so ub is
+    at least every exact score of the block: the sphere-versus-half-space test
+    of the two-phase filter (same page, Metodologia §2) summed over the
+    subspaces.  scale > 0 keeps the direction of the inequality.
+    """
+    B, Hq, D = q.shape
+    Hkv, nb, S = sk.shape[1], sk.shape[2], rad.shape[3]
+    g = Hq // Hkv
+    sc = _default_scale(D, scale)
+    out = np.zeros((B, Hq, nb))
+    for b in range(B):
+        for h in range(Hq):
+            kh = h // g
+            for s, (c0, c1) in enumerate(subspaces(D, S)):
+                qs = q[b, h, c0:c1]
+                out[b, h] += sk[b, kh, :, c0:c1] @ qs + np.linalg.norm(qs) * rad[b, kh, :, s]
+    return out * sc
+
+
+def select_threshold_pruned(q: np.ndarray, K: np.ndarray, tau: np.ndarray, block: int,
+                            S: int, scale: Optional[float] = None):
+    """O10: the half-space selection (O5) with whole blocks pruned first.
+
+    Phase one drops every block whose upper bound (O10b) is below tau[b, h];
+    phase two checks the exact score of every key of the surviving blocks
+    ("Sparse Attention as a Range Searching Problem", Metodologia §2, the
+    two-phase filter; its zero-false-negative guarantee holds because the
+    bound is rigorous).  The result equals select_threshold's.
+    Returns (lists, vals, survivors) with survivors[b][h] the ascending kept
+    block ids.
+    """
+    B, Hq, D = q.shape
+    N = K.shape[2]
+    sk = sketch(K, block)
+    rad = subspace_radius(K, sk, block, S)
+    ub = block_upper_bound(q, sk, rad, scale)
+    s = exact_scores(q, K, scale)
+    g = Hq // K.shape[1]
+    lists = [[None] * Hq for _ in range(B)]
+    vals = [[None] * Hq for _ in range(B)]
+    surv = [[None] * Hq for _ in range(B)]
+    for b in range(B):
+        for h in range(Hq):
+            alive = np.nonzero(ub[b, h] >= tau[b, h])[0]
+            toks = block_tokens(alive, block, N)
+            keep = toks[s[b, h, toks] >= tau[b, h]]
+            surv[b][h] = alive
+            lists[b][h] = keep
+            vals[b][h] = s[b, h, keep]
+    return lists, vals, surv

@@ -502,3 +502,100 @@ def test_topdelta_workload_concentrates_on_anchors():
     for h in range(wl.Hq):
         need = np.concatenate([np.arange(j * 64, (j + 1) * 64) for j in inp.needles[0, h // wl.g]])
         assert np.isin(lists[0][h], np.union1d(win, need)).mean() > 0.95
+
+
+# ------------------------------------------------------------------ O10
+def test_golden_sphere_bound():
+    g = {}
+    for k, v in read_golden("sphere_bound.txt"):
+        g.setdefault(k, []).append(v)
+    K = np.array([float(x) for x in g["keys"][0]]).reshape(1, 1, 4, 4)
+    q = np.array([float(x) for x in g["q"][0]]).reshape(1, 1, 4)
+    sk = oracle.sketch(K, 2)
+    np.testing.assert_array_equal(sk[0, 0, 0], [float(x) for x in g["centre0"][0]])
+    for row in g["rho"]:
+        S = int(row[0][1:])
+        rad = oracle.subspace_radius(K, sk, 2, S)
+        np.testing.assert_allclose(rad[0, 0, 0], [float(x) for x in row[1:]], atol=1e-15)
+        assert np.all(rad[0, 0, 1] == 0)
+    for row in g["ub"]:
+        S = int(row[0][1:])
+        rad = oracle.subspace_radius(K, sk, 2, S)
+        ub = oracle.block_upper_bound(q, sk, rad, scale=1.0)
+        np.testing.assert_allclose(ub[0, 0], [float(x) for x in row[1:]], atol=1e-14)
+    # tau = 5.1: only the box bound (S = 4) prunes block 0; nothing is kept
+    for S, alive in ((1, [0]), (2, [0]), (4, [])):
+        lists, _, surv = oracle.select_threshold_pruned(q, K, np.array([[5.1]]), 2, S, scale=1.0)
+        assert surv[0][0].tolist() == alive and lists[0][0].size == 0
+    lists, _, surv = oracle.select_threshold_pruned(q, K, np.array([[0.0]]), 2, 2, scale=1.0)
+    assert surv[0][0].tolist() == [0, 1] and lists[0][0].tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sphere_bound_dominates_every_score(seed):
+    """ub_j >= every exact score of block j, brute force, for every S dividing D,
+    partial last blocks and clustered or isotropic keys."""
+    rng = np.random.default_rng(400 + seed)
+    B, Hq, Hkv, D = 1, 4, 2, 16
+    N = int(rng.integers(20, 90))
+    block = int(rng.choice([4, 8, 16]))
+    K = rng.standard_normal((B, Hkv, N, D))
+    if seed % 2:
+        nb = -(-N // block)
+        mu = rng.standard_normal((B, Hkv, nb, D)) * 3
+        K = np.repeat(mu, block, axis=2)[:, :, :N] + 0.1 * K
+    q = rng.standard_normal((B, Hq, D))
+    s = A.exact_scores(q, K)
+    sk = oracle.sketch(K, block)
+    for S in (1, 2, 4, 8, 16):
+        rad = oracle.subspace_radius(K, sk, block, S)
+        ub = oracle.block_upper_bound(q, sk, rad)
+        for j in range(-(-N // block)):
+            lo, hi = j * block, min((j + 1) * block, N)
+            # the radius is a maximum over the block's keys, by a plain loop
+            for sub, (c0, c1) in enumerate(oracle.subspaces(D, S)):
+                r = max(math.sqrt(sum((K[0, 0, t, c] - sk[0, 0, j, c]) ** 2 for c in range(c0, c1)))
+                        for t in range(lo, hi))
+                assert abs(rad[0, 0, j, sub] - r) < 1e-12
+            assert np.all(ub[:, :, j] >= s[:, :, lo:hi].max(axis=-1) - 1e-12)
+    # the box bound (S = D) is sum_i |q_i| max_t |k_t,i - c_i|
+    rad = oracle.subspace_radius(K, sk, block, D)
+    box = (sk[0, 0] @ q[0, 0] + np.abs(q[0, 0]) @ rad[0, 0].T) / math.sqrt(D)
+    np.testing.assert_allclose(oracle.block_upper_bound(q, sk, rad)[0, 0], box, atol=1e-12)
+
+
+def test_sphere_bound_equality_case():
+    """Keys c +- rho q/||q|| attain the S = 1 bound: ub = max score exactly."""
+    D, rho = 8, 0.75
+    q = np.random.default_rng(410).standard_normal((1, 1, D))
+    u = q[0, 0] / np.linalg.norm(q[0, 0])
+    c = np.random.default_rng(411).standard_normal(D)
+    K = np.stack([c + rho * u, c - rho * u]).reshape(1, 1, 2, D)
+    sk = oracle.sketch(K, 2)
+    rad = oracle.subspace_radius(K, sk, 2, 1)
+    assert abs(rad[0, 0, 0, 0] - rho) < 1e-12
+    ub = oracle.block_upper_bound(q, sk, rad)
+    assert abs(ub[0, 0, 0] - A.exact_scores(q, K).max()) < 1e-12
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_pruned_selection_equals_threshold(S):
+    """Zero false negatives: pruning changes nothing in the kept lists, on
+    isotropic keys (nothing pruned) and on the clustered workload (most
+    blocks pruned)."""
+    for name, over in (("threshold_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 4096}),
+                       ("clustered_threshold_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 8192})):
+        wl = get_workload(name, **over)
+        inp = make_inputs(wl)
+        q, K = A.widen(inp.Q, "bf16"), A.widen(inp.K, "bf16")
+        tau64, _ = oracle.threshold_tau(q, K, wl.percentile)
+        want, wv = oracle.select_threshold(q, K, tau64)
+        got, gv, surv = oracle.select_threshold_pruned(q, K, tau64, wl.block, S)
+        alive = np.mean([len(surv[0][h]) / wl.nb for h in range(wl.Hq)])
+        for h in range(wl.Hq):
+            assert got[0][h].tolist() == want[0][h].tolist()
+            np.testing.assert_array_equal(gv[0][h], wv[0][h])
+        if name.startswith("clustered"):
+            assert alive < 0.2          # the spheres prune most blocks
+        else:
+            assert alive > 0.95         # isotropic keys: nothing to prune

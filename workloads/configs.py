@@ -39,6 +39,8 @@ class Workload:
     local: int = 0            # top-delta: trailing tokens of the pseudo-max window
     delta: float = 0.0        # top-delta: keep s >= pseudo-max - delta
     anchor_gain: float = 0.0  # sink and local keys get + anchor_gain * unit query
+    cluster_spread: float = 0.0  # > 0: keys of block j = mu_j + cluster_spread * noise
+    subspaces: int = 1        # pruned threshold: contiguous key subspaces per sphere set
     extra: dict = field(default_factory=dict)
 
     @property
@@ -88,6 +90,15 @@ WORKLOADS = {
         Hkv=8, D=128, N=32768, block=64, k=0, dtype="bf16", seed=2,
         needles=16, outlier_channels=4, outlier_scale=8.0, needle_gain=16.0,
         cap=4096, sink=64, local=64, delta=5.0, anchor_gain=16.0),
+    # The threshold selection over keys that form compact clusters, the
+    # setting in which "Sparse Attention as a Range Searching Problem"
+    # (Metodologia §2) prunes whole clusters by their bounding spheres: the
+    # keys of block j are mu_j + 0.05 * noise with mu_j ~ N(0, I).  Same
+    # shapes as the GQA decode config; tau = per-head 99th percentile.
+    "clustered_threshold_bf16": Workload(
+        name="clustered_threshold_bf16", kind="decode_threshold", B=8, Hq=32,
+        Hkv=8, D=128, N=32768, block=64, k=0, dtype="bf16", seed=4,
+        needles=16, percentile=99.0, cap=1024, cluster_spread=0.05, subspaces=1),
     # B=1, Hq=32, Hkv=4, d=128, L=64K, 128-token query and key blocks; each
     # query block keeps block 0, its diagonal block and the top-8 earlier blocks.
     "sparse_prefill_bf16": Workload(

@@ -4,7 +4,9 @@ Recipe (identical for every workload, so a reader can regenerate any array):
 
 1. ``rng = numpy.random.Generator(numpy.random.PCG64(seed))``.
 2. Draw Q, then K, then V as standard normal float32, each in layout order.
-3. Outlier channels (if any): for each kv head in order, draw that many
+3. Clusters (if cluster_spread > 0): draw mu ~ N(0, 1) of shape
+   [B, Hkv, nb, D]; the keys of block j become mu_j + cluster_spread * K.
+3b. Outlier channels (if any): for each kv head in order, draw that many
    distinct channels uniformly; multiply K and V in those channels by the
    outlier scale.  The channels are shared by every batch row.
 4. Positional drift (if any): for K, then V, draw eps ~ N(0, drift_var) of shape
@@ -122,6 +124,13 @@ def make_decode_inputs(wl: Workload, seed: Optional[int] = None) -> DecodeInputs
     Q = rng.standard_normal((B, Hq, D), dtype=np.float32)
     K = rng.standard_normal((B, Hkv, N, D), dtype=np.float32)
     V = rng.standard_normal((B, Hkv, N, D), dtype=np.float32)
+
+    if wl.cluster_spread > 0:
+        mu = rng.standard_normal((B, Hkv, nb, D), dtype=np.float32)
+        w = np.float32(wl.cluster_spread)
+        for j in range(nb):
+            K[:, :, j * wl.block:(j + 1) * wl.block] = (
+                mu[:, :, j][:, :, None, :] + w * K[:, :, j * wl.block:(j + 1) * wl.block])
 
     outl = None
     if wl.outlier_channels:
