@@ -383,6 +383,95 @@ def bench_threshold(args, which: str = "threshold") -> dict:
     return res
 
 
+def bench_pruned(args) -> dict:
+    """Sphere-pruned threshold selection on the clustered workload: the bound
+    kernel, then the scan of the live segments only, the compaction and the
+    token-mode decode.  The unpruned scan on the same arrays is timed beside it."""
+    import numpy as np
+    import torch
+    import oracle
+    import top_sparse_attention_mean_amd as sa
+    from oracle.attention import widen
+    from tests.parity_util import to_dev
+    from workloads import get_workload, make_inputs
+    wl = get_workload("clustered_threshold_bf16")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl)
+    q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
+    _, tau32 = oracle.threshold_tau(q, K, wl.percentile)        # the workload's tau (input)
+    R = 2
+    Qs = [to_dev(inp.Q, wl.dtype, dev) for _ in range(R)]
+    Kd = to_dev(inp.K, wl.dtype, dev)
+    Ks = [Kd] + [Kd.clone() for _ in range(R - 1)]
+    Vd = to_dev(inp.V, wl.dtype, dev)
+    Vs = [Vd] + [Vd.clone() for _ in range(R - 1)]
+    B, Hq, Hkv, D, N, blk, S = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N, wl.block, wl.subspaces
+    sks = [sa.sa_build_sketch(k, blk) for k in Ks]                  # built once, at prefill
+    rads = [sa.sa_build_radius(k, sk, blk, S) for k, sk in zip(Ks, sks)]
+    tau = torch.from_numpy(tau32).to(dev)
+    idx = torch.empty(B, Hq, wl.cap, dtype=torch.int32, device=dev)
+    sc = torch.empty(B, Hq, wl.cap, dtype=torch.float32, device=dev)
+    cnt = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    nseg = -(-N // 128)
+    live = torch.empty(B, Hkv, nseg, dtype=torch.uint8, device=dev)
+    O = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    pws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_PRUNED, B, Hq, Hkv, N, D, blk, wl.cap),
+                      dtype=torch.uint8, device=dev)
+    tws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_THRESHOLD, B, Hq, Hkv, N, D, 0, wl.cap),
+                      dtype=torch.uint8, device=dev)
+    dws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, 0, wl.cap),
+                      dtype=torch.uint8, device=dev)
+
+    def sel(r):
+        sa.sa_select_threshold_pruned(Qs[r], Ks[r], sks[r], rads[r], tau, wl.cap, blk, idx=idx,
+                                      score=sc, count=cnt, live=live, ws=pws)
+
+    def sel0(r):
+        sa.sa_select_threshold(Qs[r], Ks[r], tau, wl.cap, idx=idx, score=sc, count=cnt, ws=tws)
+
+    def dec(r):
+        sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], idx, cnt, mode=sa.SA_IDX_TOKENS, score=sc,
+                            O=O, lse=lse, ws=dws)
+
+    n = max(4, args.steps // 20)
+    t_sel0 = graph_time(sel0, R, n)
+    t_pass = graph_time(lambda r: (sel(r), dec(r)), R, n)
+    t_sel = graph_time(sel, R, n)
+    e = 2
+    kept = int(cnt.sum().item())
+    frac = float(live.float().mean().item())
+    nb = -(-N // blk)
+    bound_bytes = B * Hkv * nb * (D + S) * 4 + B * Hq * D * e + B * Hq * 4
+    scan_bytes = int(round(frac * B * Hkv * N * D * e))
+    ach = (bound_bytes + scan_bytes + kept * 8) / (t_sel * 1e-6) / 1e9
+    res = {
+        "workload": wl.name, "us_per_pass": round(t_pass, 2), "subspaces": S,
+        "pass": "sphere bounds + scan of the live segments + compaction "
+                "(sa_select_threshold_pruned) + token-mode decode",
+        "kernels_us": {"sa_select_threshold_pruned (k_prune + k_threshold_mfma + "
+                       "k_threshold_compact)": round(t_sel, 2),
+                       "sa_sparse_decode tokens (k_decode_tokens)": round(max(t_pass - t_sel, 0), 2),
+                       "unpruned sa_select_threshold on the same arrays": round(t_sel0, 2)},
+        "live_segment_fraction": round(frac, 4), "kept_tokens": kept,
+        "roofline": {"bound": "hbm", "kernel": "k_threshold_mfma over the live segments (the "
+                     "call also runs the bound and compaction kernels)", "achieved": round(ach, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "algorithmic_bytes": bound_bytes + scan_bytes + kept * 8,
+                     "avg_us": round(t_sel, 2)},
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        lists, _, _ = oracle.select_threshold_pruned(q, K, tau32.astype(np.float64), blk, S)
+        oracle.attend_tokens(q, K, V, lists)
+        t_cpu = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(t_cpu * 1e6, 1), "unit": "us/pass",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "sample": "one full pass (all 256 heads, float64; sketch and "
+                                         "radius included)"}
+    return res
+
+
 def bench_prefill(args) -> dict:
     """Block-sparse causal prefill (rows a1 pooling, a3, a7) at its full size."""
     import numpy as np
@@ -490,8 +579,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the threshold, top-delta and prefill variant measurements")
-    ap.add_argument("--variant", choices=["threshold", "topdelta", "prefill"],
+                    help="skip the threshold, top-delta, pruned and prefill variant measurements")
+    ap.add_argument("--variant", choices=["threshold", "topdelta", "pruned", "prefill"],
                     help="run only this variant measurement and print its JSON")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 counter passes (no timing output)")
@@ -506,6 +595,7 @@ def main(argv=None) -> int:
         res = pmc_run(args)
     elif args.variant:
         res = (bench_prefill(args) if args.variant == "prefill" else
+               bench_pruned(args) if args.variant == "pruned" else
                bench_threshold(args, args.variant))
     else:
         res = bench_decode(args)
@@ -518,6 +608,9 @@ def main(argv=None) -> int:
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"]["topdelta"] = bench_threshold(args, "topdelta")
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["variants"]["pruned"] = bench_pruned(args)
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"]["prefill"] = bench_prefill(args)

@@ -93,7 +93,8 @@ enum {
   SA_OP_SELECT_THRESHOLD = 1,
   SA_OP_SPARSE_DECODE = 2,
   SA_OP_DECODE_STEP = 3,
-  SA_OP_SELECT_TOPDELTA = 4
+  SA_OP_SELECT_TOPDELTA = 4,
+  SA_OP_SELECT_PRUNED = 5
 };
 
 /*
@@ -211,6 +212,51 @@ sa_status sa_select_topdelta(const void* Q, const void* K, int dtype, int B,
                              float delta, float scale, int cap, int32_t* idx,
                              float* score, int32_t* count, float* tau, void* ws,
                              size_t ws_bytes, void* stream);
+
+/*
+ * sa_build_radius -- bounding spheres of the key blocks per subspace ([RANGE]
+ * Metodologia §2: the key space is cut into S contiguous subspaces and every
+ * cluster gets a centre and a radius in each; here the clusters are the
+ * token blocks and the centres the block sketch rows).
+ *
+ *   X        [B, H, N, D] dtype (the keys)
+ *   sketch   [B, H, nb, D] float32 in: the centres (sa_build_sketch's output)
+ *   radius   [B, H, nb, S] float32 out: rho[j, s] >= the largest distance
+ *            ||x_t,s - c_j,s|| over the valid tokens t of block j (rounded up
+ *            by a relative 2^-16, so it never falls below the exact value)
+ *   S        subspaces of D/S consecutive channels; D/S a multiple of 8,
+ *            S <= 16 (else SA_ERR_UNSUPPORTED)
+ * NaN keys are skipped by the maximum (their block's centre is NaN anyway).
+ */
+sa_status sa_build_radius(const void* X, int dtype, int B, int H, int N, int D,
+                          int block, int S, const float* sketch, float* radius,
+                          void* stream);
+
+/*
+ * sa_select_threshold_pruned -- the half-space selection of
+ * sa_select_threshold with whole blocks pruned first ([RANGE] Metodologia §2,
+ * the two-phase filter).  Block j is dropped for query head h when
+ *     scale * sum_s (q_s . c_j,s + ||q_s|| rho_j,s) < tau[b, h],
+ * a rigorous upper bound of every score in the block (Cauchy-Schwarz per
+ * subspace), evaluated in float32 with a margin that covers its rounding.
+ * A 128-token staging segment is scanned when any of its blocks survives
+ * for any head of the kv group; the scan, the exact check and the outputs
+ * are those of sa_select_threshold, so there are no false negatives.
+ *
+ *   block    32, 64 or 128 (the blocks of sketch and radius)
+ *   S, sketch, radius   as built by sa_build_sketch and sa_build_radius on K
+ *   tau, cap, idx, score, count   as sa_select_threshold
+ *   live     [B, Hkv, ceil(N/128)] uint8 out: 1 where the segment was scanned
+ *            (NULL: kept in ws)
+ * ws: sa_workspace_bytes(SA_OP_SELECT_PRUNED, B, Hq, Hkv, N, D, block, cap).
+ */
+sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype,
+                                     int B, int Hq, int Hkv, int N, int D,
+                                     int block, int S, const float* sketch,
+                                     const float* radius, const float* tau,
+                                     float scale, int cap, int32_t* idx,
+                                     float* score, int32_t* count, uint8_t* live,
+                                     void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sa_sparse_decode -- exact attention restricted to the selected keys, as

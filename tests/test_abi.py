@@ -31,6 +31,9 @@ def lib():
     L.sa_select_topk.argtypes = [P, I, I, I, I, I, I, I, P, I, I, U, F, P, P, P, P, Z, P]
     L.sa_select_threshold.argtypes = [P, P, I, I, I, I, I, I, P, F, I, P, P, P, P, Z, P]
     L.sa_select_topdelta.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, I, P, P, P, P, P, Z, P]
+    L.sa_build_radius.argtypes = [P, I, I, I, I, I, I, I, P, P, P]
+    L.sa_select_threshold_pruned.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P, F, I, P, P, P,
+                                             P, P, Z, P]
     L.sa_sparse_decode.argtypes = [P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P, P, I, P, P, Z, P]
     L.sa_sparse_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, I, P, I, P, P]
     L.sa_decode_step.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P, P, Z, P]
@@ -50,9 +53,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-              "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step",
-              "sa_workspace_bytes",
+    for n in ["sa_build_sketch", "sa_build_radius", "sa_select_topk", "sa_select_threshold",
+              "sa_select_topdelta", "sa_select_threshold_pruned", "sa_sparse_decode",
+              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
               "sa_status_str",
               "sa_last_error", "sa_version"]:
         assert n in names
@@ -93,6 +96,8 @@ def test_workspace_sizes(lib):
     assert lib.sa_workspace_bytes(9, 1, 1, 1, 1, 64, 64, 1) == ctypes.c_size_t(-1).value
     # top-delta: the threshold staging plus one float threshold per (b, head)
     assert lib.sa_workspace_bytes(4, 8, 32, 8, 32768, 128, 0, 1024) >= a + 8 * 32 * 4
+    # pruned threshold: the staging plus one flag per (b, kv head, 128-token segment)
+    assert lib.sa_workspace_bytes(5, 8, 32, 8, 32768, 128, 64, 1024) >= a + 8 * 8 * 256
 
 
 def test_sketch_validation(lib):
@@ -163,6 +168,45 @@ def test_topdelta_validation(lib):
     assert call(4, 48) == UNSUPPORTED             # bf16 g = 6
     assert call(18, 1024) == WORKSPACE
     assert call(1, None) == INVALID               # K
+
+
+def test_radius_validation(lib):
+    f = lib.sa_build_radius
+    base = [A, 1, 1, 8, 32768, 128, 64, 1, A, A, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(7, 3) == UNSUPPORTED              # S does not divide D
+    assert call(7, 32) == UNSUPPORTED             # subspaces of 4 channels
+    a = list(base)
+    a[5], a[7] = 64, 16                           # D = 64: 4-channel subspaces
+    assert f(*a) == UNSUPPORTED
+    assert call(6, 0) == INVALID                  # block
+    assert call(9, MIS) == INVALID                # misaligned radius
+    assert call(8, None) == INVALID               # sketch
+
+
+def test_pruned_threshold_validation(lib):
+    f = lib.sa_select_threshold_pruned
+    base = [A, A, 1, 8, 32, 8, 32768, 128, 64, 1, A, A, A, 0.0, 1024, A, A, A, None, A, 1 << 30,
+            None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(8, 48) == UNSUPPORTED             # block must divide the 128-token segment
+    assert call(8, 256) == UNSUPPORTED
+    assert call(9, 5) == UNSUPPORTED              # S
+    assert call(11, None) == INVALID              # radius
+    assert call(12, None) == INVALID              # tau
+    assert call(18, MIS) == INVALID               # misaligned live
+    assert call(20, 4096) == WORKSPACE
+    assert call(4, 48) == UNSUPPORTED             # bf16 g = 6
 
 
 def test_decode_validation(lib):
@@ -237,6 +281,7 @@ def test_binding_binds_every_entry_point():
     sa = pytest.importorskip("top_sparse_attention_mean_amd")
     for n in sa.EXPORTS:
         assert hasattr(sa, "_" + n[len("sa_"):]), f"no ctypes signature for {n}"
-    for n in ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-              "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
+    for n in ["sa_build_sketch", "sa_build_radius", "sa_select_topk", "sa_select_threshold",
+              "sa_select_topdelta", "sa_select_threshold_pruned", "sa_sparse_decode",
+              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
         assert callable(getattr(sa, n)), n

@@ -96,6 +96,46 @@ def test_full_threshold():
           f"{time.time() - t0:.1f}s")
 
 
+def test_full_pruned_threshold():
+    """The clustered threshold workload whole: bounding spheres built on the GPU,
+    the pruned scan against the exact rule (zero false negatives) and against
+    the unpruned scan on every scanned segment."""
+    t0 = time.time()
+    wl = get_workload("clustered_threshold_bf16")
+    inp = make_inputs(wl)
+    q, K, V = (widen(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    tau64, tau32 = oracle.threshold_tau(q, K, wl.percentile)
+    tau = torch.from_numpy(tau32).cuda()
+    sk = sa.sa_build_sketch(Kd, wl.block)
+    rad = sa.sa_build_radius(Kd, sk, wl.block, wl.subspaces)
+    idx, score, cnt, live = sa.sa_select_threshold_pruned(Qd, Kd, sk, rad, tau, wl.cap, wl.block)
+    idx0, _, cnt0 = sa.sa_select_threshold(Qd, Kd, tau, wl.cap)
+    O32, lse = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS, score=score,
+                                   out_dtype=torch.float32)
+    s = exact_scores(q, K)
+    idx_h, cnt_h, live_h = idx.cpu().numpy(), cnt.cpu().numpy(), live.cpu().numpy()
+    idx0_h, cnt0_h = idx0.cpu().numpy(), cnt0.cpu().numpy()
+    lists = [[None] * wl.Hq for _ in range(wl.B)]
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            got = idx_h[b, h, :cnt_h[b, h]]
+            exact = np.nonzero(s[b, h] >= tau64[b, h])[0]
+            assert set(exact.tolist()) <= set(got.tolist()), f"false negative at b{b} h{h}"
+            assert np.all(s[b, h, np.setdiff1d(got, exact)] >= tau64[b, h] - 1e-3)
+            ref = idx0_h[b, h, :cnt0_h[b, h]]
+            assert np.array_equal(got, ref[live_h[b, h // wl.g][ref // 128] == 1])
+            lists[b][h] = got
+    O_ref, lse_ref = oracle.attend_tokens(q, K, V, lists)
+    err = max_abs(O32.cpu().numpy(), O_ref)
+    assert err <= 2e-3
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    frac = live_h.mean()
+    assert frac < 0.5
+    print(f"pruned threshold: {frac:.1%} of segments scanned, max-abs O error {err:.2e}, "
+          f"{time.time() - t0:.1f}s")
+
+
 def test_full_prefill():
     t0 = time.time()
     wl = get_workload("sparse_prefill_bf16")

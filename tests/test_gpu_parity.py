@@ -507,6 +507,94 @@ def test_topdelta_infinite_delta_is_dense_and_capacity():
     assert torch.equal(i3, full) and torch.equal(c3, cfull)
 
 
+PRUNE_CASES = [
+    ("clustered_threshold_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 8192, "needles": 4}, 1),
+    ("clustered_threshold_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 8192 - 77, "needles": 4}, 4),
+    ("clustered_threshold_bf16", {"B": 2, "Hq": 4, "Hkv": 4, "D": 64, "N": 3000, "needles": 2,
+                                  "block": 32}, 2),
+    ("clustered_threshold_bf16", {"B": 1, "Hq": 8, "Hkv": 1, "N": 5000, "needles": 3,
+                                  "block": 128}, 16),
+    ("clustered_threshold_bf16", {"B": 1, "Hq": 6, "Hkv": 1, "D": 64, "N": 4096 - 5,
+                                  "dtype": "f32", "needles": 2}, 8),
+    ("threshold_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 5000}, 1),      # nothing to prune
+]
+
+
+def _radius_check(K, sk_gpu, rad_gpu, block, S):
+    """The GPU radius bounds every key's distance from the GPU's own centre and
+    exceeds it by at most the stated rounding allowance."""
+    B, H, N, D = K.shape
+    sk = sk_gpu.astype(np.float64)
+    W = D // S
+    for j in range(-(-N // block)):
+        lo, hi = j * block, min((j + 1) * block, N)
+        dev = K[:, :, lo:hi, :] - sk[:, :, j][:, :, None, :]
+        r = np.sqrt((dev.reshape(B, H, hi - lo, S, W) ** 2).sum(-1)).max(axis=2)   # [B, H, S]
+        got = rad_gpu[:, :, j, :].astype(np.float64)
+        assert np.all(got >= r), j
+        assert np.all(got <= r * (1 + 1e-4) + 1e-30), j
+
+
+@pytest.mark.parametrize("name,over,S", PRUNE_CASES)
+def test_pruned_threshold_parity(name, over, S):
+    wl, inp, q, K, V = _decode_case(name, over)
+    dt, blk = wl.dtype, wl.block
+    Qd, Kd, Vd = to_dev(inp.Q, dt), to_dev(inp.K, dt), to_dev(inp.V, dt)
+    sk = sa.sa_build_sketch(Kd, blk)
+    rad = sa.sa_build_radius(Kd, sk, blk, S)
+    sk_h, rad_h = sk.cpu().numpy(), rad.cpu().numpy()
+    _radius_check(K, sk_h, rad_h, blk, S)
+    # against the oracle's own spheres (float64 centres)
+    sk_x = oracle.sketch(K, blk)
+    rad_x = oracle.subspace_radius(K, sk_x, blk, S)
+    assert max_abs(rad_h, rad_x) <= 1e-4 * max(1.0, np.abs(rad_x).max())
+    tau64, tau32 = oracle.threshold_tau(q, K, wl.percentile)
+    tau = torch.from_numpy(tau32).cuda()
+    idx, score, cnt, live = sa.sa_select_threshold_pruned(Qd, Kd, sk, rad, tau, wl.cap, blk)
+    idx_h, sc_h, cnt_h, live_h = (t.cpu().numpy() for t in (idx, score, cnt, live))
+    # the unpruned scan on the same inputs: identical on every scanned segment
+    idx0, score0, cnt0 = sa.sa_select_threshold(Qd, Kd, tau, wl.cap)
+    idx0_h, sc0_h, cnt0_h = idx0.cpu().numpy(), score0.cpu().numpy(), cnt0.cpu().numpy()
+    s = exact_scores(q, K)
+    eps = _eps_bound(q, K, wl)
+    ub = oracle.block_upper_bound(q, sk_x, rad_x)
+    g, nseg, bps = wl.g, -(-wl.N // 128), 128 // blk
+    lists = [[None] * wl.Hq for _ in range(wl.B)]
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            for seg in range(nseg):
+                blocks = range(seg * bps, min((seg + 1) * bps, wl.nb))
+                need = any(ub[b, h, j] >= tau64[b, h] for h in range(kh * g, (kh + 1) * g)
+                           for j in blocks)
+                near = any(ub[b, h, j] >= tau64[b, h] - 1e-3 * (1 + abs(tau64[b, h]))
+                           for h in range(kh * g, (kh + 1) * g) for j in blocks)
+                assert live_h[b, kh, seg] in (0, 1)
+                if need:
+                    assert live_h[b, kh, seg] == 1, (b, kh, seg)
+                if live_h[b, kh, seg]:
+                    assert near, (b, kh, seg)
+        for h in range(wl.Hq):
+            n = int(cnt_h[b, h])
+            got = idx_h[b, h, :n]
+            assert n <= wl.cap and np.all(idx_h[b, h, n:] == -1) and np.all(np.diff(got) > 0)
+            exact = np.nonzero(s[b, h] >= tau64[b, h])[0]
+            missing = set(exact.tolist()) - set(got.tolist())
+            assert not missing, f"false negatives at b{b} h{h}: {sorted(missing)[:5]}"
+            ex = np.setdiff1d(got, exact)
+            assert np.all(s[b, h, ex] >= tau64[b, h] - 2 * eps[b, h, ex])
+            ref = idx0_h[b, h, :cnt0_h[b, h]]
+            on = live_h[b, h // g][ref // 128] == 1
+            assert np.array_equal(got, ref[on])
+            np.testing.assert_array_equal(sc_h[b, h, :n], sc0_h[b, h, :cnt0_h[b, h]][on])
+            lists[b][h] = got
+    O_ref, lse_ref = oracle.attend_tokens(q, K, V, lists)
+    O32, lse = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS, score=score,
+                                   out_dtype=torch.float32)
+    assert max_abs(O32.cpu().numpy(), O_ref) <= OUT_TOL[dt]
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    print(f"{name} {over} S={S}: {live_h.mean():.1%} of segments scanned")
+
+
 PREFILL_CASES = [
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 2048, "needles": 4}),
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 1, "N": 2048 + 77, "needles": 4}),   # ragged

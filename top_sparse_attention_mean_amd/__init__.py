@@ -31,10 +31,10 @@ SA_F32, SA_BF16 = 0, 1
 SA_FORCE_SINK, SA_FORCE_LOCAL, SA_CAUSAL = 1, 2, 4
 SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
 (SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP,
- SA_OP_SELECT_TOPDELTA) = range(5)
+ SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED) = range(6)
 
-EXPORTS = ["sa_build_sketch", "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-           "sa_sparse_decode",
+EXPORTS = ["sa_build_sketch", "sa_build_radius", "sa_select_topk", "sa_select_threshold",
+           "sa_select_topdelta", "sa_select_threshold_pruned", "sa_sparse_decode",
            "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
            "sa_status_str",
            "sa_last_error", "sa_version"]
@@ -58,6 +58,9 @@ _select_topk = _sig("sa_select_topk", _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I
                     _P, _P, _P, _P, _Z, _P)
 _select_threshold = _sig("sa_select_threshold", _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I,
                          _P, _P, _P, _P, _Z, _P)
+_build_radius = _sig("sa_build_radius", _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P)
+_select_threshold_pruned = _sig("sa_select_threshold_pruned", _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                _I, _I, _P, _P, _P, _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                         _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _sparse_decode = _sig("sa_sparse_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
@@ -162,6 +165,20 @@ def sa_build_sketch(X: torch.Tensor, block: int, head_pool: int = 1, blk_begin: 
     return out
 
 
+def sa_build_radius(X: torch.Tensor, sketch: torch.Tensor, block: int, S: int = 1,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Bounding-sphere radii of X [B, H, N, D] around its block sketch
+    [B, H, nb, D], per subspace of D/S channels -> float32 [B, H, nb, S]."""
+    _dev(X, sketch, out)
+    B, H, N, D = X.shape
+    nb = -(-N // block)
+    if out is None:
+        out = torch.empty(B, H, nb, S, dtype=torch.float32, device=X.device)
+    _check(_build_radius(_ptr(X), _dt(X), B, H, N, D, block, S, _ptr(sketch), _ptr(out),
+                         _stream(stream)), "sa_build_radius")
+    return out
+
+
 def sa_select_topk(Q: torch.Tensor, ksketch: torch.Tensor, k: int,
                    flags: int = SA_FORCE_SINK | SA_FORCE_LOCAL, scale: float = 0.0,
                    Hkv: Optional[int] = None, q_block: int = 1,
@@ -222,6 +239,39 @@ def sa_select_threshold(Q: torch.Tensor, K: torch.Tensor, tau: torch.Tensor, cap
                              _ptr(idx), _ptr(score), _ptr(count), _ptr(ws), ws.numel(),
                              _stream(stream)), "sa_select_threshold")
     return idx, score, count
+
+
+def sa_select_threshold_pruned(Q: torch.Tensor, K: torch.Tensor, sketch: torch.Tensor,
+                               radius: torch.Tensor, tau: torch.Tensor, cap: int, block: int,
+                               scale: float = 0.0, idx=None, score=None, count=None, live=None,
+                               ws=None, stream=None):
+    """Half-space selection with blocks pruned by their bounding spheres first.
+
+    sketch [B, Hkv, nb, D] and radius [B, Hkv, nb, S] as built on K.  Returns
+    idx, score, count (as sa_select_threshold) and live [B, Hkv, ceil(N/128)]
+    uint8, 1 where the 128-token segment was scanned.
+    """
+    _dev(Q, K, sketch, radius, tau, idx, score, count, live)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = K.shape
+    S = radius.shape[-1]
+    dev = Q.device
+    if idx is None:
+        idx = torch.empty(B, Hq, cap, dtype=torch.int32, device=dev)
+    if score is None:
+        score = torch.empty(B, Hq, cap, dtype=torch.float32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    if live is None:
+        live = torch.empty(B, Hkv, -(-N // 128), dtype=torch.uint8, device=dev)
+    need = workspace_bytes(SA_OP_SELECT_PRUNED, B, Hq, Hkv, N, D, block, cap)
+    if ws is None:
+        ws = workspace(need, dev, ("pruned", B, Hq, Hkv, N, D, cap))
+    _check(_select_threshold_pruned(_ptr(Q), _ptr(K), _dt(Q), B, Hq, Hkv, N, D, block, S,
+                                    _ptr(sketch), _ptr(radius), _ptr(tau), scale, cap,
+                                    _ptr(idx), _ptr(score), _ptr(count), _ptr(live), _ptr(ws),
+                                    ws.numel(), _stream(stream)), "sa_select_threshold_pruned")
+    return idx, score, count, live
 
 
 def sa_select_topdelta(Q: torch.Tensor, K: torch.Tensor, sink: int, local: int, delta: float,

@@ -36,15 +36,18 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void k_threshold_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int BH, int Hq, int Hkv,
     int N, float scale, float gamma, const float* __restrict__ tau, int nseg,
-    int32_t* __restrict__ st_idx, float* __restrict__ st_val, int32_t* __restrict__ st_cnt) {
+    const uint8_t* __restrict__ live, int32_t* __restrict__ st_idx, float* __restrict__ st_val,
+    int32_t* __restrict__ st_cnt) {
   static_assert(G <= 16, "heads are the 16 columns of the score tile");
   constexpr int NST = D / 32;
   const int bh = blockIdx.x % BH, chunk = blockIdx.x / BH;
   const int b = bh / Hkv, kh = bh % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gq = lane >> 4, nn = lane & 15;
-  const int seg = chunk * 4 + wave;
+  const int seg = chunk * int(blockDim.x >> 6) + wave;
   if (seg >= nseg) return;  // no barriers below
+  // a segment pruned by its blocks' spheres has its counts zeroed already
+  if (live && !live[size_t(bh) * nseg + seg]) return;
 
   u32x4 qb[NST], qa[NST];
   float th = __builtin_inff();
@@ -129,16 +132,18 @@ template <int D>
 __global__ __launch_bounds__(256) void k_threshold_valu(
     const float* __restrict__ Q, const float* __restrict__ K, int BH, int Hq, int Hkv, int G,
     int N, float scale, float gamma, const float* __restrict__ tau, int nseg,
-    int32_t* __restrict__ st_idx, float* __restrict__ st_val, int32_t* __restrict__ st_cnt) {
+    const uint8_t* __restrict__ live, int32_t* __restrict__ st_idx, float* __restrict__ st_val,
+    int32_t* __restrict__ st_cnt) {
   __shared__ float sq[16][D];
   const int bh = blockIdx.x % BH, chunk = blockIdx.x / BH;
   const int b = bh / Hkv, kh = bh % Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int o = threadIdx.x; o < G * D; o += 256)
+  for (int o = threadIdx.x; o < G * D; o += blockDim.x)
     sq[o / D][o % D] = Q[(size_t(b) * Hq + kh * G + o / D) * D + o % D];
   __syncthreads();
-  const int seg = chunk * 4 + wave;
+  const int seg = chunk * int(blockDim.x >> 6) + wave;
   if (seg >= nseg) return;
+  if (live && !live[size_t(bh) * nseg + seg]) return;
   const float* Kb = K + size_t(bh) * N * D;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int h = 0; h < G; ++h) {
@@ -412,19 +417,23 @@ hipError_t launch_pseudo_max(const void* Q, const void* K, int dtype, int B, int
 hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
                             int N, int D, const float* tau, float scale, int cap, int32_t* idx,
                             float* score, int32_t* count, const ThrWs& w, void* ws,
-                            hipStream_t st) {
+                            hipStream_t st, const uint8_t* live) {
   const int BH = B * Hkv, G = Hq / Hkv;
   char* base = static_cast<char*>(ws);
   int32_t* si = reinterpret_cast<int32_t*>(base + w.idx_off);
   float* sv = reinterpret_cast<float*>(base + w.val_off);
   int32_t* sc = reinterpret_cast<int32_t*>(base + w.cnt_off);
-  const int chunks = cdiv(w.nseg, 4);
-  dim3 g(unsigned(long(BH) * chunks));
+  // Unpruned: 4 waves (4 consecutive segments) per workgroup.  Pruned: one
+  // wave per workgroup, so a pruned segment frees its slot at once instead of
+  // idling inside a workgroup whose other waves scan (measured: 4-wave groups
+  // with a quarter of the segments live ran at a quarter of the bandwidth).
+  const int wpb = live ? 1 : 4;
+  const dim3 g(unsigned(long(BH) * cdiv(w.nseg, wpb))), t(unsigned(64 * wpb));
   const float gamma = score_gamma(dtype, D);
   if (dtype == SA_BF16) {
     auto q = static_cast<const uint16_t*>(Q);
     auto k = static_cast<const uint16_t*>(K);
-#define SA_THR(DD, GG) k_threshold_mfma<DD, GG><<<g, 256, 0, st>>>(q, k, BH, Hq, Hkv, N, scale, gamma, tau, w.nseg, si, sv, sc)
+#define SA_THR(DD, GG) k_threshold_mfma<DD, GG><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, N, scale, gamma, tau, w.nseg, live, si, sv, sc)
     if (D == 128) {
       switch (G) { case 1: SA_THR(128, 1); break; case 2: SA_THR(128, 2); break;
                    case 4: SA_THR(128, 4); break; default: SA_THR(128, 8); break; }
@@ -436,8 +445,8 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int 
   } else {
     auto q = static_cast<const float*>(Q);
     auto k = static_cast<const float*>(K);
-    if (D == 128) k_threshold_valu<128><<<g, 256, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, si, sv, sc);
-    else          k_threshold_valu<64><<<g, 256, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, si, sv, sc);
+    if (D == 128) k_threshold_valu<128><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, live, si, sv, sc);
+    else          k_threshold_valu<64><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, live, si, sv, sc);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -197,6 +197,8 @@ size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int bloc
       return threshold_ws(B, Hq, N).bytes;
     case SA_OP_SELECT_TOPDELTA:
       return topdelta_ws_bytes(B, Hq, N);
+    case SA_OP_SELECT_PRUNED:
+      return pruned_ws_bytes(B, Hq, Hkv, N);
     case SA_OP_SPARSE_DECODE:        // k = idx_stride; block = 0 for token mode
       if (k < 1) return SIZE_MAX;
       return decode_ws(B, Hq, Hkv, D, block > 0 ? SA_IDX_BLOCKS : SA_IDX_TOKENS, block, k).bytes;
@@ -264,7 +266,7 @@ static sa_status v_threshold(const void* Q, const void* K, int dtype, int B, int
   if (dtype == SA_BF16) SUP(pow2_le8(G), "bf16 threshold selection needs g in {1, 2, 4, 8}");
   else SUP(G <= 8, "float32 threshold selection needs g <= 8");
   const ThrWs w = threshold_ws(B, Hq, N);
-  REQ(long(B) * Hkv * cdiv(w.nseg, 4) < (1L << 31), "grid too large");
+  REQ(long(B) * Hkv * w.nseg < (1L << 31), "grid too large");
   return SA_OK;
 }
 
@@ -305,6 +307,59 @@ sa_status sa_select_topdelta(const void* Q, const void* K, int dtype, int B, int
   return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, t, sc, cap, idx, score, count,
                                      w, ws, st),
                     "sa_select_topdelta (scan)");
+}
+
+static bool subspaces_ok(int D, int S) {
+  return S >= 1 && S <= 16 && D % S == 0 && (D / S) % 8 == 0;
+}
+
+sa_status sa_build_radius(const void* X, int dtype, int B, int H, int N, int D, int block, int S,
+                          const float* sketch, float* radius, void* stream) {
+  PTR(X);
+  PTR(sketch);
+  PTR(radius);
+  REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
+  REQ(B >= 1 && H >= 1 && N >= 1, "B, H, N must be >= 1");
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(block >= 1, "block must be >= 1");
+  SUP(subspaces_ok(D, S), "S (%d) must divide D (%d) into subspaces of a multiple of 8 "
+      "channels, S <= 16", S, D);
+  REQ(long(B) * H * cdiv(N, block) < (1L << 31), "too many blocks");
+  return hip_status(launch_radius(X, dtype, B, H, N, D, block, S, sketch, radius,
+                                  static_cast<hipStream_t>(stream)),
+                    "sa_build_radius");
+}
+
+sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype, int B, int Hq,
+                                     int Hkv, int N, int D, int block, int S,
+                                     const float* sketch, const float* radius, const float* tau,
+                                     float scale, int cap, int32_t* idx, float* score,
+                                     int32_t* count, uint8_t* live, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  sa_status s = v_threshold(Q, K, dtype, B, Hq, Hkv, N, D, cap, idx, score, count);
+  if (s) return s;
+  PTR(tau);
+  PTR(sketch);
+  PTR(radius);
+  if (live) PTR(live);
+  SUP(block == 32 || block == 64 || block == 128, "block must be 32, 64 or 128 (got %d)", block);
+  SUP(subspaces_ok(D, S), "S (%d) must divide D (%d) into subspaces of a multiple of 8 "
+      "channels, S <= 16", S, D);
+  const ThrWs w = threshold_ws(B, Hq, N);
+  const size_t need = pruned_ws_bytes(B, Hq, Hkv, N);
+  if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  PTR(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = eff_scale(scale, D);
+  char* base = static_cast<char*>(ws);
+  uint8_t* lv = live ? live : reinterpret_cast<uint8_t*>(base + w.bytes);
+  int32_t* cnt = reinterpret_cast<int32_t*>(base + w.cnt_off);
+  hipError_t e = launch_prune(Q, dtype, B, Hq, Hkv, N, D, block, S, sketch, radius, tau, sc,
+                              w.nseg, lv, cnt, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_threshold_pruned (bounds)");
+  return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, tau, sc, cap, idx, score,
+                                     count, w, ws, st, lv),
+                    "sa_select_threshold_pruned (scan)");
 }
 
 sa_status sa_sparse_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,

@@ -135,6 +135,11 @@ inline ThrWs threshold_ws(int B, int Hq, int N) {
 inline size_t topdelta_ws_bytes(int B, int Hq, int N) {
   return threshold_ws(B, Hq, N).bytes + align256(size_t(B) * Hq * sizeof(float));
 }
+// The sphere-pruned threshold adds one live flag per (b, kv head, segment).
+inline size_t pruned_ws_bytes(int B, int Hq, int Hkv, int N) {
+  const ThrWs w = threshold_ws(B, Hq, N);
+  return w.bytes + align256(size_t(B) * Hkv * w.nseg);
+}
 
 // ---------------------------------------------------------------- launchers
 struct SelectPlan {
@@ -182,7 +187,14 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
                             int Hq, int Hkv, int N, int D, const float* tau,
                             float scale, int cap, int32_t* idx, float* score,
                             int32_t* count, const ThrWs& w, void* ws,
-                            hipStream_t st);
+                            hipStream_t st, const uint8_t* live = nullptr);
+hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D,
+                         int block, int S, const float* sketch, float* radius,
+                         hipStream_t st);
+hipError_t launch_prune(const void* Q, int dtype, int B, int Hq, int Hkv, int N,
+                        int D, int block, int S, const float* sketch,
+                        const float* radius, const float* tau, float scale,
+                        int nseg, uint8_t* live, int32_t* st_cnt, hipStream_t st);
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B,
                           int Hq, int Hkv, int L, int D, float scale, int block,
                           const int32_t* idx, const int32_t* count, int kmax,
