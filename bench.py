@@ -440,21 +440,23 @@ def bench_pruned(args) -> dict:
     t_sel = graph_time(sel, R, n)
     e = 2
     kept = int(cnt.sum().item())
-    frac = float(live.float().mean().item())
     nb = -(-N // blk)
+    bps = 128 // blk
+    lv = live.cpu().numpy()
+    frac = float(np.stack([(lv >> i) & 1 for i in range(bps)], -1).reshape(B, Hkv, -1)[:, :, :nb].mean())
     bound_bytes = B * Hkv * nb * (D + S) * 4 + B * Hq * D * e + B * Hq * 4
     scan_bytes = int(round(frac * B * Hkv * N * D * e))
     ach = (bound_bytes + scan_bytes + kept * 8) / (t_sel * 1e-6) / 1e9
     res = {
         "workload": wl.name, "us_per_pass": round(t_pass, 2), "subspaces": S,
-        "pass": "sphere bounds + scan of the live segments + compaction "
+        "pass": "sphere bounds + scan of the live blocks + compaction "
                 "(sa_select_threshold_pruned) + token-mode decode",
         "kernels_us": {"sa_select_threshold_pruned (k_prune + k_threshold_mfma + "
                        "k_threshold_compact)": round(t_sel, 2),
                        "sa_sparse_decode tokens (k_decode_tokens)": round(max(t_pass - t_sel, 0), 2),
                        "unpruned sa_select_threshold on the same arrays": round(t_sel0, 2)},
-        "live_segment_fraction": round(frac, 4), "kept_tokens": kept,
-        "roofline": {"bound": "hbm", "kernel": "k_threshold_mfma over the live segments (the "
+        "scanned_block_fraction": round(frac, 4), "kept_tokens": kept,
+        "roofline": {"bound": "hbm", "kernel": "k_threshold_mfma over the live blocks (the "
                      "call also runs the bound and compaction kernels)", "achieved": round(ach, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
                      "traffic": None, "algorithmic_bytes": bound_bytes + scan_bytes + kept * 8,

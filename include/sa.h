@@ -239,15 +239,16 @@ sa_status sa_build_radius(const void* X, int dtype, int B, int H, int N, int D,
  *     scale * sum_s (q_s . c_j,s + ||q_s|| rho_j,s) < tau[b, h],
  * a rigorous upper bound of every score in the block (Cauchy-Schwarz per
  * subspace), evaluated in float32 with a margin that covers its rounding.
- * A 128-token staging segment is scanned when any of its blocks survives
- * for any head of the kv group; the scan, the exact check and the outputs
- * are those of sa_select_threshold, so there are no false negatives.
+ * A block is scanned when it survives for any head of the kv group; the
+ * scan, the exact check and the outputs are those of sa_select_threshold on
+ * the scanned blocks, so there are no false negatives.
  *
  *   block    32, 64 or 128 (the blocks of sketch and radius)
  *   S, sketch, radius   as built by sa_build_sketch and sa_build_radius on K
  *   tau, cap, idx, score, count   as sa_select_threshold
- *   live     [B, Hkv, ceil(N/128)] uint8 out: 1 where the segment was scanned
- *            (NULL: kept in ws)
+ *   live     [B, Hkv, ceil(N/128)] uint8 out, one byte per 128-token segment:
+ *            bit i set when the segment's i-th block was scanned (NULL: kept
+ *            in ws)
  * ws: sa_workspace_bytes(SA_OP_SELECT_PRUNED, B, Hq, Hkv, N, D, block, cap).
  */
 sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype,

@@ -559,20 +559,20 @@ def test_pruned_threshold_parity(name, over, S):
     eps = _eps_bound(q, K, wl)
     ub = oracle.block_upper_bound(q, sk_x, rad_x)
     g, nseg, bps = wl.g, -(-wl.N // 128), 128 // blk
+    # per-block scanned flags from the segment bytes
+    bits = np.stack([(live_h >> i) & 1 for i in range(bps)], -1).reshape(wl.B, wl.Hkv, -1)
+    assert np.all(live_h >> bps == 0)
+    assert np.all(bits[:, :, wl.nb:] == 0)
+    scanned = bits[:, :, :wl.nb] == 1
     lists = [[None] * wl.Hq for _ in range(wl.B)]
     for b in range(wl.B):
         for kh in range(wl.Hkv):
-            for seg in range(nseg):
-                blocks = range(seg * bps, min((seg + 1) * bps, wl.nb))
-                need = any(ub[b, h, j] >= tau64[b, h] for h in range(kh * g, (kh + 1) * g)
-                           for j in blocks)
-                near = any(ub[b, h, j] >= tau64[b, h] - 1e-3 * (1 + abs(tau64[b, h]))
-                           for h in range(kh * g, (kh + 1) * g) for j in blocks)
-                assert live_h[b, kh, seg] in (0, 1)
-                if need:
-                    assert live_h[b, kh, seg] == 1, (b, kh, seg)
-                if live_h[b, kh, seg]:
-                    assert near, (b, kh, seg)
+            hs = range(kh * g, (kh + 1) * g)
+            need = np.any([ub[b, h] >= tau64[b, h] for h in hs], axis=0)
+            near = np.any([ub[b, h] >= tau64[b, h] - 1e-3 * (1 + abs(tau64[b, h])) for h in hs],
+                          axis=0)
+            assert np.all(scanned[b, kh][need]), (b, kh)
+            assert np.all(near[scanned[b, kh]]), (b, kh)
         for h in range(wl.Hq):
             n = int(cnt_h[b, h])
             got = idx_h[b, h, :n]
@@ -583,7 +583,7 @@ def test_pruned_threshold_parity(name, over, S):
             ex = np.setdiff1d(got, exact)
             assert np.all(s[b, h, ex] >= tau64[b, h] - 2 * eps[b, h, ex])
             ref = idx0_h[b, h, :cnt0_h[b, h]]
-            on = live_h[b, h // g][ref // 128] == 1
+            on = scanned[b, h // g][ref // blk]
             assert np.array_equal(got, ref[on])
             np.testing.assert_array_equal(sc_h[b, h, :n], sc0_h[b, h, :cnt0_h[b, h]][on])
             lists[b][h] = got
@@ -592,7 +592,7 @@ def test_pruned_threshold_parity(name, over, S):
                                    out_dtype=torch.float32)
     assert max_abs(O32.cpu().numpy(), O_ref) <= OUT_TOL[dt]
     assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
-    print(f"{name} {over} S={S}: {live_h.mean():.1%} of segments scanned")
+    print(f"{name} {over} S={S}: {scanned.mean():.1%} of blocks scanned")
 
 
 PREFILL_CASES = [

@@ -249,7 +249,8 @@ def sa_select_threshold_pruned(Q: torch.Tensor, K: torch.Tensor, sketch: torch.T
 
     sketch [B, Hkv, nb, D] and radius [B, Hkv, nb, S] as built on K.  Returns
     idx, score, count (as sa_select_threshold) and live [B, Hkv, ceil(N/128)]
-    uint8, 1 where the 128-token segment was scanned.
+    uint8: bit i of a 128-token segment's byte is set when its i-th block was
+    scanned.
     """
     _dev(Q, K, sketch, radius, tau, idx, score, count, live)
     B, Hq, D = Q.shape

@@ -19,10 +19,12 @@
 // k_prune   one workgroup per (b, kv head, 64 blocks): the bound for every
 //           block and every query head of the group (one (block, head) pair
 //           per thread over the sketch rows staged transposed in LDS, so the
-//           dot products need no cross-lane reductions); a 128-token staging
-//           segment of the threshold scan stays live when any of its blocks
-//           can reach any head's tau.  Pruned segments get zero staged counts
-//           for every head, and the scan skips them.
+//           dot products need no cross-lane reductions).  A block stays live
+//           when it can reach the tau of any head of the group; the live byte
+//           of a 128-token staging segment of the threshold scan has bit i set
+//           for its live i-th block.  Segments with no live block get zero
+//           staged counts for every head and are skipped; in the others the
+//           scan loads only the tiles of live blocks.
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -199,13 +201,13 @@ __global__ __launch_bounds__(256) void k_prune(
                      kCmpRel * (fabsf(ub) + fabsf(th[h]));
     alive |= !(hi < th[h]);                // a NaN bound stays alive
   }
-  if (alive && j < nb) segf[r / bps] = 1;
+  if (alive && j < nb) atomicOr(&segf[r / bps], 1 << (r % bps));
   __syncthreads();
   const int s0 = j0 / bps, ns = min(kPruneRows / bps, nseg - s0);
   for (int i = tid; i < ns; i += 256) {
     const int seg = s0 + i;
-    const bool on = segf[i] != 0;
-    live[size_t(bh) * nseg + seg] = on ? 1 : 0;
+    const int on = segf[i];
+    live[size_t(bh) * nseg + seg] = uint8_t(on);
     if (!on) {
       for (int h = 0; h < G; ++h) st_cnt[(size_t(b) * Hq + kh * G + h) * nseg + seg] = 0;
     }

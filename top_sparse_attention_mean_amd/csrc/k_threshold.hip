@@ -36,8 +36,8 @@ template <int D, int G>
 __global__ __launch_bounds__(256) void k_threshold_mfma(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, int BH, int Hq, int Hkv,
     int N, float scale, float gamma, const float* __restrict__ tau, int nseg,
-    const uint8_t* __restrict__ live, int32_t* __restrict__ st_idx, float* __restrict__ st_val,
-    int32_t* __restrict__ st_cnt) {
+    const uint8_t* __restrict__ live, int pblock, int32_t* __restrict__ st_idx,
+    float* __restrict__ st_val, int32_t* __restrict__ st_cnt) {
   static_assert(G <= 16, "heads are the 16 columns of the score tile");
   constexpr int NST = D / 32;
   const int bh = blockIdx.x % BH, chunk = blockIdx.x / BH;
@@ -46,8 +46,11 @@ __global__ __launch_bounds__(256) void k_threshold_mfma(
   const int gq = lane >> 4, nn = lane & 15;
   const int seg = chunk * int(blockDim.x >> 6) + wave;
   if (seg >= nseg) return;  // no barriers below
-  // a segment pruned by its blocks' spheres has its counts zeroed already
-  if (live && !live[size_t(bh) * nseg + seg]) return;
+  // Pruning by block spheres: bit i of the live byte covers the segment's
+  // i-th block of `pblock` tokens; a segment with none has its counts zeroed
+  // already, and tiles of dead blocks are neither loaded nor kept.
+  const int lmask = live ? int(live[size_t(bh) * nseg + seg]) : 0xff;
+  if (lmask == 0) return;
 
   u32x4 qb[NST], qa[NST];
   float th = __builtin_inff();
@@ -77,12 +80,15 @@ __global__ __launch_bounds__(256) void k_threshold_mfma(
   for (int t0 = 0; t0 < kThrSeg / 16; t0 += kTB) {
     if (seg * kThrSeg + t0 * 16 >= N) break;
     u32x4 ka[kTB][NST];
+    bool tl[kTB];
 #pragma unroll
     for (int u = 0; u < kTB; ++u) {
+      tl[u] = (lmask >> (((t0 + u) * 16) / pblock)) & 1;
       const int kr = min(seg * kThrSeg + (t0 + u) * 16 + nn, N - 1);
       const uint16_t* kp = Kb + size_t(kr) * D + 8 * gq;
 #pragma unroll
-      for (int st = 0; st < NST; ++st) ka[u][st] = ld16(kp + 32 * st);
+      for (int st = 0; st < NST; ++st)
+        ka[u][st] = tl[u] ? ld16(kp + 32 * st) : u32x4{0u, 0u, 0u, 0u};
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -101,7 +107,7 @@ __global__ __launch_bounds__(256) void k_threshold_mfma(
         const int tok = tok0 + 4 * gq + r;
         s32[r] = sc[r] * scale;
         const float eps = gs * ab[r] + (fabsf(s32[r]) + tabs) * 9.5367431640625e-07f;  // 2^-20
-        keep[r] = nn < G && tok < N && (s32[r] + eps >= th);
+        keep[r] = tl[u] && nn < G && tok < N && (s32[r] + eps >= th);
       }
       uint64_t m[4];
 #pragma unroll
@@ -132,8 +138,8 @@ template <int D>
 __global__ __launch_bounds__(256) void k_threshold_valu(
     const float* __restrict__ Q, const float* __restrict__ K, int BH, int Hq, int Hkv, int G,
     int N, float scale, float gamma, const float* __restrict__ tau, int nseg,
-    const uint8_t* __restrict__ live, int32_t* __restrict__ st_idx, float* __restrict__ st_val,
-    int32_t* __restrict__ st_cnt) {
+    const uint8_t* __restrict__ live, int pblock, int32_t* __restrict__ st_idx,
+    float* __restrict__ st_val, int32_t* __restrict__ st_cnt) {
   __shared__ float sq[16][D];
   const int bh = blockIdx.x % BH, chunk = blockIdx.x / BH;
   const int b = bh / Hkv, kh = bh % Hkv;
@@ -143,7 +149,8 @@ __global__ __launch_bounds__(256) void k_threshold_valu(
   __syncthreads();
   const int seg = chunk * int(blockDim.x >> 6) + wave;
   if (seg >= nseg) return;
-  if (live && !live[size_t(bh) * nseg + seg]) return;
+  const int lmask = live ? int(live[size_t(bh) * nseg + seg]) : 0xff;
+  if (lmask == 0) return;
   const float* Kb = K + size_t(bh) * N * D;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int h = 0; h < G; ++h) {
@@ -152,8 +159,9 @@ __global__ __launch_bounds__(256) void k_threshold_valu(
     int run = 0;
     for (int part = 0; part < kThrSeg / 64; ++part) {
       const int tok = seg * kThrSeg + part * 64 + lane;
+      const bool tlive = (lmask >> ((part * 64 + lane) / pblock)) & 1;
       float s = 0.f, a = 0.f;
-      if (tok < N) {
+      if (tok < N && tlive) {
         const float* kp = Kb + size_t(tok) * D;
         for (int d = 0; d < D; d += 4) {
           u32x4 w = ld16(kp + d);
@@ -167,7 +175,7 @@ __global__ __launch_bounds__(256) void k_threshold_valu(
       }
       const float s32 = s * scale;
       const float eps = gamma * scale * a + (fabsf(s32) + fabsf(th)) * 9.5367431640625e-07f;
-      const bool keep = tok < N && (s32 + eps >= th);
+      const bool keep = tok < N && tlive && (s32 + eps >= th);
       const uint64_t m = __ballot(keep);
       if (keep) {
         const int pos = run + __popcll(m & below);
@@ -417,7 +425,7 @@ hipError_t launch_pseudo_max(const void* Q, const void* K, int dtype, int B, int
 hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv,
                             int N, int D, const float* tau, float scale, int cap, int32_t* idx,
                             float* score, int32_t* count, const ThrWs& w, void* ws,
-                            hipStream_t st, const uint8_t* live) {
+                            hipStream_t st, const uint8_t* live, int pblock) {
   const int BH = B * Hkv, G = Hq / Hkv;
   char* base = static_cast<char*>(ws);
   int32_t* si = reinterpret_cast<int32_t*>(base + w.idx_off);
@@ -433,7 +441,7 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int 
   if (dtype == SA_BF16) {
     auto q = static_cast<const uint16_t*>(Q);
     auto k = static_cast<const uint16_t*>(K);
-#define SA_THR(DD, GG) k_threshold_mfma<DD, GG><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, N, scale, gamma, tau, w.nseg, live, si, sv, sc)
+#define SA_THR(DD, GG) k_threshold_mfma<DD, GG><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, N, scale, gamma, tau, w.nseg, live, pblock, si, sv, sc)
     if (D == 128) {
       switch (G) { case 1: SA_THR(128, 1); break; case 2: SA_THR(128, 2); break;
                    case 4: SA_THR(128, 4); break; default: SA_THR(128, 8); break; }
@@ -445,8 +453,8 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B, int 
   } else {
     auto q = static_cast<const float*>(Q);
     auto k = static_cast<const float*>(K);
-    if (D == 128) k_threshold_valu<128><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, live, si, sv, sc);
-    else          k_threshold_valu<64><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, live, si, sv, sc);
+    if (D == 128) k_threshold_valu<128><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, live, pblock, si, sv, sc);
+    else          k_threshold_valu<64><<<g, t, 0, st>>>(q, k, BH, Hq, Hkv, G, N, scale, gamma, tau, w.nseg, live, pblock, si, sv, sc);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -358,7 +358,7 @@ sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype, in
                               w.nseg, lv, cnt, st);
   if (e != hipSuccess) return hip_status(e, "sa_select_threshold_pruned (bounds)");
   return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, tau, sc, cap, idx, score,
-                                     count, w, ws, st, lv),
+                                     count, w, ws, st, lv, block),
                     "sa_select_threshold_pruned (scan)");
 }
 

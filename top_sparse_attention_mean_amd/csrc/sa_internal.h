@@ -187,7 +187,8 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
                             int Hq, int Hkv, int N, int D, const float* tau,
                             float scale, int cap, int32_t* idx, float* score,
                             int32_t* count, const ThrWs& w, void* ws,
-                            hipStream_t st, const uint8_t* live = nullptr);
+                            hipStream_t st, const uint8_t* live = nullptr,
+                            int pblock = kThrSeg);
 hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D,
                          int block, int S, const float* sketch, float* radius,
                          hipStream_t st);
