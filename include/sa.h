@@ -226,11 +226,14 @@ sa_status sa_select_topdelta(const void* Q, const void* K, int dtype, int B,
  *            by a relative 2^-16, so it never falls below the exact value)
  *   S        subspaces of D/S consecutive channels; D/S a multiple of 8,
  *            S <= 16 (else SA_ERR_UNSUPPORTED)
+ *   [blk_begin, blk_end)  the blocks to (re)compute; the others are left as
+ *            they are (decode refreshes only the newest block, after its
+ *            sketch row, as keys are appended)
  * NaN keys are skipped by the maximum (their block's centre is NaN anyway).
  */
 sa_status sa_build_radius(const void* X, int dtype, int B, int H, int N, int D,
-                          int block, int S, const float* sketch, float* radius,
-                          void* stream);
+                          int block, int S, int blk_begin, int blk_end,
+                          const float* sketch, float* radius, void* stream);
 
 /*
  * sa_select_threshold_pruned -- the half-space selection of

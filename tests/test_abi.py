@@ -31,7 +31,7 @@ def lib():
     L.sa_select_topk.argtypes = [P, I, I, I, I, I, I, I, P, I, I, U, F, P, P, P, P, Z, P]
     L.sa_select_threshold.argtypes = [P, P, I, I, I, I, I, I, P, F, I, P, P, P, P, Z, P]
     L.sa_select_topdelta.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, I, P, P, P, P, P, Z, P]
-    L.sa_build_radius.argtypes = [P, I, I, I, I, I, I, I, P, P, P]
+    L.sa_build_radius.argtypes = [P, I, I, I, I, I, I, I, I, I, P, P, P]
     L.sa_select_threshold_pruned.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P, F, I, P, P, P,
                                              P, P, Z, P]
     L.sa_sparse_decode.argtypes = [P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P, P, I, P, P, Z, P]
@@ -172,7 +172,7 @@ def test_topdelta_validation(lib):
 
 def test_radius_validation(lib):
     f = lib.sa_build_radius
-    base = [A, 1, 1, 8, 32768, 128, 64, 1, A, A, None]
+    base = [A, 1, 1, 8, 32768, 128, 64, 1, 0, 512, A, A, None]
 
     def call(i, v):
         a = list(base)
@@ -185,8 +185,10 @@ def test_radius_validation(lib):
     a[5], a[7] = 64, 16                           # D = 64: 4-channel subspaces
     assert f(*a) == UNSUPPORTED
     assert call(6, 0) == INVALID                  # block
-    assert call(9, MIS) == INVALID                # misaligned radius
-    assert call(8, None) == INVALID               # sketch
+    assert call(11, MIS) == INVALID               # misaligned radius
+    assert call(10, None) == INVALID              # sketch
+    assert call(9, 513) == INVALID                # block range past nb
+    assert call(8, 600) == INVALID and call(8, -1) == INVALID   # begin past end / negative
 
 
 def test_pruned_threshold_validation(lib):

@@ -544,6 +544,11 @@ def test_pruned_threshold_parity(name, over, S):
     rad = sa.sa_build_radius(Kd, sk, blk, S)
     sk_h, rad_h = sk.cpu().numpy(), rad.cpu().numpy()
     _radius_check(K, sk_h, rad_h, blk, S)
+    # a range rebuild (the decode refresh of the newest blocks) writes only its blocks
+    part = torch.full_like(rad, -1.0)
+    sa.sa_build_radius(Kd, sk, blk, S, blk_begin=wl.nb - 2, blk_end=wl.nb, out=part)
+    assert torch.equal(part[:, :, wl.nb - 2:], rad[:, :, wl.nb - 2:])
+    assert torch.all(part[:, :, :wl.nb - 2] == -1.0)
     # against the oracle's own spheres (float64 centres)
     sk_x = oracle.sketch(K, blk)
     rad_x = oracle.subspace_radius(K, sk_x, blk, S)

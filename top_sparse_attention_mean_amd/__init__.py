@@ -58,7 +58,7 @@ _select_topk = _sig("sa_select_topk", _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I
                     _P, _P, _P, _P, _Z, _P)
 _select_threshold = _sig("sa_select_threshold", _I, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _I,
                          _P, _P, _P, _P, _Z, _P)
-_build_radius = _sig("sa_build_radius", _I, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P)
+_build_radius = _sig("sa_build_radius", _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P)
 _select_threshold_pruned = _sig("sa_select_threshold_pruned", _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                 _I, _I, _P, _P, _P, _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -166,16 +166,20 @@ def sa_build_sketch(X: torch.Tensor, block: int, head_pool: int = 1, blk_begin: 
 
 
 def sa_build_radius(X: torch.Tensor, sketch: torch.Tensor, block: int, S: int = 1,
+                    blk_begin: int = 0, blk_end: Optional[int] = None,
                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Bounding-sphere radii of X [B, H, N, D] around its block sketch
-    [B, H, nb, D], per subspace of D/S channels -> float32 [B, H, nb, S]."""
+    [B, H, nb, D], per subspace of D/S channels -> float32 [B, H, nb, S]
+    (only blocks [blk_begin, blk_end) are written)."""
     _dev(X, sketch, out)
     B, H, N, D = X.shape
     nb = -(-N // block)
+    if blk_end is None:
+        blk_end = nb
     if out is None:
         out = torch.empty(B, H, nb, S, dtype=torch.float32, device=X.device)
-    _check(_build_radius(_ptr(X), _dt(X), B, H, N, D, block, S, _ptr(sketch), _ptr(out),
-                         _stream(stream)), "sa_build_radius")
+    _check(_build_radius(_ptr(X), _dt(X), B, H, N, D, block, S, blk_begin, blk_end, _ptr(sketch),
+                         _ptr(out), _stream(stream)), "sa_build_radius")
     return out
 
 

@@ -14,8 +14,10 @@
 // keeps the zero-false-negative guarantee.  The float32 rounding of the bound
 // is covered by a margin (below), and the radius is rounded up.
 //
-// k_radius  one 256-thread workgroup per (b, head, block): the largest
-//           distance of the block's keys from the given centre, per subspace.
+// k_radius  one 256-thread workgroup per (b, head, block) of a block range:
+//           the largest distance of the block's keys from the given centre,
+//           per subspace (a range of one block refreshes the newest block's
+//           sphere as keys are appended, as the sketch refresh does).
 // k_prune   one workgroup per (b, kv head, 64 blocks): the bound for every
 //           block and every query head of the group (one (block, head) pair
 //           per thread over the sketch rows staged transposed in LDS, so the
@@ -36,13 +38,14 @@ constexpr float kRadiusUp = 1.0f + 1.52587890625e-05f;  // 1 + 2^-16
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_radius(const T* __restrict__ X, int H, int N, int block,
-                                                int nb, int S, const float* __restrict__ sk,
+                                                int nb, int b0, int nbr, int S,
+                                                const float* __restrict__ sk,
                                                 float* __restrict__ rad) {
   constexpr int CPT = 8;            // columns per thread
   constexpr int TPR = D / CPT;      // threads per row
   constexpr int RPP = 256 / TPR;    // rows per pass
   __shared__ float red[RPP][TPR];
-  const int j = blockIdx.x % nb, bh = blockIdx.x / nb;
+  const int j = b0 + int(blockIdx.x % nbr), bh = blockIdx.x / nbr;
   const int t0 = j * block, nj = min(block, N - t0);
   const int tr = threadIdx.x / TPR, tc = threadIdx.x % TPR;
   const int LS = (D / S) / CPT;     // threads (lanes) per subspace within a row
@@ -215,17 +218,18 @@ __global__ __launch_bounds__(256) void k_prune(
 }
 
 hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D, int block, int S,
-                         const float* sketch, float* radius, hipStream_t st) {
-  const int nb = cdiv(N, block);
-  const dim3 g(static_cast<unsigned>(long(B) * H * nb));
+                         int b0, int b1, const float* sketch, float* radius, hipStream_t st) {
+  const int nb = cdiv(N, block), nbr = b1 - b0;
+  if (nbr <= 0) return hipSuccess;
+  const dim3 g(static_cast<unsigned>(long(B) * H * nbr));
   if (dtype == SA_BF16) {
     auto x = static_cast<const uint16_t*>(X);
-    if (D == 128) k_radius<uint16_t, 128><<<g, 256, 0, st>>>(x, H, N, block, nb, S, sketch, radius);
-    else          k_radius<uint16_t, 64><<<g, 256, 0, st>>>(x, H, N, block, nb, S, sketch, radius);
+    if (D == 128) k_radius<uint16_t, 128><<<g, 256, 0, st>>>(x, H, N, block, nb, b0, nbr, S, sketch, radius);
+    else          k_radius<uint16_t, 64><<<g, 256, 0, st>>>(x, H, N, block, nb, b0, nbr, S, sketch, radius);
   } else {
     auto x = static_cast<const float*>(X);
-    if (D == 128) k_radius<float, 128><<<g, 256, 0, st>>>(x, H, N, block, nb, S, sketch, radius);
-    else          k_radius<float, 64><<<g, 256, 0, st>>>(x, H, N, block, nb, S, sketch, radius);
+    if (D == 128) k_radius<float, 128><<<g, 256, 0, st>>>(x, H, N, block, nb, b0, nbr, S, sketch, radius);
+    else          k_radius<float, 64><<<g, 256, 0, st>>>(x, H, N, block, nb, b0, nbr, S, sketch, radius);
   }
   return hipGetLastError();
 }

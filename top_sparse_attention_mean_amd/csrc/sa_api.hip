@@ -314,7 +314,8 @@ static bool subspaces_ok(int D, int S) {
 }
 
 sa_status sa_build_radius(const void* X, int dtype, int B, int H, int N, int D, int block, int S,
-                          const float* sketch, float* radius, void* stream) {
+                          int blk_begin, int blk_end, const float* sketch, float* radius,
+                          void* stream) {
   PTR(X);
   PTR(sketch);
   PTR(radius);
@@ -324,9 +325,12 @@ sa_status sa_build_radius(const void* X, int dtype, int B, int H, int N, int D, 
   REQ(block >= 1, "block must be >= 1");
   SUP(subspaces_ok(D, S), "S (%d) must divide D (%d) into subspaces of a multiple of 8 "
       "channels, S <= 16", S, D);
-  REQ(long(B) * H * cdiv(N, block) < (1L << 31), "too many blocks");
-  return hip_status(launch_radius(X, dtype, B, H, N, D, block, S, sketch, radius,
-                                  static_cast<hipStream_t>(stream)),
+  const int nb = cdiv(N, block);
+  REQ(0 <= blk_begin && blk_begin <= blk_end && blk_end <= nb,
+      "block range [%d, %d) outside [0, %d]", blk_begin, blk_end, nb);
+  REQ(long(B) * H * (blk_end - blk_begin) < (1L << 31), "too many blocks");
+  return hip_status(launch_radius(X, dtype, B, H, N, D, block, S, blk_begin, blk_end, sketch,
+                                  radius, static_cast<hipStream_t>(stream)),
                     "sa_build_radius");
 }
 

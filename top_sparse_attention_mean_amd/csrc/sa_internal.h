@@ -190,8 +190,8 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
                             hipStream_t st, const uint8_t* live = nullptr,
                             int pblock = kThrSeg);
 hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D,
-                         int block, int S, const float* sketch, float* radius,
-                         hipStream_t st);
+                         int block, int S, int b0, int b1, const float* sketch,
+                         float* radius, hipStream_t st);
 hipError_t launch_prune(const void* Q, int dtype, int B, int Hq, int Hkv, int N,
                         int D, int block, int S, const float* sketch,
                         const float* radius, const float* tau, float scale,
