@@ -18,7 +18,8 @@ Pages cited (by title, section):
     pages from the retained cache).
   * "Faster Than Flash: Exploiting Attention Sparsity for Efficient
     Long-Context Decoding" -- Metodologia §1 (scan a compact key summary, then
-    fetch exact data for the chosen parts) and §2 (sink and local tokens
+    fetch exact data for the chosen parts; 2-bit thumbnails with 8-bit
+    residuals), §3 (pseudo-max, top-delta over thumbnails, refinement) and §2 (sink and local tokens
     dominate the attention distribution, so a pseudo-maximum from them sets
     the top-delta threshold m~ - delta).
   * "Pulsar Attention" -- Fase 1 (64-token attention-sink prefix) and Fase 2
@@ -43,7 +44,8 @@ from .attention import (
     threshold_tau, select_threshold, prefill_pool_queries, prefill_select,
     prefill_attend_rows, prefill_attend, mass_oracle, decode_step,
     window_tokens, pseudo_max, select_topdelta, subspaces, subspace_radius,
-    block_upper_bound, select_threshold_pruned,
+    block_upper_bound, select_threshold_pruned, lowbit_encode, lowbit_thumbnail,
+    lowbit_reconstruct, bf16_round, select_topdelta_lowbit,
 )
 
 __all__ = [
@@ -52,5 +54,6 @@ __all__ = [
     "lse_merge", "threshold_tau", "select_threshold", "prefill_pool_queries",
     "prefill_select", "prefill_attend_rows", "prefill_attend", "mass_oracle",
     "decode_step", "window_tokens", "pseudo_max", "select_topdelta", "subspaces",
-    "subspace_radius", "block_upper_bound", "select_threshold_pruned",
+    "subspace_radius", "block_upper_bound", "select_threshold_pruned", "lowbit_encode",
+    "lowbit_thumbnail", "lowbit_reconstruct", "bf16_round", "select_topdelta_lowbit",
 ]

@@ -15,6 +15,7 @@ one function per step, in the order the method runs:
   O8 mass_oracle      exact per-block attention mass, for recall reporting
   O9 select_topdelta  pseudo-max over sink + local tokens; keep s >= m~ - delta
   O10 select_threshold_pruned  block spheres per subspace prune, exact check after
+  O11 select_topdelta_lowbit   2-bit thumbnails filter blocks, 8-bit residuals refine
      lse_merge        exact merge of attention partials over a split support
 
 Arrays: q [B, Hq, D]; Q [B, Hq, L, D]; K, V [B, Hkv, N, D]; query head h uses
@@ -577,3 +578,133 @@ def select_threshold_pruned(q: np.ndarray, K: np.ndarray, tau: np.ndarray, block
             lists[b][h] = keep
             vals[b][h] = s[b, h, keep]
     return lists, vals, surv
+
+
+# ------------------------------------------------------------------ O11
+_THIRD32 = np.float32(1.0) / np.float32(3.0)
+
+
+def lowbit_encode(K: np.ndarray, block: int):
+    """O11a: 2-bit key thumbnails with 8-bit residuals.
+
+    "Faster Than Flash" (Metodologia §1) splits the key cache into 2-bit
+    quantised thumbnails, scanned to estimate scores, and 8-bit residuals
+    that rebuild the keys close to their stored precision for the exact
+    computation.  The pages fix no codec; reading taken (asymmetric per
+    channel over each token block, which keeps outlier channels from
+    flattening the others):
+      lo, hi  = min and max of channel c over the block's tokens,
+      step    = (hi - lo) * fl32(1/3)            (four levels lo + i*step),
+      code    = [d >= step/2] + [d >= 1.5 step] + [d >= 2.5 step], d = k - lo,
+      t       = fma(code, step, lo)              (the thumbnail value),
+      rstep   = 2^(E - 8) with step = m 2^E, m in [0.5, 1)  (a power of two,
+                so r / rstep and r8 * rstep are exact),
+      r8      = clip(rint((k - t) / rstep), -127, 127).
+    Every operation is one IEEE float32 operation, so the codes are a fixed
+    function of the stored keys; fma is evaluated exactly in float64 and
+    rounded once.  Keys must be finite.
+    Returns codes uint8 [B, H, N, D] (0..3), resid int8 [B, H, N, D] and
+    meta float32 [B, H, nb, 3, D] = (lo, step, rstep).
+    """
+    X = np.asarray(K, dtype=np.float64).astype(np.float32)
+    B, H, N, D = X.shape
+    nb = -(-N // block)
+    codes = np.zeros((B, H, N, D), dtype=np.uint8)
+    resid = np.zeros((B, H, N, D), dtype=np.int8)
+    meta = np.zeros((B, H, nb, 3, D), dtype=np.float32)
+    for j in range(nb):
+        lo_t, hi_t = j * block, min((j + 1) * block, N)
+        xb = X[:, :, lo_t:hi_t, :]
+        lo = xb.min(axis=2)
+        hi = xb.max(axis=2)
+        step = (hi - lo) * _THIRD32
+        d = xb - lo[:, :, None, :]
+        s2 = step[:, :, None, :]
+        code = ((d >= s2 * np.float32(0.5)).astype(np.uint8)
+                + (d >= s2 * np.float32(1.5)).astype(np.uint8)
+                + (d >= s2 * np.float32(2.5)).astype(np.uint8))
+        t = (code.astype(np.float64) * s2.astype(np.float64)
+             + lo[:, :, None, :].astype(np.float64)).astype(np.float32)
+        E = np.frexp(step)[1]
+        rstep = np.ldexp(np.float32(1.0), E - 8).astype(np.float32)
+        r = xb - t
+        r8 = np.clip(np.rint(r / rstep[:, :, None, :]), -127, 127).astype(np.int8)
+        codes[:, :, lo_t:hi_t] = code
+        resid[:, :, lo_t:hi_t] = r8
+        meta[:, :, j, 0], meta[:, :, j, 1], meta[:, :, j, 2] = lo, step, rstep
+    return codes, resid, meta
+
+
+def lowbit_thumbnail(codes: np.ndarray, meta: np.ndarray, block: int) -> np.ndarray:
+    """O11b: the thumbnail keys t = fma(code, step, lo), float32."""
+    B, H, N, D = codes.shape
+    tok_blk = np.arange(N) // block
+    lo = meta[:, :, tok_blk, 0, :].astype(np.float64)
+    step = meta[:, :, tok_blk, 1, :].astype(np.float64)
+    return (codes.astype(np.float64) * step + lo).astype(np.float32)
+
+
+def lowbit_reconstruct(codes: np.ndarray, resid: np.ndarray, meta: np.ndarray,
+                       block: int) -> np.ndarray:
+    """O11c: the refined keys k^ = t + r8 * rstep (one float32 rounding)."""
+    N = codes.shape[2]
+    t = lowbit_thumbnail(codes, meta, block)
+    rstep = meta[:, :, np.arange(N) // block, 2, :]
+    return (t + resid.astype(np.float32) * rstep).astype(np.float32)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bf16 (ties to even), returned as float64."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
+                           meta: np.ndarray, block: int, sink: int, local: int,
+                           delta: float, margin: float, scale: Optional[float] = None):
+    """O11: top-delta block filter over the thumbnails, refined keys for the rest.
+
+    The three stages of the fused kernel of "Faster Than Flash" (Metodologia
+    §3): (1) the pseudo-maximum m~ over the sink and local tokens (O9a), here
+    with the refined keys; (2) provisional scores of every token from the
+    2-bit thumbnails, and a block is kept for a kv head when some head h of
+    its group has a provisional score >= tau_h - margin, tau = m~ - delta;
+    the blocks holding sink or local tokens are always kept (they set m~);
+    (3) exact attention over the kept blocks with the refined keys (O4).
+    Readings taken: the refined key is k^ rounded to bf16, the precision of
+    the cache it stands for, and so is the thumbnail fed to the scores;
+    `margin` (>= 0) widens the filter against the thumbnail error.
+    Returns (idx, count, tau, bmax): idx [B, Hkv, nb] ascending block ids
+    (count valid), tau [B, Hq], bmax [B, Hq, nb] the largest provisional
+    score of each block.
+    """
+    B, Hq, D = q.shape
+    _, Hkv, N, _ = codes.shape
+    g = Hq // Hkv
+    nb = -(-N // block)
+    sc = _default_scale(D, scale)
+    khat = bf16_round(lowbit_reconstruct(codes, resid, meta, block))
+    thumb = bf16_round(lowbit_thumbnail(codes, meta, block))
+    win = window_tokens(N, sink, local)
+    if win.size == 0:
+        raise ValueError("the sink and local windows are both empty")
+    forced = np.unique(win // block)
+    tau = np.zeros((B, Hq))
+    bmax = np.full((B, Hq, nb), -np.inf)
+    idx = np.full((B, Hkv, nb), -1, dtype=np.int64)
+    count = np.zeros((B, Hkv), dtype=np.int64)
+    for b in range(B):
+        for kh in range(Hkv):
+            keep = np.zeros(nb, dtype=bool)
+            keep[forced] = True
+            for h in range(kh * g, (kh + 1) * g):
+                tau[b, h] = (khat[b, kh, win] @ q[b, h]).max() * sc - float(delta)
+                prov = (thumb[b, kh] @ q[b, h]) * sc
+                for j in range(nb):
+                    bmax[b, h, j] = prov[j * block:min((j + 1) * block, N)].max()
+                keep |= bmax[b, h] >= tau[b, h] - float(margin)
+            sel = np.nonzero(keep)[0]
+            idx[b, kh, :sel.size] = sel
+            count[b, kh] = sel.size
+    return idx, count, tau, bmax

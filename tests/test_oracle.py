@@ -599,3 +599,106 @@ def test_pruned_selection_equals_threshold(S):
             assert alive < 0.2          # the spheres prune most blocks
         else:
             assert alive > 0.95         # isotropic keys: nothing to prune
+
+
+# ------------------------------------------------------------------ O11
+def test_golden_lowbit_codec():
+    g = {k: v for k, v in read_golden("lowbit_codec.txt")}
+    K = np.array([float(x) for x in g["keys"]]).reshape(1, 1, 4, 2)
+    codes, resid, meta = oracle.lowbit_encode(K, 4)
+    assert codes[0, 0, :, 0].tolist() == [int(x) for x in g["codes0"]]
+    assert codes[0, 0, :, 1].tolist() == [int(x) for x in g["codes1"]]
+    assert resid[0, 0, :, 0].tolist() == [int(x) for x in g["resid0"]]
+    assert resid[0, 0, :, 1].tolist() == [int(x) for x in g["resid1"]]
+    for row, name in enumerate(("lo", "step", "rstep")):
+        np.testing.assert_array_equal(meta[0, 0, 0, row], np.float32([float(x) for x in g[name]]))
+    khat = oracle.lowbit_reconstruct(codes, resid, meta, 4)
+    np.testing.assert_array_equal(khat[0, 0, :, 0], [0, 1, 2, 3])
+    assert np.abs(khat - K).max() <= 0.0078125 / 2
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_lowbit_codes_are_nearest_levels_and_errors_bounded(seed):
+    rng = np.random.default_rng(500 + seed)
+    B, H, N, D, block = 1, 2, 200, 16, 64
+    K = rng.standard_normal((B, H, N, D)).astype(np.float32) * np.float32(rng.uniform(0.1, 10))
+    K[0, 0, :, 3] = 1.5                                   # a constant channel: step 0
+    codes, resid, meta = oracle.lowbit_encode(K, block)
+    t = oracle.lowbit_thumbnail(codes, meta, block).astype(np.float64)
+    khat = oracle.lowbit_reconstruct(codes, resid, meta, block).astype(np.float64)
+    blk = np.arange(N) // block
+    lo, step, rstep = (meta[:, :, blk, i, :].astype(np.float64) for i in range(3))
+    X = K.astype(np.float64)
+    # nearest of the four levels, by a plain search (ties up), away from the
+    # thresholds' own float32 rounding
+    d = X - lo
+    lev = np.stack([np.abs(d - i * step) for i in range(4)], -1)
+    near = np.argmin(lev + 1e-12 * np.arange(4)[::-1], -1)   # ties to the upper level
+    clear = np.min(np.abs(d[..., None] - (np.arange(3) + 0.5) * step[..., None]), -1) > 1e-5 * (step + 1e-30)
+    assert np.array_equal(codes[clear], near[clear])
+    assert np.all(np.abs(t - X) <= step / 2 * (1 + 1e-5) + 1e-6)
+    # the refined key: within half a residual step unless the residual clipped,
+    # within one step always
+    unclipped = np.abs(resid) < 127
+    tol = 2.0 ** -23 * np.abs(X)
+    assert np.all(np.abs(khat - X)[unclipped] <= (rstep / 2 + tol)[unclipped])
+    assert np.all(np.abs(khat - X) <= rstep + tol)
+    # step 0: every threshold is 0 and d = 0 passes all three (any code decodes to lo)
+    assert np.all(khat[0, 0, :, 3] == 1.5) and np.all(codes[0, 0, :, 3] == 3)
+    # rstep is the power of two 2^(E - 8) of step
+    m, E = np.frexp(meta[:, :, :, 1, :])
+    np.testing.assert_array_equal(meta[:, :, :, 2, :], np.ldexp(np.float32(1), E - 8))
+
+
+def test_lowbit_on_grid_keys_is_exact_top_delta():
+    """Keys already on each block's four levels: thumbnails equal the keys,
+    residuals vanish, and with margin 0 the filter keeps exactly the blocks
+    holding a token at or above m~ - delta (plus the window's blocks)."""
+    rng = np.random.default_rng(520)
+    B, Hq, Hkv, N, D, block = 1, 4, 2, 512, 8, 64
+    nb = N // block
+    lo = rng.integers(-8, 8, size=(B, Hkv, nb, D)) / 4.0
+    s = 2.0 ** rng.integers(-3, 1, size=(B, Hkv, nb, D))
+    lev = rng.integers(0, 4, size=(B, Hkv, N, D))
+    lev[:, :, ::block, :] = 0                      # every level range spans 0..3
+    lev[:, :, 1::block, :] = 3
+    K = np.repeat(lo, block, 2) + lev * np.repeat(s, block, 2)
+    q = rng.integers(-4, 5, size=(B, Hq, D)) / 2.0
+    codes, resid, meta = oracle.lowbit_encode(K, block)
+    assert np.array_equal(codes, lev) and not resid.any()
+    np.testing.assert_array_equal(oracle.lowbit_reconstruct(codes, resid, meta, block), K)
+    sink, local, delta = 8, 8, 3.0
+    idx, cnt, tau, bmax = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, sink, local,
+                                                        delta, 0.0)
+    _, _, tau_x = oracle.select_topdelta(q, K, sink, local, delta)
+    np.testing.assert_allclose(tau, tau_x, atol=1e-12)
+    sx = A.exact_scores(q, K)
+    for kh in range(Hkv):
+        want = {0, nb - 1}
+        for h in range(kh * 2, kh * 2 + 2):
+            want |= {t // block for t in np.nonzero(sx[0, h] >= tau_x[0, h])[0]}
+            np.testing.assert_allclose(bmax[0, h], sx[0, h].reshape(nb, block).max(-1), atol=1e-12)
+        assert idx[0, kh, :cnt[0, kh]].tolist() == sorted(want)
+    # an infinite margin keeps every block
+    _, cnt, _, _ = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, sink, local, delta,
+                                                 np.inf)
+    assert np.all(cnt == nb)
+
+
+def test_lowbit_recall_on_the_top_delta_workload():
+    """Selection-quality study on the anchored workload: the thumbnail filter
+    keeps the blocks of (nearly) every token the exact top-delta rule keeps."""
+    wl = get_workload("lowbit_topdelta_bf16", B=1, Hq=8, Hkv=2, N=8192, needles=4)
+    inp = make_inputs(wl)
+    q, K = A.widen(inp.Q, "bf16"), A.widen(inp.K, "bf16")
+    codes, resid, meta = oracle.lowbit_encode(K, wl.block)
+    lists, _, _ = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
+    for margin, floor in ((0.0, 0.99), (wl.margin, 1.0)):
+        idx, cnt, _, _ = oracle.select_topdelta_lowbit(q, codes, resid, meta, wl.block, wl.sink,
+                                                       wl.local, wl.delta, margin)
+        rec = []
+        for h in range(wl.Hq):
+            kept = set(idx[0, h // wl.g, :cnt[0, h // wl.g]].tolist())
+            rec.append(np.mean([t // wl.block in kept for t in lists[0][h]]))
+        assert np.mean(rec) >= floor, (margin, rec)
+        assert cnt.mean() / wl.nb < 0.3

@@ -39,6 +39,7 @@ class Workload:
     local: int = 0            # top-delta: trailing tokens of the pseudo-max window
     delta: float = 0.0        # top-delta: keep s >= pseudo-max - delta
     anchor_gain: float = 0.0  # sink and local keys get + anchor_gain * unit query
+    margin: float = 0.0       # low-bit top-delta: filter at tau - margin
     cluster_spread: float = 0.0  # > 0: keys of block j = mu_j + cluster_spread * noise
     subspaces: int = 1        # pruned threshold: contiguous key subspaces per sphere set
     extra: dict = field(default_factory=dict)
@@ -99,6 +100,14 @@ WORKLOADS = {
         name="clustered_threshold_bf16", kind="decode_threshold", B=8, Hq=32,
         Hkv=8, D=128, N=32768, block=64, k=0, dtype="bf16", seed=4,
         needles=16, percentile=99.0, cap=1024, cluster_spread=0.05, subspaces=1),
+    # The top-delta arrays, scanned through 2-bit key thumbnails with 8-bit
+    # residuals ("Faster Than Flash", Metodologia §1, §3): a block stays when
+    # a provisional score reaches tau - 1 for some head of the group.
+    "lowbit_topdelta_bf16": Workload(
+        name="lowbit_topdelta_bf16", kind="decode_topdelta", B=8, Hq=32,
+        Hkv=8, D=128, N=32768, block=64, k=0, dtype="bf16", seed=2,
+        needles=16, outlier_channels=4, outlier_scale=8.0, needle_gain=16.0,
+        cap=512, sink=64, local=64, delta=5.0, anchor_gain=16.0, margin=1.0),
     # B=1, Hq=32, Hkv=4, d=128, L=64K, 128-token query and key blocks; each
     # query block keeps block 0, its diagonal block and the top-8 earlier blocks.
     "sparse_prefill_bf16": Workload(
