@@ -94,7 +94,8 @@ enum {
   SA_OP_SPARSE_DECODE = 2,
   SA_OP_DECODE_STEP = 3,
   SA_OP_SELECT_TOPDELTA = 4,
-  SA_OP_SELECT_PRUNED = 5
+  SA_OP_SELECT_PRUNED = 5,
+  SA_OP_SELECT_LOWBIT = 6
 };
 
 /*
@@ -261,6 +262,78 @@ sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype,
                                      float scale, int cap, int32_t* idx,
                                      float* score, int32_t* count, uint8_t* live,
                                      void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_encode_keys -- 2-bit key thumbnails with 8-bit residuals ([FFD]
+ * Metodologia §1: thumbnails are scanned to estimate scores, residuals rebuild
+ * the keys for the exact computation).  Per channel c over each block j:
+ *     lo, hi = min, max;  step = (hi - lo) * fl32(1/3);  d = k - lo
+ *     code = [d >= step/2] + [d >= 1.5 step] + [d >= 2.5 step]   (0..3)
+ *     t = fma(code, step, lo);  rstep = 2^(E - 8) where step = m 2^E, m in [0.5, 1)
+ *     r8 = clamp(rint((k - t) / rstep), -127, 127)
+ * all in IEEE float32, so the output is a fixed function of K.
+ *
+ *   K        [B, H, N, D] dtype (finite values)
+ *   codes    [B, H, N, D/4] uint8 out: channel 4i + e of a token in bits
+ *            2e..2e+1 of byte i
+ *   resid    [B, H, N, D] int8 out
+ *   meta     [B, H, nb, 3, D] float32 out: (lo, step, rstep) rows per block
+ *   [blk_begin, blk_end)  the blocks to (re)encode (decode appends re-encode
+ *            the newest block)
+ */
+sa_status sa_encode_keys(const void* K, int dtype, int B, int H, int N, int D,
+                         int block, int blk_begin, int blk_end, uint8_t* codes,
+                         int8_t* resid, float* meta, void* stream);
+
+/*
+ * sa_decode_keys -- the refined keys k^ = t + r8 * rstep, rounded to bf16
+ * (nearest, ties to even), written into khat [B, H, N, D] (bf16, laid out as
+ * K) for the listed blocks only: idx [B, H, idx_stride] block ids with count
+ * [B, H] valid (NULL: all idx_stride; entries < 0 are skipped), or, when idx
+ * is NULL, the block range [blk_begin, blk_end).  Other rows are untouched.
+ */
+sa_status sa_decode_keys(const uint8_t* codes, const int8_t* resid,
+                         const float* meta, int B, int H, int N, int D,
+                         int block, const int32_t* idx, const int32_t* count,
+                         int idx_stride, int blk_begin, int blk_end, void* khat,
+                         void* stream);
+
+/*
+ * sa_select_topdelta_lowbit -- the three stages of [FFD]'s fused decode
+ * (Metodologia §3) up to the attention: (1) the refined keys of the blocks
+ * holding the sink prefix [0, sink) and the local window [N - local, N) are
+ * rebuilt into khat and give tau = m~ - delta as sa_select_topdelta does;
+ * (2) every token's provisional score comes from its 2-bit thumbnail (t
+ * rounded to bf16, matrix-core dot products with Q, float32 accumulation),
+ * and block j is kept for a kv head when a head h of its group has a
+ * provisional score >= tau_h - margin, or when it holds window tokens;
+ * (3) the refined keys of the kept blocks are written into khat.  Follow
+ * with sa_sparse_decode(Q, khat, V, idx, count, SA_IDX_BLOCKS, block,
+ * idx_stride = kcap).
+ *
+ *   Q        [B, Hq, D] bf16; codes, resid, meta as sa_encode_keys built them
+ *            from K [B, Hkv, N, D]
+ *   block    64 or 128 (the encoding's block); g in {1, 2, 4, 8}
+ *   delta, margin  >= 0
+ *   idx      [B, Hkv, kcap] int32 out, ascending kept block ids (-1 padded)
+ *   count    [B, Hkv] int32 out, the TRUE number kept (may exceed kcap; only
+ *            the first kcap are listed and rebuilt)
+ *   tau      [B, Hq] float32 out (NULL: kept in ws);  bmax [B, Hq, nb]
+ *            float32 out, each block's largest provisional score (NULL: none)
+ *   khat     [B, Hkv, N, D] bf16: rows of window and kept blocks written
+ * Selection is not exact against the full-precision keys: the thumbnail
+ * error decides which blocks reach the filter (margin trades bytes for
+ * recall); attention over the kept blocks uses the refined keys.
+ * ws: sa_workspace_bytes(SA_OP_SELECT_LOWBIT, B, Hq, Hkv, N, D, block, kcap).
+ */
+sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes,
+                                    const int8_t* resid, const float* meta, int B,
+                                    int Hq, int Hkv, int N, int D, int block,
+                                    int sink, int local, float delta, float margin,
+                                    float scale, int kcap, int32_t* idx,
+                                    int32_t* count, float* tau, float* bmax,
+                                    void* khat, void* ws, size_t ws_bytes,
+                                    void* stream);
 
 /*
  * sa_sparse_decode -- exact attention restricted to the selected keys, as

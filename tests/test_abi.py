@@ -32,6 +32,10 @@ def lib():
     L.sa_select_threshold.argtypes = [P, P, I, I, I, I, I, I, P, F, I, P, P, P, P, Z, P]
     L.sa_select_topdelta.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, I, P, P, P, P, P, Z, P]
     L.sa_build_radius.argtypes = [P, I, I, I, I, I, I, I, I, I, P, P, P]
+    L.sa_encode_keys.argtypes = [P, I, I, I, I, I, I, I, I, P, P, P, P]
+    L.sa_decode_keys.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, I, P, P]
+    L.sa_select_topdelta_lowbit.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, F, F, F, I, P, P,
+                                            P, P, P, P, Z, P]
     L.sa_select_threshold_pruned.argtypes = [P, P, I, I, I, I, I, I, I, I, P, P, P, F, I, P, P, P,
                                              P, P, Z, P]
     L.sa_sparse_decode.argtypes = [P, P, P, I, I, I, I, I, I, F, I, I, P, P, I, P, P, I, P, P, Z, P]
@@ -53,8 +57,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["sa_build_sketch", "sa_build_radius", "sa_select_topk", "sa_select_threshold",
-              "sa_select_topdelta", "sa_select_threshold_pruned", "sa_sparse_decode",
+    for n in ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
+              "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
+              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_sparse_decode",
               "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
               "sa_status_str",
               "sa_last_error", "sa_version"]:
@@ -211,6 +216,46 @@ def test_pruned_threshold_validation(lib):
     assert call(4, 48) == UNSUPPORTED             # bf16 g = 6
 
 
+def test_lowbit_validation(lib):
+    enc = lib.sa_encode_keys
+    eb = [A, 1, 1, 8, 32768, 128, 64, 0, 512, A, A, A, None]
+
+    def ecall(i, v):
+        a = list(eb)
+        a[i] = v
+        return enc(*a)
+
+    assert ecall(5, 96) == UNSUPPORTED            # D
+    assert ecall(8, 513) == INVALID               # block range
+    assert ecall(9, None) == INVALID              # codes
+    assert ecall(11, MIS) == INVALID              # misaligned meta
+    dec = lib.sa_decode_keys
+    db = [A, A, A, 1, 8, 32768, 128, 64, None, None, 0, 0, 600, A, None]
+    assert dec(*db) == INVALID                    # range past nb (no list)
+    a = list(db)
+    a[8], a[10] = A, 0                            # a list with stride 0
+    assert dec(*a) == INVALID
+    sel = lib.sa_select_topdelta_lowbit
+    sb = [A, A, A, A, 1, 64, 8, 32768, 128, 64, 64, 64, 5.0, 1.0, 0.0, 512, A, A, None, None, A,
+          A, 1 << 30, None]
+
+    def scall(i, v):
+        a = list(sb)
+        a[i] = v
+        return sel(*a)
+
+    assert scall(9, 32) == UNSUPPORTED            # block
+    assert scall(5, 48) == UNSUPPORTED            # g = 6
+    assert scall(13, -1.0) == INVALID             # margin
+    assert scall(12, float("nan")) == INVALID     # delta
+    assert scall(15, 0) == INVALID                # kcap
+    assert scall(20, None) == INVALID             # khat
+    assert scall(22, 100) == WORKSPACE
+    a = list(sb)
+    a[10], a[11] = 0, 0                           # empty window
+    assert sel(*a) == INVALID
+
+
 def test_decode_validation(lib):
     f = lib.sa_sparse_decode
     base = [A, A, A, 1, 1, 64, 8, 262144, 128, 0.0, 0, 64, A, A, 82, None, A, 1, A, A, 1 << 30, None]
@@ -283,7 +328,8 @@ def test_binding_binds_every_entry_point():
     sa = pytest.importorskip("top_sparse_attention_mean_amd")
     for n in sa.EXPORTS:
         assert hasattr(sa, "_" + n[len("sa_"):]), f"no ctypes signature for {n}"
-    for n in ["sa_build_sketch", "sa_build_radius", "sa_select_topk", "sa_select_threshold",
-              "sa_select_topdelta", "sa_select_threshold_pruned", "sa_sparse_decode",
+    for n in ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
+              "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
+              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_sparse_decode",
               "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
         assert callable(getattr(sa, n)), n

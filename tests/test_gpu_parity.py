@@ -600,6 +600,121 @@ def test_pruned_threshold_parity(name, over, S):
     print(f"{name} {over} S={S}: {scanned.mean():.1%} of blocks scanned")
 
 
+def _unpack_codes(packed):
+    """[..., D/4] uint8 -> [..., D] codes (channel 4i + e in bits 2e of byte i)."""
+    p = packed.astype(np.uint8)
+    return np.stack([(p >> (2 * e)) & 3 for e in range(4)], -1).reshape(*p.shape[:-1], -1)
+
+
+LOWBIT_CODEC_CASES = [
+    ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 5000, "needles": 4}, 64),  # outliers
+    ("tiny_decode_f32", {"N": 3001}, 37),                                           # fp32, odd block
+    ("long_decode_bf16", {"Hq": 8, "Hkv": 1, "N": 4096 + 100}, 128),                 # drift
+]
+
+
+@pytest.mark.parametrize("name,over,block", LOWBIT_CODEC_CASES)
+def test_lowbit_codec_parity(name, over, block):
+    wl, inp, q, K, V = _decode_case(name, over)
+    Kd = to_dev(inp.K, wl.dtype)
+    codes, resid, meta = sa.sa_encode_keys(Kd, block)
+    c_x, r_x, m_x = oracle.lowbit_encode(K, block)
+    assert np.array_equal(_unpack_codes(codes.cpu().numpy()), c_x)
+    assert np.array_equal(resid.cpu().numpy(), r_x)
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32), m_x.view(np.uint32))
+    # refined keys of a block list, bit for bit; other rows untouched
+    nb = -(-wl.N // block)
+    rng = np.random.default_rng(7)
+    lst = np.full((wl.B, wl.Hkv, 6), -1, dtype=np.int32)
+    cnt = np.zeros((wl.B, wl.Hkv), dtype=np.int32)
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            sel = np.sort(rng.choice(nb, size=min(5, nb), replace=False))
+            sel[-1] = nb - 1                                      # the partial last block
+            sel = np.unique(sel)
+            lst[b, kh, :sel.size] = sel
+            cnt[b, kh] = sel.size
+    kh_d = sa.sa_decode_keys(codes, resid, meta, block, idx=torch.from_numpy(lst).cuda(),
+                             count=torch.from_numpy(cnt).cuda())
+    got = kh_d.float().cpu().numpy().astype(np.float64)
+    want = oracle.bf16_round(oracle.lowbit_reconstruct(c_x, r_x, m_x, block))
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            rows = block_tokens(lst[b, kh, :cnt[b, kh]], block, wl.N)
+            assert np.array_equal(got[b, kh, rows], want[b, kh, rows])
+            other = np.setdiff1d(np.arange(wl.N), rows)
+            assert not got[b, kh, other].any()
+    # a re-encode of a block range leaves the rest as it was
+    c2, r2, m2 = sa.sa_encode_keys(Kd, block, blk_begin=nb - 1, blk_end=nb)
+    last = slice((nb - 1) * block, wl.N)
+    assert np.array_equal(_unpack_codes(c2.cpu().numpy())[:, :, last], c_x[:, :, last])
+    assert not c2.cpu().numpy()[:, :, :(nb - 1) * block].any()
+    print(f"{name} {over} block {block}: max |k^ - k| {np.abs(want - K).max():.3g}")
+
+
+LOWBIT_CASES = [
+    ("lowbit_topdelta_bf16", {"B": 2, "N": 8192, "needles": 4, "cap": 128}),            # g = 4
+    ("lowbit_topdelta_bf16", {"B": 1, "Hq": 8, "Hkv": 1, "N": 5000, "needles": 3,        # g = 8, ragged
+                              "cap": 79, "margin": 0.0}),
+    ("lowbit_topdelta_bf16", {"B": 1, "Hq": 4, "Hkv": 4, "D": 64, "N": 3001, "needles": 2,
+                              "sink": 16, "local": 100, "cap": 47}),                     # g = 1, D = 64
+    ("lowbit_topdelta_bf16", {"B": 1, "Hq": 4, "Hkv": 2, "N": 6000, "needles": 2, "block": 128,
+                              "cap": 47, "delta": 7.0}),                                 # g = 2, block 128
+    ("lowbit_topdelta_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 4096, "needles": 2, "cap": 8,
+                              "margin": 3.0}),                                           # capacity overflow
+]
+
+
+@pytest.mark.parametrize("name,over", LOWBIT_CASES)
+def test_lowbit_topdelta_parity(name, over):
+    wl, inp, q, K, V = _decode_case(name, over)
+    blk = wl.block
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    codes, resid, meta = sa.sa_encode_keys(Kd, blk)
+    idx, cnt, tau, bmax, khat = sa.sa_select_topdelta_lowbit(
+        Qd, codes, resid, meta, blk, wl.sink, wl.local, wl.delta, wl.margin, wl.cap,
+        want_bmax=True)
+    c_x, r_x, m_x = oracle.lowbit_encode(K, blk)
+    i_x, n_x, t_x, b_x = oracle.select_topdelta_lowbit(q, c_x, r_x, m_x, blk, wl.sink, wl.local,
+                                                       wl.delta, wl.margin)
+    tau_h, bmax_h = tau.cpu().numpy(), bmax.cpu().numpy()
+    assert np.all(tau_h <= t_x + 1e-6 * (1 + np.abs(t_x)))
+    assert np.all(tau_h >= t_x - 1e-3 * (1 + np.abs(t_x)))
+    assert max_abs(bmax_h, b_x) <= 1e-4 * (1 + np.abs(b_x).max())
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    g, nb = wl.g, wl.nb
+    win = np.unique(oracle.window_tokens(wl.N, wl.sink, wl.local) // blk)
+    khat_x = oracle.bf16_round(oracle.lowbit_reconstruct(c_x, r_x, m_x, blk))
+    khat_h = khat.float().cpu().numpy().astype(np.float64)
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            n = int(cnt_h[b, kh])
+            got = idx_h[b, kh, :min(n, wl.cap)]
+            assert np.all(np.diff(got) > 0) and np.all(idx_h[b, kh, min(n, wl.cap):] == -1)
+            hs = range(kh * g, (kh + 1) * g)
+            tol = 2e-3 * (1 + np.abs(t_x[b, list(hs)]).max())
+            must = np.zeros(nb, bool)
+            may = np.zeros(nb, bool)
+            must[win] = may[win] = True
+            for h in hs:
+                must |= b_x[b, h] >= t_x[b, h] - wl.margin + tol
+                may |= b_x[b, h] >= t_x[b, h] - wl.margin - tol
+            full = np.nonzero(must)[0]
+            assert n >= full.size and n <= int(may.sum())
+            if n <= wl.cap:
+                assert set(full.tolist()) <= set(got.tolist())
+                assert np.all(may[got])
+            rows = block_tokens(got, blk, wl.N)
+            assert np.array_equal(khat_h[b, kh, rows], khat_x[b, kh, rows])
+    # refinement: attention over the kept blocks with the refined keys
+    O32, lse = sa.sa_sparse_decode(Qd, khat, Vd, idx, cnt, block=blk, out_dtype=torch.float32)
+    O_ref, lse_ref = oracle.attend_blocks(q, khat_x, V, idx_h, blk, count=np.minimum(cnt_h, wl.cap))
+    err = max_abs(O32.cpu().numpy(), O_ref)
+    assert err <= OUT_TOL["bf16"], err
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    print(f"{name} {over}: {cnt_h.mean() / nb:.1%} of blocks kept, max-abs O error {err:.2e}")
+
+
 PREFILL_CASES = [
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 2048, "needles": 4}),
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 1, "N": 2048 + 77, "needles": 4}),   # ragged

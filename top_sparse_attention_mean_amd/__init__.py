@@ -31,10 +31,11 @@ SA_F32, SA_BF16 = 0, 1
 SA_FORCE_SINK, SA_FORCE_LOCAL, SA_CAUSAL = 1, 2, 4
 SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
 (SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP,
- SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED) = range(6)
+ SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED, SA_OP_SELECT_LOWBIT) = range(7)
 
-EXPORTS = ["sa_build_sketch", "sa_build_radius", "sa_select_topk", "sa_select_threshold",
-           "sa_select_topdelta", "sa_select_threshold_pruned", "sa_sparse_decode",
+EXPORTS = ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
+           "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
+           "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_sparse_decode",
            "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
            "sa_status_str",
            "sa_last_error", "sa_version"]
@@ -61,6 +62,11 @@ _select_threshold = _sig("sa_select_threshold", _I, _P, _P, _I, _I, _I, _I, _I, 
 _build_radius = _sig("sa_build_radius", _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P)
 _select_threshold_pruned = _sig("sa_select_threshold_pruned", _I, _P, _P, _I, _I, _I, _I, _I, _I,
                                 _I, _I, _P, _P, _P, _F, _I, _P, _P, _P, _P, _P, _Z, _P)
+_encode_keys = _sig("sa_encode_keys", _I, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P)
+_decode_keys = _sig("sa_decode_keys", _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _I, _I, _I, _P,
+                    _P)
+_select_topdelta_lowbit = _sig("sa_select_topdelta_lowbit", _I, _P, _P, _P, _P, _I, _I, _I, _I,
+                               _I, _I, _I, _I, _F, _F, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P)
 _select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                         _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _sparse_decode = _sig("sa_sparse_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
@@ -183,6 +189,48 @@ def sa_build_radius(X: torch.Tensor, sketch: torch.Tensor, block: int, S: int = 
     return out
 
 
+def sa_encode_keys(K: torch.Tensor, block: int, blk_begin: int = 0,
+                   blk_end: Optional[int] = None, codes=None, resid=None, meta=None,
+                   stream=None):
+    """2-bit thumbnails + 8-bit residuals of K [B, H, N, D] -> codes uint8
+    [B, H, N, D/4], resid int8 [B, H, N, D], meta float32 [B, H, nb, 3, D]."""
+    _dev(K, codes, resid, meta)
+    B, H, N, D = K.shape
+    nb = -(-N // block)
+    if blk_end is None:
+        blk_end = nb
+    dev = K.device
+    if codes is None:
+        codes = torch.zeros(B, H, N, D // 4, dtype=torch.uint8, device=dev)
+    if resid is None:
+        resid = torch.zeros(B, H, N, D, dtype=torch.int8, device=dev)
+    if meta is None:
+        meta = torch.zeros(B, H, nb, 3, D, dtype=torch.float32, device=dev)
+    _check(_encode_keys(_ptr(K), _dt(K), B, H, N, D, block, blk_begin, blk_end, _ptr(codes),
+                        _ptr(resid), _ptr(meta), _stream(stream)), "sa_encode_keys")
+    return codes, resid, meta
+
+
+def sa_decode_keys(codes: torch.Tensor, resid: torch.Tensor, meta: torch.Tensor, block: int,
+                   idx: Optional[torch.Tensor] = None, count: Optional[torch.Tensor] = None,
+                   blk_begin: int = 0, blk_end: Optional[int] = None,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Refined bf16 keys of the listed blocks (or a block range) into out
+    [B, H, N, D] (zeros elsewhere when out is allocated here)."""
+    _dev(codes, resid, meta, idx, count, out)
+    B, H, N, D = resid.shape
+    nb = -(-N // block)
+    if blk_end is None:
+        blk_end = nb
+    if out is None:
+        out = torch.zeros(B, H, N, D, dtype=torch.bfloat16, device=codes.device)
+    stride = idx.shape[-1] if idx is not None else 0
+    _check(_decode_keys(_ptr(codes), _ptr(resid), _ptr(meta), B, H, N, D, block, _ptr(idx),
+                        _ptr(count), stride, blk_begin, blk_end, _ptr(out), _stream(stream)),
+           "sa_decode_keys")
+    return out
+
+
 def sa_select_topk(Q: torch.Tensor, ksketch: torch.Tensor, k: int,
                    flags: int = SA_FORCE_SINK | SA_FORCE_LOCAL, scale: float = 0.0,
                    Hkv: Optional[int] = None, q_block: int = 1,
@@ -277,6 +325,38 @@ def sa_select_threshold_pruned(Q: torch.Tensor, K: torch.Tensor, sketch: torch.T
                                     _ptr(idx), _ptr(score), _ptr(count), _ptr(live), _ptr(ws),
                                     ws.numel(), _stream(stream)), "sa_select_threshold_pruned")
     return idx, score, count, live
+
+
+def sa_select_topdelta_lowbit(Q: torch.Tensor, codes: torch.Tensor, resid: torch.Tensor,
+                              meta: torch.Tensor, block: int, sink: int, local: int, delta: float,
+                              margin: float, kcap: int, scale: float = 0.0, khat=None, idx=None,
+                              count=None, tau=None, want_bmax: bool = False, ws=None,
+                              stream=None):
+    """Top-delta block filter over 2-bit thumbnails; refined keys of the kept
+    blocks into khat.  Returns idx [B, Hkv, kcap], count [B, Hkv], tau [B, Hq],
+    bmax [B, Hq, nb] (or None) and khat [B, Hkv, N, D] bf16."""
+    _dev(Q, codes, resid, meta, khat, idx, count, tau)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = resid.shape
+    nb = -(-N // block)
+    dev = Q.device
+    if khat is None:
+        khat = torch.zeros(B, Hkv, N, D, dtype=torch.bfloat16, device=dev)
+    if idx is None:
+        idx = torch.empty(B, Hkv, kcap, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if tau is None:
+        tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    bmax = torch.empty(B, Hq, nb, dtype=torch.float32, device=dev) if want_bmax else None
+    need = workspace_bytes(SA_OP_SELECT_LOWBIT, B, Hq, Hkv, N, D, block, kcap)
+    if ws is None:
+        ws = workspace(need, dev, ("lowbit", B, Hq, Hkv, N, D, block))
+    _check(_select_topdelta_lowbit(_ptr(Q), _ptr(codes), _ptr(resid), _ptr(meta), B, Hq, Hkv, N,
+                                   D, block, sink, local, delta, margin, scale, kcap, _ptr(idx),
+                                   _ptr(count), _ptr(tau), _ptr(bmax), _ptr(khat), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "sa_select_topdelta_lowbit")
+    return idx, count, tau, bmax, khat
 
 
 def sa_select_topdelta(Q: torch.Tensor, K: torch.Tensor, sink: int, local: int, delta: float,

@@ -199,6 +199,9 @@ size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int bloc
       return topdelta_ws_bytes(B, Hq, N);
     case SA_OP_SELECT_PRUNED:
       return pruned_ws_bytes(B, Hq, Hkv, N);
+    case SA_OP_SELECT_LOWBIT:        // block = the block size
+      if (block < 1) return SIZE_MAX;
+      return lowbit_ws_bytes(B, Hq, Hkv, N, block);
     case SA_OP_SPARSE_DECODE:        // k = idx_stride; block = 0 for token mode
       if (k < 1) return SIZE_MAX;
       return decode_ws(B, Hq, Hkv, D, block > 0 ? SA_IDX_BLOCKS : SA_IDX_TOKENS, block, k).bytes;
@@ -364,6 +367,113 @@ sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype, in
   return hip_status(launch_threshold(Q, K, dtype, B, Hq, Hkv, N, D, tau, sc, cap, idx, score,
                                      count, w, ws, st, lv, block),
                     "sa_select_threshold_pruned (scan)");
+}
+
+sa_status sa_encode_keys(const void* K, int dtype, int B, int H, int N, int D, int block,
+                         int blk_begin, int blk_end, uint8_t* codes, int8_t* resid, float* meta,
+                         void* stream) {
+  PTR(K);
+  PTR(codes);
+  PTR(resid);
+  PTR(meta);
+  REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
+  REQ(B >= 1 && H >= 1 && N >= 1, "B, H, N must be >= 1");
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(block >= 1, "block must be >= 1");
+  const int nb = cdiv(N, block);
+  REQ(0 <= blk_begin && blk_begin <= blk_end && blk_end <= nb,
+      "block range [%d, %d) outside [0, %d]", blk_begin, blk_end, nb);
+  REQ(long(B) * H * (blk_end - blk_begin) < (1L << 31), "too many blocks");
+  return hip_status(launch_encode(K, dtype, B, H, N, D, block, blk_begin, blk_end, codes, resid,
+                                  meta, static_cast<hipStream_t>(stream)),
+                    "sa_encode_keys");
+}
+
+sa_status sa_decode_keys(const uint8_t* codes, const int8_t* resid, const float* meta, int B,
+                         int H, int N, int D, int block, const int32_t* idx,
+                         const int32_t* count, int idx_stride, int blk_begin, int blk_end,
+                         void* khat, void* stream) {
+  PTR(codes);
+  PTR(resid);
+  PTR(meta);
+  PTR(khat);
+  REQ(B >= 1 && H >= 1 && N >= 1, "B, H, N must be >= 1");
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  REQ(block >= 1, "block must be >= 1");
+  const int nb = cdiv(N, block);
+  if (idx) {
+    PTR(idx);
+    if (count) PTR(count);
+    REQ(idx_stride >= 1, "idx_stride must be >= 1");
+    REQ(long(B) * H * idx_stride < (1L << 31), "too many list entries");
+  } else {
+    REQ(0 <= blk_begin && blk_begin <= blk_end && blk_end <= nb,
+        "block range [%d, %d) outside [0, %d]", blk_begin, blk_end, nb);
+  }
+  return hip_status(launch_decode_keys(codes, resid, meta, B, H, N, D, block, idx, count,
+                                       idx_stride, blk_begin, blk_end,
+                                       static_cast<uint16_t*>(khat),
+                                       static_cast<hipStream_t>(stream)),
+                    "sa_decode_keys");
+}
+
+sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes, const int8_t* resid,
+                                    const float* meta, int B, int Hq, int Hkv, int N, int D,
+                                    int block, int sink, int local, float delta, float margin,
+                                    float scale, int kcap, int32_t* idx, int32_t* count,
+                                    float* tau, float* bmax, void* khat, void* ws,
+                                    size_t ws_bytes, void* stream) {
+  PTR(Q);
+  PTR(codes);
+  PTR(resid);
+  PTR(meta);
+  PTR(idx);
+  PTR(count);
+  PTR(khat);
+  if (tau) PTR(tau);
+  if (bmax) PTR(bmax);
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  SUP(block == 64 || block == 128, "block must be 64 or 128 (got %d)", block);
+  SUP(pow2_le8(Hq / Hkv), "the low-bit filter needs g in {1, 2, 4, 8}");
+  REQ(N >= 1 && kcap >= 1, "N and kcap must be >= 1");
+  REQ(sink >= 0 && local >= 0, "sink and local must be >= 0 (got %d, %d)", sink, local);
+  REQ(sink > 0 || local > 0, "the sink and local windows are both empty");
+  REQ(delta >= 0.f, "delta must be >= 0 (got %g)", double(delta));
+  REQ(margin >= 0.f, "margin must be >= 0 (got %g)", double(margin));
+  const int nb = cdiv(N, block);
+  REQ(long(B) * Hkv * cdiv(nb, 4) < (1L << 31), "grid too large");
+  const size_t need = lowbit_ws_bytes(B, Hq, Hkv, N, block);
+  if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  PTR(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float sc = eff_scale(scale, D);
+  char* base = static_cast<char*>(ws);
+  uint8_t* flag = reinterpret_cast<uint8_t*>(base);
+  float* t = tau ? tau : reinterpret_cast<float*>(base + align256(size_t(B) * Hkv * nb));
+  uint16_t* kh = static_cast<uint16_t*>(khat);
+  // the window's blocks: [0, f1) holds the sink tokens, [f2, nb) the local ones
+  const int ns = sink < N ? sink : N;
+  const int lt = N - (local < N ? local : N);
+  const int tw = lt > ns ? lt : ns;
+  const int f1 = cdiv(ns, block), f2 = tw < N ? tw / block : nb;
+  hipError_t e = launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, nullptr, nullptr, 0,
+                                    0, f1, kh, st);
+  if (e == hipSuccess)
+    e = launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, nullptr, nullptr, 0, f2, nb,
+                           kh, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (window keys)");
+  e = launch_pseudo_max(Q, kh, SA_BF16, B, Hq, Hkv, N, D, sink, local, delta, sc, t, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (pseudo-max)");
+  e = launch_thumb_scan(static_cast<const uint16_t*>(Q), codes, meta, B, Hq, Hkv, N, D, block, sc,
+                        t, margin, 0, f1, f2, nb, bmax, flag, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (thumbnail scan)");
+  e = launch_block_list(flag, B * Hkv, nb, kcap, idx, count, st);
+  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (block list)");
+  return hip_status(launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, idx, count, kcap,
+                                       0, 0, kh, st),
+                    "sa_select_topdelta_lowbit (refined keys)");
 }
 
 sa_status sa_sparse_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,

@@ -135,6 +135,11 @@ inline ThrWs threshold_ws(int B, int Hq, int N) {
 inline size_t topdelta_ws_bytes(int B, int Hq, int N) {
   return threshold_ws(B, Hq, N).bytes + align256(size_t(B) * Hq * sizeof(float));
 }
+// The low-bit top-delta filter: one keep flag per (b, kv head, block), then
+// the per-head thresholds [B, Hq].
+inline size_t lowbit_ws_bytes(int B, int Hq, int Hkv, int N, int block) {
+  return align256(size_t(B) * Hkv * cdiv(N, block)) + align256(size_t(B) * Hq * sizeof(float));
+}
 // The sphere-pruned threshold adds one live flag per (b, kv head, segment).
 inline size_t pruned_ws_bytes(int B, int Hq, int Hkv, int N) {
   const ThrWs w = threshold_ws(B, Hq, N);
@@ -189,6 +194,21 @@ hipError_t launch_threshold(const void* Q, const void* K, int dtype, int B,
                             int32_t* count, const ThrWs& w, void* ws,
                             hipStream_t st, const uint8_t* live = nullptr,
                             int pblock = kThrSeg);
+hipError_t launch_encode(const void* K, int dtype, int B, int H, int N, int D,
+                         int block, int b0, int b1, uint8_t* codes, int8_t* resid,
+                         float* meta, hipStream_t st);
+hipError_t launch_decode_keys(const uint8_t* codes, const int8_t* resid,
+                              const float* meta, int B, int H, int N, int D,
+                              int block, const int32_t* idx, const int32_t* count,
+                              int idx_stride, int b0, int b1, uint16_t* khat,
+                              hipStream_t st);
+hipError_t launch_thumb_scan(const uint16_t* Q, const uint8_t* codes,
+                             const float* meta, int B, int Hq, int Hkv, int N,
+                             int D, int block, float scale, const float* tau,
+                             float margin, int f0, int f1, int f2, int f3,
+                             float* bmax, uint8_t* flag, hipStream_t st);
+hipError_t launch_block_list(const uint8_t* flag, int BH, int nb, int kcap,
+                             int32_t* idx, int32_t* count, hipStream_t st);
 hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D,
                          int block, int S, int b0, int b1, const float* sketch,
                          float* radius, hipStream_t st);
