@@ -474,6 +474,114 @@ def bench_pruned(args) -> dict:
     return res
 
 
+def bench_lowbit(args) -> dict:
+    """Top-delta over 2-bit key thumbnails (pseudo-max from the window's refined
+    keys, thumbnail scan and block filter, refined keys of the kept blocks) and
+    block-mode attention over them; the codec runs once, when the cache is
+    written.  The exact top-delta pass on the same arrays is timed beside it."""
+    import numpy as np
+    import torch
+    import oracle
+    import top_sparse_attention_mean_amd as sa
+    from oracle.attention import widen
+    from tests.parity_util import to_dev
+    from workloads import get_workload, make_inputs
+    wl = get_workload("lowbit_topdelta_bf16")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl)
+    R = 2
+    Qs = [to_dev(inp.Q, wl.dtype, dev) for _ in range(R)]
+    Kd = to_dev(inp.K, wl.dtype, dev)
+    Ks = [Kd] + [Kd.clone() for _ in range(R - 1)]
+    Vd = to_dev(inp.V, wl.dtype, dev)
+    Vs = [Vd] + [Vd.clone() for _ in range(R - 1)]
+    B, Hq, Hkv, D, N, blk = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N, wl.block
+    nb = -(-N // blk)
+    enc = [sa.sa_encode_keys(k, blk) for k in Ks]
+    torch.cuda.synchronize()
+    t_e0 = time.perf_counter()
+    sa.sa_encode_keys(Ks[0], blk, codes=enc[0][0], resid=enc[0][1], meta=enc[0][2])
+    torch.cuda.synchronize()
+    t_enc = (time.perf_counter() - t_e0) * 1e6
+    khats = [torch.zeros(B, Hkv, N, D, dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    idx = torch.empty(B, Hkv, wl.cap, dtype=torch.int32, device=dev)
+    cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    O = torch.empty(B, Hq, D, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    lws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_LOWBIT, B, Hq, Hkv, N, D, blk, wl.cap),
+                      dtype=torch.uint8, device=dev)
+    dws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, blk, wl.cap),
+                      dtype=torch.uint8, device=dev)
+    # the exact top-delta pass on the same arrays
+    tcap = 4096
+    tidx = torch.empty(B, Hq, tcap, dtype=torch.int32, device=dev)
+    tsc = torch.empty(B, Hq, tcap, dtype=torch.float32, device=dev)
+    tcnt = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    tws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_TOPDELTA, B, Hq, Hkv, N, D, 0, tcap),
+                      dtype=torch.uint8, device=dev)
+    tdws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, 0, tcap),
+                       dtype=torch.uint8, device=dev)
+
+    def sel(r):
+        c, rs, m = enc[r]
+        sa.sa_select_topdelta_lowbit(Qs[r], c, rs, m, blk, wl.sink, wl.local, wl.delta, wl.margin,
+                                     wl.cap, khat=khats[r], idx=idx, count=cnt, tau=tau, ws=lws)
+
+    def dec(r):
+        sa.sa_sparse_decode(Qs[r], khats[r], Vs[r], idx, cnt, block=blk, O=O, lse=lse, ws=dws)
+
+    def exact(r):
+        sa.sa_select_topdelta(Qs[r], Ks[r], wl.sink, wl.local, wl.delta, tcap, idx=tidx, score=tsc,
+                              count=tcnt, ws=tws)
+        sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], tidx, tcnt, mode=sa.SA_IDX_TOKENS, score=tsc, O=O,
+                            lse=lse, ws=tdws)
+
+    n = max(4, args.steps // 20)
+    t_pass = graph_time(lambda r: (sel(r), dec(r)), R, n)
+    t_sel = graph_time(sel, R, n)
+    t_exact = graph_time(exact, R, n)
+    kept = int(cnt.sum().item())
+    e = 2
+    scan_bytes = B * Hkv * (N * D // 4 + nb * 2 * D * 4) + B * Hq * D * e + B * Hq * 4
+    refine_bytes = kept * blk * D * (1 + 1 / 4) + kept * 3 * D * 4 + kept * blk * D * e
+    ach = scan_bytes / (t_sel * 1e-6) / 1e9
+    res = {
+        "workload": wl.name, "us_per_pass": round(t_pass, 2), "margin": wl.margin,
+        "pass": "window refined keys + pseudo-max + thumbnail scan + block list + refined keys "
+                "of kept blocks (sa_select_topdelta_lowbit) + block-mode decode",
+        "kernels_us": {"sa_select_topdelta_lowbit": round(t_sel, 2),
+                       "sa_sparse_decode blocks over the refined keys": round(max(t_pass - t_sel, 0), 2),
+                       "exact top-delta pass on the same arrays (sa_select_topdelta + token "
+                       "decode)": round(t_exact, 2),
+                       "sa_encode_keys, once per cache (host-timed, one call)": round(t_enc, 1)},
+        "kept_block_fraction": round(kept / (B * Hkv * nb), 4),
+        "scan_bytes_per_token": D // 4 + 2 * D * 4 / blk,
+        "roofline": {"bound": "hbm", "kernel": "k_thumb_scan (2-bit codes + block ranges; the "
+                     "call also runs the window decode, pseudo-max, list and refine kernels)",
+                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes": int(scan_bytes),
+                     "refine_bytes": int(refine_bytes), "avg_us": round(t_sel, 2)},
+    }
+    if not args.no_cpu:
+        q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
+        t0 = time.perf_counter()
+        c_x, r_x, m_x = oracle.lowbit_encode(K, blk)
+        t_cpu_enc = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        i_x, n_x, _, _ = oracle.select_topdelta_lowbit(q, c_x, r_x, m_x, blk, wl.sink, wl.local,
+                                                       wl.delta, wl.margin)
+        kx = oracle.bf16_round(oracle.lowbit_reconstruct(c_x, r_x, m_x, blk))
+        oracle.attend_blocks(q, kx, V, i_x, blk, count=n_x)
+        t_cpu = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(t_cpu * 1e6, 1), "unit": "us/pass",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "sample": f"one full pass (all 256 heads, float64); the codec "
+                                         f"({t_cpu_enc:.1f} s) not included"}
+    return res
+
+
 def bench_prefill(args) -> dict:
     """Block-sparse causal prefill (rows a1 pooling, a3, a7) at its full size."""
     import numpy as np
@@ -581,8 +689,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the threshold, top-delta, pruned and prefill variant measurements")
-    ap.add_argument("--variant", choices=["threshold", "topdelta", "pruned", "prefill"],
+                    help="skip the threshold, top-delta, pruned, low-bit and prefill variant "
+                    "measurements")
+    ap.add_argument("--variant", choices=["threshold", "topdelta", "pruned", "lowbit", "prefill"],
                     help="run only this variant measurement and print its JSON")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 counter passes (no timing output)")
@@ -598,6 +707,7 @@ def main(argv=None) -> int:
     elif args.variant:
         res = (bench_prefill(args) if args.variant == "prefill" else
                bench_pruned(args) if args.variant == "pruned" else
+               bench_lowbit(args) if args.variant == "lowbit" else
                bench_threshold(args, args.variant))
     else:
         res = bench_decode(args)
@@ -613,6 +723,9 @@ def main(argv=None) -> int:
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"]["pruned"] = bench_pruned(args)
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["variants"]["lowbit"] = bench_lowbit(args)
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"]["prefill"] = bench_prefill(args)

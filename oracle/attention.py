@@ -673,8 +673,12 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
     the blocks holding sink or local tokens are always kept (they set m~);
     (3) exact attention over the kept blocks with the refined keys (O4).
     Readings taken: the refined key is k^ rounded to bf16, the precision of
-    the cache it stands for, and so is the thumbnail fed to the scores;
-    `margin` (>= 0) widens the filter against the thumbnail error.
+    the cache it stands for; the provisional score of token t in block j is
+    the thumbnail dot product split into the block's offset and its code
+    term, scale * (q . lo_j + sum_c bf16(fl32(q_c step_j,c)) code_t,c), whose
+    per-channel weights the matrix cores take in bf16 (the codes 0..3 are
+    exact there); `margin` (>= 0) widens the filter against the thumbnail
+    error.
     Returns (idx, count, tau, bmax): idx [B, Hkv, nb] ascending block ids
     (count valid), tau [B, Hq], bmax [B, Hq, nb] the largest provisional
     score of each block.
@@ -685,7 +689,6 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
     nb = -(-N // block)
     sc = _default_scale(D, scale)
     khat = bf16_round(lowbit_reconstruct(codes, resid, meta, block))
-    thumb = bf16_round(lowbit_thumbnail(codes, meta, block))
     win = window_tokens(N, sink, local)
     if win.size == 0:
         raise ValueError("the sink and local windows are both empty")
@@ -700,9 +703,14 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
             keep[forced] = True
             for h in range(kh * g, (kh + 1) * g):
                 tau[b, h] = (khat[b, kh, win] @ q[b, h]).max() * sc - float(delta)
-                prov = (thumb[b, kh] @ q[b, h]) * sc
+                q32 = q[b, h].astype(np.float32)
                 for j in range(nb):
-                    bmax[b, h, j] = prov[j * block:min((j + 1) * block, N)].max()
+                    lo_j, step_j = meta[b, kh, j, 0], meta[b, kh, j, 1]
+                    w = bf16_round(q32 * step_j)
+                    rows = slice(j * block, min((j + 1) * block, N))
+                    prov = (float(q[b, h] @ lo_j.astype(np.float64))
+                            + codes[b, kh, rows].astype(np.float64) @ w) * sc
+                    bmax[b, h, j] = prov.max()
                 keep |= bmax[b, h] >= tau[b, h] - float(margin)
             sel = np.nonzero(keep)[0]
             idx[b, kh, :sel.size] = sel

@@ -139,6 +139,50 @@ def test_full_pruned_threshold():
           f"{time.time() - t0:.1f}s")
 
 
+def test_full_lowbit_topdelta():
+    """The low-bit top-delta workload whole: codec bit-exact, the thumbnail
+    filter against the oracle's within its band, recall of the exact top-delta
+    rule on the full-precision keys, attention over the refined keys."""
+    t0 = time.time()
+    wl = get_workload("lowbit_topdelta_bf16")
+    inp = make_inputs(wl)
+    q, K, V = (widen(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    codes, resid, meta = sa.sa_encode_keys(Kd, wl.block)
+    idx, cnt, tau, bmax, khat = sa.sa_select_topdelta_lowbit(
+        Qd, codes, resid, meta, wl.block, wl.sink, wl.local, wl.delta, wl.margin, wl.cap,
+        want_bmax=True)
+    O32, lse = sa.sa_sparse_decode(Qd, khat, Vd, idx, cnt, block=wl.block, out_dtype=torch.float32)
+    c_x, r_x, m_x = oracle.lowbit_encode(K, wl.block)
+    assert np.array_equal(resid.cpu().numpy(), r_x)
+    assert np.array_equal(meta.cpu().numpy().view(np.uint32), m_x.view(np.uint32))
+    i_x, n_x, t_x, b_x = oracle.select_topdelta_lowbit(q, c_x, r_x, m_x, wl.block, wl.sink,
+                                                       wl.local, wl.delta, wl.margin)
+    assert max_abs(bmax.cpu().numpy(), b_x) <= 1e-4 * (1 + np.abs(b_x).max())
+    assert max_abs(tau.cpu().numpy(), t_x) <= 1e-3 * (1 + np.abs(t_x).max())
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert cnt_h.max() <= wl.cap
+    # the oracle's kept set, away from the band, is the GPU's
+    agree = np.mean([set(idx_h[b, k, :cnt_h[b, k]].tolist()) == set(i_x[b, k, :n_x[b, k]].tolist())
+                     for b in range(wl.B) for k in range(wl.Hkv)])
+    assert agree >= 0.9
+    # recall of the exact top-delta rule on the full-precision keys
+    lists, _, _ = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
+    rec = []
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            kept = set(idx_h[b, h // wl.g, :cnt_h[b, h // wl.g]].tolist())
+            rec.append(np.mean([t // wl.block in kept for t in lists[b][h]]))
+    assert np.mean(rec) >= 0.999
+    khat_x = oracle.bf16_round(oracle.lowbit_reconstruct(c_x, r_x, m_x, wl.block))
+    O_ref, lse_ref = oracle.attend_blocks(q, khat_x, V, idx_h, wl.block, count=cnt_h)
+    err = max_abs(O32.cpu().numpy(), O_ref)
+    assert err <= 2e-3
+    print(f"low-bit top-delta: {cnt_h.mean() / wl.nb:.1%} of blocks kept, recall "
+          f"{np.mean(rec):.4f}, lists equal to the oracle's on {agree:.0%} of heads, max-abs O "
+          f"error {err:.2e}, {time.time() - t0:.1f}s")
+
+
 def test_full_prefill():
     t0 = time.time()
     wl = get_workload("sparse_prefill_bf16")

@@ -19,7 +19,7 @@
 // fixed function of the keys.  Storage per token and kv head: D/4 bytes of
 // codes (4 per byte, channel 4i + e in bits 2e..2e+1) and D bytes of residuals;
 // per block: (lo, step, rstep) float32 rows of D.  The scan reads the codes
-// and lo/step only: D/4 + 8 D / block bytes per token (40 B at D = 128, block
+// and lo/step only: D/4 + 8 D / block bytes per token (48 B at D = 128, block
 // 64) instead of 2 D (256 B).
 //
 // Kernels:
@@ -27,10 +27,11 @@
 //                  residuals (run when the cache is written; a block range).
 //   k_decode_keys  one workgroup per listed block (or per block of a range):
 //                  k^ rounded to bf16 into a key buffer laid out as K.
-//   k_thumb_scan   one wave per (b, kv head, block): thumbnails decoded to
-//                  bf16 in registers, provisional scores on the matrix cores
-//                  for the g heads, the block maximum per head, and the keep
-//                  flag (some head reaches tau_h - margin, or a window block).
+//   k_thumb_scan   one wave per (b, kv head, block): provisional scores from
+//                  the codes on the matrix cores for the g heads (block offset
+//                  q . lo plus the codes against bf16 weights q_c step_c), the
+//                  block maximum per head, and the keep flag (some head reaches
+//                  tau_h - margin, or a window block).
 //   k_block_list   one workgroup per (b, kv head): flags -> ascending list.
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -39,10 +40,7 @@ namespace sa {
 
 constexpr float kThird = 0.3333333432674408f;   // fl32(1/3)
 
-__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
+
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int N, int block, int nb,
@@ -128,22 +126,31 @@ __global__ __launch_bounds__(256) void k_decode_keys(
     const size_t row = size_t(bh) * N + t0 + r;
     const uint32_t cw = *reinterpret_cast<const uint16_t*>(codes + row * (D / 4) + c0 / 4);
     const u32x2 rw = ld8(resid + row * D + c0);
-    uint32_t outw[4];
+    float kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int code = int((cw >> (2 * e)) & 3u);
       const int r8 = int(int8_t((rw[e / 4] >> (8 * (e % 4))) & 0xffu));
       const float t = fmaf(float(code), st[e], lo[e]);
-      const float kh = t + float(r8) * rs[e];
-      const uint32_t bits = bf16_bits_rne(kh);
-      if (e & 1) outw[e / 2] |= bits << 16;
-      else outw[e / 2] = bits;
+      kh[e] = t + float(r8) * rs[e];
     }
+    uint32_t outw[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) outw[p] = pack_bf16x2(kh[2 * p], kh[2 * p + 1]);
     *reinterpret_cast<u32x4*>(khat + row * D + c0) = u32x4{outw[0], outw[1], outw[2], outw[3]};
   }
 }
 
 // One wave per (b, kv head, block); 4 waves per workgroup.
+//
+// The provisional score of token t in block j is the thumbnail dot product
+// split into the block offset and the code term:
+//     s~ = scale * (q . lo_j + sum_c w_c code_t,c),   w_c = bf16(q_c step_j,c)
+// so a tile needs only its codes turned into bf16 0..3 (exact) as the A
+// operand; the weights w are the B operand, built once per block.  The codes
+// become bf16 with one byte permutation per pair: a selector with code c in
+// byte 0 and c + 4 in byte 1 picks the low and high bytes of bf16(c) from two
+// 4-entry tables.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_thumb_scan(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ codes,
@@ -152,59 +159,92 @@ __global__ __launch_bounds__(256) void k_thumb_scan(
     float* __restrict__ bmax, uint8_t* __restrict__ flag) {
   static_assert(G <= 16, "heads are the 16 columns of the score tile");
   constexpr int NST = D / 32;
+  constexpr uint32_t kLutLo = 0x40008000u;   // low bytes of bf16(0), bf16(1), bf16(2), bf16(3)
+  constexpr uint32_t kLutHi = 0x40403f00u;   // their high bytes
   const int nbw = (nb + 3) / 4;
   const int bh = blockIdx.x / nbw;
   const int j = (blockIdx.x % nbw) * 4 + int(threadIdx.x >> 6);
   if (j >= nb) return;                        // no barriers in this kernel
   const int b = bh / Hkv, kh = bh % Hkv;
   const int lane = threadIdx.x & 63, gq = lane >> 4, nn = lane & 15;
+  const int t0 = j * block, nj = min(block, N - t0);
+  const uint8_t* cb = codes + (size_t(bh) * N + t0) * (D / 4);
+  // every tile's codes first (a block is at most 8 tiles; token row 16 u + nn,
+  // rows past the block repeat its last row), then the query and the ranges
+  constexpr int MT = 8;
+  uint32_t cw[MT][NST];
+#pragma unroll
+  for (int u = 0; u < MT; ++u) {
+    const int r = min(16 * u + nn, nj - 1);
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+      cw[u][st] = 16 * u < nj
+          ? *reinterpret_cast<const uint16_t*>(cb + size_t(r) * (D / 4) + 2 * gq + 8 * st) : 0u;
+  }
   u32x4 qb[NST];
   const uint16_t* qp = Q + (size_t(b) * Hq + kh * G + min(nn, G - 1)) * D + 8 * gq;
 #pragma unroll
   for (int st = 0; st < NST; ++st) qb[st] = nn < G ? ld16(qp + 32 * st) : u32x4{0u, 0u, 0u, 0u};
   const float th = nn < G ? tau[size_t(b) * Hq + kh * G + nn] : 0.f;
-  // this lane's channels 8 gq + 32 st + e: their (lo, step) of block j
+  // the block's (lo, step) rows (2 D floats) through this wave's LDS slice:
+  // one 16-byte load per lane instead of one per lane and channel group
+  __shared__ __attribute__((aligned(16))) float sm[4][2 * D];
+  float* mw = sm[threadIdx.x >> 6];
   const float* mrow = meta + (size_t(bh) * nb + j) * 3 * D;
-  float lo[NST][8], sp[NST][8];
+  if (lane < D / 2) *reinterpret_cast<u32x4*>(mw + 4 * lane) = ld16(mrow + 4 * lane);
+  __builtin_amdgcn_wave_barrier();
+  // this lane's channels 8 gq + 32 st + e of head nn: the offset part and the
+  // bf16 weights
+  float off = 0.f;
+  u32x4 wb[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    const u32x4 a0 = ld16(mrow + 8 * gq + 32 * st), a1 = ld16(mrow + 8 * gq + 32 * st + 4);
-    const u32x4 s0 = ld16(mrow + D + 8 * gq + 32 * st), s1 = ld16(mrow + D + 8 * gq + 32 * st + 4);
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(mw + 8 * gq + 32 * st);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(mw + 8 * gq + 32 * st + 4);
+    const u32x4 s0 = *reinterpret_cast<const u32x4*>(mw + D + 8 * gq + 32 * st);
+    const u32x4 s1 = *reinterpret_cast<const u32x4*>(mw + D + 8 * gq + 32 * st + 4);
+    uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lo[st][e] = __uint_as_float(a0[e]); lo[st][4 + e] = __uint_as_float(a1[e]);
-      sp[st][e] = __uint_as_float(s0[e]); sp[st][4 + e] = __uint_as_float(s1[e]);
+    for (int p = 0; p < 4; ++p) {
+      const float qa = bf16lo(qb[st][p]), qc = bf16hi(qb[st][p]);
+      const float la = __uint_as_float(p < 2 ? a0[2 * p] : a1[2 * p - 4]);
+      const float lb = __uint_as_float(p < 2 ? a0[2 * p + 1] : a1[2 * p - 3]);
+      const float sa_ = __uint_as_float(p < 2 ? s0[2 * p] : s1[2 * p - 4]);
+      const float sb = __uint_as_float(p < 2 ? s0[2 * p + 1] : s1[2 * p - 3]);
+      off += qa * la + qc * lb;
+      w[p] = pack_bf16x2(qa * sa_, qc * sb);
     }
+    wb[st] = u32x4{w[0], w[1], w[2], w[3]};
   }
-  const int t0 = j * block, nj = min(block, N - t0);
-  const uint8_t* cb = codes + (size_t(bh) * N + t0) * (D / 4);
+  off += __shfl_xor(off, 16);
+  off += __shfl_xor(off, 32);
   float m = -__builtin_inff();
-  for (int u0 = 0; u0 < nj; u0 += 16) {
-    // token row u0 + nn of the tile; rows past the block repeat its last row
-    const int r = min(u0 + nn, nj - 1);
-    uint32_t cw[NST];
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
-      cw[st] = *reinterpret_cast<const uint16_t*>(cb + size_t(r) * (D / 4) + 2 * gq + 8 * st);
+  for (int u = 0; u < MT; ++u) {
+    if (16 * u >= nj) break;
     f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      uint32_t w[4];
+      // split the 8 codes into even and odd channels, 4 bits apart, then one
+      // selector per channel pair
+      const uint32_t x = cw[u][st];
+      const uint32_t t = (x & 0x3333u) | (((x >> 2) & 0x3333u) << 16);
+      uint32_t a[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float ta = fmaf(float((cw[st] >> (4 * p)) & 3u), sp[st][2 * p], lo[st][2 * p]);
-        const float tb = fmaf(float((cw[st] >> (4 * p + 2)) & 3u), sp[st][2 * p + 1], lo[st][2 * p + 1]);
-        w[p] = bf16_bits_rne(ta) | (bf16_bits_rne(tb) << 16);
+        const uint32_t sel = ((t >> (4 * p)) & 0x00030003u) * 0x0101u + 0x04000400u;
+        a[p] = __builtin_amdgcn_perm(kLutHi, kLutLo, sel);
       }
-      sc = mfma16x16x32(u32x4{w[0], w[1], w[2], w[3]}, qb[st], sc);
+      sc = mfma16x16x32(u32x4{a[0], a[1], a[2], a[3]}, wb[st], sc);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      if (u0 + 4 * gq + rr < nj) m = fmaxf(m, sc[rr] * scale);
+      if (16 * u + 4 * gq + rr < nj) m = fmaxf(m, sc[rr]);
   }
   // lanes nn, nn + 16, nn + 32, nn + 48 hold head nn's rows
   m = fmaxf(m, __shfl_xor(m, 16));
   m = fmaxf(m, __shfl_xor(m, 32));
+  m = scale * (off + m);
   if (bmax && gq == 0 && nn < G) bmax[(size_t(b) * Hq + kh * G + nn) * nb + j] = m;
   const bool win = (j >= f0 && j < f1) || (j >= f2 && j < f3);
   const uint64_t any = __ballot(gq == 0 && nn < G && m >= th - margin);
