@@ -34,9 +34,9 @@ Pages cited (by title, section):
 Where the pages are silent or ambiguous, each function's docstring states the
 reading it takes.
 
-Parity status: every function is pinned by tests/test_oracle.py except
-``mass_oracle`` (O8), whose selection is "parity unpinned" beyond its
-invariants (block masses sum to one; closed form on identical keys).
+Parity status: every function is pinned by tests/test_oracle.py (``mass_oracle``
+(O8) against per-row softmax from scipy and brute-force top-k, besides its
+invariants).
 """
 from .attention import (
     widen, dense, dense_causal_rows, sketch, block_scores, select_topk,

@@ -398,7 +398,6 @@ def mass_oracle(Q: np.ndarray, K: np.ndarray, block: int, k_free: int = 8,
     Attention is Necessary?" (§2.1) at block granularity, with the head average
     of its token-importance distribution and a block-shared support.
     Returns {(b, kh, i): (mass [nb], S_mass ascending)}.
-    Parity unpinned beyond its invariants (see the package docstring).
     """
     B, Hq, L, D = Q.shape
     Hkv = K.shape[1]

@@ -332,7 +332,45 @@ def test_mass_oracle_invariants_and_identical_keys():
         assert sel.tolist() == list(range(1, 1 + min(3, max(i - 1, 0))))
 
 
-# ------------------------------------------------------------------ needles
+@pytest.mark.parametrize("seed", range(3))
+def test_mass_oracle_equals_row_softmax_by_scipy(seed):
+    """Per-row causal softmax from scipy, summed per key block, averaged over
+    the block's rows and the group's heads; top-k of [1, i-1] by brute force
+    over all subsets (largest total mass, ties to the smallest indices)."""
+    rng = np.random.default_rng(600 + seed)
+    B, Hq, Hkv, blk = 1, 4, 2, 6
+    L = int(rng.integers(20, 40))
+    D = 8
+    Q = rng.standard_normal((B, Hq, L, D)) * 1.5
+    K = rng.standard_normal((B, Hkv, L, D))
+    kf = 2
+    res = oracle.mass_oracle(Q, K, blk, k_free=kf)
+    nb = -(-L // blk)
+    for kh in range(Hkv):
+        for i in range(nb):
+            rows = range(i * blk, min((i + 1) * blk, L))
+            want = np.zeros(nb)
+            n = 0
+            for h in (2 * kh, 2 * kh + 1):
+                for t in rows:
+                    s = np.array([Q[0, h, t] @ K[0, kh, u] for u in range(t + 1)]) / math.sqrt(D)
+                    p = softmax(s)
+                    for u in range(t + 1):
+                        want[u // blk] += p[u]
+                    n += 1
+            want /= n
+            mass, sel = res[(0, kh, i)]
+            np.testing.assert_allclose(mass, want, atol=1e-12)
+            cand = list(range(1, i))
+            best = None
+            for sub in itertools.combinations(cand, min(kf, len(cand))):
+                key = (-sum(want[j] for j in sub), list(sub))
+                if best is None or key < best:
+                    best = key
+            assert sel.tolist() == (best[1] if best else [])
+
+
+# ------------------------------------------------------------------ needles# ------------------------------------------------------------------ needles
 @pytest.mark.parametrize("name,over", [
     ("tiny_decode_f32", {}),
     ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2}),
