@@ -95,7 +95,8 @@ enum {
   SA_OP_DECODE_STEP = 3,
   SA_OP_SELECT_TOPDELTA = 4,
   SA_OP_SELECT_PRUNED = 5,
-  SA_OP_SELECT_LOWBIT = 6
+  SA_OP_SELECT_LOWBIT = 6,
+  SA_OP_MASS_SELECT = 7
 };
 
 /*
@@ -334,6 +335,31 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes,
                                     int32_t* count, float* tau, float* bmax,
                                     void* khat, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/*
+ * sa_mass_select -- the attention-mass top-k oracle of [ORACLE] §2.1 on the
+ * GPU, at block granularity with a block-shared support: for query block i
+ * of kv head kh, dense causal softmax for each of its rows and each head of
+ * the group, each row's probability summed over every key block j, averaged
+ * over the rows and heads -> mass[i][j]; the k_free blocks j in [1, i-1] with
+ * the largest mass (ties to the lower j) are listed ascending.  A reference
+ * for the recall of the sketch selector, not a fast path: it runs dense
+ * causal attention, one pass per 128 key blocks (the prefill kernel with V
+ * replaced by one-hot block indicators).
+ *
+ *   Q [B, Hq, L, D], K [B, Hkv, L, D] bf16; D = 128, block = 128
+ *   mass     [B, Hkv, M, M] float32 out (M = ceil(L / 128); entries j > i are
+ *            0), or NULL (kept in ws)
+ *   idx      [B, Hkv, M, k_free] int32 out, ascending (-1 padded)
+ *   count    [B, Hkv, M] int32 out, min(k_free, max(i - 1, 0))
+ *   k_free   1..64
+ * ws: sa_workspace_bytes(SA_OP_MASS_SELECT, B, Hq, Hkv, L, D, block, k_free):
+ *     about L * (Hkv * 256 + Hq * 512) bytes per batch row plus the lists.
+ */
+sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq,
+                         int Hkv, int L, int D, int block, int k_free,
+                         float scale, float* mass, int32_t* idx, int32_t* count,
+                         void* ws, size_t ws_bytes, void* stream);
 
 /*
  * sa_sparse_decode -- exact attention restricted to the selected keys, as

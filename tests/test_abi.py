@@ -33,6 +33,7 @@ def lib():
     L.sa_select_topdelta.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, I, P, P, P, P, P, Z, P]
     L.sa_build_radius.argtypes = [P, I, I, I, I, I, I, I, I, I, P, P, P]
     L.sa_encode_keys.argtypes = [P, I, I, I, I, I, I, I, I, P, P, P, P]
+    L.sa_mass_select.argtypes = [P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, Z, P]
     L.sa_decode_keys.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, I, P, P]
     L.sa_select_topdelta_lowbit.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, F, F, F, I, P, P,
                                             P, P, P, P, Z, P]
@@ -59,8 +60,9 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
               "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_sparse_decode",
-              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
+              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
+              "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step",
+              "sa_workspace_bytes",
               "sa_status_str",
               "sa_last_error", "sa_version"]:
         assert n in names
@@ -256,6 +258,24 @@ def test_lowbit_validation(lib):
     assert sel(*a) == INVALID
 
 
+def test_mass_select_validation(lib):
+    f = lib.sa_mass_select
+    base = [A, A, 1, 1, 32, 4, 65536, 128, 128, 8, 0.0, None, A, A, A, 1 << 40, None]
+
+    def call(i, v):
+        a = list(base)
+        a[i] = v
+        return f(*a)
+
+    assert call(2, 0) == UNSUPPORTED              # fp32
+    assert call(7, 64) == UNSUPPORTED             # D
+    assert call(8, 64) == UNSUPPORTED             # block
+    assert call(9, 0) == INVALID and call(9, 65) == INVALID   # k_free
+    assert call(12, None) == INVALID              # idx
+    assert call(15, 1024) == WORKSPACE
+    assert call(4, 30) == INVALID                 # Hq % Hkv
+
+
 def test_decode_validation(lib):
     f = lib.sa_sparse_decode
     base = [A, A, A, 1, 1, 64, 8, 262144, 128, 0.0, 0, 64, A, A, 82, None, A, 1, A, A, 1 << 30, None]
@@ -330,6 +350,6 @@ def test_binding_binds_every_entry_point():
         assert hasattr(sa, "_" + n[len("sa_"):]), f"no ctypes signature for {n}"
     for n in ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
               "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_sparse_decode",
-              "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
+              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
+              "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
         assert callable(getattr(sa, n)), n

@@ -715,6 +715,51 @@ def test_lowbit_topdelta_parity(name, over):
     print(f"{name} {over}: {cnt_h.mean() / nb:.1%} of blocks kept, max-abs O error {err:.2e}")
 
 
+MASS_TOL = 5e-5
+
+MASS_CASES = [
+    ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 2048, "needles": 4}, None),
+    ("sparse_prefill_bf16", {"Hq": 4, "Hkv": 1, "N": 128 * 130 + 37, "needles": 6},   # 2 chunks
+     [0, 1, 2, 63, 127, 128, 129, 130]),
+]
+
+
+@pytest.mark.parametrize("name,over,qblocks", MASS_CASES)
+def test_mass_select_parity(name, over, qblocks):
+    wl, inp, Q, K, V = _decode_case(name, over)
+    Qd, Kd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16")
+    kf = 8
+    idx, cnt, mass = sa.sa_mass_select(Qd, Kd, kf, want_mass=True)
+    idx_h, cnt_h, mass_h = idx.cpu().numpy(), cnt.cpu().numpy(), mass.cpu().numpy()
+    M = wl.nb
+    res = oracle.mass_oracle(Q, K, wl.block, k_free=kf, qblocks=qblocks)
+    worst = 0.0
+    for (b, kh, i), (m_x, sel_x) in res.items():
+        m_g = mass_h[b, kh, i]
+        worst = max(worst, float(np.abs(m_g[:M] - m_x).max()))
+        # the dense pass takes each probability into the PV product as bf16
+        # hi + lo (about 16 significant bits): <= 2^-16 relative per term
+        assert np.abs(m_g - m_x).max() <= MASS_TOL, (b, kh, i)
+        n = int(cnt_h[b, kh, i])
+        assert n == min(kf, max(i - 1, 0))
+        got = idx_h[b, kh, i, :n]
+        assert np.all(np.diff(got) > 0) and np.all(idx_h[b, kh, i, n:] == -1)
+        if n:
+            cand = np.arange(1, i)
+            order = cand[np.lexsort((cand, -m_x[1:i]))]
+            cut = m_x[order[n - 1]]
+            band = 2 * MASS_TOL
+            must = set(cand[m_x[1:i] > cut + band].tolist())
+            may = set(cand[m_x[1:i] >= cut - band].tolist())
+            assert must <= set(got.tolist()) <= may, (b, kh, i)
+            if not (set(got.tolist()) ^ set(sel_x.tolist())):
+                continue
+            # a differing choice lies inside the tie band
+            for j in set(got.tolist()) ^ set(sel_x.tolist()):
+                assert abs(m_x[j] - cut) <= band, (b, kh, i, j)
+    print(f"{name} {over}: max |mass - oracle| {worst:.2e} over {len(res)} query blocks")
+
+
 PREFILL_CASES = [
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 2048, "needles": 4}),
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 1, "N": 2048 + 77, "needles": 4}),   # ragged

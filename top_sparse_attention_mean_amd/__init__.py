@@ -31,11 +31,12 @@ SA_F32, SA_BF16 = 0, 1
 SA_FORCE_SINK, SA_FORCE_LOCAL, SA_CAUSAL = 1, 2, 4
 SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
 (SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP,
- SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED, SA_OP_SELECT_LOWBIT) = range(7)
+ SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED, SA_OP_SELECT_LOWBIT, SA_OP_MASS_SELECT) = range(8)
 
 EXPORTS = ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
            "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-           "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_sparse_decode",
+           "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
+           "sa_sparse_decode",
            "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
            "sa_status_str",
            "sa_last_error", "sa_version"]
@@ -67,6 +68,8 @@ _decode_keys = _sig("sa_decode_keys", _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P
                     _P)
 _select_topdelta_lowbit = _sig("sa_select_topdelta_lowbit", _I, _P, _P, _P, _P, _I, _I, _I, _I,
                                _I, _I, _I, _I, _F, _F, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P)
+_mass_select = _sig("sa_mass_select", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
+                    _P, _Z, _P)
 _select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                         _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _sparse_decode = _sig("sa_sparse_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
@@ -357,6 +360,31 @@ def sa_select_topdelta_lowbit(Q: torch.Tensor, codes: torch.Tensor, resid: torch
                                    _ptr(count), _ptr(tau), _ptr(bmax), _ptr(khat), _ptr(ws),
                                    ws.numel(), _stream(stream)), "sa_select_topdelta_lowbit")
     return idx, count, tau, bmax, khat
+
+
+def sa_mass_select(Q: torch.Tensor, K: torch.Tensor, k_free: int, block: int = 128,
+                   scale: float = 0.0, want_mass: bool = False, idx=None, count=None, ws=None,
+                   stream=None):
+    """Attention-mass top-k per (b, kv head, query block) from dense causal
+    attention: idx [B, Hkv, M, k_free] ascending, count [B, Hkv, M] and, when
+    asked, mass [B, Hkv, M, M]."""
+    _dev(Q, K, idx, count)
+    B, Hq, L, D = Q.shape
+    Hkv = K.shape[1]
+    M = -(-L // block)
+    dev = Q.device
+    if idx is None:
+        idx = torch.empty(B, Hkv, M, k_free, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, M, dtype=torch.int32, device=dev)
+    mass = torch.empty(B, Hkv, M, M, dtype=torch.float32, device=dev) if want_mass else None
+    need = workspace_bytes(SA_OP_MASS_SELECT, B, Hq, Hkv, L, D, block, k_free)
+    if ws is None:
+        ws = workspace(need, dev, ("mass", B, Hq, Hkv, L, D, block))
+    _check(_mass_select(_ptr(Q), _ptr(K), _dt(Q), B, Hq, Hkv, L, D, block, k_free, scale,
+                        _ptr(mass), _ptr(idx), _ptr(count), _ptr(ws), ws.numel(),
+                        _stream(stream)), "sa_mass_select")
+    return idx, count, mass
 
 
 def sa_select_topdelta(Q: torch.Tensor, K: torch.Tensor, sink: int, local: int, delta: float,

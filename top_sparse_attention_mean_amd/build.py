@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libsa.so")
 
 SOURCES = ["sa_api.hip", "k_sketch.hip", "k_select.hip", "k_decode.hip",
            "k_threshold.hip", "k_prune.hip", "k_lowbit.hip",
-           "k_prefill.hip"]
+           "k_mass.hip", "k_prefill.hip"]
 
 ARCH = "gfx950"
 CFLAGS = [

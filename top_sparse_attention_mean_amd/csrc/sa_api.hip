@@ -199,6 +199,9 @@ size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int bloc
       return topdelta_ws_bytes(B, Hq, N);
     case SA_OP_SELECT_PRUNED:
       return pruned_ws_bytes(B, Hq, Hkv, N);
+    case SA_OP_MASS_SELECT:          // N = L, block = the block size
+      if (block < 1) return SIZE_MAX;
+      return mass_ws(B, Hq, Hkv, N, block).bytes;
     case SA_OP_SELECT_LOWBIT:        // block = the block size
       if (block < 1) return SIZE_MAX;
       return lowbit_ws_bytes(B, Hq, Hkv, N, block);
@@ -474,6 +477,32 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes, const i
   return hip_status(launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, idx, count, kcap,
                                        0, 0, kh, st),
                     "sa_select_topdelta_lowbit (refined keys)");
+}
+
+sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv, int L,
+                         int D, int block, int k_free, float scale, float* mass, int32_t* idx,
+                         int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+  PTR(Q);
+  PTR(K);
+  PTR(idx);
+  PTR(count);
+  if (mass) PTR(mass);
+  REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  SUP(dtype == SA_BF16, "the dense pass runs on bf16 matrix cores: dtype must be SA_BF16");
+  SUP(D == 128, "the mass selector supports D = 128");
+  SUP(block == 128, "the mass selector supports 128-token blocks");
+  REQ(L >= 1, "L must be >= 1");
+  REQ(k_free >= 1 && k_free <= 64, "k_free must be in [1, 64] (got %d)", k_free);
+  const long units = long(B) * Hkv * cdiv(L, block);
+  REQ(cdiv(units, 8) * 8L * (Hq / Hkv) < (1L << 31), "grid too large");
+  const MassWs w = mass_ws(B, Hq, Hkv, L, block);
+  if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);
+  PTR(ws);
+  return hip_status(launch_mass_select(Q, K, B, Hq, Hkv, L, D, eff_scale(scale, D), block, k_free,
+                                       mass, idx, count, w, ws, static_cast<hipStream_t>(stream)),
+                    "sa_mass_select");
 }
 
 sa_status sa_sparse_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,

@@ -140,6 +140,23 @@ inline size_t topdelta_ws_bytes(int B, int Hq, int N) {
 inline size_t lowbit_ws_bytes(int B, int Hq, int Hkv, int N, int block) {
   return align256(size_t(B) * Hkv * cdiv(N, block)) + align256(size_t(B) * Hq * sizeof(float));
 }
+// The attention-mass selector: one-hot V [B, Hkv, L, 128] bf16, the dense
+// pass's output [B, Hq, L, 128] f32, the dense causal block lists [B, Hkv, M, M]
+// and counts, and the masses [B, Hkv, M, M] f32 (unless the caller takes them).
+struct MassWs {
+  size_t v_off, o_off, list_off, lcnt_off, mass_off, bytes;
+};
+inline MassWs mass_ws(int B, int Hq, int Hkv, int L, int block) {
+  MassWs w{};
+  const size_t M = size_t(cdiv(L, block));
+  w.v_off = 0;
+  w.o_off = align256(size_t(B) * Hkv * L * 128 * 2);
+  w.list_off = w.o_off + align256(size_t(B) * Hq * L * 128 * 4);
+  w.lcnt_off = w.list_off + align256(size_t(B) * Hkv * M * M * 4);
+  w.mass_off = w.lcnt_off + align256(size_t(B) * Hkv * M * 4);
+  w.bytes = w.mass_off + align256(size_t(B) * Hkv * M * M * 4);
+  return w;
+}
 // The sphere-pruned threshold adds one live flag per (b, kv head, segment).
 inline size_t pruned_ws_bytes(int B, int Hq, int Hkv, int N) {
   const ThrWs w = threshold_ws(B, Hq, N);
@@ -209,6 +226,10 @@ hipError_t launch_thumb_scan(const uint16_t* Q, const uint8_t* codes,
                              float* bmax, uint8_t* flag, hipStream_t st);
 hipError_t launch_block_list(const uint8_t* flag, int BH, int nb, int kcap,
                              int32_t* idx, int32_t* count, hipStream_t st);
+hipError_t launch_mass_select(const void* Q, const void* K, int B, int Hq, int Hkv,
+                              int L, int D, float scale, int block, int kfree,
+                              float* mass, int32_t* idx, int32_t* count,
+                              const MassWs& w, void* ws, hipStream_t st);
 hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D,
                          int block, int S, int b0, int b1, const float* sketch,
                          float* radius, hipStream_t st);
