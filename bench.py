@@ -654,6 +654,75 @@ def bench_prefill(args) -> dict:
     return res
 
 
+def bench_mass(args) -> dict:
+    """The attention-mass selector at the prefill size (dense causal attention,
+    one pass per 128 key blocks) and the recall of the sketch selector against
+    it over every query block."""
+    import numpy as np
+    import torch
+    import oracle
+    import top_sparse_attention_mean_amd as sa
+    from oracle.attention import widen
+    from tests.parity_util import to_dev
+    from workloads import get_workload, make_inputs
+    wl = get_workload("sparse_prefill_bf16")
+    dev = torch.device("cuda:0")
+    inp = make_inputs(wl)
+    Qd, Kd = (to_dev(x, wl.dtype, dev) for x in (inp.Q, inp.K))
+    B, Hq, Hkv, D, L, blk = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N, wl.block
+    M, kf = wl.nb, wl.k - 2
+    flags = sa.SA_FORCE_SINK | sa.SA_FORCE_LOCAL | sa.SA_CAUSAL
+    sk = sa.sa_build_sketch(Kd, blk)
+    sidx, scnt, _ = sa.sa_select_topk(Qd, sk, wl.k, flags=flags, q_block=blk)
+    midx = torch.empty(B, Hkv, M, kf, dtype=torch.int32, device=dev)
+    mcnt = torch.empty(B, Hkv, M, dtype=torch.int32, device=dev)
+    mws = torch.zeros(sa.workspace_bytes(sa.SA_OP_MASS_SELECT, B, Hq, Hkv, L, D, blk, kf),
+                      dtype=torch.uint8, device=dev)
+
+    def run(r):
+        sa.sa_mass_select(Qd, Kd, kf, block=blk, idx=midx, count=mcnt, ws=mws)
+
+    n = 3
+    t_mass = graph_time(run, 1, n, warmup=1)
+    si, sc = sidx.cpu().numpy(), scnt.cpu().numpy()
+    mi, mc = midx.cpu().numpy(), mcnt.cpu().numpy()
+    rec = []
+    for b in range(B):
+        for kh in range(Hkv):
+            for i in range(2, M):
+                want = set(mi[b, kh, i, :mc[b, kh, i]].tolist())
+                got = set(si[b, kh, i, :sc[b, kh, i]].tolist()) - {0, i}
+                rec.append(len(want & got) / len(want))
+    tiles = B * Hkv * M * (M + 1) // 2 * (Hq // Hkv)
+    passes = -(-M // 128)
+    flops = passes * tiles * 4.0 * blk * blk * D
+    tflops = flops / (t_mass * 1e-6) / 1e12
+    res = {
+        "workload": wl.name, "us_per_call": round(t_mass, 1), "k_free": kf,
+        "dense_passes": passes,
+        "sketch_recall_of_mass_topk": round(float(np.mean(rec)), 4),
+        "query_blocks": len(rec),
+        "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 over every earlier block, V = "
+                     "one-hot block indicators (the call also builds V, reduces and selects)",
+                     "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 4), "traffic": None,
+                     "flops_per_call": flops, "avg_us": round(t_mass, 1)},
+    }
+    if not args.no_cpu:
+        Q, K = (widen(x, wl.dtype) for x in (inp.Q, inp.K))
+        qb = [M - 4, M - 3, M - 2, M - 1]
+        t0 = time.perf_counter()
+        oracle.mass_oracle(Q, K, blk, k_free=kf, qblocks=qb)
+        t_cpu = time.perf_counter() - t0
+        work = sum(i + 1 for i in qb) / (M * (M + 1) / 2)
+        res["cpu_baseline"] = {"value": round(t_cpu / work * 1e6, 1), "unit": "us/call",
+                               "cores": _blas_threads(), "kind": "oracle",
+                               "sample": f"the last 4 query blocks of each kv head timed "
+                                         f"({t_cpu:.1f} s) and scaled by their share of the "
+                                         f"causal work ({work:.4f})"}
+    return res
+
+
 def pmc_run(args) -> dict:
     """Short run for rocprofv3 counter passes: a plain device copy of known size
     (the counters' calibration) and the dominant kernel on every layer copy."""
@@ -691,7 +760,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the threshold, top-delta, pruned, low-bit and prefill variant "
                     "measurements")
-    ap.add_argument("--variant", choices=["threshold", "topdelta", "pruned", "lowbit", "prefill"],
+    ap.add_argument("--variant",
+                    choices=["threshold", "topdelta", "pruned", "lowbit", "prefill", "mass"],
                     help="run only this variant measurement and print its JSON")
     ap.add_argument("--pmc-run", action="store_true",
                     help="short run for rocprofv3 counter passes (no timing output)")
@@ -706,6 +776,7 @@ def main(argv=None) -> int:
         res = pmc_run(args)
     elif args.variant:
         res = (bench_prefill(args) if args.variant == "prefill" else
+               bench_mass(args) if args.variant == "mass" else
                bench_pruned(args) if args.variant == "pruned" else
                bench_lowbit(args) if args.variant == "lowbit" else
                bench_threshold(args, args.variant))

@@ -26,7 +26,7 @@
 //   A-operand layout of v_mfma_f32_16x16x16_bf16 for P V.  V rows are loaded as
 //   row vectors and transposed in registers with v_perm_b32 so the value
 //   columns land in the B operand (column d = (D/16)*n + e of MFMA e).  P is
-//   split exactly as p = hi + lo (two bf16) and the lo part fills the padding
+//   split as p ~ hi + lo (two bf16) and the lo part fills the padding
 //   rows g..2g-1 of the 16-row tile, so the value product is accurate to about
 //   2^-17 relative with float32 accumulation.  Workgroup id % (B*Hkv) selects
 //   the (b, kv head): all splits of one kv head share an XCD and its L2.

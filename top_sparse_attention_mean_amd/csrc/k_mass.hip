@@ -11,8 +11,9 @@
 // The dense pass reuses the block-sparse prefill kernel with every earlier
 // block listed: with V replaced by one-hot block indicators (row t of V has a
 // 1 in column j - 128 c when token t lies in key block j of chunk c), the
-// attention output of row t is exactly its softmax mass per key block, and the
-// kernel's split of P into bf16 hi + lo keeps it float32-accurate.  128 blocks
+// attention output of row t is its softmax mass per key block; the kernel
+// takes each probability as bf16 hi + lo (about 16 significant bits, so a mass
+// is off by at most 2^-17 of itself plus float32 rounding).  128 blocks
 // fit in the 128 columns of one pass; longer sequences take one pass per
 // chunk of 128 blocks.
 //
