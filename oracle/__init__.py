@@ -45,7 +45,7 @@ from .attention import (
     prefill_attend_rows, prefill_attend, mass_oracle, decode_step,
     window_tokens, pseudo_max, select_topdelta, subspaces, subspace_radius,
     block_upper_bound, select_threshold_pruned, lowbit_encode, lowbit_thumbnail,
-    lowbit_reconstruct, bf16_round, select_topdelta_lowbit,
+    lowbit_reconstruct, bf16_round, select_topdelta_lowbit, mass_oracle_rows,
 )
 
 __all__ = [
@@ -56,4 +56,5 @@ __all__ = [
     "decode_step", "window_tokens", "pseudo_max", "select_topdelta", "subspaces",
     "subspace_radius", "block_upper_bound", "select_threshold_pruned", "lowbit_encode",
     "lowbit_thumbnail", "lowbit_reconstruct", "bf16_round", "select_topdelta_lowbit",
+    "mass_oracle_rows",
 ]

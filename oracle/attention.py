@@ -715,3 +715,42 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
             idx[b, kh, :sel.size] = sel
             count[b, kh] = sel.size
     return idx, count, tau, bmax
+
+
+def mass_oracle_rows(Q: np.ndarray, K: np.ndarray, block: int, k_free: int = 8,
+                     scale: Optional[float] = None, rows: Optional[Iterable[int]] = None):
+    """O8 with a per-query support (b_sel = 1): row t of kv head kh ranks the
+    key blocks by its own attention mass, averaged over the group's heads,
+    and keeps the k_free largest of blocks [1, i - 1], i = t // block (ties
+    to the lower block); the sink block 0 and the row's own block are the
+    forced ones, as in the block-shared rule.  "How Much Dense Attention is
+    Necessary?" (§2.1) compares this per-query support with supports shared
+    by b_sel consecutive queries.
+    Returns {(b, kh, t): (mass [nb], S ascending)}.
+    """
+    B, Hq, L, D = Q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    nb = -(-L // block)
+    sc = _default_scale(D, scale)
+    rows = range(L) if rows is None else rows
+    out = {}
+    for b in range(B):
+        for kh in range(Hkv):
+            for t in rows:
+                mass = np.zeros(nb)
+                for h in range(kh * g, (kh + 1) * g):
+                    s = (K[b, kh, :t + 1] @ Q[b, h, t]) * sc
+                    p = np.exp(s - s.max())
+                    p /= p.sum()
+                    for j in range(t // block + 1):
+                        mass[j] += p[j * block:min((j + 1) * block, t + 1)].sum()
+                mass /= g
+                i = t // block
+                if i >= 2:
+                    cand = np.arange(1, i)
+                    sel = np.sort(cand[np.lexsort((cand, -mass[1:i]))][:min(k_free, i - 1)])
+                else:
+                    sel = np.zeros(0, dtype=np.int64)
+                out[(b, kh, t)] = (mass, sel)
+    return out

@@ -370,7 +370,36 @@ def test_mass_oracle_equals_row_softmax_by_scipy(seed):
             assert sel.tolist() == (best[1] if best else [])
 
 
-# ------------------------------------------------------------------ needles# ------------------------------------------------------------------ needles
+def test_mass_oracle_rows_by_scipy_and_block_average():
+    """Per-row masses from scipy's softmax (head-averaged); their mean over a
+    block's rows is the block-shared mass of mass_oracle."""
+    rng = np.random.default_rng(610)
+    B, Hq, Hkv, blk, L, D = 1, 4, 2, 5, 23, 8
+    Q = rng.standard_normal((B, Hq, L, D)) * 1.5
+    K = rng.standard_normal((B, Hkv, L, D))
+    res = oracle.mass_oracle_rows(Q, K, blk, k_free=2)
+    shared = oracle.mass_oracle(Q, K, blk, k_free=2)
+    nb = -(-L // blk)
+    for kh in range(Hkv):
+        for t in range(L):
+            want = np.zeros(nb)
+            for h in (2 * kh, 2 * kh + 1):
+                p = softmax(np.array([Q[0, h, t] @ K[0, kh, u] for u in range(t + 1)]) / math.sqrt(D))
+                for u in range(t + 1):
+                    want[u // blk] += p[u] / 2
+            mass, sel = res[(0, kh, t)]
+            np.testing.assert_allclose(mass, want, atol=1e-12)
+            i = t // blk
+            cand = list(range(1, i))
+            top = sorted(sorted(cand, key=lambda j: (-want[j], j))[:min(2, len(cand))])
+            assert sel.tolist() == top
+        for i in range(nb):
+            rows = range(i * blk, min((i + 1) * blk, L))
+            avg = np.mean([res[(0, kh, t)][0] for t in rows], axis=0)
+            np.testing.assert_allclose(avg, shared[(0, kh, i)][0], atol=1e-12)
+
+
+# ------------------------------------------------------------------ needles# ------------------------------------------------------------------ needles# ------------------------------------------------------------------ needles
 @pytest.mark.parametrize("name,over", [
     ("tiny_decode_f32", {}),
     ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2}),
