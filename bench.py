@@ -684,6 +684,21 @@ def bench_mass(args) -> dict:
 
     n = 3
     t_mass = graph_time(run, 1, n, warmup=1)
+    # per-query supports once, eagerly: how much of each row's own top-k the
+    # block-shared top-k of its query block holds (b_sel = 1 against 128)
+    _, _, _, rows = sa.sa_mass_select(Qd, Kd, kf, block=blk, per_row=True, ws=mws)
+    torch.cuda.synchronize()
+    ri, rc = rows[0].cpu().numpy(), rows[1].cpu().numpy()
+    del rows
+    mi_all = midx.cpu().numpy()
+    shared = []
+    for b in range(B):
+        for kh in range(Hkv):
+            for t in range(2 * blk, L, 7):
+                n_r = int(rc[b, kh, t])
+                own = set(ri[b, kh, t, :n_r].tolist())
+                blk_sel = set(mi_all[b, kh, t // blk].tolist()) - {-1}
+                shared.append(len(own & blk_sel) / n_r)
     si, sc = sidx.cpu().numpy(), scnt.cpu().numpy()
     mi, mc = midx.cpu().numpy(), mcnt.cpu().numpy()
     rec = []
@@ -701,6 +716,7 @@ def bench_mass(args) -> dict:
         "workload": wl.name, "us_per_call": round(t_mass, 1), "k_free": kf,
         "dense_passes": passes,
         "sketch_recall_of_mass_topk": round(float(np.mean(rec)), 4),
+        "per_row_topk_held_by_block_shared_topk": round(float(np.mean(shared)), 4),
         "query_blocks": len(rec),
         "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 over every earlier block, V = "
                      "one-hot block indicators (the call also builds V, reduces and selects)",

@@ -352,6 +352,11 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes,
  *            0), or NULL (kept in ws)
  *   idx      [B, Hkv, M, k_free] int32 out, ascending (-1 padded)
  *   count    [B, Hkv, M] int32 out, min(k_free, max(i - 1, 0))
+ *   row_mass, row_idx, row_count  per-query supports (b_sel = 1), all three or
+ *            none (NULL): row_mass [B, Hkv, L, M] float32 out, each row's own
+ *            masses averaged over the group's heads; row_idx [B, Hkv, L, k_free]
+ *            its k_free largest of blocks [1, i - 1], i = t / 128, ascending;
+ *            row_count [B, Hkv, L]
  *   k_free   1..64
  * ws: sa_workspace_bytes(SA_OP_MASS_SELECT, B, Hq, Hkv, L, D, block, k_free):
  *     about L * (Hkv * 256 + Hq * 512) bytes per batch row plus the lists.
@@ -359,6 +364,7 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes,
 sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq,
                          int Hkv, int L, int D, int block, int k_free,
                          float scale, float* mass, int32_t* idx, int32_t* count,
+                         float* row_mass, int32_t* row_idx, int32_t* row_count,
                          void* ws, size_t ws_bytes, void* stream);
 
 /*

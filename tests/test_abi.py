@@ -33,7 +33,7 @@ def lib():
     L.sa_select_topdelta.argtypes = [P, P, I, I, I, I, I, I, I, I, F, F, I, P, P, P, P, P, Z, P]
     L.sa_build_radius.argtypes = [P, I, I, I, I, I, I, I, I, I, P, P, P]
     L.sa_encode_keys.argtypes = [P, I, I, I, I, I, I, I, I, P, P, P, P]
-    L.sa_mass_select.argtypes = [P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, Z, P]
+    L.sa_mass_select.argtypes = [P, P, I, I, I, I, I, I, I, I, F, P, P, P, P, P, P, P, Z, P]
     L.sa_decode_keys.argtypes = [P, P, P, I, I, I, I, I, P, P, I, I, I, P, P]
     L.sa_select_topdelta_lowbit.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, F, F, F, I, P, P,
                                             P, P, P, P, Z, P]
@@ -260,7 +260,8 @@ def test_lowbit_validation(lib):
 
 def test_mass_select_validation(lib):
     f = lib.sa_mass_select
-    base = [A, A, 1, 1, 32, 4, 65536, 128, 128, 8, 0.0, None, A, A, A, 1 << 40, None]
+    base = [A, A, 1, 1, 32, 4, 65536, 128, 128, 8, 0.0, None, A, A, None, None, None, A, 1 << 40,
+            None]
 
     def call(i, v):
         a = list(base)
@@ -272,8 +273,9 @@ def test_mass_select_validation(lib):
     assert call(8, 64) == UNSUPPORTED             # block
     assert call(9, 0) == INVALID and call(9, 65) == INVALID   # k_free
     assert call(12, None) == INVALID              # idx
-    assert call(15, 1024) == WORKSPACE
+    assert call(18, 1024) == WORKSPACE
     assert call(4, 30) == INVALID                 # Hq % Hkv
+    assert call(15, A) == INVALID                 # row_idx without row_mass / row_count
 
 
 def test_decode_validation(lib):

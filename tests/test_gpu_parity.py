@@ -729,7 +729,7 @@ def test_mass_select_parity(name, over, qblocks):
     wl, inp, Q, K, V = _decode_case(name, over)
     Qd, Kd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16")
     kf = 8
-    idx, cnt, mass = sa.sa_mass_select(Qd, Kd, kf, want_mass=True)
+    idx, cnt, mass, rows = sa.sa_mass_select(Qd, Kd, kf, want_mass=True, per_row=True)
     idx_h, cnt_h, mass_h = idx.cpu().numpy(), cnt.cpu().numpy(), mass.cpu().numpy()
     M = wl.nb
     res = oracle.mass_oracle(Q, K, wl.block, k_free=kf, qblocks=qblocks)
@@ -738,7 +738,8 @@ def test_mass_select_parity(name, over, qblocks):
         m_g = mass_h[b, kh, i]
         worst = max(worst, float(np.abs(m_g[:M] - m_x).max()))
         # the dense pass takes each probability into the PV product as bf16
-        # hi + lo (about 16 significant bits): <= 2^-16 relative per term
+        # hi + lo (about 16 significant bits): <= 2^-17 of each mass, plus
+        # float32 rounding of the scores and sums
         assert np.abs(m_g - m_x).max() <= MASS_TOL, (b, kh, i)
         n = int(cnt_h[b, kh, i])
         assert n == min(kf, max(i - 1, 0))
@@ -757,7 +758,27 @@ def test_mass_select_parity(name, over, qblocks):
             # a differing choice lies inside the tie band
             for j in set(got.tolist()) ^ set(sel_x.tolist()):
                 assert abs(m_x[j] - cut) <= band, (b, kh, i, j)
-    print(f"{name} {over}: max |mass - oracle| {worst:.2e} over {len(res)} query blocks")
+    # per-query supports on sampled rows (block edges included)
+    ri, rc, rm = (t.cpu().numpy() for t in rows)
+    L, blk = wl.N, wl.block
+    sample = sorted({0, 1, blk - 1, blk, 2 * blk + 5, 3 * blk - 1, L // 2, L - blk - 1, L - 1}
+                    | set(np.random.default_rng(3).integers(0, L, 8).tolist()))
+    rres = oracle.mass_oracle_rows(Q, K, blk, k_free=kf, rows=sample)
+    rworst = 0.0
+    for (b, kh, t), (m_x, sel_x) in rres.items():
+        rworst = max(rworst, float(np.abs(rm[b, kh, t] - m_x).max()))
+        assert np.abs(rm[b, kh, t] - m_x).max() <= MASS_TOL, (b, kh, t)
+        i = t // blk
+        n = int(rc[b, kh, t])
+        assert n == min(kf, max(i - 1, 0))
+        got = ri[b, kh, t, :n]
+        assert np.all(np.diff(got) > 0) and np.all(ri[b, kh, t, n:] == -1)
+        for j in set(got.tolist()) ^ set(sel_x.tolist()):
+            cand = np.arange(1, i)
+            cut = np.sort(m_x[1:i])[::-1][n - 1]
+            assert abs(m_x[j] - cut) <= 2 * MASS_TOL, (b, kh, t, j)
+    print(f"{name} {over}: max |mass - oracle| {worst:.2e} over {len(res)} query blocks, "
+          f"per-row {rworst:.2e} over {len(rres)} rows")
 
 
 PREFILL_CASES = [

@@ -69,7 +69,7 @@ _decode_keys = _sig("sa_decode_keys", _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P
 _select_topdelta_lowbit = _sig("sa_select_topdelta_lowbit", _I, _P, _P, _P, _P, _I, _I, _I, _I,
                                _I, _I, _I, _I, _F, _F, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P)
 _mass_select = _sig("sa_mass_select", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
-                    _P, _Z, _P)
+                    _P, _P, _P, _P, _Z, _P)
 _select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                         _F, _I, _P, _P, _P, _P, _P, _Z, _P)
 _sparse_decode = _sig("sa_sparse_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _I,
@@ -363,11 +363,13 @@ def sa_select_topdelta_lowbit(Q: torch.Tensor, codes: torch.Tensor, resid: torch
 
 
 def sa_mass_select(Q: torch.Tensor, K: torch.Tensor, k_free: int, block: int = 128,
-                   scale: float = 0.0, want_mass: bool = False, idx=None, count=None, ws=None,
-                   stream=None):
+                   scale: float = 0.0, want_mass: bool = False, per_row: bool = False,
+                   idx=None, count=None, ws=None, stream=None):
     """Attention-mass top-k per (b, kv head, query block) from dense causal
-    attention: idx [B, Hkv, M, k_free] ascending, count [B, Hkv, M] and, when
-    asked, mass [B, Hkv, M, M]."""
+    attention: idx [B, Hkv, M, k_free] ascending, count [B, Hkv, M], mass
+    [B, Hkv, M, M] when asked, and with per_row the per-query supports
+    (row_idx [B, Hkv, L, k_free], row_count [B, Hkv, L], row_mass [B, Hkv, L, M]);
+    returns (idx, count, mass, rows) with rows = (row_idx, row_count, row_mass) or None."""
     _dev(Q, K, idx, count)
     B, Hq, L, D = Q.shape
     Hkv = K.shape[1]
@@ -378,13 +380,19 @@ def sa_mass_select(Q: torch.Tensor, K: torch.Tensor, k_free: int, block: int = 1
     if count is None:
         count = torch.empty(B, Hkv, M, dtype=torch.int32, device=dev)
     mass = torch.empty(B, Hkv, M, M, dtype=torch.float32, device=dev) if want_mass else None
+    rows = None
+    if per_row:
+        rows = (torch.empty(B, Hkv, L, k_free, dtype=torch.int32, device=dev),
+                torch.empty(B, Hkv, L, dtype=torch.int32, device=dev),
+                torch.empty(B, Hkv, L, M, dtype=torch.float32, device=dev))
+    ri, rc, rm = rows if rows else (None, None, None)
     need = workspace_bytes(SA_OP_MASS_SELECT, B, Hq, Hkv, L, D, block, k_free)
     if ws is None:
         ws = workspace(need, dev, ("mass", B, Hq, Hkv, L, D, block))
     _check(_mass_select(_ptr(Q), _ptr(K), _dt(Q), B, Hq, Hkv, L, D, block, k_free, scale,
-                        _ptr(mass), _ptr(idx), _ptr(count), _ptr(ws), ws.numel(),
-                        _stream(stream)), "sa_mass_select")
-    return idx, count, mass
+                        _ptr(mass), _ptr(idx), _ptr(count), _ptr(rm), _ptr(ri), _ptr(rc),
+                        _ptr(ws), ws.numel(), _stream(stream)), "sa_mass_select")
+    return idx, count, mass, rows
 
 
 def sa_select_topdelta(Q: torch.Tensor, K: torch.Tensor, sink: int, local: int, delta: float,

@@ -11,9 +11,10 @@
 // The dense pass reuses the block-sparse prefill kernel with every earlier
 // block listed: with V replaced by one-hot block indicators (row t of V has a
 // 1 in column j - 128 c when token t lies in key block j of chunk c), the
-// attention output of row t is its softmax mass per key block; the kernel
-// takes each probability as bf16 hi + lo (about 16 significant bits, so a mass
-// is off by at most 2^-17 of itself plus float32 rounding).  128 blocks
+// attention output of row t is its softmax mass per key block.  The kernel is
+// asked to take every probability as bf16 hi + lo (about 16 significant bits,
+// so a mass is off by at most 2^-17 of itself plus float32 rounding; the plain
+// bf16 P of the sparse prefill would allow 2^-9).  128 blocks
 // fit in the 128 columns of one pass; longer sequences take one pass per
 // chunk of 128 blocks.
 //
@@ -23,6 +24,8 @@
 //                  columns summed over the block's rows and the group's heads
 //   k_mass_select  one workgroup per (b, kv head, query block): the k largest
 //                  masses of blocks 1..i-1 (ties to the lower block), ascending
+//   k_row_mass     per-query supports (b_sel = 1): each row's own masses,
+//                  averaged over the group's heads, then k_mass_select per row
 #include "sa_device.h"
 #include "sa_internal.h"
 
@@ -79,12 +82,15 @@ __global__ __launch_bounds__(256) void k_mass_reduce(const float* __restrict__ O
 // The k largest masses among blocks 1..i-1, ties to the lower block index,
 // listed ascending.  Masses are >= 0, so their float bits order them; the key
 // (bits << 32 | ~j) makes the lower j win a tie.
+// Per query block (rows of [B, Hkv, M] mass rows, i = r % M) or per query
+// row (rows of [B, Hkv, L], i = (r % L) / block when L > 0).
 __global__ __launch_bounds__(256) void k_mass_select(const float* __restrict__ mass, int M,
-                                                     int k, int32_t* __restrict__ idx,
+                                                     int k, int L, int block,
+                                                     int32_t* __restrict__ idx,
                                                      int32_t* __restrict__ count) {
   __shared__ uint64_t wbest[4];
   __shared__ int chosen[64];
-  const int r = blockIdx.x, i = r % M;
+  const int r = blockIdx.x, i = L > 0 ? (r % L) / block : r % M;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* mrow = mass + size_t(r) * M;
   const int n = min(k, max(i - 1, 0));
@@ -125,9 +131,28 @@ __global__ __launch_bounds__(256) void k_mass_select(const float* __restrict__ m
   for (int q = tid; q < k; q += 256) idx[size_t(r) * k + q] = q < n ? chosen[q] : -1;
 }
 
+// row_mass[b, kh, t, 128 c + col] = mean over the group's heads of O[b, h, t, col]
+// (0 for blocks after the row's own).
+__global__ __launch_bounds__(256) void k_row_mass(const float* __restrict__ O, int Hq, int Hkv,
+                                                  int L, int block, int M, int c, long rows,
+                                                  float* __restrict__ row_mass) {
+  const long o = long(blockIdx.x) * 256 + threadIdx.x;   // (b, kv head, t, col)
+  const long bt = o >> 7;                                // row of [B, Hkv, L]
+  if (bt >= rows) return;
+  const int col = int(o & 127);
+  const int t = int(bt % L);
+  const int bh = int(bt / L), b = bh / Hkv, kh = bh % Hkv, G = Hq / Hkv;
+  const int j = 128 * c + col;
+  if (j >= M) return;
+  float acc = 0.f;
+  for (int h = kh * G; h < (kh + 1) * G; ++h) acc += O[((size_t(b) * Hq + h) * L + t) * 128 + col];
+  row_mass[(size_t(bh) * L + t) * M + j] = j <= t / block ? acc / float(G) : 0.f;
+}
+
 hipError_t launch_mass_select(const void* Q, const void* K, int B, int Hq, int Hkv, int L, int D,
                               float scale, int block, int kfree, float* mass, int32_t* idx,
-                              int32_t* count, const MassWs& w, void* ws, hipStream_t st) {
+                              int32_t* count, float* row_mass, int32_t* row_idx,
+                              int32_t* row_count, const MassWs& w, void* ws, hipStream_t st) {
   char* base = static_cast<char*>(ws);
   uint16_t* v1 = reinterpret_cast<uint16_t*>(base + w.v_off);
   float* O = reinterpret_cast<float*>(base + w.o_off);
@@ -144,13 +169,24 @@ hipError_t launch_mass_select(const void* Q, const void* K, int B, int Hq, int H
     k_onehot_v<<<dim3(unsigned(cdiv(vrows * 16, 256))), 256, 0, st>>>(L, block, c, vrows, v1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     e = launch_prefill(Q, K, v1, B, Hq, Hkv, L, D, scale, block, lst, lcnt, M, O, SA_F32,
-                       nullptr, st);
+                       nullptr, st, true);
     if (e != hipSuccess) return e;
     k_mass_reduce<<<dim3(unsigned(lrows)), 256, 0, st>>>(O, Hq, Hkv, L, block, M, c, ms);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (row_mass) {
+      k_row_mass<<<dim3(unsigned(cdiv(vrows * 128, 256))), 256, 0, st>>>(O, Hq, Hkv, L, block, M,
+                                                                         c, vrows, row_mass);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
-  k_mass_select<<<dim3(unsigned(lrows)), 256, 0, st>>>(ms, M, kfree, idx, count);
-  return hipGetLastError();
+  k_mass_select<<<dim3(unsigned(lrows)), 256, 0, st>>>(ms, M, kfree, 0, block, idx, count);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (row_mass) {
+    k_mass_select<<<dim3(unsigned(vrows)), 256, 0, st>>>(row_mass, M, kfree, L, block, row_idx,
+                                                          row_count);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace sa

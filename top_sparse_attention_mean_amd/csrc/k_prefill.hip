@@ -19,7 +19,8 @@
 // lane-local apart from one exchange with the lane 32 apart.  The score tile's
 // output layout is the B-operand layout of the value product, so P goes from
 // registers straight into the matrix cores (as bf16; query block 0, whose rows
-// see at most 128 keys, splits P exactly into two bf16 parts instead).
+// see at most 128 keys, splits P into two bf16 parts hi + lo instead, about 16
+// significant bits, and so does every block when the caller asks for it).
 // Workgroup ids are ordered so that all heads of one (kv head, query block)
 // land on the same XCD (id % 8) and are dispatched together: their shared K/V
 // tiles are fetched into that XCD's L2 once.
@@ -70,6 +71,12 @@ __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const 
   }
 }
 
+// MODE 0: every query block but the first, P in bf16 (the sparse prefill's
+//         bulk); MODE 2: only the first query block of each (b, kv head), P as
+//         bf16 hi + lo (its rows see at most 128 keys); MODE 1: every block
+//         with P as hi + lo.  Keeping the hi + lo path out of MODE 0 keeps that
+//         kernel within its registers (one inlined copy of the value product).
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int Hq, int Hkv, int L, int M, int units, float sl2,
@@ -82,9 +89,13 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
   const int id = blockIdx.x;
   const int grp = id / (8 * G), rem = id % (8 * G);
   const int hh = rem / 8;
-  const int u = grp * 8 + rem % 8;
+  int u = grp * 8 + rem % 8;
   if (u >= units) return;  // uniform, before any barrier
+  if constexpr (MODE == 2) u *= M;
   const int i = u % M, bkh = u / M;
+  if constexpr (MODE == 0) {
+    if (i == 0) return;
+  }
   const int b = bkh / Hkv, kh = bkh % Hkv;
   const int h = kh * G + hh;
 
@@ -214,8 +225,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
       }
-      if (i == 0) pv_tiles<true>(vt_lds, sfr, 2 * sb, acc, lane);
-      else        pv_tiles<false>(vt_lds, sfr, 2 * sb, acc, lane);
+      pv_tiles<MODE != 0>(vt_lds, sfr, 2 * sb, acc, lane);
     }
     __syncthreads();
   }
@@ -249,17 +259,31 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
                           int L, int D, float scale, int block, const int32_t* idx,
                           const int32_t* count, int kmax, void* O, int out_dtype, float* lse,
-                          hipStream_t st) {
+                          hipStream_t st, bool split_p) {
   (void)D;
   (void)block;
   const int M = cdiv(L, PF_BLK);
   const int G = Hq / Hkv;
-  const int units = B * Hkv * M;
+  const int units = B * Hkv * M, firsts = B * Hkv;
+  auto q = static_cast<const uint16_t*>(Q);
+  auto k = static_cast<const uint16_t*>(K);
+  auto v = static_cast<const uint16_t*>(V);
+  const float sl2 = scale * kLog2e;
+  const int ob = out_dtype == SA_BF16;
+  if (split_p) {
+    const long grid = long(cdiv(units, 8)) * 8 * G;
+    k_prefill_bf16<1><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, st>>>(
+        q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
+    return hipGetLastError();
+  }
   const long grid = long(cdiv(units, 8)) * 8 * G;
-  k_prefill_bf16<<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, st>>>(
-      static_cast<const uint16_t*>(Q), static_cast<const uint16_t*>(K),
-      static_cast<const uint16_t*>(V), Hq, Hkv, L, M, units, scale * kLog2e, idx, count, kmax, O,
-      out_dtype == SA_BF16, lse);
+  k_prefill_bf16<0><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, st>>>(
+      q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long grid0 = long(cdiv(firsts, 8)) * 8 * G;
+  k_prefill_bf16<2><<<dim3(static_cast<unsigned>(grid0)), dim3(256), 0, st>>>(
+      q, k, v, Hq, Hkv, L, M, firsts, sl2, idx, count, kmax, O, ob, lse);
   return hipGetLastError();
 }
 

@@ -481,12 +481,20 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes, const i
 
 sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv, int L,
                          int D, int block, int k_free, float scale, float* mass, int32_t* idx,
-                         int32_t* count, void* ws, size_t ws_bytes, void* stream) {
+                         int32_t* count, float* row_mass, int32_t* row_idx,
+                         int32_t* row_count, void* ws, size_t ws_bytes, void* stream) {
   PTR(Q);
   PTR(K);
   PTR(idx);
   PTR(count);
   if (mass) PTR(mass);
+  REQ((row_mass == nullptr) == (row_idx == nullptr) && (row_idx == nullptr) == (row_count == nullptr),
+      "row_mass, row_idx and row_count go together (all NULL or none)");
+  if (row_mass) {
+    PTR(row_mass);
+    PTR(row_idx);
+    PTR(row_count);
+  }
   REQ(dtype_ok(dtype), "unknown dtype %d", dtype);
   sa_status s = check_heads(B, Hq, Hkv);
   if (s) return s;
@@ -501,7 +509,8 @@ sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq,
   if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);
   PTR(ws);
   return hip_status(launch_mass_select(Q, K, B, Hq, Hkv, L, D, eff_scale(scale, D), block, k_free,
-                                       mass, idx, count, w, ws, static_cast<hipStream_t>(stream)),
+                                       mass, idx, count, row_mass, row_idx, row_count, w, ws,
+                                       static_cast<hipStream_t>(stream)),
                     "sa_mass_select");
 }
 

@@ -229,6 +229,7 @@ hipError_t launch_block_list(const uint8_t* flag, int BH, int nb, int kcap,
 hipError_t launch_mass_select(const void* Q, const void* K, int B, int Hq, int Hkv,
                               int L, int D, float scale, int block, int kfree,
                               float* mass, int32_t* idx, int32_t* count,
+                              float* row_mass, int32_t* row_idx, int32_t* row_count,
                               const MassWs& w, void* ws, hipStream_t st);
 hipError_t launch_radius(const void* X, int dtype, int B, int H, int N, int D,
                          int block, int S, int b0, int b1, const float* sketch,
@@ -240,6 +241,7 @@ hipError_t launch_prune(const void* Q, int dtype, int B, int Hq, int Hkv, int N,
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B,
                           int Hq, int Hkv, int L, int D, float scale, int block,
                           const int32_t* idx, const int32_t* count, int kmax,
-                          void* O, int out_dtype, float* lse, hipStream_t st);
+                          void* O, int out_dtype, float* lse, hipStream_t st,
+                          bool split_p = false);
 
 }  // namespace sa
