@@ -883,3 +883,77 @@ def test_decode_step_graph_replay_matches_eager():
         step()                                   # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(O, ref[1])
+
+
+def test_selectors_graph_replay_match_eager():
+    """Top-delta (with its token decode), the sphere-pruned threshold and the
+    low-bit filter (with its block decode), captured together in one HIP graph,
+    give the eager results on every replay, with eager calls between replays."""
+    wl, inp, q, K, V = _decode_case("topdelta_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2, "N": 4096,
+                                                             "needles": 2, "cap": 1024})
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    B, Hq, Hkv, D, N, blk = wl.B, wl.Hq, wl.Hkv, wl.D, wl.N, wl.block
+    dev = "cuda"
+    z = lambda n: torch.zeros(n, dtype=torch.uint8, device=dev)  # noqa: E731
+    # top-delta + token decode
+    t_idx = torch.empty(B, Hq, wl.cap, dtype=torch.int32, device=dev)
+    t_sc = torch.empty(B, Hq, wl.cap, dtype=torch.float32, device=dev)
+    t_cnt = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    t_tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    t_O = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    t_ws = z(sa.workspace_bytes(sa.SA_OP_SELECT_TOPDELTA, B, Hq, Hkv, N, D, 0, wl.cap))
+    t_dws = z(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, 0, wl.cap))
+    # sphere-pruned threshold
+    sk = sa.sa_build_sketch(Kd, blk)
+    rad = sa.sa_build_radius(Kd, sk, blk, 2)
+    tau = torch.full((B, Hq), 1.5, device=dev)
+    p_idx = torch.empty(B, Hq, wl.cap, dtype=torch.int32, device=dev)
+    p_sc = torch.empty(B, Hq, wl.cap, dtype=torch.float32, device=dev)
+    p_cnt = torch.empty(B, Hq, dtype=torch.int32, device=dev)
+    p_live = torch.empty(B, Hkv, -(-N // 128), dtype=torch.uint8, device=dev)
+    p_ws = z(sa.workspace_bytes(sa.SA_OP_SELECT_PRUNED, B, Hq, Hkv, N, D, blk, wl.cap))
+    # low-bit filter + block decode
+    codes, resid, meta = sa.sa_encode_keys(Kd, blk)
+    nb = wl.nb
+    l_idx = torch.empty(B, Hkv, nb, dtype=torch.int32, device=dev)
+    l_cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    l_tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    khat = torch.zeros(B, Hkv, N, D, dtype=torch.bfloat16, device=dev)
+    l_O = torch.empty(B, Hq, D, dtype=torch.float32, device=dev)
+    l_ws = z(sa.workspace_bytes(sa.SA_OP_SELECT_LOWBIT, B, Hq, Hkv, N, D, blk, nb))
+    l_dws = z(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, N, D, blk, nb))
+
+    def run():
+        sa.sa_select_topdelta(Qd, Kd, wl.sink, wl.local, wl.delta, wl.cap, idx=t_idx, score=t_sc,
+                              count=t_cnt, tau=t_tau, ws=t_ws)
+        sa.sa_sparse_decode(Qd, Kd, Vd, t_idx, t_cnt, mode=sa.SA_IDX_TOKENS, score=t_sc, O=t_O,
+                            out_dtype=torch.float32, ws=t_dws)
+        sa.sa_select_threshold_pruned(Qd, Kd, sk, rad, tau, wl.cap, blk, idx=p_idx, score=p_sc,
+                                      count=p_cnt, live=p_live, ws=p_ws)
+        sa.sa_select_topdelta_lowbit(Qd, codes, resid, meta, blk, wl.sink, wl.local, wl.delta, 1.0,
+                                     nb, khat=khat, idx=l_idx, count=l_cnt, tau=l_tau, ws=l_ws)
+        sa.sa_sparse_decode(Qd, khat, Vd, l_idx, l_cnt, block=blk, O=l_O, out_dtype=torch.float32,
+                            ws=l_dws)
+
+    outs = (t_idx, t_sc, t_cnt, t_tau, t_O, p_idx, p_sc, p_cnt, p_live, l_idx, l_cnt, l_tau, l_O)
+    run()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b_ in zip(outs, ref):
+            assert torch.equal(a, b_), rep
+        run()                                    # eager work between replays
+        torch.cuda.synchronize()
+        for a, b_ in zip(outs, ref):
+            assert torch.equal(a, b_), rep
