@@ -275,8 +275,10 @@ sa_status sa_select_threshold_pruned(const void* Q, const void* K, int dtype,
  * all in IEEE float32, so the output is a fixed function of K.
  *
  *   K        [B, H, N, D] dtype (finite values)
- *   codes    [B, H, N, D/4] uint8 out: channel 4i + e of a token in bits
- *            2e..2e+1 of byte i
+ *   codes    [B, H, N, D/4] uint8 out: one little-endian 32-bit word per 16
+ *            channels; channel 16 g + i of a token sits at bit 8 (i % 4) +
+ *            2 (i / 4) of word g (so a shift and a mask give the codes of 4
+ *            consecutive channels as 4 bytes)
  *   resid    [B, H, N, D] int8 out
  *   meta     [B, H, nb, 3, D] float32 out: (lo, step, rstep) rows per block
  *   [blk_begin, blk_end)  the blocks to (re)encode (decode appends re-encode
@@ -304,8 +306,9 @@ sa_status sa_decode_keys(const uint8_t* codes, const int8_t* resid,
  * (Metodologia §3) up to the attention: (1) the refined keys of the blocks
  * holding the sink prefix [0, sink) and the local window [N - local, N) are
  * rebuilt into khat and give tau = m~ - delta as sa_select_topdelta does;
- * (2) every token's provisional score comes from its 2-bit thumbnail (t
- * rounded to bf16, matrix-core dot products with Q, float32 accumulation),
+ * (2) every token's provisional score comes from its 2-bit thumbnail: the
+ * block offset q . lo plus ws * sum_c w8_c code_c, with int8 weights w8 of
+ * q_c step_c (scale ws) on the int8 matrix cores,
  * and block j is kept for a kv head when a head h of its group has a
  * provisional score >= tau_h - margin, or when it holds window tokens;
  * (3) the refined keys of the kept blocks are written into khat.  Follow

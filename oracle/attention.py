@@ -581,6 +581,7 @@ def select_threshold_pruned(q: np.ndarray, K: np.ndarray, tau: np.ndarray, block
 
 # ------------------------------------------------------------------ O11
 _THIRD32 = np.float32(1.0) / np.float32(3.0)
+_INV127_32 = np.float32(1.0) / np.float32(127.0)
 
 
 def lowbit_encode(K: np.ndarray, block: int):
@@ -674,10 +675,13 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
     Readings taken: the refined key is k^ rounded to bf16, the precision of
     the cache it stands for; the provisional score of token t in block j is
     the thumbnail dot product split into the block's offset and its code
-    term, scale * (q . lo_j + sum_c bf16(fl32(q_c step_j,c)) code_t,c), whose
-    per-channel weights the matrix cores take in bf16 (the codes 0..3 are
-    exact there); `margin` (>= 0) widens the filter against the thumbnail
-    error.
+    term, with the per-channel weights w_c = fl32(q_c step_j,c) quantised to
+    int8 for the matrix cores (the codes 0..3 are exact there):
+        scale * (q . lo_j + ws * sum_c w8_c code_t,c),
+        ws = fl32(max_c |w_c| * fl32(1/127)),
+        w8_c = clip(rint(fl32(w_c * fl32(127 / max_c |w_c|))), +-127)
+    (every step one float32 operation; w8 = 0 when the maximum is 0); `margin` (>= 0)
+    widens the filter against the thumbnail error.
     Returns (idx, count, tau, bmax): idx [B, Hkv, nb] ascending block ids
     (count valid), tau [B, Hq], bmax [B, Hq, nb] the largest provisional
     score of each block.
@@ -705,10 +709,18 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
                 q32 = q[b, h].astype(np.float32)
                 for j in range(nb):
                     lo_j, step_j = meta[b, kh, j, 0], meta[b, kh, j, 1]
-                    w = bf16_round(q32 * step_j)
+                    w = q32 * step_j
+                    wmax = np.float32(np.abs(w).max())
+                    ws = wmax * _INV127_32
+                    if wmax > 0:
+                        winv = np.float32(127.0) / wmax
+                        w8 = np.clip(np.rint(w * winv), -127, 127).astype(np.int64)
+                    else:
+                        w8 = np.zeros(w.shape, dtype=np.int64)
                     rows = slice(j * block, min((j + 1) * block, N))
+                    acc = codes[b, kh, rows].astype(np.int64) @ w8
                     prov = (float(q[b, h] @ lo_j.astype(np.float64))
-                            + codes[b, kh, rows].astype(np.float64) @ w) * sc
+                            + float(ws) * acc.astype(np.float64)) * sc
                     bmax[b, h, j] = prov.max()
                 keep |= bmax[b, h] >= tau[b, h] - float(margin)
             sel = np.nonzero(keep)[0]

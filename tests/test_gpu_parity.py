@@ -601,9 +601,12 @@ def test_pruned_threshold_parity(name, over, S):
 
 
 def _unpack_codes(packed):
-    """[..., D/4] uint8 -> [..., D] codes (channel 4i + e in bits 2e of byte i)."""
-    p = packed.astype(np.uint8)
-    return np.stack([(p >> (2 * e)) & 3 for e in range(4)], -1).reshape(*p.shape[:-1], -1)
+    """[..., D/4] uint8 -> [..., D] codes: one little-endian 32-bit word per 16
+    channels, channel 16 g + i at bit 8 (i % 4) + 2 (i / 4) of word g."""
+    w = np.ascontiguousarray(packed).view(np.uint32)
+    i = np.arange(16)
+    shift = (8 * (i % 4) + 2 * (i // 4)).astype(np.uint32)
+    return ((w[..., None] >> shift) & 3).astype(np.uint8).reshape(*packed.shape[:-1], -1)
 
 
 LOWBIT_CODEC_CASES = [

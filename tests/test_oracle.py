@@ -719,22 +719,25 @@ def test_lowbit_codes_are_nearest_levels_and_errors_bounded(seed):
 
 def test_lowbit_on_grid_keys_is_exact_top_delta():
     """Keys already on each block's four levels: thumbnails equal the keys,
-    residuals vanish, and with margin 0 the filter keeps exactly the blocks
-    holding a token at or above m~ - delta (plus the window's blocks)."""
+    residuals vanish, and with one step per block and q in {-1, 0, 1} the
+    int8 weights are exact (+-127 ws), so the provisional block maxima are the
+    exact ones up to float32 rounding and, at margin 0, the filter keeps
+    exactly the blocks holding a token at or above m~ - delta (plus the
+    window's blocks)."""
     rng = np.random.default_rng(520)
     B, Hq, Hkv, N, D, block = 1, 4, 2, 512, 8, 64
     nb = N // block
     lo = rng.integers(-8, 8, size=(B, Hkv, nb, D)) / 4.0
-    s = 2.0 ** rng.integers(-3, 1, size=(B, Hkv, nb, D))
+    s = np.broadcast_to(2.0 ** rng.integers(-3, 1, size=(B, Hkv, nb, 1)), (B, Hkv, nb, D))
     lev = rng.integers(0, 4, size=(B, Hkv, N, D))
     lev[:, :, ::block, :] = 0                      # every level range spans 0..3
     lev[:, :, 1::block, :] = 3
     K = np.repeat(lo, block, 2) + lev * np.repeat(s, block, 2)
-    q = rng.integers(-4, 5, size=(B, Hq, D)) / 2.0
+    q = rng.integers(-1, 2, size=(B, Hq, D)).astype(float)
     codes, resid, meta = oracle.lowbit_encode(K, block)
     assert np.array_equal(codes, lev) and not resid.any()
     np.testing.assert_array_equal(oracle.lowbit_reconstruct(codes, resid, meta, block), K)
-    sink, local, delta = 8, 8, 3.0
+    sink, local, delta = 8, 8, 3.1                 # delta off the dyadic grid: no exact ties
     idx, cnt, tau, bmax = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, sink, local,
                                                         delta, 0.0)
     _, _, tau_x = oracle.select_topdelta(q, K, sink, local, delta)
@@ -743,8 +746,10 @@ def test_lowbit_on_grid_keys_is_exact_top_delta():
     for kh in range(Hkv):
         want = {0, nb - 1}
         for h in range(kh * 2, kh * 2 + 2):
+            exact_max = sx[0, h].reshape(nb, block).max(-1)
+            np.testing.assert_allclose(bmax[0, h], exact_max, rtol=1e-6, atol=1e-6)
+            assert np.all(np.abs(exact_max - tau_x[0, h]) > 1e-3)
             want |= {t // block for t in np.nonzero(sx[0, h] >= tau_x[0, h])[0]}
-            np.testing.assert_allclose(bmax[0, h], sx[0, h].reshape(nb, block).max(-1), atol=1e-12)
         assert idx[0, kh, :cnt[0, kh]].tolist() == sorted(want)
     # an infinite margin keeps every block
     _, cnt, _, _ = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, sink, local, delta,

@@ -17,7 +17,8 @@
 //   r8     = clamp(rint((k - t) / rstep), -127, 127);   k^ = t + r8 * rstep
 // Every step is one IEEE float32 operation, so codes and residuals are a
 // fixed function of the keys.  Storage per token and kv head: D/4 bytes of
-// codes (4 per byte, channel 4i + e in bits 2e..2e+1) and D bytes of residuals;
+// codes (one 32-bit word per 16 channels, channel 16 g + i at bit
+// 8 (i % 4) + 2 (i / 4) of word g) and D bytes of residuals;
 // per block: (lo, step, rstep) float32 rows of D.  The scan reads the codes
 // and lo/step only: D/4 + 8 D / block bytes per token (48 B at D = 128, block
 // 64) instead of 2 D (256 B).
@@ -28,10 +29,10 @@
 //   k_decode_keys  one workgroup per listed block (or per block of a range):
 //                  k^ rounded to bf16 into a key buffer laid out as K.
 //   k_thumb_scan   one wave per (b, kv head, block): provisional scores from
-//                  the codes on the matrix cores for the g heads (block offset
-//                  q . lo plus the codes against bf16 weights q_c step_c), the
-//                  block maximum per head, and the keep flag (some head reaches
-//                  tau_h - margin, or a window block).
+//                  the codes on the int8 matrix cores for the g heads (block
+//                  offset q . lo plus the codes against int8 weights of
+//                  q_c step_c), the block maximum per head, and the keep flag
+//                  (some head reaches tau_h - margin, or a window block).
 //   k_block_list   one workgroup per (b, kv head): flags -> ascending list.
 #include "sa_device.h"
 #include "sa_internal.h"
@@ -90,9 +91,13 @@ __global__ __launch_bounds__(256) void k_encode(const T* __restrict__ K, int N, 
     const int r8 = int(fminf(fmaxf(q, -127.f), 127.f));
     const size_t row = size_t(bh) * N + t0 + r;
     resid[row * D + c] = int8_t(r8);
-    // pack the codes of channels 4i..4i+3 (consecutive lanes) into one byte
-    const int c1 = __shfl(code, lane + 1), c2 = __shfl(code, lane + 2), c3 = __shfl(code, lane + 3);
-    if ((c & 3) == 0) codes[row * (D / 4) + c / 4] = uint8_t(code | (c1 << 2) | (c2 << 4) | (c3 << 6));
+    // pack the codes of channels 16 g .. 16 g + 15 (consecutive lanes) into one
+    // word, channel 16 g + i at bit 8 (i % 4) + 2 (i / 4)
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      word |= uint32_t(__shfl(code, (lane & ~15) + i)) << (8 * (i & 3) + 2 * (i >> 2));
+    if ((c & 15) == 0) *reinterpret_cast<uint32_t*>(codes + row * (D / 4) + c / 4) = word;
   }
 }
 
@@ -124,12 +129,14 @@ __global__ __launch_bounds__(256) void k_decode_keys(
   for (int e = 0; e < 8; ++e) { lo[e] = mrow[c0 + e]; st[e] = mrow[D + c0 + e]; rs[e] = mrow[2 * D + c0 + e]; }
   for (int r = tr; r < nj; r += RPP) {
     const size_t row = size_t(bh) * N + t0 + r;
-    const uint32_t cw = *reinterpret_cast<const uint16_t*>(codes + row * (D / 4) + c0 / 4);
+    // channels c0 .. c0 + 7 are the half h of their 16-channel word
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + row * (D / 4) + (c0 / 16) * 4);
+    const int h = (c0 & 15) >> 3;
     const u32x2 rw = ld8(resid + row * D + c0);
     float kh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int code = int((cw >> (2 * e)) & 3u);
+      const int code = int((cw >> (8 * (e & 3) + 2 * (2 * h + (e >> 2)))) & 3u);
       const int r8 = int(int8_t((rw[e / 4] >> (8 * (e % 4))) & 0xffu));
       const float t = fmaf(float(code), st[e], lo[e]);
       kh[e] = t + float(r8) * rs[e];
@@ -144,13 +151,17 @@ __global__ __launch_bounds__(256) void k_decode_keys(
 // One wave per (b, kv head, block); 4 waves per workgroup.
 //
 // The provisional score of token t in block j is the thumbnail dot product
-// split into the block offset and the code term:
-//     s~ = scale * (q . lo_j + sum_c w_c code_t,c),   w_c = bf16(q_c step_j,c)
-// so a tile needs only its codes turned into bf16 0..3 (exact) as the A
-// operand; the weights w are the B operand, built once per block.  The codes
-// become bf16 with one byte permutation per pair: a selector with code c in
-// byte 0 and c + 4 in byte 1 picks the low and high bytes of bf16(c) from two
-// 4-entry tables.
+// split into the block offset and the code term, the latter on int8 matrix
+// cores:
+//     s~ = scale * (q . lo_j + ws * sum_c w8_c code_t,c),
+//     w_c = fl(q_c step_j,c),  ws = max_c |w_c| * fl(1/127),
+//     w8_c = clamp(rint(w_c * fl(127 / max_c |w_c|)), -127, 127)
+// The codes word of 16 channels holds channel i at bit 8 (i % 4) + 2 (i / 4), so
+// (word >> 2m) & 0x03030303 is the 4 int8 codes of channels 4m .. 4m + 3: the
+// A operand costs two operations per 4 channels.  The weights w8 (B operand)
+// and the offset are built once per block.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_thumb_scan(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ codes,
@@ -158,9 +169,7 @@ __global__ __launch_bounds__(256) void k_thumb_scan(
     const float* __restrict__ tau, float margin, int f0, int f1, int f2, int f3,
     float* __restrict__ bmax, uint8_t* __restrict__ flag) {
   static_assert(G <= 16, "heads are the 16 columns of the score tile");
-  constexpr int NST = D / 32;
-  constexpr uint32_t kLutLo = 0x40008000u;   // low bytes of bf16(0), bf16(1), bf16(2), bf16(3)
-  constexpr uint32_t kLutHi = 0x40403f00u;   // their high bytes
+  constexpr int NST = D / 64;                 // 64 channels per int8 product
   const int nbw = (nb + 3) / 4;
   const int bh = blockIdx.x / nbw;
   const int j = (blockIdx.x % nbw) * 4 + int(threadIdx.x >> 6);
@@ -169,8 +178,9 @@ __global__ __launch_bounds__(256) void k_thumb_scan(
   const int lane = threadIdx.x & 63, gq = lane >> 4, nn = lane & 15;
   const int t0 = j * block, nj = min(block, N - t0);
   const uint8_t* cb = codes + (size_t(bh) * N + t0) * (D / 4);
-  // every tile's codes first (a block is at most 8 tiles; token row 16 u + nn,
-  // rows past the block repeat its last row), then the query and the ranges
+  // every tile's code words first (a block is at most 8 tiles; token row
+  // 16 u + nn, rows past the block repeat its last row): channels
+  // 64 st + 16 gq .. + 15 of the row, one word each
   constexpr int MT = 8;
   uint32_t cw[MT][NST];
 #pragma unroll
@@ -179,72 +189,98 @@ __global__ __launch_bounds__(256) void k_thumb_scan(
 #pragma unroll
     for (int st = 0; st < NST; ++st)
       cw[u][st] = 16 * u < nj
-          ? *reinterpret_cast<const uint16_t*>(cb + size_t(r) * (D / 4) + 2 * gq + 8 * st) : 0u;
+          ? *reinterpret_cast<const uint32_t*>(cb + size_t(r) * (D / 4) + 4 * (4 * st + gq)) : 0u;
   }
-  u32x4 qb[NST];
-  const uint16_t* qp = Q + (size_t(b) * Hq + kh * G + min(nn, G - 1)) * D + 8 * gq;
-#pragma unroll
-  for (int st = 0; st < NST; ++st) qb[st] = nn < G ? ld16(qp + 32 * st) : u32x4{0u, 0u, 0u, 0u};
-  const float th = nn < G ? tau[size_t(b) * Hq + kh * G + nn] : 0.f;
-  // the block's (lo, step) rows (2 D floats) through this wave's LDS slice:
-  // one 16-byte load per lane instead of one per lane and channel group
+  // the block's (lo, step) rows (2 D floats) through this wave's LDS slice
   __shared__ __attribute__((aligned(16))) float sm[4][2 * D];
-  float* mw = sm[threadIdx.x >> 6];
+  __shared__ __attribute__((aligned(16))) int8_t swt[4][8][D];   // int8 weights per head
+  __shared__ float soff[4][8], sws[4][8];
+  const int wv = threadIdx.x >> 6;
+  float* mw = sm[wv];
   const float* mrow = meta + (size_t(bh) * nb + j) * 3 * D;
   if (lane < D / 2) *reinterpret_cast<u32x4*>(mw + 4 * lane) = ld16(mrow + 4 * lane);
   __builtin_amdgcn_wave_barrier();
-  // this lane's channels 8 gq + 32 st + e of head nn: the offset part and the
-  // bf16 weights
-  float off = 0.f;
-  u32x4 wb[NST];
+  // weights of the group's heads, 4 heads at a time: lane (hh, cc) takes head
+  // hh and channels (D / 16) cc .. + D / 16, then the 16 lanes of a head reduce
+  constexpr int CPL = D / 16;
+  const int hh0 = lane >> 4, cc = lane & 15;
+  for (int hb = 0; hb < G; hb += 4) {
+    const int hh = hb + hh0;
+    const bool real = hh < G;
+    const uint16_t* qh = Q + (size_t(b) * Hq + kh * G + min(hh, G - 1)) * D + CPL * cc;
+    static_assert(CPL == 4 || CPL == 8, "D is 64 or 128");
+    uint32_t qw[CPL / 2];
+    if constexpr (CPL == 8) {
+      const u32x4 v = real ? ld16(qh) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int p = 0; p < 4; ++p) qw[p] = v[p];
+    } else {
+      const u32x2 v = real ? ld8(qh) : u32x2{0u, 0u};
+      qw[0] = v[0];
+      qw[1] = v[1];
+    }
+    float wv8[CPL];
+    float off = 0.f, wmax = 0.f;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      const float qf = (e & 1) ? bf16hi(qw[e >> 1]) : bf16lo(qw[e >> 1]);
+      const int c = CPL * cc + e;
+      off += qf * mw[c];
+      wv8[e] = qf * mw[D + c];
+      wmax = fmaxf(wmax, fabsf(wv8[e]));
+    }
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      off += __shfl_xor(off, o);
+      wmax = fmaxf(wmax, __shfl_xor(wmax, o));
+    }
+    const float winv = wmax > 0.f ? __fdiv_rn(127.f, wmax) : 0.f;
+#pragma unroll
+    for (int e0 = 0; e0 < CPL; e0 += 4) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = __builtin_amdgcn_fmed3f(rintf(wv8[e0 + e] * winv), -127.f, 127.f);
+        word |= uint32_t(int(x) & 0xff) << (8 * e);
+      }
+      if (real) *reinterpret_cast<uint32_t*>(&swt[wv][hh][CPL * cc + e0]) = word;
+    }
+    if (real && cc == 0) {
+      soff[wv][hh] = off;
+      sws[wv][hh] = wmax * 0.007874015718698502f;   // fl32(1/127)
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // B operand: head nn's int8 weights at channels 64 st + 16 gq .. + 15
+  i32x4 wb[NST];
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(mw + 8 * gq + 32 * st);
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(mw + 8 * gq + 32 * st + 4);
-    const u32x4 s0 = *reinterpret_cast<const u32x4*>(mw + D + 8 * gq + 32 * st);
-    const u32x4 s1 = *reinterpret_cast<const u32x4*>(mw + D + 8 * gq + 32 * st + 4);
-    uint32_t w[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float qa = bf16lo(qb[st][p]), qc = bf16hi(qb[st][p]);
-      const float la = __uint_as_float(p < 2 ? a0[2 * p] : a1[2 * p - 4]);
-      const float lb = __uint_as_float(p < 2 ? a0[2 * p + 1] : a1[2 * p - 3]);
-      const float sa_ = __uint_as_float(p < 2 ? s0[2 * p] : s1[2 * p - 4]);
-      const float sb = __uint_as_float(p < 2 ? s0[2 * p + 1] : s1[2 * p - 3]);
-      off += qa * la + qc * lb;
-      w[p] = pack_bf16x2(qa * sa_, qc * sb);
-    }
-    wb[st] = u32x4{w[0], w[1], w[2], w[3]};
+    const u32x4 wq = nn < G ? *reinterpret_cast<const u32x4*>(&swt[wv][min(nn, G - 1)][64 * st + 16 * gq])
+                            : u32x4{0u, 0u, 0u, 0u};
+    wb[st] = i32x4{int(wq[0]), int(wq[1]), int(wq[2]), int(wq[3])};
   }
-  off += __shfl_xor(off, 16);
-  off += __shfl_xor(off, 32);
+  const float off = soff[wv][min(nn, G - 1)], ws = sws[wv][min(nn, G - 1)];
+  const float th = nn < G ? tau[size_t(b) * Hq + kh * G + nn] : 0.f;
   float m = -__builtin_inff();
 #pragma unroll
   for (int u = 0; u < MT; ++u) {
     if (16 * u >= nj) break;
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+    i32x4 acc = i32x4{0, 0, 0, 0};
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      // split the 8 codes into even and odd channels, 4 bits apart, then one
-      // selector per channel pair
       const uint32_t x = cw[u][st];
-      const uint32_t t = (x & 0x3333u) | (((x >> 2) & 0x3333u) << 16);
-      uint32_t a[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const uint32_t sel = ((t >> (4 * p)) & 0x00030003u) * 0x0101u + 0x04000400u;
-        a[p] = __builtin_amdgcn_perm(kLutHi, kLutLo, sel);
-      }
-      sc = mfma16x16x32(u32x4{a[0], a[1], a[2], a[3]}, wb[st], sc);
+      const i32x4 a = i32x4{int(x & 0x03030303u), int((x >> 2) & 0x03030303u),
+                            int((x >> 4) & 0x03030303u), int((x >> 6) & 0x03030303u)};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, wb[st], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr)
-      if (16 * u + 4 * gq + rr < nj) m = fmaxf(m, sc[rr]);
+      if (16 * u + 4 * gq + rr < nj) m = fmaxf(m, float(acc[rr]));
   }
   // lanes nn, nn + 16, nn + 32, nn + 48 hold head nn's rows
   m = fmaxf(m, __shfl_xor(m, 16));
   m = fmaxf(m, __shfl_xor(m, 32));
-  m = scale * (off + m);
+  m = scale * (off + ws * m);
   if (bmax && gq == 0 && nn < G) bmax[(size_t(b) * Hq + kh * G + nn) * nb + j] = m;
   const bool win = (j >= f0 && j < f1) || (j >= f2 && j < f3);
   const uint64_t any = __ballot(gq == 0 && nn < G && m >= th - margin);
