@@ -96,6 +96,43 @@ def test_full_threshold():
           f"{time.time() - t0:.1f}s")
 
 
+def test_full_topdelta():
+    """The top-delta workload whole: the GPU's tau against the pseudo-max rule,
+    zero false negatives against the exact rule, attention over the lists."""
+    t0 = time.time()
+    wl = get_workload("topdelta_decode_bf16")
+    inp = make_inputs(wl)
+    q, K, V = (widen(x, "bf16") for x in (inp.Q, inp.K, inp.V))
+    Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")
+    idx, score, cnt, tau = sa.sa_select_topdelta(Qd, Kd, wl.sink, wl.local, wl.delta, wl.cap)
+    O32, lse = sa.sa_sparse_decode(Qd, Kd, Vd, idx, cnt, mode=sa.SA_IDX_TOKENS, score=score,
+                                   out_dtype=torch.float32)
+    lists_x, _, tau_x = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
+    s = exact_scores(q, K)
+    tau_h, idx_h, cnt_h = tau.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy()
+    assert np.all(tau_h <= tau_x + 1e-6 * (1 + np.abs(tau_x)))
+    assert np.all(tau_h >= tau_x - 1e-3)
+    lists = [[None] * wl.Hq for _ in range(wl.B)]
+    extra = 0
+    for b in range(wl.B):
+        for h in range(wl.Hq):
+            n = int(cnt_h[b, h])
+            assert n <= wl.cap
+            got = idx_h[b, h, :n]
+            assert set(lists_x[b][h].tolist()) <= set(got.tolist()), f"false negative at b{b} h{h}"
+            ex = np.setdiff1d(got, lists_x[b][h])
+            assert np.all(s[b, h, ex] >= tau_x[b, h] - 1e-3)
+            extra += ex.size
+            lists[b][h] = got
+    O_ref, lse_ref = oracle.attend_tokens(q, K, V, lists)
+    err = max_abs(O32.cpu().numpy(), O_ref)
+    assert err <= 2e-3
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    kept = int(cnt_h.sum())
+    print(f"top-delta: kept {kept} ({kept / (wl.B * wl.Hq * wl.N):.2%}), extra keys {extra}, "
+          f"max-abs O error {err:.2e}, {time.time() - t0:.1f}s")
+
+
 def test_full_pruned_threshold():
     """The clustered threshold workload whole: bounding spheres built on the GPU,
     the pruned scan against the exact rule (zero false negatives) and against
