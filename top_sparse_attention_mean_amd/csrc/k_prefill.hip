@@ -40,13 +40,14 @@ constexpr int PF_BLK = 128;         // query and key block
 constexpr int PF_D = 128;
 constexpr int PF_KS = PF_D + 8;     // K tile row stride (elements)
 constexpr int PF_VS = PF_BLK + 4;   // V^T tile row stride (elements)
+constexpr int PF_KT = 2;            // 32-key tiles per online-softmax step (4: spills)
 
-template <bool SPLITP>
+template <bool SPLITP, int NKT>
 __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const f32x16* sfr,
                                          int kt0, f32x16* acc, int lane) {
   const int h = lane >> 5, col = lane & 31;
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < NKT; ++kk) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       u32x4 pb, pl;
@@ -125,13 +126,20 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
-  const int ldc = tid & 15, ldr = tid >> 4;   // tile loaders: 16-byte chunk, row group
+  const int ldc = tid & 15, ldr = tid >> 4;   // K loaders: 16-byte chunk, row group
+  // V^T loaders: key group vk (4 rows) and column group vc (8 columns); they
+  // write 8 V^T rows x 4 keys.  The 16 lanes of one LDS write phase differ in
+  // vk, so their 8-byte stores fall 2 dwords apart in distinct banks (with the
+  // column group varying inside a phase, rows 8 apart at a stride of 66
+  // dwords met in two bank pairs: an 8-way conflict).
+  const int vk = tid & 15, vc = tid >> 4;
 
   for (int e = 0; e < cnt; ++e) {
     const int jb = lst[e];
     if (jb < 0 || jb > i) continue;          // uniform
     const int key0 = jb * PF_BLK;
-    // ---- stage K (row-major) and V^T
+    // ---- stage K (row-major) and V^T; all 16 loads of a thread are in flight
+    //      at once
 #pragma unroll
     for (int p0 = 0; p0 < 8; p0 += 4) {
       u32x4 w[4];
@@ -143,37 +151,35 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
       for (int p = 0; p < 4; ++p)
         *reinterpret_cast<u32x4*>(&kt_lds[(ldr + 16 * (p0 + p)) * PF_KS + 8 * ldc]) = w[p];
-      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const int k0 = 4 * ldr + 64 * p;
+      const int k0 = 4 * vk + 64 * p;
       u32x4 w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int vr = min(key0 + k0 + j, L - 1);
-        w[j] = bld16(rV, (vr * PF_D + 8 * ldc) * 2);
+        w[j] = bld16(rV, (vr * PF_D + 8 * vc) * 2);
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x2 ev = u32x2{pack_lo(w[0][c], w[1][c]), pack_lo(w[2][c], w[3][c])};
         const u32x2 od = u32x2{pack_hi(w[0][c], w[1][c]), pack_hi(w[2][c], w[3][c])};
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * ldc + 2 * c) * PF_VS + k0]) = ev;
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * ldc + 2 * c + 1) * PF_VS + k0]) = od;
+        *reinterpret_cast<u32x2*>(&vt_lds[(8 * vc + 2 * c) * PF_VS + k0]) = ev;
+        *reinterpret_cast<u32x2*>(&vt_lds[(8 * vc + 2 * c + 1) * PF_VS + k0]) = od;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
 
-    // ---- two halves of 64 keys: S^T = K Q^T, online softmax, O^T += V^T P^T
+    // ---- steps of 32 PF_KT keys: S^T = K Q^T, online softmax, O^T += V^T P^T
     const bool diag = jb == i;
     const bool tail = key0 + PF_BLK > L;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      f32x16 sfr[2];
+    for (int sb = 0; sb < 4 / PF_KT; ++sb) {
+      f32x16 sfr[PF_KT];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* kr = kt_lds + ((2 * sb + kk) * 32 + col) * PF_KS + 8 * half;
+      for (int kk = 0; kk < PF_KT; ++kk) {
+        const uint16_t* kr = kt_lds + ((PF_KT * sb + kk) * 32 + col) * PF_KS + 8 * half;
         sfr[kk] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr), qf[0], f32x16{});
 #pragma unroll
         for (int st = 1; st < PF_D / 16; ++st) {
@@ -184,20 +190,20 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       // the row maximum of the raw scores (the scale sl2 > 0 keeps the order)
       float mraw = -__builtin_inff();
       if (diag || tail) {  // uniform: mask keys past this row or past L
-        // key offset (2 sb + kk) 32 + 8 (r/4) + (r%4) is kept when <= lim
+        // key offset (PF_KT sb + kk) 32 + 8 (r/4) + (r%4) is kept when <= lim
         const int lim = min(qrow, L - 1) - key0 - 4 * half;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
+        for (int kk = 0; kk < PF_KT; ++kk) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int ko = (2 * sb + kk) * 32 + 8 * (r >> 2) + (r & 3);
+            const int ko = (PF_KT * sb + kk) * 32 + 8 * (r >> 2) + (r & 3);
             sfr[kk][r] = ko <= lim ? sfr[kk][r] : -__builtin_inff();
             mraw = fmaxf(mraw, sfr[kk][r]);
           }
         }
       } else {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < PF_KT; ++kk)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sfr[kk][r]);
       }
@@ -208,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       const float alpha = exp2_fast(m - m_use);
       float ls = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < PF_KT; ++kk) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = exp2_fast(__builtin_fmaf(sfr[kk][r], sl2, -m_use));
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
       }
-      pv_tiles<MODE != 0>(vt_lds, sfr, 2 * sb, acc, lane);
+      pv_tiles<MODE != 0, PF_KT>(vt_lds, sfr, PF_KT * sb, acc, lane);
     }
     __syncthreads();
   }
