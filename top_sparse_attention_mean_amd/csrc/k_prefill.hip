@@ -174,19 +174,24 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
     // ---- steps of 32 PF_KT keys: S^T = K Q^T, online softmax, O^T += V^T P^T
     const bool diag = jb == i;
     const bool tail = key0 + PF_BLK > L;
+    // the second step's scores are issued before the first step's softmax, so
+    // the matrix cores compute them while the vector ALUs run that softmax
+    f32x16 sall[4 / PF_KT][PF_KT];
 #pragma unroll
-    for (int sb = 0; sb < 4 / PF_KT; ++sb) {
-      f32x16 sfr[PF_KT];
+    for (int sb = 0; sb < 4 / PF_KT; ++sb)
 #pragma unroll
       for (int kk = 0; kk < PF_KT; ++kk) {
         const uint16_t* kr = kt_lds + ((PF_KT * sb + kk) * 32 + col) * PF_KS + 8 * half;
-        sfr[kk] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr), qf[0], f32x16{});
+        sall[sb][kk] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr), qf[0], f32x16{});
 #pragma unroll
         for (int st = 1; st < PF_D / 16; ++st) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(kr + 16 * st);
-          sfr[kk] = mfma32x32x16(a, qf[st], sfr[kk]);
+          sall[sb][kk] = mfma32x32x16(a, qf[st], sall[sb][kk]);
         }
       }
+#pragma unroll
+    for (int sb = 0; sb < 4 / PF_KT; ++sb) {
+      f32x16* sfr = sall[sb];
       // the row maximum of the raw scores (the scale sl2 > 0 keeps the order)
       float mraw = -__builtin_inff();
       if (diag || tail) {  // uniform: mask keys past this row or past L
