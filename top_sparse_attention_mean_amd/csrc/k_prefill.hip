@@ -40,7 +40,7 @@ constexpr int PF_BLK = 128;         // query and key block
 constexpr int PF_D = 128;
 constexpr int PF_KS = PF_D + 8;     // K tile row stride (elements)
 constexpr int PF_VS = PF_BLK + 4;   // V^T tile row stride (elements)
-constexpr int PF_KT = 2;            // 32-key tiles per online-softmax step (4: spills)
+constexpr int PF_KT = 2;            // 32-key tiles per exponent + value-product step (4: spills)
 
 template <bool SPLITP, int NKT>
 __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const f32x16* sfr,
@@ -171,11 +171,13 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
     }
     __syncthreads();
 
-    // ---- steps of 32 PF_KT keys: S^T = K Q^T, online softmax, O^T += V^T P^T
+    // ---- S^T = K Q^T for the block, online softmax, O^T += V^T P^T in steps of
+    //      32 PF_KT keys
     const bool diag = jb == i;
     const bool tail = key0 + PF_BLK > L;
-    // the second step's scores are issued before the first step's softmax, so
-    // the matrix cores compute them while the vector ALUs run that softmax
+    // all scores of the block first: the masking, the row maximum and the
+    // rescale then run once per block, and the second half's exponents run on
+    // the vector ALUs while the matrix cores do the first half's value product
     f32x16 sall[4 / PF_KT][PF_KT];
 #pragma unroll
     for (int sb = 0; sb < 4 / PF_KT; ++sb)
@@ -189,34 +191,46 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
           sall[sb][kk] = mfma32x32x16(a, qf[st], sall[sb][kk]);
         }
       }
+    // one maximum, rescale and exponent base for the whole block
+    float mraw = -__builtin_inff();
+    if (diag || tail) {  // uniform: mask keys past this row or past L
+      // key offset (PF_KT sb + kk) 32 + 8 (r/4) + (r%4) is kept when <= lim
+      const int lim = min(qrow, L - 1) - key0 - 4 * half;
 #pragma unroll
-    for (int sb = 0; sb < 4 / PF_KT; ++sb) {
-      f32x16* sfr = sall[sb];
-      // the row maximum of the raw scores (the scale sl2 > 0 keeps the order)
-      float mraw = -__builtin_inff();
-      if (diag || tail) {  // uniform: mask keys past this row or past L
-        // key offset (PF_KT sb + kk) 32 + 8 (r/4) + (r%4) is kept when <= lim
-        const int lim = min(qrow, L - 1) - key0 - 4 * half;
-#pragma unroll
-        for (int kk = 0; kk < PF_KT; ++kk) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = (PF_KT * sb + kk) * 32 + 8 * (r >> 2) + (r & 3);
-            sfr[kk][r] = ko <= lim ? sfr[kk][r] : -__builtin_inff();
-            mraw = fmaxf(mraw, sfr[kk][r]);
-          }
-        }
-      } else {
+      for (int sb = 0; sb < 4 / PF_KT; ++sb)
 #pragma unroll
         for (int kk = 0; kk < PF_KT; ++kk)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sfr[kk][r]);
-      }
-      mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
-      const float m_new = fmaxf(m, mraw * sl2);
-      // with no key seen yet (m_new = -inf) every p and alpha below is 0
-      const float m_use = m_new != -__builtin_inff() ? m_new : 0.f;
-      const float alpha = exp2_fast(m - m_use);
+          for (int r = 0; r < 16; ++r) {
+            const int ko = (PF_KT * sb + kk) * 32 + 8 * (r >> 2) + (r & 3);
+            sall[sb][kk][r] = ko <= lim ? sall[sb][kk][r] : -__builtin_inff();
+            mraw = fmaxf(mraw, sall[sb][kk][r]);
+          }
+    } else {
+#pragma unroll
+      for (int sb = 0; sb < 4 / PF_KT; ++sb)
+#pragma unroll
+        for (int kk = 0; kk < PF_KT; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sall[sb][kk][r]);
+    }
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    const float m_new = fmaxf(m, mraw * sl2);
+    // with no key seen yet (m_new = -inf) every p and alpha below is 0
+    const float m_use = m_new != -__builtin_inff() ? m_new : 0.f;
+    const float alpha = exp2_fast(m - m_use);
+    l *= alpha;
+    m = m_new;
+    // the accumulators change only where a row's maximum moved
+    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+    }
+#pragma unroll
+    for (int sb = 0; sb < 4 / PF_KT; ++sb) {
+      f32x16* sfr = sall[sb];
       float ls = 0.f;
 #pragma unroll
       for (int kk = 0; kk < PF_KT; ++kk) {
@@ -227,15 +241,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
           ls += p;
         }
       }
-      l = l * alpha + ls;
-      m = m_new;
-      // the accumulators change only where a row's maximum moved
-      if (__ballot(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
-      }
+      l += ls;
       pv_tiles<MODE != 0, PF_KT>(vt_lds, sfr, PF_KT * sb, acc, lane);
     }
     __syncthreads();
