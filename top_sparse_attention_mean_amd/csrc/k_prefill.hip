@@ -30,6 +30,9 @@
 namespace sa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+struct f32x2_pair {
+  float a, b;
+};
 
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -41,6 +44,15 @@ constexpr int PF_D = 128;
 constexpr int PF_KS = PF_D + 8;     // K tile row stride (elements)
 constexpr int PF_VS = PF_BLK + 4;   // V^T tile row stride (elements)
 constexpr int PF_KT = 2;            // 32-key tiles per exponent + value-product step (4: spills)
+
+// The two lanes of a query row (l and l ^ 32) combine their values with
+// v_permlane32_swap: swapping lanes 32..63 of the first operand with lanes
+// 0..31 of the second, both holding x, leaves every lane with x of itself and
+// of its partner, in a register and without an LDS round trip.
+__device__ __forceinline__ f32x2_pair pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2_pair{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
 
 template <bool SPLITP, int NKT>
 __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const f32x16* sfr,
@@ -214,7 +226,10 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 #pragma unroll
           for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sall[sb][kk][r]);
     }
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32, 64));
+    {
+      const f32x2_pair pr = pair32(mraw);
+      mraw = fmaxf(pr.a, pr.b);
+    }
     const float m_new = fmaxf(m, mraw * sl2);
     // with no key seen yet (m_new = -inf) every p and alpha below is 0
     const float m_use = m_new != -__builtin_inff() ? m_new : 0.f;
@@ -248,7 +263,8 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
   }
 
   // ---- epilogue: lane holds O^T[d = 32 dt + 8 (r/4) + 4 half + r%4][qrow]
-  const float lt = l + __shfl_xor(l, 32, 64);
+  const f32x2_pair lp = pair32(l);
+  const float lt = lp.a + lp.b;
   if (qrow < L) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     const size_t ob = ((size_t(b) * Hq + h) * L + qrow) * PF_D;
