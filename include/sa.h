@@ -350,7 +350,8 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes,
  * causal attention, one pass per 128 key blocks (the prefill kernel with V
  * replaced by one-hot block indicators).
  *
- *   Q [B, Hq, L, D], K [B, Hkv, L, D] bf16; D = 128, block = 128
+ *   Q [B, Hq, L, D], K [B, Hkv, L, D] bf16; D = 128, block = 128,
+ *            L * D * 2 <= 0x7f000000 (else SA_ERR_UNSUPPORTED)
  *   mass     [B, Hkv, M, M] float32 out (M = ceil(L / 128); entries j > i are
  *            0), or NULL (kept in ws)
  *   idx      [B, Hkv, M, k_free] int32 out, ascending (-1 padded)
@@ -406,7 +407,8 @@ sa_status sa_sparse_decode(const void* Q, const void* K, const void* V,
  * Block-Sparse prefill; [ORACLE] §2.1 block-shared support).
  *
  *   Q [B, Hq, L, D], K, V [B, Hkv, L, D] dtype (SA_BF16 only; bf16 matrix cores;
- *            D = 128)
+ *            D = 128; each kv head is read through a 32-bit buffer range:
+ *            L * D * 2 <= 0x7f000000, else SA_ERR_UNSUPPORTED)
  *   block    query and key block size (128)
  *   idx      [B, Hkv, M, kmax] int32 ascending key blocks per query block
  *            (M = ceil(L / block)), count [B, Hkv, M]; entries must be <= i

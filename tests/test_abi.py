@@ -276,6 +276,7 @@ def test_mass_select_validation(lib):
     assert call(18, 1024) == WORKSPACE
     assert call(4, 30) == INVALID                 # Hq % Hkv
     assert call(15, A) == INVALID                 # row_idx without row_mass / row_count
+    assert call(6, 9 * 1024 * 1024) == UNSUPPORTED   # one kv head past the 32-bit buffer range
 
 
 def test_decode_validation(lib):
@@ -312,6 +313,7 @@ def test_prefill_validation(lib):
     assert call(8, 64) == UNSUPPORTED             # D = 64
     assert call(12, None) == INVALID              # count
     assert call(13, 0) == INVALID                 # kmax
+    assert call(7, 9 * 1024 * 1024) == UNSUPPORTED   # one kv head past the 32-bit buffer range
 
 
 def test_decode_step_validation(lib):

@@ -157,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       u32x4 w[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int kr = min(key0 + ldr + 16 * (p0 + p), L - 1);
+        const int kr = key0 + ldr + 16 * (p0 + p);   // rows past L read as 0
         w[p] = bld16(rK, (kr * PF_D + 8 * ldc) * 2);
       }
 #pragma unroll
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       u32x4 w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int vr = min(key0 + k0 + j, L - 1);
+        const int vr = key0 + k0 + j;
         w[j] = bld16(rV, (vr * PF_D + 8 * vc) * 2);
       }
 #pragma unroll

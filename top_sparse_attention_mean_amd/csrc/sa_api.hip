@@ -501,6 +501,8 @@ sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq,
   SUP(dtype == SA_BF16, "the dense pass runs on bf16 matrix cores: dtype must be SA_BF16");
   SUP(D == 128, "the mass selector supports D = 128");
   SUP(block == 128, "the mass selector supports 128-token blocks");
+  SUP(long(L) * D * 2 <= 0x7f000000L, "the dense pass reads one kv head through a buffer "
+      "resource of at most 0x7f000000 bytes (L * D * 2 = %ld)", long(L) * D * 2);
   REQ(L >= 1, "L must be >= 1");
   REQ(k_free >= 1 && k_free <= 64, "k_free must be in [1, 64] (got %d)", k_free);
   const long units = long(B) * Hkv * cdiv(L, block);
@@ -551,6 +553,8 @@ sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V, int dty
   SUP(dtype == SA_BF16, "prefill runs on bf16 matrix cores: dtype must be SA_BF16");
   SUP(D == 128, "prefill supports D = 128");
   SUP(block == 128, "prefill supports 128-token blocks");
+  SUP(long(L) * D * 2 <= 0x7f000000L, "prefill reads one kv head through a buffer resource of "
+      "at most 0x7f000000 bytes (L * D * 2 = %ld)", long(L) * D * 2);
   const long units = long(B) * Hkv * cdiv(L, block);
   REQ(cdiv(units, 8) * 8L * (Hq / Hkv) < (1L << 31), "grid too large");
   return hip_status(launch_prefill(Q, K, V, B, Hq, Hkv, L, D, eff_scale(scale, D), block, idx,
