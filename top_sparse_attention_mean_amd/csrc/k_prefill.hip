@@ -126,8 +126,6 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
   }
 
   const size_t kvbase = (size_t(b) * Hkv + kh) * size_t(L) * PF_D;
-  const __amdgpu_buffer_rsrc_t rK = make_rsrc(K + kvbase, uint32_t(L) * PF_D * 2);
-  const __amdgpu_buffer_rsrc_t rV = make_rsrc(V + kvbase, uint32_t(L) * PF_D * 2);
   const int32_t* lst = idx + (size_t(bkh) * M + i) * kmax;
   const int cnt = min(max(count[size_t(bkh) * M + i], 0), kmax);
 
@@ -151,14 +149,19 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
     if (jb < 0 || jb > i) continue;          // uniform
     const int key0 = jb * PF_BLK;
     // ---- stage K (row-major) and V^T; all 16 loads of a thread are in flight
-    //      at once
+    //      at once.  The block's rows go through resources based at its first
+    //      row (scalar work), so each load's lane offset is the same for every
+    //      block; rows past L lie beyond the resource's range and read as 0.
+    const size_t boff = kvbase + size_t(key0) * PF_D;
+    const uint32_t bbytes = uint32_t(L - key0) * PF_D * 2;
+    const __amdgpu_buffer_rsrc_t rKb = make_rsrc(K + boff, bbytes);
+    const __amdgpu_buffer_rsrc_t rVb = make_rsrc(V + boff, bbytes);
 #pragma unroll
     for (int p0 = 0; p0 < 8; p0 += 4) {
       u32x4 w[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const int kr = key0 + ldr + 16 * (p0 + p);   // rows past L read as 0
-        w[p] = bld16(rK, (kr * PF_D + 8 * ldc) * 2);
+        w[p] = bld16(rKb, ((ldr + 16 * (p0 + p)) * PF_D + 8 * ldc) * 2);
       }
 #pragma unroll
       for (int p = 0; p < 4; ++p)
@@ -170,8 +173,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       u32x4 w[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int vr = key0 + k0 + j;
-        w[j] = bld16(rV, (vr * PF_D + 8 * vc) * 2);
+        w[j] = bld16(rVb, ((k0 + j) * PF_D + 8 * vc) * 2);
       }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
