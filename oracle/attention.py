@@ -581,7 +581,6 @@ def select_threshold_pruned(q: np.ndarray, K: np.ndarray, tau: np.ndarray, block
 
 # ------------------------------------------------------------------ O11
 _THIRD32 = np.float32(1.0) / np.float32(3.0)
-_INV127_32 = np.float32(1.0) / np.float32(127.0)
 
 
 def lowbit_encode(K: np.ndarray, block: int):
@@ -654,10 +653,19 @@ def lowbit_reconstruct(codes: np.ndarray, resid: np.ndarray, meta: np.ndarray,
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bf16 (ties to even), returned as float64."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+    """float32 -> nearest bf16 (ties to even), returned as float64.
+
+    The plain IEEE rule on the bit pattern: add half a bf16 unit minus one,
+    plus the lowest kept bit (so exact halves go to the even neighbour), and
+    drop the low 16 bits.  Finite values past the largest bf16 round to
+    infinity, infinities stay, and a NaN stays a NaN (quiet, sign kept).
+    """
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    nan = np.isnan(f)
+    r = np.where(nan, (u & 0xFFFF0000) | 0x00400000, r)
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)
 
 
 def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
@@ -672,16 +680,11 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
     its group has a provisional score >= tau_h - margin, tau = m~ - delta;
     the blocks holding sink or local tokens are always kept (they set m~);
     (3) exact attention over the kept blocks with the refined keys (O4).
-    Readings taken: the refined key is k^ rounded to bf16, the precision of
-    the cache it stands for; the provisional score of token t in block j is
-    the thumbnail dot product split into the block's offset and its code
-    term, with the per-channel weights w_c = fl32(q_c step_j,c) quantised to
-    int8 for the matrix cores (the codes 0..3 are exact there):
-        scale * (q . lo_j + ws * sum_c w8_c code_t,c),
-        ws = fl32(max_c |w_c| * fl32(1/127)),
-        w8_c = clip(rint(fl32(w_c * fl32(127 / max_c |w_c|))), +-127)
-    (every step one float32 operation; w8 = 0 when the maximum is 0); `margin` (>= 0)
-    widens the filter against the thumbnail error.
+    Readings taken: the provisional score of token t is the plain thumbnail
+    dot product scale * q . t_t, in float64, with t = fma(code, step, lo) the
+    float32 thumbnail of the codec (O11b); the refined key is k^ rounded to
+    bf16, the precision of the cache it stands for; `margin` (>= 0) widens
+    the filter against the thumbnail error.
     Returns (idx, count, tau, bmax): idx [B, Hkv, nb] ascending block ids
     (count valid), tau [B, Hq], bmax [B, Hq, nb] the largest provisional
     score of each block.
@@ -692,6 +695,7 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
     nb = -(-N // block)
     sc = _default_scale(D, scale)
     khat = bf16_round(lowbit_reconstruct(codes, resid, meta, block))
+    thumb = lowbit_thumbnail(codes, meta, block).astype(np.float64)
     win = window_tokens(N, sink, local)
     if win.size == 0:
         raise ValueError("the sink and local windows are both empty")
@@ -706,22 +710,9 @@ def select_topdelta_lowbit(q: np.ndarray, codes: np.ndarray, resid: np.ndarray,
             keep[forced] = True
             for h in range(kh * g, (kh + 1) * g):
                 tau[b, h] = (khat[b, kh, win] @ q[b, h]).max() * sc - float(delta)
-                q32 = q[b, h].astype(np.float32)
+                prov = (thumb[b, kh] @ q[b, h]) * sc
                 for j in range(nb):
-                    lo_j, step_j = meta[b, kh, j, 0], meta[b, kh, j, 1]
-                    w = q32 * step_j
-                    wmax = np.float32(np.abs(w).max())
-                    ws = wmax * _INV127_32
-                    if wmax > 0:
-                        winv = np.float32(127.0) / wmax
-                        w8 = np.clip(np.rint(w * winv), -127, 127).astype(np.int64)
-                    else:
-                        w8 = np.zeros(w.shape, dtype=np.int64)
-                    rows = slice(j * block, min((j + 1) * block, N))
-                    acc = codes[b, kh, rows].astype(np.int64) @ w8
-                    prov = (float(q[b, h] @ lo_j.astype(np.float64))
-                            + float(ws) * acc.astype(np.float64)) * sc
-                    bmax[b, h, j] = prov.max()
+                    bmax[b, h, j] = prov[j * block:min((j + 1) * block, N)].max()
                 keep |= bmax[b, h] >= tau[b, h] - float(margin)
             sel = np.nonzero(keep)[0]
             idx[b, kh, :sel.size] = sel

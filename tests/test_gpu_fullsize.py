@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 from oracle.attention import exact_scores, widen
-from tests.parity_util import check_topk_row, max_abs, to_dev
+from tests.parity_util import (check_topk_row, lowbit_bmax_bound, lowbit_kept_band, max_abs,
+                                 to_dev)
 from workloads import get_workload, make_inputs
 
 pytestmark = pytest.mark.gpu
@@ -195,14 +196,28 @@ def test_full_lowbit_topdelta():
     assert np.array_equal(meta.cpu().numpy().view(np.uint32), m_x.view(np.uint32))
     i_x, n_x, t_x, b_x = oracle.select_topdelta_lowbit(q, c_x, r_x, m_x, wl.block, wl.sink,
                                                        wl.local, wl.delta, wl.margin)
-    assert max_abs(bmax.cpu().numpy(), b_x) <= 1e-4 * (1 + np.abs(b_x).max())
-    assert max_abs(tau.cpu().numpy(), t_x) <= 1e-3 * (1 + np.abs(t_x).max())
+    tau_h, bmax_h = tau.cpu().numpy(), bmax.cpu().numpy()
+    tau_up = 1e-6 * (1 + np.abs(t_x))
+    tau_down = 1e-3 * (1 + np.abs(t_x))
+    assert np.all(tau_h <= t_x + tau_up) and np.all(tau_h >= t_x - tau_down)
+    delta, _ = lowbit_bmax_bound(q, c_x, m_x, wl.block, 1.0 / math.sqrt(wl.D))
+    dev = np.abs(bmax_h - b_x)
+    assert np.all(dev <= delta), float((dev - delta).max())
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     assert cnt_h.max() <= wl.cap
-    # the oracle's kept set, away from the band, is the GPU's
-    agree = np.mean([set(idx_h[b, k, :cnt_h[b, k]].tolist()) == set(i_x[b, k, :n_x[b, k]].tolist())
-                     for b in range(wl.B) for k in range(wl.Hkv)])
-    assert agree >= 0.9
+    # the oracle's kept set outside the bound's band is the GPU's
+    win = np.unique(oracle.window_tokens(wl.N, wl.sink, wl.local) // wl.block)
+    agree = []
+    for b in range(wl.B):
+        for kh in range(wl.Hkv):
+            got = set(idx_h[b, kh, :cnt_h[b, kh]].tolist())
+            hs = list(range(kh * wl.g, (kh + 1) * wl.g))
+            must, may = lowbit_kept_band(b_x[b], t_x[b], delta[b], wl.margin, win, hs,
+                                         tau_up[b], tau_down[b])
+            assert set(np.nonzero(must)[0].tolist()) <= got
+            assert all(may[j] for j in got)
+            agree.append(got == set(i_x[b, kh, :n_x[b, kh]].tolist()))
+    agree = float(np.mean(agree))
     # recall of the exact top-delta rule on the full-precision keys
     lists, _, _ = oracle.select_topdelta(q, K, wl.sink, wl.local, wl.delta)
     rec = []

@@ -399,7 +399,7 @@ def test_mass_oracle_rows_by_scipy_and_block_average():
             np.testing.assert_allclose(avg, shared[(0, kh, i)][0], atol=1e-12)
 
 
-# ------------------------------------------------------------------ needles# ------------------------------------------------------------------ needles# ------------------------------------------------------------------ needles
+# ------------------------------------------------------------------ needles
 @pytest.mark.parametrize("name,over", [
     ("tiny_decode_f32", {}),
     ("gqa_decode_bf16", {"B": 1, "Hq": 8, "Hkv": 2}),
@@ -436,6 +436,37 @@ def test_bf16_rounding_matches_torch():
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(ours, ref)
     np.testing.assert_array_equal(bf16_bits_to_f32(ours), A.widen(ours, "bf16").astype(np.float32))
+
+
+def test_golden_bf16_round():
+    """oracle.bf16_round against hand-derived bit patterns (ties to even,
+    subnormals, overflow, signed zeros, infinities)."""
+    rows = [v for k, v in read_golden("bf16_round.txt") if k == "case"]
+    assert len(rows) >= 15
+    src = np.array([int(a, 16) for a, _ in rows], dtype=np.uint32).view(np.float32)
+    want = np.array([int(b, 16) << 16 for _, b in rows], dtype=np.uint32)
+    got = A.bf16_round(src).astype(np.float32).view(np.uint32)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_bf16_round_matches_torch():
+    """oracle.bf16_round equals torch's float32 -> bfloat16 conversion on
+    random values of every magnitude, on exact ties, on subnormals and on the
+    non-finite values (a NaN stays a NaN)."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(51)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    ties = (rng.integers(0, 2 ** 16, size=4000, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    sub = rng.integers(0, 0x00800000, size=4000, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0x7F800000, 0xFF800000, 0x7FC00000, 0xFFC00000, 0x7F800001,
+                        0xFFFFFFFF, 0x7F7FFFFF, 0xFF7FFFFF, 0x00000000, 0x80000000],
+                       dtype=np.uint32)
+    x = np.concatenate([bits, ties, sub, sub | 0x80000000, special]).view(np.float32)
+    got = A.bf16_round(x)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan].view(np.uint64), ref[~nan].view(np.uint64))
 
 
 def test_inputs_are_seeded():
@@ -719,25 +750,23 @@ def test_lowbit_codes_are_nearest_levels_and_errors_bounded(seed):
 
 def test_lowbit_on_grid_keys_is_exact_top_delta():
     """Keys already on each block's four levels: thumbnails equal the keys,
-    residuals vanish, and with one step per block and q in {-1, 0, 1} the
-    int8 weights are exact (+-127 ws), so the provisional block maxima are the
-    exact ones up to float32 rounding and, at margin 0, the filter keeps
-    exactly the blocks holding a token at or above m~ - delta (plus the
-    window's blocks)."""
+    residuals vanish, and with margin 0 the filter keeps exactly the blocks
+    holding a token at or above m~ - delta (plus the window's blocks).  Every
+    value is dyadic, so the float64 provisional maxima are the exact ones."""
     rng = np.random.default_rng(520)
     B, Hq, Hkv, N, D, block = 1, 4, 2, 512, 8, 64
     nb = N // block
     lo = rng.integers(-8, 8, size=(B, Hkv, nb, D)) / 4.0
-    s = np.broadcast_to(2.0 ** rng.integers(-3, 1, size=(B, Hkv, nb, 1)), (B, Hkv, nb, D))
+    s = 2.0 ** rng.integers(-3, 1, size=(B, Hkv, nb, D))
     lev = rng.integers(0, 4, size=(B, Hkv, N, D))
     lev[:, :, ::block, :] = 0                      # every level range spans 0..3
     lev[:, :, 1::block, :] = 3
     K = np.repeat(lo, block, 2) + lev * np.repeat(s, block, 2)
-    q = rng.integers(-1, 2, size=(B, Hq, D)).astype(float)
+    q = rng.integers(-4, 5, size=(B, Hq, D)) / 2.0
     codes, resid, meta = oracle.lowbit_encode(K, block)
     assert np.array_equal(codes, lev) and not resid.any()
     np.testing.assert_array_equal(oracle.lowbit_reconstruct(codes, resid, meta, block), K)
-    sink, local, delta = 8, 8, 3.1                 # delta off the dyadic grid: no exact ties
+    sink, local, delta = 8, 8, 3.0
     idx, cnt, tau, bmax = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, sink, local,
                                                         delta, 0.0)
     _, _, tau_x = oracle.select_topdelta(q, K, sink, local, delta)
@@ -746,15 +775,42 @@ def test_lowbit_on_grid_keys_is_exact_top_delta():
     for kh in range(Hkv):
         want = {0, nb - 1}
         for h in range(kh * 2, kh * 2 + 2):
-            exact_max = sx[0, h].reshape(nb, block).max(-1)
-            np.testing.assert_allclose(bmax[0, h], exact_max, rtol=1e-6, atol=1e-6)
-            assert np.all(np.abs(exact_max - tau_x[0, h]) > 1e-3)
             want |= {t // block for t in np.nonzero(sx[0, h] >= tau_x[0, h])[0]}
+            np.testing.assert_allclose(bmax[0, h], sx[0, h].reshape(nb, block).max(-1), atol=1e-12)
         assert idx[0, kh, :cnt[0, kh]].tolist() == sorted(want)
     # an infinite margin keeps every block
     _, cnt, _, _ = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, sink, local, delta,
                                                  np.inf)
     assert np.all(cnt == nb)
+
+
+def test_lowbit_provisional_scores_are_thumbnail_products():
+    """Off the grid: each block's provisional maximum is the largest scaled
+    product of the query with a thumbnail row, the thumbnail being the codec's
+    level lo + code * step (rounded to float32, so within half a float32 unit
+    of that level), checked by a plain loop over tokens and channels."""
+    rng = np.random.default_rng(521)
+    B, Hq, Hkv, N, D, block = 1, 2, 1, 150, 16, 64
+    K = rng.standard_normal((B, Hkv, N, D)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, D))
+    codes, resid, meta = oracle.lowbit_encode(K, block)
+    _, _, _, bmax = oracle.select_topdelta_lowbit(q, codes, resid, meta, block, 4, 4, 5.0, 0.0)
+    sc = 1.0 / math.sqrt(D)
+    for h in range(Hq):
+        for j in range(-(-N // block)):
+            best = -np.inf
+            for t in range(j * block, min((j + 1) * block, N)):
+                acc = 0.0
+                for c in range(D):
+                    lo_c, st_c = float(meta[0, 0, j, 0, c]), float(meta[0, 0, j, 1, c])
+                    level = lo_c + int(codes[0, 0, t, c]) * st_c
+                    acc += q[0, h, c] * level
+                best = max(best, acc * sc)
+            # float32 thumbnails: each level moves by at most half a unit
+            slack = sc * sum(abs(q[0, h, c]) * 2.0 ** -24 *
+                             (abs(float(meta[0, 0, j, 0, c])) + 3 * float(meta[0, 0, j, 1, c]))
+                             for c in range(D)) + 1e-12
+            assert abs(bmax[0, h, j] - best) <= slack, (h, j, bmax[0, h, j], best)
 
 
 def test_lowbit_recall_on_the_top_delta_workload():
