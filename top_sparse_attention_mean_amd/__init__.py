@@ -124,12 +124,57 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _dev(*ts):
+    dev = None
     for t in ts:
         if t is not None:
             if not t.is_cuda:
                 raise ValueError("tensors must live on the GPU")
             if not t.is_contiguous():
                 raise ValueError("tensors must be contiguous")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"tensors must live on one device ({dev} and {t.device})")
+
+
+_FP = (torch.bfloat16, torch.float32)
+_I32 = (torch.int32,)
+_F32 = (torch.float32,)
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape=None, dtypes=None) -> None:
+    """Raise ValueError unless t (when given) has this shape and one of these
+    dtypes.  Runs before anything is launched: a wrong size or element type
+    would otherwise make a kernel read or write past the end of a buffer."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)} "
+                         f"(got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)} "
+                         f"(got {tuple(t.shape)})")
+
+
+def _rank(t: torch.Tensor, name: str, n: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions (got shape {tuple(t.shape)})")
+
+
+def _qk_shapes(Q: torch.Tensor, K: torch.Tensor):
+    """(B, Hq, D, Hkv, N) of a decode query [B, Hq, D] and a cache [B, Hkv, N, D]
+    of the same dtype."""
+    _rank(Q, "Q", 3)
+    _rank(K, "K", 4)
+    B, Hq, D = Q.shape
+    Hkv, N = K.shape[1], K.shape[2]
+    _need(Q, "Q", None, _FP)
+    _need(K, "K", (B, Hkv, N, D), (Q.dtype,))
+    return B, Hq, D, Hkv, N
 
 
 def _stream(stream=None) -> int:
@@ -162,9 +207,14 @@ def sa_build_sketch(X: torch.Tensor, block: int, head_pool: int = 1, blk_begin: 
                     blk_end: Optional[int] = None, out: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
     """Per-block mean sketch of X [B, H, N, D] -> float32 [B, H/head_pool, nb, D]."""
-    _dev(X, out)
+    _rank(X, "X", 4)
+    _need(X, "X", None, _FP)
     B, H, N, D = X.shape
     nb = -(-N // block)
+    if head_pool < 1 or H % head_pool:
+        raise ValueError(f"head_pool ({head_pool}) must divide H ({H})")
+    _need(out, "out", (B, H // head_pool, nb, D), _F32)
+    _dev(X, out)
     if blk_end is None:
         blk_end = nb
     if out is None:
@@ -180,9 +230,13 @@ def sa_build_radius(X: torch.Tensor, sketch: torch.Tensor, block: int, S: int = 
     """Bounding-sphere radii of X [B, H, N, D] around its block sketch
     [B, H, nb, D], per subspace of D/S channels -> float32 [B, H, nb, S]
     (only blocks [blk_begin, blk_end) are written)."""
-    _dev(X, sketch, out)
+    _rank(X, "X", 4)
+    _need(X, "X", None, _FP)
     B, H, N, D = X.shape
     nb = -(-N // block)
+    _need(sketch, "sketch", (B, H, nb, D), _F32)
+    _need(out, "out", (B, H, nb, S), _F32)
+    _dev(X, sketch, out)
     if blk_end is None:
         blk_end = nb
     if out is None:
@@ -197,9 +251,14 @@ def sa_encode_keys(K: torch.Tensor, block: int, blk_begin: int = 0,
                    stream=None):
     """2-bit thumbnails + 8-bit residuals of K [B, H, N, D] -> codes uint8
     [B, H, N, D/4], resid int8 [B, H, N, D], meta float32 [B, H, nb, 3, D]."""
-    _dev(K, codes, resid, meta)
+    _rank(K, "K", 4)
+    _need(K, "K", None, _FP)
     B, H, N, D = K.shape
     nb = -(-N // block)
+    _need(codes, "codes", (B, H, N, D // 4), (torch.uint8,))
+    _need(resid, "resid", (B, H, N, D), (torch.int8,))
+    _need(meta, "meta", (B, H, nb, 3, D), _F32)
+    _dev(K, codes, resid, meta)
     if blk_end is None:
         blk_end = nb
     dev = K.device
@@ -220,9 +279,20 @@ def sa_decode_keys(codes: torch.Tensor, resid: torch.Tensor, meta: torch.Tensor,
                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Refined bf16 keys of the listed blocks (or a block range) into out
     [B, H, N, D] (zeros elsewhere when out is allocated here)."""
-    _dev(codes, resid, meta, idx, count, out)
+    _rank(resid, "resid", 4)
+    _need(resid, "resid", None, (torch.int8,))
     B, H, N, D = resid.shape
     nb = -(-N // block)
+    _need(codes, "codes", (B, H, N, D // 4), (torch.uint8,))
+    _need(meta, "meta", (B, H, nb, 3, D), _F32)
+    if idx is not None:
+        _rank(idx, "idx", 3)
+        _need(idx, "idx", (B, H, idx.shape[-1]), _I32)
+        if count is None:
+            raise ValueError("a block list needs its count")
+    _need(count, "count", (B, H), _I32)
+    _need(out, "out", (B, H, N, D), (torch.bfloat16,))
+    _dev(codes, resid, meta, idx, count, out)
     if blk_end is None:
         blk_end = nb
     if out is None:
@@ -246,14 +316,23 @@ def sa_select_topk(Q: torch.Tensor, ksketch: torch.Tensor, k: int,
     Causal prefill (flags & SA_CAUSAL): Q [B, Hq, L, D], q_block = key block ->
     idx [B, Hkv, M, k], count [B, Hkv, M] (score [B, Hkv, M, nb]).
     """
-    _dev(Q, ksketch, idx, count, score)
+    _rank(ksketch, "ksketch", 4)
+    _need(ksketch, "ksketch", None, _F32)
     B, Hkv_, nb, D = ksketch.shape
     Hkv = Hkv or Hkv_
-    Hq = Q.shape[1]
     causal = bool(flags & SA_CAUSAL)
+    _rank(Q, "Q", 4 if causal else 3)
+    Hq = Q.shape[1]
     Lq = Q.shape[2] if causal else 1
+    _need(Q, "Q", (B, Hq, Lq, D) if causal else (B, Hq, D), _FP)
+    if causal and Hkv != Hkv_:
+        raise ValueError(f"the key sketch has {Hkv_} kv heads, Hkv = {Hkv}")
     M = -(-Lq // q_block)
     rows = (B, Hkv, M) if causal else (B, Hkv)
+    _need(idx, "idx", (*rows, k), _I32)
+    _need(count, "count", rows, _I32)
+    _need(score, "score", (*rows, nb), _F32)
+    _dev(Q, ksketch, idx, count, score)
     if idx is None:
         idx = torch.empty(*rows, k, dtype=torch.int32, device=Q.device)
     if count is None:
@@ -277,9 +356,12 @@ def sa_select_threshold(Q: torch.Tensor, K: torch.Tensor, tau: torch.Tensor, cap
     Returns idx [B, Hq, cap] (ascending, -1 padded), score [B, Hq, cap] and
     count [B, Hq] (the true count, which may exceed cap).
     """
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    _need(tau, "tau", (B, Hq), _F32)
+    _need(idx, "idx", (B, Hq, cap), _I32)
+    _need(score, "score", (B, Hq, cap), _F32)
+    _need(count, "count", (B, Hq), _I32)
     _dev(Q, K, tau, idx, score, count)
-    B, Hq, D = Q.shape
-    _, Hkv, N, _ = K.shape
     dev = Q.device
     if idx is None:
         idx = torch.empty(B, Hq, cap, dtype=torch.int32, device=dev)
@@ -307,10 +389,18 @@ def sa_select_threshold_pruned(Q: torch.Tensor, K: torch.Tensor, sketch: torch.T
     uint8: bit i of a 128-token segment's byte is set when its i-th block was
     scanned.
     """
-    _dev(Q, K, sketch, radius, tau, idx, score, count, live)
-    B, Hq, D = Q.shape
-    _, Hkv, N, _ = K.shape
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    nb = -(-N // block)
+    _rank(radius, "radius", 4)
     S = radius.shape[-1]
+    _need(sketch, "sketch", (B, Hkv, nb, D), _F32)
+    _need(radius, "radius", (B, Hkv, nb, S), _F32)
+    _need(tau, "tau", (B, Hq), _F32)
+    _need(idx, "idx", (B, Hq, cap), _I32)
+    _need(score, "score", (B, Hq, cap), _F32)
+    _need(count, "count", (B, Hq), _I32)
+    _need(live, "live", (B, Hkv, -(-N // 128)), (torch.uint8,))
+    _dev(Q, K, sketch, radius, tau, idx, score, count, live)
     dev = Q.device
     if idx is None:
         idx = torch.empty(B, Hq, cap, dtype=torch.int32, device=dev)
@@ -338,10 +428,20 @@ def sa_select_topdelta_lowbit(Q: torch.Tensor, codes: torch.Tensor, resid: torch
     """Top-delta block filter over 2-bit thumbnails; refined keys of the kept
     blocks into khat.  Returns idx [B, Hkv, kcap], count [B, Hkv], tau [B, Hq],
     bmax [B, Hq, nb] (or None) and khat [B, Hkv, N, D] bf16."""
-    _dev(Q, codes, resid, meta, khat, idx, count, tau)
+    _rank(Q, "Q", 3)
+    _rank(resid, "resid", 4)
     B, Hq, D = Q.shape
     _, Hkv, N, _ = resid.shape
     nb = -(-N // block)
+    _need(Q, "Q", None, (torch.bfloat16,))
+    _need(resid, "resid", (B, Hkv, N, D), (torch.int8,))
+    _need(codes, "codes", (B, Hkv, N, D // 4), (torch.uint8,))
+    _need(meta, "meta", (B, Hkv, nb, 3, D), _F32)
+    _need(khat, "khat", (B, Hkv, N, D), (torch.bfloat16,))
+    _need(idx, "idx", (B, Hkv, kcap), _I32)
+    _need(count, "count", (B, Hkv), _I32)
+    _need(tau, "tau", (B, Hq), _F32)
+    _dev(Q, codes, resid, meta, khat, idx, count, tau)
     dev = Q.device
     if khat is None:
         khat = torch.zeros(B, Hkv, N, D, dtype=torch.bfloat16, device=dev)
@@ -370,10 +470,16 @@ def sa_mass_select(Q: torch.Tensor, K: torch.Tensor, k_free: int, block: int = 1
     [B, Hkv, M, M] when asked, and with per_row the per-query supports
     (row_idx [B, Hkv, L, k_free], row_count [B, Hkv, L], row_mass [B, Hkv, L, M]);
     returns (idx, count, mass, rows) with rows = (row_idx, row_count, row_mass) or None."""
-    _dev(Q, K, idx, count)
+    _rank(Q, "Q", 4)
+    _rank(K, "K", 4)
     B, Hq, L, D = Q.shape
     Hkv = K.shape[1]
     M = -(-L // block)
+    _need(Q, "Q", None, _FP)
+    _need(K, "K", (B, Hkv, L, D), (Q.dtype,))
+    _need(idx, "idx", (B, Hkv, M, k_free), _I32)
+    _need(count, "count", (B, Hkv, M), _I32)
+    _dev(Q, K, idx, count)
     dev = Q.device
     if idx is None:
         idx = torch.empty(B, Hkv, M, k_free, dtype=torch.int32, device=dev)
@@ -405,9 +511,12 @@ def sa_select_topdelta(Q: torch.Tensor, K: torch.Tensor, sink: int, local: int, 
     count [B, Hq] (the true count, which may exceed cap) and tau [B, Hq], the
     threshold the scan used.
     """
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    _need(idx, "idx", (B, Hq, cap), _I32)
+    _need(score, "score", (B, Hq, cap), _F32)
+    _need(count, "count", (B, Hq), _I32)
+    _need(tau, "tau", (B, Hq), _F32)
     _dev(Q, K, idx, score, count, tau)
-    B, Hq, D = Q.shape
-    _, Hkv, N, _ = K.shape
     dev = Q.device
     if idx is None:
         idx = torch.empty(B, Hq, cap, dtype=torch.int32, device=dev)
@@ -433,11 +542,18 @@ def sa_sparse_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: tor
                      lse: Optional[torch.Tensor] = None, want_lse: bool = True, ws=None,
                      stream=None):
     """Exact attention over the selected blocks/tokens: O [B, Hq, D], lse [B, Hq]."""
-    _dev(Q, K, V, idx, count, score, O, lse)
-    B, Hq, D = Q.shape
-    _, Hkv, N, _ = K.shape
-    dev = Q.device
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    _need(V, "V", (B, Hkv, N, D), (Q.dtype,))
+    rows = (B, Hkv) if mode == SA_IDX_BLOCKS else (B, Hq)
+    _rank(idx, "idx", 3)
+    _need(idx, "idx", (*rows, idx.shape[-1]), _I32)
+    _need(count, "count", rows, _I32)
+    _need(score, "score", (B, Hq, idx.shape[-1]) if mode == SA_IDX_TOKENS else None, _F32)
     od = out_dtype or Q.dtype
+    _need(O, "O", (B, Hq, D), (od,) if out_dtype else _FP)
+    _need(lse, "lse", (B, Hq), _F32)
+    _dev(Q, K, V, idx, count, score, O, lse)
+    dev = Q.device
     if O is None:
         O = torch.empty(B, Hq, D, dtype=od, device=dev)
     if lse is None and want_lse:
@@ -458,11 +574,22 @@ def sa_sparse_prefill(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: to
                       out_dtype: Optional[torch.dtype] = None, O=None, lse=None,
                       want_lse: bool = True, stream=None):
     """Block-sparse causal prefill: O [B, Hq, L, D], lse [B, Hq, L]."""
-    _dev(Q, K, V, idx, count, O, lse)
+    _rank(Q, "Q", 4)
+    _rank(K, "K", 4)
     B, Hq, L, D = Q.shape
     Hkv = K.shape[1]
-    dev = Q.device
+    M = -(-L // block)
+    _need(Q, "Q", None, _FP)
+    _need(K, "K", (B, Hkv, L, D), (Q.dtype,))
+    _need(V, "V", (B, Hkv, L, D), (Q.dtype,))
+    _rank(idx, "idx", 4)
+    _need(idx, "idx", (B, Hkv, M, idx.shape[-1]), _I32)
+    _need(count, "count", (B, Hkv, M), _I32)
     od = out_dtype or Q.dtype
+    _need(O, "O", (B, Hq, L, D), (od,) if out_dtype else _FP)
+    _need(lse, "lse", (B, Hq, L), _F32)
+    _dev(Q, K, V, idx, count, O, lse)
+    dev = Q.device
     if O is None:
         O = torch.empty(B, Hq, L, D, dtype=od, device=dev)
     if lse is None and want_lse:
@@ -478,9 +605,16 @@ def sa_decode_step(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksketch: t
                    out_dtype=None, idx=None, count=None, score=None, O=None, lse=None,
                    want_lse: bool = True, ws=None, stream=None):
     """One decode step: optional sketch update of one block, top-k select, sparse attention."""
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    nb = -(-N // block)
+    _need(V, "V", (B, Hkv, N, D), (Q.dtype,))
+    _need(ksketch, "ksketch", (B, Hkv, nb, D), _F32)
+    _need(idx, "idx", (B, Hkv, k), _I32)
+    _need(count, "count", (B, Hkv), _I32)
+    _need(score, "score", (B, Hkv, nb), _F32)
+    _need(O, "O", (B, Hq, D), (out_dtype,) if out_dtype else _FP)
+    _need(lse, "lse", (B, Hq), _F32)
     _dev(Q, K, V, ksketch, idx, count, score, O, lse)
-    B, Hq, D = Q.shape
-    _, Hkv, N, _ = K.shape
     dev = Q.device
     if idx is None:
         idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
@@ -505,9 +639,15 @@ def sa_select_decode(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, score: t
                      scale: float = 0.0, out_dtype=None, idx=None, count=None, O=None, lse=None,
                      want_lse: bool = True, ws=None, stream=None):
     """Top-k selection from block scores fused with the split-K sparse decode."""
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    nb = -(-N // block)
+    _need(V, "V", (B, Hkv, N, D), (Q.dtype,))
+    _need(score, "score", (B, Hkv, nb), _F32)
+    _need(idx, "idx", (B, Hkv, k), _I32)
+    _need(count, "count", (B, Hkv), _I32)
+    _need(O, "O", (B, Hq, D), (out_dtype,) if out_dtype else _FP)
+    _need(lse, "lse", (B, Hq), _F32)
     _dev(Q, K, V, score, idx, count, O, lse)
-    B, Hq, D = Q.shape
-    _, Hkv, N, _ = K.shape
     dev = Q.device
     if idx is None:
         idx = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
