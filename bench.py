@@ -64,33 +64,50 @@ def time_loop(fn, n, stream):
     return start.elapsed_time(end) * 1e3 / n   # us per call
 
 
-def graph_time(fn, R, n_replay, warmup=3):
-    """Capture fn(0..R-1) once as a HIP graph; time n_replay replays with HIP
-    events on the replay stream.  Returns microseconds per fn call."""
+def graph_trials(fn, calls, R, trials=10, warmup=1):
+    """Capture `calls` calls fn(i % R) as one HIP graph and replay it `trials`
+    times after `warmup` untimed replays.  Each replay is timed with HIP events
+    recorded on the replay stream, the stream the kernels run on; a short
+    device-side spin queued first keeps the stream busy while the host
+    enqueues the replay, so the start event cannot run ahead of the graph.
+    Returns (median, min, max) microseconds per call over the trials."""
     import torch
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for r in range(R):              # one eager pass outside capture
+        for r in range(min(calls, R)):  # one eager pass outside capture
             fn(r)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        for r in range(R):
-            fn(r)
+        for i in range(calls):
+            fn(i % R)
     torch.cuda.synchronize()
+    per = []
     with torch.cuda.stream(s):
         for _ in range(warmup):
             g.replay()
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(s)
-        for _ in range(n_replay):
+        for _ in range(trials):
+            start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(200000)
+            start.record(s)
             g.replay()
-        end.record(s)
+            end.record(s)
+            end.synchronize()
+            per.append(start.elapsed_time(end) * 1e3 / calls)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) * 1e3 / (n_replay * R)
+    per.sort()
+    return per[len(per) // 2], per[0], per[-1]
+
+
+def graph_time(fn, R, n_replay, warmup=3):
+    """Median microseconds per call of fn(0..R-1) over at least ten timed
+    graph replays (see graph_trials)."""
+    reps = max(1, n_replay // 10)
+    med, _, _ = graph_trials(fn, R * reps, R, trials=10, warmup=max(1, warmup // reps))
+    return med
 
 
 def _blas_threads() -> int:
@@ -124,10 +141,10 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0) -> dict:
                       f"BLAS threads={threads}); sketch build excluded (amortised at prefill)"}
 
 
-# The sources the counted kernels (the selecting decode and the scoring scan)
-# and their launch configuration are built from.
-COUNTED_SOURCES = ["k_decode.hip", "k_select.hip", "sa_device.h", "sa_internal.h",
-                   "sa_score_core.h", "sa_select_core.h"]
+# The sources the counted kernel (the selecting split-K decode of the step)
+# and its launch configuration are built from.
+COUNTED_SOURCES = ["k_decode.hip", "sa_decode_core.h", "sa_device.h", "sa_internal.h",
+                   "sa_select_core.h", "sa_api.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -177,105 +194,140 @@ def _layers(wl, R, dev):
     return inp, Qs, Ks, Vs, sks, scores
 
 
-def bench_decode(args) -> dict:
+DOMINANT_BF16 = "k_decode_blocks_mfma (sa_select_decode: top-k + split-K attention + merge)"
+DOMINANT_F32 = "k_decode_blocks_valu (sa_sparse_decode on the step's lists: split-K + merge)"
+
+
+def bench_decode(args, name=None, calls=None, layers=None, extras=True) -> dict:
+    """One decode step per call (sa_decode_step), timed as HIP-graph replays of
+    `calls` steps cycling `layers` layer copies, median of args.trials replays."""
+    import math
     import torch
     import top_sparse_attention_mean_amd as sa
     from workloads import get_workload
 
-    wl = get_workload(args.workload)
+    wl = get_workload(name or args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    R = args.layers
+    R = layers or args.layers
+    K = calls or args.steps
     inp, Qs, Ks, Vs, sks, scores = _layers(wl, R, dev)
     B, Hq, Hkv, D = wl.B, wl.Hq, wl.Hkv, wl.D
     idx = torch.empty(B, Hkv, wl.k, dtype=torch.int32, device=dev)
     cnt = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
     O = torch.empty(B, Hq, D, dtype=Qs[0].dtype, device=dev)
     lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
-    ws = torch.zeros(sa.workspace_bytes(sa.SA_OP_DECODE_STEP, B, Hq, Hkv, wl.N, D, wl.block,
-                                        wl.k), dtype=torch.uint8, device=dev)
+    wsb = sa.workspace_bytes(sa.SA_OP_DECODE_STEP, B, Hq, Hkv, wl.N, D, wl.block, wl.k)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
     st = torch.cuda.current_stream()
     upd = wl.nb - 1
 
-    def step(i):
+    def step(i, w=ws):
         r = i % R
         sa.sa_decode_step(Qs[r], Ks[r], Vs[r], sks[r], wl.k, block=wl.block, update_block=upd,
-                          idx=idx, count=cnt, O=O, lse=lse, ws=ws)
+                          idx=idx, count=cnt, O=O, lse=lse, ws=w)
 
-    # the timed region: HIP-graph replays of one step per layer copy, launched
-    # back to back on one stream (no host launch cost inside the region)
-    n_rep = max(1, args.steps // R)
-    steps = n_rep * R
-    us_step = graph_time(step, R, n_rep, warmup=max(1, args.warmup // R))
-    us_eager = time_loop(step, min(args.steps, 500), st)
-
-    # the step's two kernels: the fused select + split-K + merge kernel timed on
-    # its own (sa_select_decode on each layer's block scores); the scoring kernel
-    # (sketch scan + newest-block refresh) is the remainder of the step
-    dws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, wl.N, D, wl.block,
-                                         wl.k), dtype=torch.uint8, device=dev)
-    t_sd = graph_time(lambda r: sa.sa_select_decode(Qs[r], Ks[r], Vs[r], scores[r], wl.k,
-                                                    block=wl.block, idx=idx, count=cnt, O=O,
-                                                    lse=lse, ws=dws), R, n_rep)
-    t_score = max(us_step - t_sd, 0.0)
-    # unfused path for context: standalone selection kernel, then block decode
-    sws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_TOPK, B, Hq, Hkv, 1, D, 1, wl.nb),
-                      dtype=torch.uint8, device=dev)
-    t_sel = graph_time(lambda r: sa.sa_select_topk(Qs[r], sks[r], wl.k, idx=idx, count=cnt,
-                                                   ws=sws), R, n_rep)
-    t_dec = graph_time(lambda r: sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], idx, cnt,
-                                                     block=wl.block, O=O, lse=lse, ws=dws), R, n_rep)
-    # dense reference: the same decode kernel with every block selected
-    all_idx = torch.arange(wl.nb, dtype=torch.int32, device=dev).repeat(B, Hkv, 1).contiguous()
-    all_cnt = torch.full((B, Hkv), wl.nb, dtype=torch.int32, device=dev)
-    dn_ws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, wl.N, D, wl.block,
-                                           wl.nb), dtype=torch.uint8, device=dev)
-    t_dense = graph_time(lambda r: sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], all_idx, all_cnt,
-                                                       block=wl.block, O=O, lse=lse, ws=dn_ws),
-                         R, max(2, n_rep // 10))
-
+    warm = max(1, math.ceil(args.warmup / K))
+    med, lo, hi = graph_trials(step, K, R, trials=args.trials, warmup=warm)
     by = decode_bytes(wl)
-    gbps = by["total"] / (us_step * 1e-6) / 1e9
-    # the dominant kernel: select + split-K + merge; its algorithmic bytes are the
-    # selected K and V blocks, the score rows, Q, O + lse and the index lists
-    sd_bytes = by["kv"] + by["q"] + by["out"] + by["select_io"] + wl.B * wl.Hkv * wl.nb * 4
-    ach = sd_bytes / (t_sd * 1e-6) / 1e9
+    gbps = by["total"] / (med * 1e-6) / 1e9
+    bf = wl.dtype == "bf16"
+    # the dominant kernel on its own, same graph timing: the selecting split-K
+    # decode on each layer's block scores (bf16), or the block decode on the
+    # step's lists (float32); its algorithmic bytes are the selected K and V
+    # blocks, Q, O + lse and the index lists
+    dws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, wl.N, D,
+                                         wl.block, wl.k), dtype=torch.uint8, device=dev)
+    step(0)
+    if bf:
+        dom = lambda i: sa.sa_select_decode(Qs[i % R], Ks[i % R], Vs[i % R], scores[i % R], wl.k,
+                                            block=wl.block, idx=idx, count=cnt, O=O, lse=lse,
+                                            ws=dws)
+    else:
+        idx0, cnt0 = idx.clone(), cnt.clone()
+        dom = lambda i: sa.sa_sparse_decode(Qs[i % R], Ks[i % R], Vs[i % R], idx0, cnt0,
+                                            block=wl.block, O=O, lse=lse, ws=dws)
+    t_dom, _, _ = graph_trials(dom, K, R, trials=args.trials, warmup=warm)
+    dom_bytes = by["kv"] + by["q"] + by["out"] + by["select_io"]
+    ach = dom_bytes / (t_dom * 1e-6) / 1e9
     res = {
         "metric": METRIC,
-        "value": round(us_step, 3),
+        "value": round(med, 3),
         "unit": "us/step",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": K,
         "warmup": args.warmup,
-        "ms_per_step": round(us_step / 1e3, 6),
+        "ms_per_step": round(med / 1e3, 6),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded N(0,1) K/V/Q, AR(1) drift, planted needle blocks)",
+        "data": "synthetic (seeded N(0,1) K/V/Q, " + (
+            "AR(1) drift, " if wl.drift_var else "") + (
+            "4 outlier channels x8, " if wl.outlier_channels else "") + "planted needle blocks)",
         "config": {"workload": wl.name, "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "N": wl.N,
                    "block": wl.block, "k": wl.k, "layers_cycled": R,
                    "step": "sketch update (newest block) + score + top-k + split-K + merge"},
+        "trials": {"count": args.trials, "steps_per_trial": K, "us_per_step_min": round(lo, 3),
+                   "us_per_step_median": round(med, 3), "us_per_step_max": round(hi, 3)},
         "achieved_GBps": round(gbps, 1),
         "pct_of_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_step": by["total"],
-        "timing": "HIP graph replay of one step per layer copy (eager Python launches: "
-                  f"{us_eager:.2f} us/step)",
-        "kernels_us": {"k_decode_blocks_mfma (select + split-K + merge)": round(t_sd, 3),
-                       "k_score (sketch scan + newest-block refresh), step minus the above":
-                           round(t_score, 3)},
-        "unfused_us": {"sa_select_topk": round(t_sel, 3), "sa_sparse_decode": round(t_dec, 3)},
-        "dense_decode_us": round(t_dense, 2),
-        "sparse_vs_dense_speedup": round(t_dense / us_step, 2),
+        "algorithmic_bytes": {k2: v for k2, v in by.items() if k2 != "total"},
+        "timing": f"HIP graph of {K} steps (one per layer copy, {R} copies cycled) replayed "
+                  f"{args.trials} times after {warm} untimed replay(s), HIP events on the replay "
+                  "stream; value = median over the replays",
+        "kernels_us": {"dominant kernel alone": round(t_dom, 3),
+                       "rest of the step (scoring kernel, newest-block refresh, boundary)":
+                           round(max(med - t_dom, 0.0), 3)},
         "roofline": {"bound": "hbm",
-                     "kernel": "k_decode_blocks_mfma (sa_select_decode: top-k + split-K + merge)",
+                     "kernel": DOMINANT_BF16 if bf else DOMINANT_F32,
                      "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBPS, 4),
-                     "traffic": load_traffic("select_decode", wl.name),
-                     "algorithmic_bytes": sd_bytes, "avg_us": round(t_sd, 3)},
+                     "traffic": load_traffic("select_decode", wl.name) if bf else None,
+                     "traffic_source": (f"profiles/traffic_select_decode_{wl.name}.md: rocprofv3 "
+                                        "--pmc FETCH_SIZE and WRITE_SIZE of this kernel, scaled by "
+                                        "the same counters on a plain copy of known size; null "
+                                        "when the kernel sources changed since they were taken")
+                     if bf else None,
+                     "algorithmic_bytes": dom_bytes, "avg_us": round(t_dom, 3)},
     }
+    if not bf:
+        res["roofline"]["note"] = ("latency-bound: one launch moves under 0.3 MB, so GB/s says "
+                                   "little; the figure is the step time")
+    if extras:
+        res["eager_us_per_step"] = round(time_loop(step, min(args.steps, 500), st), 3)
+        # the one-launch form of the same step (k_step.hip), its own workspace
+        os.environ["SA_STEP_MODE"] = "1"
+        try:
+            ws2 = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+            t_one, _, _ = graph_trials(lambda i: step(i, ws2), min(K, 10 * R), R,
+                                       trials=args.trials)
+        finally:
+            del os.environ["SA_STEP_MODE"]
+        # unfused path for context: standalone selection kernel, then block decode
+        sws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SELECT_TOPK, B, Hq, Hkv, 1, D, 1, wl.nb),
+                          dtype=torch.uint8, device=dev)
+        n_rep = max(10, min(K, 10 * R) // R)
+        t_sel = graph_time(lambda r: sa.sa_select_topk(Qs[r], sks[r], wl.k, idx=idx, count=cnt,
+                                                       ws=sws), R, n_rep)
+        t_dec = graph_time(lambda r: sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], idx, cnt,
+                                                         block=wl.block, O=O, lse=lse, ws=dws),
+                           R, n_rep)
+        # dense reference: the same block decode with every block selected
+        all_idx = torch.arange(wl.nb, dtype=torch.int32, device=dev).repeat(B, Hkv, 1).contiguous()
+        all_cnt = torch.full((B, Hkv), wl.nb, dtype=torch.int32, device=dev)
+        dn_ws = torch.zeros(sa.workspace_bytes(sa.SA_OP_SPARSE_DECODE, B, Hq, Hkv, wl.N, D,
+                                               wl.block, wl.nb), dtype=torch.uint8, device=dev)
+        t_dense = graph_time(lambda r: sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], all_idx, all_cnt,
+                                                           block=wl.block, O=O, lse=lse,
+                                                           ws=dn_ws), R, 10)
+        res["one_launch_step_us"] = round(t_one, 3)
+        res["unfused_us"] = {"sa_select_topk": round(t_sel, 3), "sa_sparse_decode": round(t_dec, 3)}
+        res["dense_decode_us"] = round(t_dense, 2)
+        res["sparse_vs_dense_speedup"] = round(t_dense / med, 2)
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget)
+        res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_budget if extras else 6.0)
     return res
 
 
@@ -754,13 +806,16 @@ def pmc_run(args) -> dict:
     for _ in range(3):
         y.copy_(x)
     R = args.layers
-    _, Qs, Ks, Vs, _, scores = _layers(wl, R, dev)
+    _, Qs, Ks, Vs, sks, _ = _layers(wl, R, dev)
+    ws = torch.zeros(sa.workspace_bytes(sa.SA_OP_DECODE_STEP, wl.B, wl.Hq, wl.Hkv, wl.N, wl.D,
+                                        wl.block, wl.k), dtype=torch.uint8, device=dev)
     for _ in range(3):
         for r in range(R):
-            sa.sa_select_decode(Qs[r], Ks[r], Vs[r], scores[r], wl.k, block=wl.block)
+            sa.sa_decode_step(Qs[r], Ks[r], Vs[r], sks[r], wl.k, block=wl.block,
+                              update_block=wl.nb - 1, ws=ws)
     torch.cuda.synchronize()
     return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes,
-            "select_decode_dispatches": 3 * R, "workload": wl.name,
+            "decode_step_dispatches": 3 * R, "workload": wl.name,
             "source_sha256": kernel_source_hash()}
 
 
@@ -771,6 +826,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="long_decode_bf16")
     ap.add_argument("--layers", type=int, default=16)
+    ap.add_argument("--trials", type=int, default=10, help="timed graph replays (median taken)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-variants", action="store_true",
@@ -801,6 +857,16 @@ def main(argv=None) -> int:
         if not args.no_variants:
             import gc
             import torch
+            # the other decode configurations at their full sizes (reported beside the metric)
+            res["configs"] = {}
+            for nm, calls, layers in (("tiny_decode_f32", 200, 4), ("gqa_decode_bf16", 200, 8)):
+                gc.collect()
+                torch.cuda.empty_cache()
+                c = bench_decode(args, name=nm, calls=calls, layers=layers, extras=False)
+                res["configs"][nm] = {k2: c[k2] for k2 in (
+                    "value", "unit", "dtype", "config", "trials", "achieved_GBps",
+                    "pct_of_hbm_peak", "algorithmic_bytes_per_step", "roofline", "cpu_baseline")
+                    if k2 in c}
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"] = {"threshold": bench_threshold(args)}

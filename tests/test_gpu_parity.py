@@ -124,9 +124,8 @@ def test_decode_step_equals_separate_calls():
 @pytest.mark.parametrize("D,upd", [(128, 5), (128, -1), (64, 7)])
 def test_decode_step_scores_and_paths(D, upd):
     """The decode step's scores equal the standalone selection's bit for bit
-    (the refreshed block, anywhere in the row, to rounding); D = 128 runs the
-    selecting decode kernel after the score kernel, D = 64 the standalone
-    selection and the block decode."""
+    (the refreshed block, anywhere in the row, to rounding), for D = 128 and
+    D = 64, with the newest-block refresh anywhere in the row or skipped."""
     wl, inp, q, K, V = _decode_case("gqa_decode_bf16", {"B": 2, "Hq": 8, "Hkv": 2, "D": D,
                                                         "N": 6000})
     Qd, Kd, Vd = to_dev(inp.Q, "bf16"), to_dev(inp.K, "bf16"), to_dev(inp.V, "bf16")

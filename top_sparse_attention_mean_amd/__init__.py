@@ -153,9 +153,8 @@ def _need(t: Optional[torch.Tensor], name: str, shape=None, dtypes=None) -> None
     if dtypes is not None and t.dtype not in dtypes:
         raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)} "
                          f"(got {t.dtype})")
-    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
-        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)} "
-                         f"(got {tuple(t.shape)})")
+    if shape is not None and t.shape != shape:
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
 
 
 def _rank(t: torch.Tensor, name: str, n: int) -> None:

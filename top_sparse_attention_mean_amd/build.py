@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsa.so")
 
-SOURCES = ["sa_api.hip", "k_sketch.hip", "k_select.hip", "k_decode.hip",
+SOURCES = ["sa_api.hip", "k_sketch.hip", "k_select.hip", "k_decode.hip", "k_step.hip",
            "k_threshold.hip", "k_prune.hip", "k_lowbit.hip",
            "k_mass.hip", "k_prefill.hip"]
 

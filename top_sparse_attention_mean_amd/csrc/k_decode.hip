@@ -12,28 +12,19 @@
 // all partials.
 //
 // k_decode_blocks_mfma (bf16): one 256-thread workgroup per (b, kv head,
-//   split); a split takes an equal share of the head's 16-token tiles.  A
-//   tile is one wave's unit of work; each wave issues the loads of up to four
-//   tiles before computing any of them.  The selecting variant first runs the
-//   selection pre-filter of its head from the score row, then takes its tiles
-//   from its own slice of the candidate list (ranking only those candidates)
-//   or, when the list does not suit slices, from the fully ranked selection.  Scores of the g
-//   heads for 16 tokens are one chain of v_mfma_f32_16x16x32_bf16 with the key
-//   rows as the A operand and the group's queries as the B operand -- both
-//   read in their natural row-major layout (contraction over d), so keys go
-//   straight from HBM into matrix-core registers.  The score tile comes out
-//   with lane l holding head l%16 for tokens 4*(l/16)+r, which is exactly the
-//   A-operand layout of v_mfma_f32_16x16x16_bf16 for P V.  V rows are loaded as
-//   row vectors and transposed in registers with v_perm_b32 so the value
-//   columns land in the B operand (column d = (D/16)*n + e of MFMA e).  P is
-//   split as p ~ hi + lo (two bf16) and the lo part fills the padding
-//   rows g..2g-1 of the 16-row tile, so the value product is accurate to about
-//   2^-17 relative with float32 accumulation.  Workgroup id % (B*Hkv) selects
-//   the (b, kv head): all splits of one kv head share an XCD and its L2.
+//   split); a split takes an equal share of the head's 16-token tiles and runs
+//   them through the tile pipeline of sa_decode_core.h (scores and P V on the
+//   matrix cores, up to four tiles' loads in flight per wave).  The selecting
+//   variant first runs the selection pre-filter of its head from the score
+//   row, then takes its tiles from its own slice of the candidate list
+//   (ranking only those candidates) or, when the list does not suit slices,
+//   from the fully ranked selection.  Workgroup id % (B*Hkv) selects the
+//   (b, kv head): all splits of one kv head share an XCD and its L2.
 // k_decode_blocks_valu (float32): per-thread dot products, LDS softmax over
 //   1024-token chunks, (head, column)-parallel value pass; float32 throughout.
 // k_decode_tokens: per (b, query head, split) over an explicit token list
 //   (threshold selection), reusing the selector's scores when given.
+#include "sa_decode_core.h"
 #include "sa_device.h"
 #include "sa_internal.h"
 #include "sa_select_core.h"
@@ -91,141 +82,15 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, int total, int* f
   return true;
 }
 
-// Merge the S partials of query heads h0 .. h0+nh-1 (rows of [B*Hq]):
-// M = max m_s, L = sum l_s 2^(m_s - M), O = sum acc_s 2^(m_s - M) / L,
-// lse = (M + log2 L) ln 2 (scores are kept in log2 units).
-// Thread t owns head t / (D/4) and 4 consecutive columns (nh * D / 4 <= 256).
-// Its first kMergeChunk partial loads and the (m, l) pair loads are issued
-// first; mid() (all threads call it) runs while they are in flight.  The
-// pairs are staged in LDS, one row per head of stride Sp (S up to
-// kMergeRegSplits: Sp = kMergeRegSplits, so one unrolled branch-free pass of
-// 16-byte LDS reads serves every split; else S rounded up to 4), padded with
-// m = -inf, l = 0.  Beyond kMergeRegSplits the rest follow 8 at a time.
-constexpr int kMergeChunk = 32;
-constexpr int kMergeRegSplits = 32;
-
-struct NoMid {
-  __device__ void operator()() const {}
-};
-
-template <int D, typename Mid = NoMid>
-__device__ void merge_tail(const DecodeArgs& a, int h0, int nh, float* w, float* lv,
-                           Mid mid = Mid()) {
-  constexpr int CH = kMergeChunk, SR = kMergeRegSplits;
-  static_assert(SR == CH && CH % 4 == 0, "one chunk holds the register path");
-  const int S = a.S, Sp = S <= SR ? SR : (S + 3) & ~3, tid = threadIdx.x;
-  const bool act = tid < nh * (D / 4);
-  const int h = act ? tid / (D / 4) : 0, d0 = (tid % (D / 4)) * 4;
-  // the head group's partials through one buffer resource: a lane offset plus
-  // a scalar offset per split
-  const __amdgpu_buffer_rsrc_t rP =
-      make_rsrc(a.pacc + size_t(h0) * S * D, uint32_t(nh) * S * D * sizeof(float));
-  const int voff = (h * S * D + d0) * int(sizeof(float));
-  u32x4 v[CH];
-#pragma unroll
-  for (int u = 0; u < CH; ++u) v[u] = bld16c(rP, voff, min(u, S - 1) * D * int(sizeof(float)));
-  // (m, l) pairs: nh * S <= 8 * kMaxSplits = 4 per thread
-  static_assert(8 * kMaxSplits <= 4 * 256, "pairs per thread");
-  const int np = nh * S;
-  const __amdgpu_buffer_rsrc_t rM = make_rsrc(a.pml + 2 * size_t(h0) * S, uint32_t(np) * 8);
-  u32x2 ml[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) ml[q] = bld8c(rM, min(tid + 256 * q, np - 1) * 8);
-  mid();
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = tid + 256 * q;
-    if (i < np) {
-      const int hh = i / S, ss = i - hh * S;
-      w[hh * Sp + ss] = __uint_as_float(ml[q][0]);
-      lv[hh * Sp + ss] = __uint_as_float(ml[q][1]);
-    }
-  }
-  for (int i = tid; i < nh * (Sp - S); i += 256) {
-    const int hh = i / (Sp - S), ss = S + i % (Sp - S);
-    w[hh * Sp + ss] = -__builtin_inff();
-    lv[hh * Sp + ss] = 0.f;
-  }
-  __syncthreads();
-  if (!act) return;
-  const float* wh = w + h * Sp;
-  const float* lh = lv + h * Sp;
-  float M = -__builtin_inff();
-  float L = 0.f;
-  f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (S <= SR) {
-    // every partial is already loaded: M from the staged m row, then one
-    // unrolled pass of (m, l) 16-byte LDS reads (the -inf padding weighs 0)
-    f32x4 m4[SR / 4];
-#pragma unroll
-    for (int q = 0; q < SR / 4; ++q) {
-      m4[q] = *reinterpret_cast<const f32x4*>(wh + 4 * q);
-      M = fmaxf(M, fmaxf(fmaxf(m4[q][0], m4[q][1]), fmaxf(m4[q][2], m4[q][3])));
-    }
-    if (M != -__builtin_inff()) {
-#pragma unroll
-      for (int q = 0; q < SR / 4; ++q) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lh + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float f = exp2_fast(m4[q][e] - M);
-          L += l4[e] * f;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) A[c] += __uint_as_float(v[4 * q + e][c]) * f;
-        }
-      }
-    }
-  } else {
-    for (int s = 0; s < S; ++s) M = fmaxf(M, wh[s]);
-    if (M != -__builtin_inff()) {
-      // the first CH partials are loaded; the rest follow 8 at a time
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        const float f = exp2_fast(wh[u] - M);
-        L += lh[u] * f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) A[c] += __uint_as_float(v[u][c]) * f;
-      }
-      for (int s0 = CH; s0 < S; s0 += 8) {
-        u32x4 w8[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          w8[u] = bld16c(rP, voff, min(s0 + u, S - 1) * D * int(sizeof(float)));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (s0 + u < S) {
-            const float f = exp2_fast(wh[s0 + u] - M);
-            L += lh[s0 + u] * f;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) A[c] += __uint_as_float(w8[u][c]) * f;
-          }
-        }
-      }
-    }
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  const size_t oi = size_t(h0 + h) * D + d0;
-  if (a.out_bf16) {
-    const u32x2 pk = u32x2{pack_bf16x2(A[0] * inv, A[1] * inv), pack_bf16x2(A[2] * inv, A[3] * inv)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.O) + oi) = pk;
-  } else {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.O) + oi) = f32x4{A[0] * inv, A[1] * inv, A[2] * inv, A[3] * inv};
-  }
-  if (a.lse && d0 == 0) a.lse[h0 + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : -__builtin_inff();
-}
-
 // ---------------------------------------------------------------- bf16 MFMA
-constexpr int kTileBatch = 4;
 
 template <int D, int G, int BLOCK, int SELKPT>
 __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   constexpr bool SEL = SELKPT > 0;
   static_assert(2 * G <= 16, "g must be at most 8");
   constexpr int NST = D / 32;      // contraction steps of the score MFMA
-  constexpr int EPL = D / 16;      // value columns per lane = PV MFMAs per tile
   constexpr int TPB = BLOCK / 16;  // 16-token tiles per block
-  __shared__ __attribute__((aligned(16))) float s_acc[4][2 * G][D + 4];
-  __shared__ float s_m[4][G], s_l[4][G];
+  __shared__ CombineLds<D, G> s_cmb;
   __shared__ __attribute__((aligned(16))) float s_w[G * kMaxSplits], s_lv[G * kMaxSplits];
   __shared__ int s_flag;
 
@@ -233,7 +98,6 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   const int bh = blockIdx.x % BH, s = blockIdx.x / BH;
   const int b = bh / a.Hkv, kh = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int gq = lane >> 4, nn = lane & 15;
 
   // Work is split by 16-token tiles: split s takes tiles [g0, g0 + tps) of
   // the head's slot list (slot = tile / TPB).  The range comes from
@@ -340,21 +204,10 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
     ib = a.idx + size_t(bh) * a.idx_stride;
   }
 
-  const uint16_t* Q = static_cast<const uint16_t*>(a.Q);
   u32x4 qb[NST];
-  if (nn < G) {
-    const uint16_t* qp = Q + (size_t(b) * a.Hq + kh * G + nn) * D + 8 * gq;
-#pragma unroll
-    for (int st = 0; st < NST; ++st) qb[st] = ld16(qp + 32 * st);
-  } else {
-#pragma unroll
-    for (int st = 0; st < NST; ++st) qb[st] = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  f32x4 acc[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  tile_q_operand<D, G>(static_cast<const uint16_t*>(a.Q) + (size_t(b) * a.Hq + kh * G) * D, qb);
+  TileAcc<D> ta;
+  tile_acc_init(ta);
 
   // per-(b, kv head) buffer resources: rows past N (and invalid tiles) read as
   // zeros, so every load of a batch issues unconditionally
@@ -363,140 +216,22 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rV =
       make_rsrc(static_cast<const uint16_t*>(a.V) + size_t(bh) * N * D, uint32_t(N) * D * 2);
   const int nbk = (N + BLOCK - 1) / BLOCK;
-  const float sl2 = a.sl2;
-
-  for (int tb = wave; tb < ntiles; tb += 4 * kTileBatch) {
-    u32x4 ka[kTileBatch][NST];
-    uint32_t vw[kTileBatch][4][EPL / 2];
-    int tok0s[kTileBatch];
-    // issue every load of the batch first
-#pragma unroll
-    for (int u = 0; u < kTileBatch; ++u) {
-      const int t = tb + 4 * u;
-      int tok0 = -1;
-      if (t < ntiles) {
-        if (SEL && cmode) {
-          tok0 = wl[t];
-        } else if ((g0 + t) / TPB < cnt) {
-          const int blk = ib[(g0 + t) / TPB];
-          if (blk >= 0 && blk < nbk) {
-            tok0 = blk * BLOCK + ((g0 + t) % TPB) * 16;
-            if (tok0 >= N) tok0 = -1;
-          }
-        }
-      }
-      tok0s[u] = tok0;
-      const int koff = tok0 >= 0 ? ((tok0 + nn) * D + 8 * gq) * 2 : kBufOOB;
-      const int voff = tok0 >= 0 ? ((tok0 + 4 * gq) * D + EPL * nn) * 2 : kBufOOB;
-#pragma unroll
-      for (int st = 0; st < NST; ++st) ka[u][st] = bld16(rK, koff + 64 * st);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (EPL == 8) {
-          const u32x4 w = bld16(rV, voff + j * D * 2);
-          vw[u][j][0] = w[0]; vw[u][j][1] = w[1]; vw[u][j][2] = w[2]; vw[u][j][3] = w[3];
-        } else {
-          const u32x2 w = bld8(rV, voff + j * D * 2);
-          vw[u][j][0] = w[0]; vw[u][j][1] = w[1];
-        }
+  run_tiles<D, G>(ta, qb, rK, rV, N, a.sl2, ntiles, [&](int t) {
+    if (SEL && cmode) return wl[t];
+    if ((g0 + t) / TPB < cnt) {
+      const int blk = ib[(g0 + t) / TPB];
+      if (blk >= 0 && blk < nbk) {
+        const int tok0 = blk * BLOCK + ((g0 + t) % TPB) * 16;
+        return tok0 < N ? tok0 : -1;
       }
     }
-#pragma unroll
-    for (int u = 0; u < kTileBatch; ++u) {
-      const int tok0 = tok0s[u];
-      if (tok0 < 0) continue;  // uniform across the wave
-      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < NST; ++st) sc = mfma16x16x32(ka[u][st], qb[st], sc);
-      float sv[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = tok0 + 4 * gq + r < N ? sc[r] * sl2 : -__builtin_inff();
-      float tm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      tm = fmaxf(tm, __shfl_xor(tm, 16, 64));
-      tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
-      const float m_new = fmaxf(m_run, tm);          // finite: the tile has a valid token
-      const float alpha = exp2_fast(m_run - m_new);  // 0 on the first tile
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = exp2_fast(sv[r] - m_new);
-      l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      m_run = m_new;
-      // rescale accumulator row 4*gq+r by the factor of the head it belongs to
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * gq + r;
-        const int hs = row < G ? row : (row < 2 * G ? row - G : 0);
-        const float al = __shfl(alpha, hs, 64);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e][r] *= al;
-      }
-      // P operand: rows 0..g-1 carry bf16(p), rows g..2g-1 carry bf16(p - bf16(p))
-      const uint32_t h01 = pack_bf16x2(p[0], p[1]);
-      const uint32_t h23 = pack_bf16x2(p[2], p[3]);
-      const uint32_t l01 = pack_bf16x2(p[0] - bf16lo(h01), p[1] - bf16hi(h01));
-      const uint32_t l23 = pack_bf16x2(p[2] - bf16lo(h23), p[3] - bf16hi(h23));
-      const int src = (lane - G) & 63;
-      const uint32_t l01s = __shfl(l01, src, 64);
-      const uint32_t l23s = __shfl(l23, src, 64);
-      u32x2 pa;
-      if (nn < G) pa = u32x2{h01, h23};
-      else if (nn < 2 * G) pa = u32x2{l01s, l23s};
-      else pa = u32x2{0u, 0u};
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const int c = e >> 1;
-        u32x2 bv;
-        if (e & 1) bv = u32x2{pack_hi(vw[u][0][c], vw[u][1][c]), pack_hi(vw[u][2][c], vw[u][3][c])};
-        else       bv = u32x2{pack_lo(vw[u][0][c], vw[u][1][c]), pack_lo(vw[u][2][c], vw[u][3][c])};
-        acc[e] = mfma16x16x16(pa, bv, acc[e]);
-      }
-    }
-  }
+    return -1;
+  });
 
-  // per-wave results -> LDS (16-byte stores)
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (gq == 0 && nn < G) { s_m[wave][nn] = m_run; s_l[wave][nn] = l_tot; }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * gq + r;
-    if (row < 2 * G) {
-#pragma unroll
-      for (int e0 = 0; e0 < EPL; e0 += 4)
-        *reinterpret_cast<f32x4*>(&s_acc[wave][row][EPL * nn + e0]) =
-            f32x4{acc[e0][r], acc[e0 + 1][r], acc[e0 + 2][r], acc[e0 + 3][r]};
-    }
-  }
-  __syncthreads();
-
-  // combine the 4 waves and the hi/lo rows: one head and 4 columns per thread
+  // combine the 4 waves and the hi/lo rows into this split's partials
   const int h0 = b * a.Hq + kh * G;
-  const __amdgpu_buffer_rsrc_t rPw =
-      make_rsrc(a.pacc + size_t(h0) * a.S * D, uint32_t(G) * a.S * D * sizeof(float));
-  const __amdgpu_buffer_rsrc_t rMw = make_rsrc(a.pml + 2 * size_t(h0) * a.S, uint32_t(G) * a.S * 8);
-  for (int o4 = tid; o4 < G * D / 4; o4 += 256) {
-    const int h = o4 / (D / 4), d0 = (o4 % (D / 4)) * 4;
-    float mw[4], lw[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) { mw[w] = s_m[w][h]; lw[w] = s_l[w][h]; }
-    const float M = fmaxf(fmaxf(mw[0], mw[1]), fmaxf(mw[2], mw[3]));
-    float Ls = 0.f;
-    f32x4 A = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (M != -__builtin_inff()) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float f = exp2_fast(mw[w] - M);
-        Ls += lw[w] * f;
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(&s_acc[w][h][d0]);
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(&s_acc[w][h + G][d0]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) A[q] += (hi[q] + lo[q]) * f;
-      }
-    }
-    const int pi = h * a.S + s;   // partial within the head group
-    bst16c(rPw, (pi * D + d0) * int(sizeof(float)), __builtin_bit_cast(u32x4, A));
-    if (d0 == 0) bst8c(rMw, pi * 8, u32x2{__float_as_uint(M), __float_as_uint(Ls)});
-  }
+  store_partial<D, G>(ta, s_cmb, a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S,
+                      a.S, s, true);
   int32_t* gent = nullptr;
   if constexpr (SEL) {
     gent = a.sel_ent + size_t(bh) * kSelEntCap;
@@ -530,9 +265,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
       for (int j = tot + tid; j < a.k; j += 256) orow[j] = -1;
       if (tid == 0) a.sel_count[bh] = tot;
     };
-    merge_tail<D>(a, h0, G, s_w, s_lv, write_idx);
+    merge_tail<D>(a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S, a.S,
+                  MergeDst{a.O, a.out_bf16, a.lse}, h0, G, s_w, s_lv,
+                  write_idx);
   } else {
-    merge_tail<D>(a, h0, G, s_w, s_lv);
+    merge_tail<D>(a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S, a.S,
+                  MergeDst{a.O, a.out_bf16, a.lse}, h0, G, s_w, s_lv);
   }
 }
 
@@ -652,7 +390,8 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
     }
   }
   if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
-  merge_tail<D>(a, h0, G, s_w, s_lv);
+  merge_tail<D>(a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S, a.S,
+                  MergeDst{a.O, a.out_bf16, a.lse}, h0, G, s_w, s_lv);
 }
 
 // ---------------------------------------------------------------- token lists
@@ -822,7 +561,8 @@ __global__ __launch_bounds__(256) void k_decode_tokens(DecodeArgs a) {
     }
   }
   if (!arrive_last(&a.counter[bhq * kCounterStride], a.S, &s_flag)) return;
-  merge_tail<D>(a, bhq, 1, s_w, s_lv);
+  merge_tail<D>(a.pacc + size_t(bhq) * a.S * D, a.pml + 2 * size_t(bhq) * a.S, a.S,
+                MergeDst{a.O, a.out_bf16, a.lse}, bhq, 1, s_w, s_lv);
 }
 
 // ---------------------------------------------------------------- launchers

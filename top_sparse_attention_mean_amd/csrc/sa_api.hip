@@ -4,6 +4,7 @@
 // before any HIP runtime call, so invalid calls fail the same way with or
 // without a GPU.  Launches are asynchronous on the caller's stream.
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -34,6 +35,20 @@ bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool dtype_ok(int dt) { return dt == SA_F32 || dt == SA_BF16; }
 float eff_scale(float scale, int D) { return scale > 0.f ? scale : 1.0f / sqrtf(float(D)); }
 bool pow2_le8(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+// Knob SA_STEP_MODE of sa_decode_step: 0 (default) the two-kernel step
+// (scoring kernel, then the selecting split-K decode); 1 the one-launch step
+// (k_step.hip) with plain stores inside an XCD team, 2 the same with
+// device-coherent stores throughout, 3 the same with every workgroup acting as
+// if it ran off its team's XCD.  The one-launch step is slower at the long
+// decode shape (its cross-workgroup selection costs more than the kernel
+// boundary it removes), so it is kept for measurement and tests only.
+int step_mode() {
+  const char* e = getenv("SA_STEP_MODE");
+  if (!e) return 0;
+  const int m = atoi(e);
+  return m >= 0 && m <= 3 ? m : 0;
+}
 
 #define REQ(cond, ...)                                   \
   do {                                                   \
@@ -209,10 +224,15 @@ size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int bloc
       if (k < 1) return SIZE_MAX;
       return decode_ws(B, Hq, Hkv, D, block > 0 ? SA_IDX_BLOCKS : SA_IDX_TOKENS, block, k).bytes;
     case SA_OP_DECODE_STEP: {
+      // room for both paths (the one-launch step serves bf16 shapes only; the
+      // dtype is not an argument here)
       if (k < 1 || block < 1) return SIZE_MAX;
       const int nb = cdiv(N, block);
-      return select_ws_bytes(B, Hkv, 1, D, 1, nb) +
-             decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k).bytes;
+      const size_t two = select_ws_bytes(B, Hkv, 1, D, 1, nb) +
+                         decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k).bytes;
+      const size_t one = step_fusable(SA_BF16, B, Hq, Hkv, N, D, block, k)
+                             ? step_ws(B, Hq, Hkv, D).bytes : 0;
+      return std::max(two, one);
     }
     default:
       return SIZE_MAX;
@@ -587,6 +607,15 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V, int dtype,
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float sc = eff_scale(scale, D);
+  const int mode = step_mode();
+  if (mode != 0 && step_fusable(dtype, B, Hq, Hkv, N, D, block, k)) {
+    const size_t need = step_ws(B, Hq, Hkv, D).bytes;
+    if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+    return hip_status(launch_decode_step(Q, K, V, B, Hq, Hkv, N, D, block, ksketch, update_block,
+                                         k, SA_FORCE_SINK | SA_FORCE_LOCAL, sc, idx, count, score,
+                                         O, out_dtype, lse, ws, mode - 1, st),
+                      "sa_decode_step");
+  }
   const SelectWs sw = select_ws(B, Hkv, 1, D, 1, nb);
   float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + sw.score_off);
   hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, K, N, block, update_block, sc,

@@ -84,6 +84,14 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// Plain buffer stores: they land in this XCD's L2, where sc1 loads from the
+// same XCD see them (but not loads from another XCD).
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
 // Agent-coherent accesses (cache policy sc1, the policy the compiler gives
 // agent-scope atomic loads and stores): a completed sc1 store is visible to
 // sc1 loads from every compute unit of the device, whatever its L2 holds.

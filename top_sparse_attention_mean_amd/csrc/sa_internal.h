@@ -94,6 +94,59 @@ inline DecodeWs decode_ws(int B, int Hq, int Hkv, int D, int mode, int block,
   return w;
 }
 
+// The one-launch decode step (k_step.hip): one team of kStepTeam workgroups
+// per XCD (one per compute unit), kv head bh on team bh % 8 with S = team /
+// (heads of the team) splits; split s scores the sketch rows s, s + S, ...
+// (at most kStepMaxRows of them) and publishes up to kStepPubCap candidates.
+constexpr int kStepTeam = 32;
+constexpr int kStepMaxRows = 256;
+constexpr int kStepPubWords = 64;                 // 2 header words + the candidates
+constexpr int kStepPubCap = kStepPubWords - 2;
+constexpr int kStepSpinLimit = 1 << 21;           // polls of one wait (seconds)
+constexpr int kStepMaxCand = 512;                 // bracketed candidates ranked per head
+constexpr int kStepMergeEnt = 320;                // (split, 4-column chunk) entries of a merge share
+
+// Workspace of the one-launch step: an error word at offset 0 (nonzero once a
+// wait ran out; never cleared by the library), three counters per head (two
+// barriers and the merge arrivals, zero between calls) in a region sized for
+// the most heads any shape can have (so the same buffer serves every shape:
+// the rest is always written before it is read), the published candidates
+// [BH, team, kStepPubWords] u64, the scores in slot order [BH, team,
+// kStepMaxRows], and the partials [B*Hq, team, D] + (m, l) [B*Hq, team, 2].
+constexpr int kStepMaxHeads = 8 * kStepTeam;
+constexpr size_t kStepCtrBytes = size_t(kStepMaxHeads) * 3 * kCounterStride * sizeof(uint32_t);
+struct StepWs {
+  size_t ctr_off, pub_off, srow_off, acc_off, ml_off, bytes;
+};
+inline StepWs step_ws(int B, int Hq, int Hkv, int D) {
+  const size_t BH = size_t(B) * Hkv, W = kStepTeam;
+  StepWs w{};
+  w.ctr_off = 256;
+  w.pub_off = w.ctr_off + kStepCtrBytes;
+  w.srow_off = w.pub_off + align256(BH * W * kStepPubWords * sizeof(uint64_t));
+  w.acc_off = w.srow_off + align256(BH * W * kStepMaxRows * sizeof(float));
+  w.ml_off = w.acc_off + align256(size_t(B) * Hq * W * D * sizeof(float));
+  w.bytes = w.ml_off + align256(size_t(B) * Hq * W * 2 * sizeof(float));
+  return w;
+}
+// Shapes the one-launch step covers (bf16, D 64 or 128, g in {1, 2, 4, 8},
+// blocks of 64 or 128, at most kStepTeam heads per XCD, at most kStepMaxRows
+// sketch rows per split, k <= kMaxKFused).
+inline bool step_fusable(int dtype, int B, int Hq, int Hkv, int N, int D, int block, int k) {
+  if (dtype != SA_BF16 || !(D == 64 || D == 128) || !(block == 64 || block == 128)) return false;
+  if (Hkv < 1 || Hq % Hkv) return false;
+  const int G = Hq / Hkv;
+  if (!(G == 1 || G == 2 || G == 4 || G == 8)) return false;
+  const long BH = long(B) * Hkv;
+  const long Hx = (BH + 7) / 8;
+  if (Hx > kStepTeam) return false;
+  const int S = kStepTeam / int(Hx);
+  const int nb = cdiv(N, block);
+  if (cdiv(nb, S) > kStepMaxRows || nb > kMaxNbDecode) return false;
+  if (k < 1 || k > kMaxKFused) return false;
+  return long(N) * D * 2 <= 0x7f000000L;
+}
+
 // Workspace of the top-k selection.  Decode: the block scores.
 // Prefill: the pooled query blocks.
 struct SelectWs {
@@ -186,6 +239,13 @@ hipError_t launch_decode_select_blocks(const void* Q, const void* K, const void*
                                        const float* scores, int nb, int k, unsigned flags,
                                        int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
                                        void* O, int out_dtype, float* lse, hipStream_t st);
+// The one-launch decode step (bf16; step_fusable shapes).  coh_mode: 0 plain
+// stores inside an XCD team, 1 device-coherent stores throughout, 2 every
+// workgroup acts as if it ran off its team's XCD (both for tests).
+hipError_t launch_decode_step(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
+                              int N, int D, int block, float* sk, int upd, int k, unsigned flags,
+                              float scale, int32_t* idx, int32_t* count, float* score, void* O,
+                              int out_dtype, float* lse, void* ws, int coh_mode, hipStream_t st);
 hipError_t launch_prefill_select(const float* qbar, const float* ksk, int BH,
                                  int M, int nb, int D, int k, unsigned flags,
                                  float scale, int32_t* idx, int32_t* count,
