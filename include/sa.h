@@ -35,7 +35,8 @@
  *     Query head h reads kv head h / g, g = Hq / Hkv (Hq % Hkv == 0).
  *   - Every pointer is DEVICE memory owned by the caller.  Inputs are const.
  *     The library allocates nothing and keeps no state between calls apart
- *     from a cached device-property query.
+ *     from a cached device-property query and the per-GPU scratch array of
+ *     sa_decode_step_noalloc.
  *   - `ws` is a caller-provided device workspace of at least
  *     sa_workspace_bytes(...) bytes.  It holds partial results plus arrival
  *     counters and histograms that must read zero when a call starts: zero-fill
@@ -439,6 +440,27 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V,
                          float scale, int32_t* idx, int32_t* count,
                          float* score, void* O, int out_dtype, float* lse,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * sa_decode_step_noalloc -- sa_decode_step without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc).  Arguments, layouts and
+ * results are those of sa_decode_step (bitwise the same outputs).  The
+ * workspace is a scratch array of 16 MiB that the library holds on each GPU
+ * it runs on, until the process ends; it calls no allocator.  Each call first
+ * zeroes the scratch words the step needs at zero (a small fill kernel on
+ * `stream`, capturable), so consecutive calls may use different shapes.
+ * Calls that overlap in time on one GPU (other streams or threads) share the
+ * scratch and race: serialise them.  A shape whose workspace
+ * (sa_workspace_bytes(SA_OP_DECODE_STEP, ...)) exceeds 16 MiB returns
+ * SA_ERR_WORKSPACE; the scratch lookup failing returns SA_ERR_HIP.
+ */
+sa_status sa_decode_step_noalloc(const void* Q, const void* K, const void* V,
+                                 int dtype, int B, int Hq, int Hkv, int N, int D,
+                                 int block, float* ksketch, int update_block,
+                                 int k, float scale, int32_t* idx,
+                                 int32_t* count, float* score, void* O,
+                                 int out_dtype, float* lse, void* stream);
 
 /*
  * sa_select_decode -- the selection and attention half of a decode step, as

@@ -43,6 +43,8 @@ def lib():
     L.sa_sparse_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, I, P, I, P, P]
     L.sa_decode_step.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P, P, Z, P]
     L.sa_select_decode.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, U, F, P, P, P, I, P, P, Z, P]
+    L.sa_decode_step_noalloc.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P,
+                                         P]
     L.sa_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     L.sa_workspace_bytes.restype = Z
     L.sa_status_str.restype = ctypes.c_char_p
@@ -62,7 +64,7 @@ def test_header_declares_the_boundary():
               "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
               "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
               "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step",
-              "sa_workspace_bytes",
+              "sa_decode_step_noalloc", "sa_workspace_bytes",
               "sa_status_str",
               "sa_last_error", "sa_version"]:
         assert n in names
@@ -326,6 +328,26 @@ def test_decode_step_validation(lib):
     a = list(base)
     a[21] = 128                                   # workspace
     assert f(*a) == WORKSPACE
+
+
+def test_decode_step_noalloc_validation(lib):
+    """Argument errors return before the scratch lookup (no HIP call), and a
+    shape whose workspace exceeds the 16 MiB scratch is refused."""
+    f = lib.sa_decode_step_noalloc
+    base = [A, A, A, 1, 1, 64, 8, 262144, 128, 64, A, 4095, 82, 0.0, A, A, None, A, 1, A, None]
+    a = list(base)
+    a[11] = 4096                                  # update_block past the last block
+    assert f(*a) == INVALID
+    a = list(base)
+    a[5] = 63                                     # Hq not a multiple of Hkv
+    assert f(*a) == INVALID
+    a = list(base)
+    a[10] = MIS                                   # misaligned sketch
+    assert f(*a) == INVALID
+    a = list(base)
+    a[4], a[5], a[6] = 64, 64 * 64, 64 * 8        # B = 64: far more than 16 MiB of workspace
+    assert f(*a) == WORKSPACE
+    assert b"16 MiB" in lib.sa_last_error()
 
 
 def test_select_decode_validation(lib):

@@ -37,7 +37,8 @@ EXPORTS = ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_ke
            "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
            "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
            "sa_sparse_decode",
-           "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_workspace_bytes",
+           "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_decode_step_noalloc",
+           "sa_workspace_bytes",
            "sa_status_str",
            "sa_last_error", "sa_version"]
 
@@ -78,6 +79,8 @@ _sparse_prefill = _sig("sa_sparse_prefill", _I, _P, _P, _P, _I, _I, _I, _I, _I, 
                        _P, _I, _P, _I, _P, _P)
 _decode_step = _sig("sa_decode_step", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _I, _F,
                     _P, _P, _P, _P, _I, _P, _P, _Z, _P)
+_decode_step_noalloc = _sig("sa_decode_step_noalloc", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                            _P, _I, _I, _F, _P, _P, _P, _P, _I, _P, _P)
 _select_decode = _sig("sa_select_decode", _I, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _I, _U,
                       _F, _P, _P, _P, _I, _P, _P, _Z, _P)
 _workspace_bytes = _sig("sa_workspace_bytes", _Z, _I, _I, _I, _I, _I, _I, _I, _I)
@@ -630,6 +633,32 @@ def sa_decode_step(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, ksketch: t
                         _ptr(ksketch), update_block, k, scale, _ptr(idx), _ptr(count),
                         _ptr(score), _ptr(O), _dt(O), _ptr(lse), _ptr(ws), ws.numel(),
                         _stream(stream)), "sa_decode_step")
+    return O, lse, idx, count
+
+
+def sa_decode_step_noalloc(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                           ksketch: torch.Tensor, k: int, block: int = 64, update_block: int = -1,
+                           scale: float = 0.0, idx=None, count=None, score=None, O=None, lse=None,
+                           stream=None):
+    """sa_decode_step with the library's per-GPU scratch as its workspace.  The
+    caller passes every output (idx, count, O; lse and score optional), so the
+    call allocates nothing."""
+    B, Hq, D, Hkv, N = _qk_shapes(Q, K)
+    nb = -(-N // block)
+    _need(V, "V", (B, Hkv, N, D), (Q.dtype,))
+    _need(ksketch, "ksketch", (B, Hkv, nb, D), _F32)
+    _need(idx, "idx", (B, Hkv, k), _I32)
+    _need(count, "count", (B, Hkv), _I32)
+    _need(score, "score", (B, Hkv, nb), _F32)
+    _need(O, "O", (B, Hq, D), _FP)
+    _need(lse, "lse", (B, Hq), _F32)
+    _dev(Q, K, V, ksketch, idx, count, score, O, lse)
+    if idx is None or count is None or O is None:
+        raise ValueError("sa_decode_step_noalloc needs idx, count and O from the caller")
+    _check(_decode_step_noalloc(_ptr(Q), _ptr(K), _ptr(V), _dt(Q), B, Hq, Hkv, N, D, block,
+                                _ptr(ksketch), update_block, k, scale, _ptr(idx), _ptr(count),
+                                _ptr(score), _ptr(O), _dt(O), _ptr(lse), _stream(stream)),
+           "sa_decode_step_noalloc")
     return O, lse, idx, count
 
 

@@ -185,6 +185,79 @@ static sa_status run_select_decode(const void* Q, const void* K, const void* V, 
                     what);
 }
 
+namespace {
+
+// Fills n 32-bit words with zero (a kernel, not a memset, so that the call can
+// be captured into a HIP graph).
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+}  // namespace
+
+namespace sa {
+
+sa_status report(sa_status s, const char* what) { return fail(s, "%s", what); }
+
+sa_status decode_step(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                      int Hkv, int N, int D, int block, float* ksketch, int update_block, int k,
+                      float scale, int32_t* idx, int32_t* count, float* score, void* O,
+                      int out_dtype, float* lse, void* ws, size_t ws_bytes, hipStream_t st,
+                      StepPhase phase) {
+  PTR(ksketch);
+  REQ(block >= 1, "block must be >= 1");
+  const int nb = cdiv(N, block);
+  REQ(update_block >= -1 && update_block < nb, "update_block %d outside [-1, %d)", update_block, nb);
+  const size_t sel = select_ws_bytes(B, Hkv, 1, D, 1, nb);
+  sa_status s = v_select(Q, dtype, B, Hq, Hkv, 1, D, 1, ksketch, nb, k,
+                         SA_FORCE_SINK | SA_FORCE_LOCAL, idx, count, score, ws, ws_bytes);
+  if (s) return s;
+  if (ws_bytes < sel) return fail(SA_ERR_WORKSPACE, "workspace too small");
+  void* dws = static_cast<char*>(ws) + sel;
+  s = v_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, SA_IDX_BLOCKS, block, idx, count, k, nullptr, O,
+               out_dtype, lse, dws, ws_bytes - sel);
+  if (s) return s;
+  if (update_block >= 0) {
+    s = v_sketch(K, dtype, B, Hkv, N, D, block, 1, update_block, update_block + 1, ksketch);
+    if (s) return s;
+  }
+  const int mode = step_mode();
+  const bool one = mode != 0 && step_fusable(dtype, B, Hq, Hkv, N, D, block, k);
+  if (one) {
+    const size_t need = step_ws(B, Hq, Hkv, D).bytes;
+    if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  }
+  if (phase == StepPhase::kCheck) return SA_OK;
+  const float sc = eff_scale(scale, D);
+  if (phase == StepPhase::kClearAndLaunch) {
+    // the words that must read zero when a step starts: the one-launch step's
+    // error word and counters, or the selecting decode's arrival counters
+    const size_t off = one ? 0 : sel + decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k).cnt_off;
+    const size_t bytes = one ? step_ws(B, Hq, Hkv, D).pub_off
+                             : size_t(B) * Hq * kCounterStride * sizeof(uint32_t);
+    const int n = int(bytes / sizeof(uint32_t));
+    k_zero_words<<<dim3(std::min(cdiv(n, 256), 64)), 256, 0, st>>>(
+        reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + off), n);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_status(e, "sa_decode_step (workspace clear)");
+  }
+  if (one)
+    return hip_status(launch_decode_step(Q, K, V, B, Hq, Hkv, N, D, block, ksketch, update_block,
+                                         k, SA_FORCE_SINK | SA_FORCE_LOCAL, sc, idx, count, score,
+                                         O, out_dtype, lse, ws, mode - 1, st),
+                      "sa_decode_step");
+  const SelectWs sw = select_ws(B, Hkv, 1, D, 1, nb);
+  float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + sw.score_off);
+  hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, K, N, block, update_block, sc,
+                              scores, st);
+  if (e != hipSuccess) return hip_status(e, "sa_decode_step (score)");
+  return run_select_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, block, scores, nb, k,
+                           SA_FORCE_SINK | SA_FORCE_LOCAL, sc, idx, count, O, out_dtype, lse, dws,
+                           st, "sa_decode_step (select + decode)");
+}
+
+}  // namespace sa
+
 extern "C" {
 
 int sa_version(void) { return 100; }
@@ -588,42 +661,9 @@ sa_status sa_decode_step(const void* Q, const void* K, const void* V, int dtype,
                          int k, float scale, int32_t* idx, int32_t* count, float* score,
                          void* O, int out_dtype, float* lse, void* ws, size_t ws_bytes,
                          void* stream) {
-  PTR(ksketch);
-  REQ(block >= 1, "block must be >= 1");
-  const int nb = cdiv(N, block);
-  REQ(update_block >= -1 && update_block < nb, "update_block %d outside [-1, %d)", update_block, nb);
-  const size_t sel = select_ws_bytes(B, Hkv, 1, D, 1, nb);
-  sa_status s = v_select(Q, dtype, B, Hq, Hkv, 1, D, 1, ksketch, nb, k,
-                         SA_FORCE_SINK | SA_FORCE_LOCAL, idx, count, score, ws, ws_bytes);
-  if (s) return s;
-  if (ws_bytes < sel) return fail(SA_ERR_WORKSPACE, "workspace too small");
-  void* dws = static_cast<char*>(ws) + sel;
-  s = v_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, SA_IDX_BLOCKS, block, idx, count, k, nullptr, O,
-               out_dtype, lse, dws, ws_bytes - sel);
-  if (s) return s;
-  if (update_block >= 0) {
-    s = v_sketch(K, dtype, B, Hkv, N, D, block, 1, update_block, update_block + 1, ksketch);
-    if (s) return s;
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const float sc = eff_scale(scale, D);
-  const int mode = step_mode();
-  if (mode != 0 && step_fusable(dtype, B, Hq, Hkv, N, D, block, k)) {
-    const size_t need = step_ws(B, Hq, Hkv, D).bytes;
-    if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-    return hip_status(launch_decode_step(Q, K, V, B, Hq, Hkv, N, D, block, ksketch, update_block,
-                                         k, SA_FORCE_SINK | SA_FORCE_LOCAL, sc, idx, count, score,
-                                         O, out_dtype, lse, ws, mode - 1, st),
-                      "sa_decode_step");
-  }
-  const SelectWs sw = select_ws(B, Hkv, 1, D, 1, nb);
-  float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + sw.score_off);
-  hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, K, N, block, update_block, sc,
-                              scores, st);
-  if (e != hipSuccess) return hip_status(e, "sa_decode_step (score)");
-  return run_select_decode(Q, K, V, dtype, B, Hq, Hkv, N, D, block, scores, nb, k,
-                           SA_FORCE_SINK | SA_FORCE_LOCAL, sc, idx, count, O, out_dtype, lse, dws,
-                           st, "sa_decode_step (select + decode)");
+  return decode_step(Q, K, V, dtype, B, Hq, Hkv, N, D, block, ksketch, update_block, k, scale,
+                     idx, count, score, O, out_dtype, lse, ws, ws_bytes,
+                     static_cast<hipStream_t>(stream), StepPhase::kLaunch);
 }
 
 sa_status sa_select_decode(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,

@@ -246,6 +246,18 @@ hipError_t launch_decode_step(const void* Q, const void* K, const void* V, int B
                               int N, int D, int block, float* sk, int upd, int k, unsigned flags,
                               float scale, int32_t* idx, int32_t* count, float* score, void* O,
                               int out_dtype, float* lse, void* ws, int coh_mode, hipStream_t st);
+// sa_decode_step in phases: kCheck runs only the host-side argument checks
+// (nothing is enqueued and no HIP call is made); kLaunch enqueues the step;
+// kClearAndLaunch first zeroes, on the stream, the workspace words that must
+// read zero when a step starts (arrival counters, the error word).
+enum class StepPhase { kCheck, kLaunch, kClearAndLaunch };
+sa_status decode_step(const void* Q, const void* K, const void* V, int dtype, int B, int Hq,
+                      int Hkv, int N, int D, int block, float* ksketch, int update_block, int k,
+                      float scale, int32_t* idx, int32_t* count, float* score, void* O,
+                      int out_dtype, float* lse, void* ws, size_t ws_bytes, hipStream_t st,
+                      StepPhase phase);
+// Records `what` as the calling thread's sa_last_error() message; returns s.
+sa_status report(sa_status s, const char* what);
 hipError_t launch_prefill_select(const float* qbar, const float* ksk, int BH,
                                  int M, int nb, int D, int k, unsigned flags,
                                  float scale, int32_t* idx, int32_t* count,
