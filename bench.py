@@ -144,32 +144,40 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0) -> dict:
 # The sources the counted kernel (the selecting split-K decode of the step)
 # and its launch configuration are built from.
 COUNTED_SOURCES = ["k_decode.hip", "sa_decode_core.h", "sa_device.h", "sa_internal.h",
-                   "sa_select_core.h", "sa_api.hip"]
+                   "sa_select_core.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     """SHA-256 over the sources of the counted kernels (counter data goes stale with them)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "top_sparse_attention_mean_amd", "csrc")
-    for path in [os.path.join(csrc, f) for f in COUNTED_SOURCES]:
+    for path in [os.path.join(csrc, f) for f in (sources or COUNTED_SOURCES)]:
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+PREFILL_SOURCES = ["k_prefill.hip", "sa_device.h", "sa_internal.h"]
+
+
+def load_counter_json(kind: str, workload: str, sources):
+    """The committed counter summary profiles/<kind>_<workload>.json, or None
+    when there is none or the listed kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kind}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("source_sha256") != kernel_source_hash():
-        return None
-    return d.get("hbm_bytes_per_launch")
+    return d if d.get("source_sha256") == kernel_source_hash(sources) else None
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    d = load_counter_json(f"traffic_{kernel}", workload, COUNTED_SOURCES)
+    return d and d.get("hbm_bytes_per_launch")
 
 
 def _layers(wl, R, dev):
@@ -673,7 +681,12 @@ def bench_prefill(args) -> dict:
     t_att = graph_time(attend, 1, n)
     tiles = int(cnt.sum().item()) * (Hq // Hkv)
     flops = tiles * 4.0 * blk * blk * D                   # QK^T + PV per 128x128 tile
+    # causal-exact: the diagonal tile of each query block holds blk (blk + 1) / 2
+    # (query, key) pairs, not blk^2
+    diag = B * Hq * M
+    flops_exact = (tiles - diag) * 4.0 * blk * blk * D + diag * 4.0 * D * blk * (blk + 1) / 2
     tflops = flops / (t_att * 1e-6) / 1e12
+    busy = load_counter_json("mfma_prefill", wl.name, PREFILL_SOURCES)
     res = {
         "workload": wl.name, "us_per_pass": round(t_sk + t_sel + t_att, 2),
         "pass": "key sketch (blocks of 128) + pooled-query selection + MFMA sparse attention",
@@ -684,7 +697,13 @@ def bench_prefill(args) -> dict:
         "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 (bf16 32x32x16 MFMA, fp32 accumulate)",
                      "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "traffic": None,
-                     "flops_per_launch": flops, "avg_us": round(t_att, 2)},
+                     "flops_per_launch": flops, "avg_us": round(t_att, 2),
+                     "causal_exact_flops": flops_exact,
+                     "causal_exact_frac": round(flops_exact / (t_att * 1e-6) / 1e12 / 2500.0, 4),
+                     "mfma_busy": busy and busy.get("mfma_busy_frac"),
+                     "mfma_busy_source": (f"profiles/mfma_prefill_{wl.name}.md: rocprofv3 --pmc "
+                                          "SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE of this "
+                                          "kernel; null when its sources changed since")},
     }
     if not args.no_cpu:
         # the oracle: selection for every row of every kv head, attention on a row sample
@@ -753,10 +772,13 @@ def bench_mass(args) -> dict:
                 shared.append(len(own & blk_sel) / n_r)
     si, sc = sidx.cpu().numpy(), scnt.cpu().numpy()
     mi, mc = midx.cpu().numpy(), mcnt.cpu().numpy()
+    # recall of the sketch selector's free blocks against the mass top-k, over
+    # the query blocks i >= 9 of every kv head (below, nearly every earlier
+    # block is kept and the recall is 1 by construction)
     rec = []
     for b in range(B):
         for kh in range(Hkv):
-            for i in range(2, M):
+            for i in range(9, M):
                 want = set(mi[b, kh, i, :mc[b, kh, i]].tolist())
                 got = set(si[b, kh, i, :sc[b, kh, i]].tolist()) - {0, i}
                 rec.append(len(want & got) / len(want))
@@ -768,6 +790,7 @@ def bench_mass(args) -> dict:
         "workload": wl.name, "us_per_call": round(t_mass, 1), "k_free": kf,
         "dense_passes": passes,
         "sketch_recall_of_mass_topk": round(float(np.mean(rec)), 4),
+        "recall_over": f"query blocks 9..{M - 1} of every kv head ({len(rec)} blocks)",
         "per_row_topk_held_by_block_shared_topk": round(float(np.mean(shared)), 4),
         "query_blocks": len(rec),
         "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 over every earlier block, V = "
@@ -780,8 +803,19 @@ def bench_mass(args) -> dict:
         Q, K = (widen(x, wl.dtype) for x in (inp.Q, inp.K))
         qb = [M - 4, M - 3, M - 2, M - 1]
         t0 = time.perf_counter()
-        oracle.mass_oracle(Q, K, blk, k_free=kf, qblocks=qb)
+        o8 = oracle.mass_oracle(Q, K, blk, k_free=kf, qblocks=qb)
         t_cpu = time.perf_counter() - t0
+        # the same recall against O8 itself on these blocks, and whether the GPU
+        # mass selector's lists equal O8's there
+        r8, same = [], []
+        for (b, kh, i), (_, sel8) in o8.items():
+            want = set(sel8.tolist())
+            got = set(si[b, kh, i, :sc[b, kh, i]].tolist()) - {0, i}
+            r8.append(len(want & got) / len(want))
+            same.append(want == set(mi[b, kh, i, :mc[b, kh, i]].tolist()))
+        res["o8_check"] = {"query_blocks": qb, "kv_heads": Hkv,
+                           "sketch_recall_vs_o8": round(float(np.mean(r8)), 4),
+                           "gpu_mass_lists_equal_o8": f"{sum(same)}/{len(same)}"}
         work = sum(i + 1 for i in qb) / (M * (M + 1) / 2)
         res["cpu_baseline"] = {"value": round(t_cpu / work * 1e6, 1), "unit": "us/call",
                                "cores": _blas_threads(), "kind": "oracle",
@@ -882,6 +916,17 @@ def main(argv=None) -> int:
             gc.collect()
             torch.cuda.empty_cache()
             res["variants"]["prefill"] = bench_prefill(args)
+            gc.collect()
+            torch.cuda.empty_cache()
+            res["variants"]["mass"] = bench_mass(args)
+            mv = res["variants"]["mass"]
+            res["mass_recall"] = {
+                "value": mv["sketch_recall_of_mass_topk"],
+                "what": "recall of the pooled-sketch prefill selector's 8 free blocks against "
+                        "the attention-mass top-8 (O8's rule), mean over " + mv["recall_over"] +
+                        " of sparse_prefill_bf16; masses from the GPU mass selector, whose "
+                        "lists are checked against the CPU oracle O8 in o8_check",
+                "o8_check": mv.get("o8_check")}
     print(json.dumps(res), flush=True)
     return 0
 

@@ -275,26 +275,33 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- float32 VALU
-template <int D>
+template <int D, int G>
 __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
-  constexpr int CH = kValuTokensPerWG;
-  constexpr int OPT = 8 * D / 256;       // (head, column) outputs per thread for g <= 8
-  __shared__ float sq[8][D];
-  __shared__ float sp[8][CH];
+  constexpr int CH = 256;                // tokens per round: 64 per wave
+  constexpr int OPT = (G * D + 255) / 256;   // (head, column) outputs per thread
+  constexpr int LPR = D / 4;             // lanes per K/V row (16-byte segments)
+  constexpr int RPI = 64 / LPR;          // rows per wave load
+  constexpr int NL = 64 / RPI;           // loads per lane for the wave's 64 tokens
+  constexpr int NC = NL > 16 ? 16 : NL;  // K and V loads per lane in flight
+  __shared__ float sp[G][CH];
   __shared__ int stok[CH];
-  __shared__ float red[8][4];
+  __shared__ __attribute__((aligned(16))) float sv[CH * D];
+  __shared__ float red[G][4];
   __shared__ __attribute__((aligned(16))) float s_w[8 * kMaxSplits], s_lv[8 * kMaxSplits];
   __shared__ int s_flag;
 
-  const int BH = a.B * a.Hkv, G = a.G, N = a.N, block = a.block;
+  const int BH = a.B * a.Hkv, N = a.N, block = a.block;
   const int bh = blockIdx.x % BH, s = blockIdx.x / BH;
   const int b = bh / a.Hkv, kh = bh % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cnt = a.count ? min(max(a.count[bh], 0), a.idx_stride) : a.idx_stride;
-  const int bps = (cnt + a.S - 1) / a.S;
+  const int sub = lane / LPR, lc = lane % LPR;
+  // split s takes the list slots [blk0, blk1) of idx_stride, so the index
+  // loads do not wait for count; slots at or past count are skipped
+  const int bps = (a.idx_stride + a.S - 1) / a.S;
   const int blk0 = s * bps;
-  const int blk1 = min(blk0 + bps, cnt);
+  const int blk1 = min(blk0 + bps, a.idx_stride);
   const int ntok = max(blk1 - blk0, 0) * block;
+  const int cnt = a.count ? min(max(a.count[bh], 0), a.idx_stride) : a.idx_stride;
   const int nbk = (N + block - 1) / block;
   const int32_t* ib = a.idx + size_t(bh) * a.idx_stride;
   const float* Kb = static_cast<const float*>(a.K) + size_t(bh) * N * D;
@@ -302,76 +309,108 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
   const float* Q = static_cast<const float*>(a.Q);
   const int h0 = b * a.Hq + kh * G;
 
-  for (int o = tid; o < G * D; o += 256) sq[o / D][o % D] = Q[size_t(h0 + o / D) * D + o % D];
-  float m_run[8], l_run[8], acc[OPT];
+  // query columns 4*lc .. 4*lc+3 of the group's heads
+  u32x4 qc[G];
 #pragma unroll
-  for (int h = 0; h < 8; ++h) { m_run[h] = -__builtin_inff(); l_run[h] = 0.f; }
+  for (int h = 0; h < G; ++h) qc[h] = ld16(Q + size_t(h0 + h) * D + 4 * lc);
+  float m_run[G], l_run[G], acc[OPT];
+#pragma unroll
+  for (int h = 0; h < G; ++h) { m_run[h] = -__builtin_inff(); l_run[h] = 0.f; }
 #pragma unroll
   for (int i = 0; i < OPT; ++i) acc[i] = 0.f;
-  __syncthreads();
 
   for (int c0 = 0; c0 < ntok; c0 += CH) {
     const int n = min(CH, ntok - c0);
-    for (int tt = tid; tt < n; tt += 256) {
-      const int blk = ib[blk0 + (c0 + tt) / block];
-      const bool okb = blk >= 0 && blk < nbk;
-      const int tok = okb ? blk * block + (c0 + tt) % block : N;
-      const bool ok = tok < N;
-      stok[tt] = ok ? tok : -1;
-      for (int h = 0; h < G; ++h) {
-        float v = 0.f;
-        if (ok) {
-          const float* kp = Kb + size_t(tok) * D;
-          for (int d = 0; d < D; d += 4) {
-            const u32x4 w = ld16(kp + d);
-            v += sq[h][d] * __uint_as_float(w[0]) + sq[h][d + 1] * __uint_as_float(w[1]) +
-                 sq[h][d + 2] * __uint_as_float(w[2]) + sq[h][d + 3] * __uint_as_float(w[3]);
-          }
+    {
+      // thread tt resolves token c0 + tt of the split (-1: none)
+      int tok = -1;
+      const int slot = blk0 + (c0 + tid) / block;
+      if (tid < n) {
+        const int blk = ib[slot];
+        if (blk >= 0 && blk < nbk && slot < cnt) tok = blk * block + (c0 + tid) % block;
+        if (tok >= N) tok = -1;
+      }
+      stok[tid] = tok;
+    }
+    __syncthreads();
+    // K and V rows of the wave's 64 tokens, LPR lanes per row (coalesced): the
+    // key segments give each head's score (summed over the row's lanes), the
+    // value rows go to LDS (zero rows for missing tokens, whose p is 0)
+#pragma unroll
+    for (int i0 = 0; i0 < NL; i0 += NC) {
+      u32x4 kw[NC], vw[NC];
+      int tk[NC];
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        tk[i] = stok[wave * 64 + (i0 + i) * RPI + sub];
+        const size_t row = size_t(tk[i] >= 0 ? tk[i] : 0) * D + 4 * lc;
+        kw[i] = ld16(Kb + row);
+        vw[i] = ld16(Vb + row);
+      }
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int t = wave * 64 + (i0 + i) * RPI + sub;
+        const bool ok = tk[i] >= 0;
+        reinterpret_cast<u32x4*>(sv)[t * LPR + lc] = ok ? vw[i] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          float p = __uint_as_float(qc[h][0]) * __uint_as_float(kw[i][0]) +
+                    __uint_as_float(qc[h][1]) * __uint_as_float(kw[i][1]) +
+                    __uint_as_float(qc[h][2]) * __uint_as_float(kw[i][2]) +
+                    __uint_as_float(qc[h][3]) * __uint_as_float(kw[i][3]);
+          p = group_sum_to_last<LPR>(p);
+          if (lc == LPR - 1) sp[h][t] = ok ? p * a.sl2 : -__builtin_inff();
         }
-        sp[h][tt] = ok ? v * a.sl2 : -__builtin_inff();
       }
     }
     __syncthreads();
+#pragma unroll
     for (int h = 0; h < G; ++h) {
-      float m = -__builtin_inff();
-      for (int tt = tid; tt < n; tt += 256) m = fmaxf(m, sp[h][tt]);
+      float m = tid < n ? sp[h][tid] : -__builtin_inff();
       m = wave_max(m);
       if (lane == 0) red[h][wave] = m;
     }
     __syncthreads();
-    float alpha[8], mnew[8];
+    float alpha[G], mnew[G];
+#pragma unroll
     for (int h = 0; h < G; ++h) {
       const float cm = fmaxf(fmaxf(red[h][0], red[h][1]), fmaxf(red[h][2], red[h][3]));
       mnew[h] = fmaxf(m_run[h], cm);
       alpha[h] = mnew[h] == -__builtin_inff() ? 1.f : exp2_fast(m_run[h] - mnew[h]);
     }
     __syncthreads();
+#pragma unroll
     for (int h = 0; h < G; ++h) {
       float l = 0.f;
-      for (int tt = tid; tt < n; tt += 256) {
-        const float pv = mnew[h] == -__builtin_inff() ? 0.f : exp2_fast(sp[h][tt] - mnew[h]);
-        sp[h][tt] = pv;
-        l += pv;
+      if (tid < n) {
+        const float pv = mnew[h] == -__builtin_inff() ? 0.f : exp2_fast(sp[h][tid] - mnew[h]);
+        sp[h][tid] = pv;
+        l = pv;
       }
       l = wave_sum(l);
       if (lane == 0) red[h][wave] = l;
     }
     __syncthreads();
+#pragma unroll
     for (int h = 0; h < G; ++h) {
       l_run[h] = l_run[h] * alpha[h] + ((red[h][0] + red[h][1]) + (red[h][2] + red[h][3]));
       m_run[h] = mnew[h];
     }
+    // values from LDS: thread (head, column) outputs over the round's tokens
 #pragma unroll
     for (int i = 0; i < OPT; ++i) {
       const int o = tid + 256 * i;
       if (o < G * D) {
         const int h = o / D, d = o % D;
-        float v = acc[i] * alpha[h];
-        for (int tt = 0; tt < n; ++tt) {
-          const int tok = stok[tt];
-          if (tok >= 0) v += sp[h][tt] * Vb[size_t(tok) * D + d];
+        // four independent partial sums, so the LDS reads of a step overlap
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
+        int tt = 0;
+        for (; tt + 8 <= n; tt += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u & 3] += sp[h][tt + u] * sv[(tt + u) * D + d];
         }
-        acc[i] = v;
+        for (; tt < n; ++tt) v[0] += sp[h][tt] * sv[tt * D + d];
+        acc[i] = acc[i] * alpha[h] + ((v[0] + v[1]) + (v[2] + v[3]));
       }
     }
     __syncthreads();
@@ -597,22 +636,37 @@ static void launch_mfma_g(const DecodeArgs& a, dim3 g, size_t lds, hipStream_t s
   }
 }
 
+template <int D>
+static void launch_valu_g(const DecodeArgs& a, int G, dim3 g, hipStream_t st) {
+  switch (G) {
+    case 1: k_decode_blocks_valu<D, 1><<<g, 256, 0, st>>>(a); break;
+    case 2: k_decode_blocks_valu<D, 2><<<g, 256, 0, st>>>(a); break;
+    case 3: k_decode_blocks_valu<D, 3><<<g, 256, 0, st>>>(a); break;
+    case 4: k_decode_blocks_valu<D, 4><<<g, 256, 0, st>>>(a); break;
+    case 5: k_decode_blocks_valu<D, 5><<<g, 256, 0, st>>>(a); break;
+    case 6: k_decode_blocks_valu<D, 6><<<g, 256, 0, st>>>(a); break;
+    case 7: k_decode_blocks_valu<D, 7><<<g, 256, 0, st>>>(a); break;
+    default: k_decode_blocks_valu<D, 8><<<g, 256, 0, st>>>(a); break;
+  }
+}
+
 hipError_t launch_decode_blocks(const void* Q, const void* K, const void* V, int dtype, int B,
                                 int Hq, int Hkv, int N, int D, float scale, int block,
                                 const int32_t* idx, const int32_t* count, int idx_stride,
                                 const DecodeWs& w, void* ws, void* O, int out_dtype, float* lse,
                                 hipStream_t st) {
-  const DecodeArgs a = make_args(Q, K, V, B, Hq, Hkv, N, block, scale, idx, count, idx_stride,
-                                 nullptr, w, ws, O, out_dtype, lse);
-  const dim3 g(static_cast<unsigned>(long(B) * Hkv * w.S));
+  DecodeArgs a = make_args(Q, K, V, B, Hq, Hkv, N, block, scale, idx, count, idx_stride,
+                           nullptr, w, ws, O, out_dtype, lse);
+  if (dtype != SA_BF16) a.S = decode_valu_splits(idx_stride, block);   // sized for by decode_ws
+  const dim3 g(static_cast<unsigned>(long(B) * Hkv * a.S));
   if (dtype == SA_BF16) {
     if (D == 128 && block == 64) launch_mfma_g<128, 64, 0>(a, g, 0, st);
     else if (D == 128)           launch_mfma_g<128, 128, 0>(a, g, 0, st);
     else if (block == 64)        launch_mfma_g<64, 64, 0>(a, g, 0, st);
     else                         launch_mfma_g<64, 128, 0>(a, g, 0, st);
   } else {
-    if (D == 128) k_decode_blocks_valu<128><<<g, 256, 0, st>>>(a);
-    else          k_decode_blocks_valu<64><<<g, 256, 0, st>>>(a);
+    if (D == 128) launch_valu_g<128>(a, Hq / Hkv, g, st);
+    else          launch_valu_g<64>(a, Hq / Hkv, g, st);
   }
   return hipGetLastError();
 }

@@ -151,7 +151,8 @@ sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B
     return fail(SA_ERR_INVALID, "unknown mode %d", mode);
   }
   const DecodeWs w = decode_ws(B, Hq, Hkv, D, mode, block, idx_stride);
-  const int Sg = mode == SA_IDX_BLOCKS ? std::max(w.S, decode_sel_splits(B * Hkv, idx_stride, block))
+  const int Sg = mode == SA_IDX_BLOCKS ? std::max({w.S, decode_sel_splits(B * Hkv, idx_stride, block),
+                                                   decode_valu_splits(idx_stride, block)})
                                        : w.S;
   REQ(long(B) * (mode == SA_IDX_BLOCKS ? Hkv : Hq) * Sg < (1L << 31), "grid too large");
   if (ws_bytes < w.bytes) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", w.bytes, ws_bytes);

@@ -23,7 +23,7 @@ constexpr int kMaxSplits = 128;       // partials merged by one workgroup
 constexpr int kMaxKFused = 1024;      // k of the decode step that selects inside the decode kernel
 constexpr int kTokensPerSplit = 256;  // block-mode split target: 16 tiles of 16 tokens
 constexpr int kCounterStride = 64;    // arrival counters 256 B apart (own cache lines)
-constexpr int kScoreRows = 64;        // sketch rows per scoring workgroup
+constexpr int kScoreRows = 32;        // sketch rows per scoring workgroup
 
 // Number of splits per (b, kv head) for the block-mode split-K decode: about
 // 256 selected tokens per workgroup (4 waves x 4 tiles of 16 tokens, all loads
@@ -31,6 +31,16 @@ constexpr int kScoreRows = 64;        // sketch rows per scoring workgroup
 // evenly over the splits; the last split to finish merges them.
 inline int decode_block_splits(int idx_stride, int block) {
   int S = cdiv(long(idx_stride) * block, kTokensPerSplit);
+  if (S > idx_stride) S = idx_stride;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  return S;
+}
+// Splits per (b, kv head) of the float32 block decode: one compute unit pulls
+// only a few tens of GB/s, so each split takes about one 64-token block.
+constexpr int kValuTokensPerSplit = 64;
+inline int decode_valu_splits(int idx_stride, int block) {
+  int S = cdiv(long(idx_stride) * block, kValuTokensPerSplit);
   if (S > idx_stride) S = idx_stride;
   if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
@@ -80,8 +90,10 @@ inline DecodeWs decode_ws(int B, int Hq, int Hkv, int D, int mode, int block,
   if (blocks) {
     const int Sp = decode_block_splits(idx_stride, block);
     const int Sf = decode_sel_splits(B * Hkv, idx_stride, block);
+    const int Sv = decode_valu_splits(idx_stride, block);
     w.S = fused ? Sf : Sp;
     Ssz = Sp > Sf ? Sp : Sf;
+    if (Sv > Ssz) Ssz = Sv;
   } else {
     w.S = Ssz = decode_token_splits(B * Hq, idx_stride);
   }
