@@ -407,15 +407,21 @@ sa_status sa_sparse_decode(const void* Q, const void* K, const void* V,
  * sa_sparse_prefill -- block-sparse causal attention ([FRONTIER] Contributi §2
  * Block-Sparse prefill; [ORACLE] §2.1 block-shared support).
  *
- *   Q [B, Hq, L, D], K, V [B, Hkv, L, D] dtype (SA_BF16 only; bf16 matrix cores;
- *            D = 128; each kv head is read through a 32-bit buffer range:
- *            L * D * 2 <= 0x7f000000, else SA_ERR_UNSUPPORTED)
- *   block    query and key block size (128)
+ *   Q [B, Hq, L, D], K, V [B, Hkv, L, D] dtype (SA_BF16 only: this is the
+ *            path's one dense contraction and runs on the bf16 matrix cores;
+ *            float32 inputs return SA_ERR_UNSUPPORTED.  D = 64 or 128; each kv
+ *            head is read through a 32-bit buffer range: L * D * 2 <=
+ *            0x7f000000, else SA_ERR_UNSUPPORTED)
+ *   block    query and key block size (64 or 128)
  *   idx      [B, Hkv, M, kmax] int32 ascending key blocks per query block
  *            (M = ceil(L / block)), count [B, Hkv, M]; entries must be <= i
  *   Row t of query block i attends to every token of its listed blocks at
  *   position <= t.
  *   O        [B, Hq, L, D] out_dtype;  lse [B, Hq, L] float32 (NULL to skip)
+ * Accumulation is float32.  The probabilities enter the value product as
+ * bf16 (relative rounding <= 2^-8), so a row's output lies within
+ * 2^-8 * sum_t p_t |v_t| of the exact one plus float32 rounding; rows of the
+ * first query block use a bf16 hi + lo split of P (about 2^-16).
  */
 sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V,
                             int dtype, int B, int Hq, int Hkv, int L, int D,

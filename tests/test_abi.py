@@ -311,8 +311,8 @@ def test_prefill_validation(lib):
         return f(*a)
 
     assert call(3, 0) == UNSUPPORTED              # float32 prefill
-    assert call(10, 64) == UNSUPPORTED            # 64-token blocks
-    assert call(8, 64) == UNSUPPORTED             # D = 64
+    assert call(10, 32) == UNSUPPORTED            # 32-token blocks (64 and 128 only)
+    assert call(8, 96) == UNSUPPORTED             # D = 96 (64 and 128 only)
     assert call(12, None) == INVALID              # count
     assert call(13, 0) == INVALID                 # kmax
     assert call(7, 9 * 1024 * 1024) == UNSUPPORTED   # one kv head past the 32-bit buffer range

@@ -39,11 +39,25 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-constexpr int PF_BLK = 128;         // query and key block
-constexpr int PF_D = 128;
-constexpr int PF_KS = PF_D + 8;     // K tile row stride (elements)
-constexpr int PF_VS = PF_BLK + 4;   // V^T tile row stride (elements)
 constexpr int PF_KT = 2;            // 32-key tiles per exponent + value-product step (4: spills)
+
+// Tile geometry of one (D, BLK) instance: BLK query rows per workgroup, one
+// wave per 32 rows; K staged row-major with rows padded to D + 8 elements,
+// V^T staged with rows padded to BLK + 4.
+template <int D, int BLK>
+struct PfGeom {
+  static constexpr int NT = 2 * BLK;          // threads: BLK / 32 waves
+  static constexpr int KS = D + 8;            // K tile row stride (elements)
+  static constexpr int VS = BLK + 4;          // V^T tile row stride (elements)
+  static constexpr int CPR = D / 8;           // 16-byte chunks per K row
+  static constexpr int RPP = NT / CPR;        // K rows per staging pass
+  static constexpr int KP = BLK / RPP;        // K staging passes
+  static constexpr int CG = D / 8;            // V^T column groups (8 columns each)
+  static constexpr int KG = NT / CG;          // V^T key groups (4 keys each) per pass
+  static constexpr int VP = BLK / (4 * KG);   // V^T staging passes
+  static constexpr int NKT = BLK / 32;        // 32-key score tiles per block
+  static_assert(KP >= 1 && VP >= 1 && NKT % PF_KT == 0, "tile geometry");
+};
 
 // The two lanes of a query row (l and l ^ 32) combine their values with
 // v_permlane32_swap: swapping lanes 32..63 of the first operand with lanes
@@ -54,7 +68,7 @@ __device__ __forceinline__ f32x2_pair pair32(float x) {
   return f32x2_pair{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
 
-template <bool SPLITP, int NKT>
+template <bool SPLITP, int NKT, int D, int VS>
 __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const f32x16* sfr,
                                          int kt0, f32x16* acc, int lane) {
   const int h = lane >> 5, col = lane & 31;
@@ -72,8 +86,8 @@ __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const 
       }
       const int key = (kt0 + kk) * 32 + 16 * half + 4 * h;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* row = vt + (dt * 32 + col) * PF_VS + key;
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const uint16_t* row = vt + (dt * 32 + col) * VS + key;
         const u32x2 a0 = *reinterpret_cast<const u32x2*>(row);
         const u32x2 a1 = *reinterpret_cast<const u32x2*>(row + 8);
         const u32x4 av = u32x4{a0[0], a0[1], a1[0], a1[1]};
@@ -86,17 +100,18 @@ __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const 
 
 // MODE 0: every query block but the first, P in bf16 (the sparse prefill's
 //         bulk); MODE 2: only the first query block of each (b, kv head), P as
-//         bf16 hi + lo (its rows see at most 128 keys); MODE 1: every block
+//         bf16 hi + lo (its rows see at most BLK keys); MODE 1: every block
 //         with P as hi + lo.  Keeping the hi + lo path out of MODE 0 keeps that
 //         kernel within its registers (one inlined copy of the value product).
-template <int MODE>
-__global__ __launch_bounds__(256, 2) void k_prefill_bf16(
+template <int MODE, int D, int BLK>
+__global__ __launch_bounds__(2 * BLK, 2) void k_prefill_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int Hq, int Hkv, int L, int M, int units, float sl2,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int kmax,
     void* __restrict__ O, int out_bf16, float* __restrict__ lse) {
-  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[PF_BLK * PF_KS];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[PF_D * PF_VS];
+  using Gm = PfGeom<D, BLK>;
+  __shared__ __attribute__((aligned(16))) uint16_t kt_lds[BLK * Gm::KS];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * Gm::VS];
 
   const int G = Hq / Hkv;
   const int id = blockIdx.x;
@@ -114,73 +129,72 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 31, half = lane >> 5;
-  const int qrow = i * PF_BLK + wave * 32 + col;     // this lane's query position
+  const int qrow = i * BLK + wave * 32 + col;        // this lane's query position
 
   // Q^T operand: query row qrow, d = 16*st + 8*half .. +7
-  u32x4 qf[PF_D / 16];
+  u32x4 qf[D / 16];
   {
     const int qr = min(qrow, L - 1);
-    const uint16_t* qp = Q + ((size_t(b) * Hq + h) * L + qr) * PF_D + 8 * half;
+    const uint16_t* qp = Q + ((size_t(b) * Hq + h) * L + qr) * D + 8 * half;
 #pragma unroll
-    for (int st = 0; st < PF_D / 16; ++st) qf[st] = ld16(qp + 16 * st);
+    for (int st = 0; st < D / 16; ++st) qf[st] = ld16(qp + 16 * st);
   }
 
-  const size_t kvbase = (size_t(b) * Hkv + kh) * size_t(L) * PF_D;
+  const size_t kvbase = (size_t(b) * Hkv + kh) * size_t(L) * D;
   const int32_t* lst = idx + (size_t(bkh) * M + i) * kmax;
   const int cnt = min(max(count[size_t(bkh) * M + i], 0), kmax);
 
   float m = -__builtin_inff(), l = 0.f;
-  f32x16 acc[4];
+  f32x16 acc[D / 32];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
-  const int ldc = tid & 15, ldr = tid >> 4;   // K loaders: 16-byte chunk, row group
+  const int ldc = tid % Gm::CPR, ldr = tid / Gm::CPR;   // K loaders: 16-byte chunk, row
   // V^T loaders: key group vk (4 rows) and column group vc (8 columns); they
-  // write 8 V^T rows x 4 keys.  The 16 lanes of one LDS write phase differ in
-  // vk, so their 8-byte stores fall 2 dwords apart in distinct banks (with the
-  // column group varying inside a phase, rows 8 apart at a stride of 66
-  // dwords met in two bank pairs: an 8-way conflict).
-  const int vk = tid & 15, vc = tid >> 4;
+  // write 8 V^T rows x 4 keys.  With 16 key groups the 16 lanes of one LDS
+  // write phase differ in vk, so their 8-byte stores fall 2 dwords apart in
+  // distinct banks (with the column group varying inside a phase, rows 8 apart
+  // at a stride of 66 dwords met in two bank pairs: an 8-way conflict).
+  const int vk = tid % Gm::KG, vc = tid / Gm::KG;
 
   for (int e = 0; e < cnt; ++e) {
     const int jb = lst[e];
     if (jb < 0 || jb > i) continue;          // uniform
-    const int key0 = jb * PF_BLK;
-    // ---- stage K (row-major) and V^T; all 16 loads of a thread are in flight
-    //      at once.  The block's rows go through resources based at its first
-    //      row (scalar work), so each load's lane offset is the same for every
-    //      block; rows past L lie beyond the resource's range and read as 0.
-    const size_t boff = kvbase + size_t(key0) * PF_D;
-    const uint32_t bbytes = uint32_t(L - key0) * PF_D * 2;
+    const int key0 = jb * BLK;
+    // ---- stage K (row-major) and V^T; a thread's loads of a pass group are
+    //      in flight at once.  The block's rows go through resources based at
+    //      its first row (scalar work), so each load's lane offset is the same
+    //      for every block; rows past L lie beyond the resource's range and
+    //      read as 0.
+    const size_t boff = kvbase + size_t(key0) * D;
+    const uint32_t bbytes = uint32_t(L - key0) * D * 2;
     const __amdgpu_buffer_rsrc_t rKb = make_rsrc(K + boff, bbytes);
     const __amdgpu_buffer_rsrc_t rVb = make_rsrc(V + boff, bbytes);
+    constexpr int KB = Gm::KP < 4 ? Gm::KP : 4;    // K rows loaded per group
 #pragma unroll
-    for (int p0 = 0; p0 < 8; p0 += 4) {
-      u32x4 w[4];
+    for (int p0 = 0; p0 < Gm::KP; p0 += KB) {
+      u32x4 w[KB];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        w[p] = bld16(rKb, ((ldr + 16 * (p0 + p)) * PF_D + 8 * ldc) * 2);
-      }
+      for (int p = 0; p < KB; ++p)
+        w[p] = bld16(rKb, ((ldr + Gm::RPP * (p0 + p)) * D + 8 * ldc) * 2);
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        *reinterpret_cast<u32x4*>(&kt_lds[(ldr + 16 * (p0 + p)) * PF_KS + 8 * ldc]) = w[p];
+      for (int p = 0; p < KB; ++p)
+        *reinterpret_cast<u32x4*>(&kt_lds[(ldr + Gm::RPP * (p0 + p)) * Gm::KS + 8 * ldc]) = w[p];
     }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int k0 = 4 * vk + 64 * p;
+    for (int p = 0; p < Gm::VP; ++p) {
+      const int k0 = 4 * vk + 4 * Gm::KG * p;
       u32x4 w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[j] = bld16(rVb, ((k0 + j) * PF_D + 8 * vc) * 2);
-      }
+      for (int j = 0; j < 4; ++j) w[j] = bld16(rVb, ((k0 + j) * D + 8 * vc) * 2);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u32x2 ev = u32x2{pack_lo(w[0][c], w[1][c]), pack_lo(w[2][c], w[3][c])};
         const u32x2 od = u32x2{pack_hi(w[0][c], w[1][c]), pack_hi(w[2][c], w[3][c])};
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * vc + 2 * c) * PF_VS + k0]) = ev;
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * vc + 2 * c + 1) * PF_VS + k0]) = od;
+        *reinterpret_cast<u32x2*>(&vt_lds[(8 * vc + 2 * c) * Gm::VS + k0]) = ev;
+        *reinterpret_cast<u32x2*>(&vt_lds[(8 * vc + 2 * c + 1) * Gm::VS + k0]) = od;
       }
     }
     __syncthreads();
@@ -188,19 +202,20 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
     // ---- S^T = K Q^T for the block, online softmax, O^T += V^T P^T in steps of
     //      32 PF_KT keys
     const bool diag = jb == i;
-    const bool tail = key0 + PF_BLK > L;
+    const bool tail = key0 + BLK > L;
     // all scores of the block first: the masking, the row maximum and the
-    // rescale then run once per block, and the second half's exponents run on
-    // the vector ALUs while the matrix cores do the first half's value product
-    f32x16 sall[4 / PF_KT][PF_KT];
+    // rescale then run once per block, and the later steps' exponents run on
+    // the vector ALUs while the matrix cores do the earlier value products
+    constexpr int NSB = Gm::NKT / PF_KT;
+    f32x16 sall[NSB][PF_KT];
 #pragma unroll
-    for (int sb = 0; sb < 4 / PF_KT; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int kk = 0; kk < PF_KT; ++kk) {
-        const uint16_t* kr = kt_lds + ((PF_KT * sb + kk) * 32 + col) * PF_KS + 8 * half;
+        const uint16_t* kr = kt_lds + ((PF_KT * sb + kk) * 32 + col) * Gm::KS + 8 * half;
         sall[sb][kk] = mfma32x32x16(*reinterpret_cast<const u32x4*>(kr), qf[0], f32x16{});
 #pragma unroll
-        for (int st = 1; st < PF_D / 16; ++st) {
+        for (int st = 1; st < D / 16; ++st) {
           const u32x4 a = *reinterpret_cast<const u32x4*>(kr + 16 * st);
           sall[sb][kk] = mfma32x32x16(a, qf[st], sall[sb][kk]);
         }
@@ -211,7 +226,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
       // key offset (PF_KT sb + kk) 32 + 8 (r/4) + (r%4) is kept when <= lim
       const int lim = min(qrow, L - 1) - key0 - 4 * half;
 #pragma unroll
-      for (int sb = 0; sb < 4 / PF_KT; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int kk = 0; kk < PF_KT; ++kk)
 #pragma unroll
@@ -222,7 +237,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
           }
     } else {
 #pragma unroll
-      for (int sb = 0; sb < 4 / PF_KT; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
         for (int kk = 0; kk < PF_KT; ++kk)
 #pragma unroll
@@ -241,12 +256,12 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
     // the accumulators change only where a row's maximum moved
     if (__ballot(alpha != 1.f)) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
     }
 #pragma unroll
-    for (int sb = 0; sb < 4 / PF_KT; ++sb) {
+    for (int sb = 0; sb < NSB; ++sb) {
       f32x16* sfr = sall[sb];
       float ls = 0.f;
 #pragma unroll
@@ -259,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
         }
       }
       l += ls;
-      pv_tiles<MODE != 0, PF_KT>(vt_lds, sfr, PF_KT * sb, acc, lane);
+      pv_tiles<MODE != 0, PF_KT, D, Gm::VS>(vt_lds, sfr, PF_KT * sb, acc, lane);
     }
     __syncthreads();
   }
@@ -269,9 +284,9 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
   const float lt = lp.a + lp.b;
   if (qrow < L) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const size_t ob = ((size_t(b) * Hq + h) * L + qrow) * PF_D;
+    const size_t ob = ((size_t(b) * Hq + h) * L + qrow) * D;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d = dt * 32 + 8 * a + 4 * half;
@@ -291,35 +306,52 @@ __global__ __launch_bounds__(256, 2) void k_prefill_bf16(
   }
 }
 
+template <int D, int BLK>
+static hipError_t launch_prefill_db(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                    int B, int Hq, int Hkv, int L, float sl2, const int32_t* idx,
+                                    const int32_t* count, int kmax, void* O, int ob, float* lse,
+                                    hipStream_t st, bool split_p) {
+  const int M = cdiv(L, BLK);
+  const int G = Hq / Hkv;
+  const int units = B * Hkv * M, firsts = B * Hkv;
+  const dim3 blk(2 * BLK);
+  if (split_p) {
+    const long grid = long(cdiv(units, 8)) * 8 * G;
+    k_prefill_bf16<1, D, BLK><<<dim3(static_cast<unsigned>(grid)), blk, 0, st>>>(
+        q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
+    return hipGetLastError();
+  }
+  const long grid = long(cdiv(units, 8)) * 8 * G;
+  k_prefill_bf16<0, D, BLK><<<dim3(static_cast<unsigned>(grid)), blk, 0, st>>>(
+      q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long grid0 = long(cdiv(firsts, 8)) * 8 * G;
+  k_prefill_bf16<2, D, BLK><<<dim3(static_cast<unsigned>(grid0)), blk, 0, st>>>(
+      q, k, v, Hq, Hkv, L, M, firsts, sl2, idx, count, kmax, O, ob, lse);
+  return hipGetLastError();
+}
+
 hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B, int Hq, int Hkv,
                           int L, int D, float scale, int block, const int32_t* idx,
                           const int32_t* count, int kmax, void* O, int out_dtype, float* lse,
                           hipStream_t st, bool split_p) {
-  (void)D;
-  (void)block;
-  const int M = cdiv(L, PF_BLK);
-  const int G = Hq / Hkv;
-  const int units = B * Hkv * M, firsts = B * Hkv;
   auto q = static_cast<const uint16_t*>(Q);
   auto k = static_cast<const uint16_t*>(K);
   auto v = static_cast<const uint16_t*>(V);
   const float sl2 = scale * kLog2e;
   const int ob = out_dtype == SA_BF16;
-  if (split_p) {
-    const long grid = long(cdiv(units, 8)) * 8 * G;
-    k_prefill_bf16<1><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, st>>>(
-        q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
-    return hipGetLastError();
-  }
-  const long grid = long(cdiv(units, 8)) * 8 * G;
-  k_prefill_bf16<0><<<dim3(static_cast<unsigned>(grid)), dim3(256), 0, st>>>(
-      q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long grid0 = long(cdiv(firsts, 8)) * 8 * G;
-  k_prefill_bf16<2><<<dim3(static_cast<unsigned>(grid0)), dim3(256), 0, st>>>(
-      q, k, v, Hq, Hkv, L, M, firsts, sl2, idx, count, kmax, O, ob, lse);
-  return hipGetLastError();
+  if (D == 128 && block == 128)
+    return launch_prefill_db<128, 128>(q, k, v, B, Hq, Hkv, L, sl2, idx, count, kmax, O, ob, lse,
+                                       st, split_p);
+  if (D == 128)
+    return launch_prefill_db<128, 64>(q, k, v, B, Hq, Hkv, L, sl2, idx, count, kmax, O, ob, lse,
+                                      st, split_p);
+  if (block == 128)
+    return launch_prefill_db<64, 128>(q, k, v, B, Hq, Hkv, L, sl2, idx, count, kmax, O, ob, lse,
+                                      st, split_p);
+  return launch_prefill_db<64, 64>(q, k, v, B, Hq, Hkv, L, sl2, idx, count, kmax, O, ob, lse, st,
+                                   split_p);
 }
 
 }  // namespace sa

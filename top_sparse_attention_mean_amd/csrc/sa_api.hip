@@ -645,8 +645,8 @@ sa_status sa_sparse_prefill(const void* Q, const void* K, const void* V, int dty
   if (s) return s;
   REQ(L >= 1 && kmax >= 1 && block >= 1, "L, kmax and block must be >= 1");
   SUP(dtype == SA_BF16, "prefill runs on bf16 matrix cores: dtype must be SA_BF16");
-  SUP(D == 128, "prefill supports D = 128");
-  SUP(block == 128, "prefill supports 128-token blocks");
+  SUP(D == 64 || D == 128, "prefill supports D = 64 or 128 (got %d)", D);
+  SUP(block == 64 || block == 128, "prefill supports blocks of 64 or 128 tokens (got %d)", block);
   SUP(long(L) * D * 2 <= 0x7f000000L, "prefill reads one kv head through a buffer resource of "
       "at most 0x7f000000 bytes (L * D * 2 = %ld)", long(L) * D * 2);
   const long units = long(B) * Hkv * cdiv(L, block);
