@@ -597,7 +597,25 @@ def bench_lowbit(args) -> dict:
         sa.sa_sparse_decode(Qs[r], Ks[r], Vs[r], tidx, tcnt, mode=sa.SA_IDX_TOKENS, score=tsc, O=O,
                             lse=lse, ws=tdws)
 
+    fws = torch.zeros(sa.workspace_bytes(sa.SA_OP_DECODE_LOWBIT, B, Hq, Hkv, N, D, blk, wl.cap),
+                      dtype=torch.uint8, device=dev)
+
+    def fused(r):
+        c, rs, m = enc[r]
+        sa.sa_decode_topdelta_lowbit(Qs[r], c, rs, m, Vs[r], blk, wl.sink, wl.local, wl.delta,
+                                     wl.margin, wl.cap, khat=khats[r], idx=idx, count=cnt,
+                                     tau=tau, O=O, lse=lse, ws=fws)
+
+    def fused0(r):
+        c, rs, m = enc[r]
+        sa.sa_decode_topdelta_lowbit(Qs[r], c, rs, m, Vs[r], blk, wl.sink, wl.local, wl.delta,
+                                     0.0, wl.cap, khat=khats[r], idx=idx, count=cnt, tau=tau,
+                                     O=O, lse=lse, ws=fws)
+
     n = max(4, args.steps // 20)
+    t_fused0 = graph_time(fused0, R, n)
+    kept0 = int(cnt.sum().item())
+    t_fused = graph_time(fused, R, n)
     t_pass = graph_time(lambda r: (sel(r), dec(r)), R, n)
     t_sel = graph_time(sel, R, n)
     t_exact = graph_time(exact, R, n)
@@ -607,15 +625,23 @@ def bench_lowbit(args) -> dict:
     refine_bytes = kept * blk * D * (1 + 1 / 4) + kept * 3 * D * 4 + kept * blk * D * e
     ach = scan_bytes / (t_sel * 1e-6) / 1e9
     res = {
-        "workload": wl.name, "us_per_pass": round(t_pass, 2), "margin": wl.margin,
-        "pass": "window refined keys + pseudo-max + thumbnail scan + block list + refined keys "
-                "of kept blocks (sa_select_topdelta_lowbit) + block-mode decode",
-        "kernels_us": {"sa_select_topdelta_lowbit": round(t_sel, 2),
-                       "sa_sparse_decode blocks over the refined keys": round(max(t_pass - t_sel, 0), 2),
+        "workload": wl.name, "us_per_pass": round(t_fused, 2), "margin": wl.margin,
+        "pass": "window refined keys + pseudo-max + thumbnail scan + block list + split-K "
+                "attention over the kept blocks with keys rebuilt from codes and residuals in "
+                "the kernel (sa_decode_topdelta_lowbit)",
+        "kernels_us": {"sa_decode_topdelta_lowbit (fused refinement)": round(t_fused, 2),
+                       "two-pass form: sa_select_topdelta_lowbit (refined keys written)":
+                           round(t_sel, 2),
+                       "two-pass form: sa_sparse_decode blocks over the refined keys":
+                           round(max(t_pass - t_sel, 0), 2),
+                       "two-pass form, whole": round(t_pass, 2),
                        "exact top-delta pass on the same arrays (sa_select_topdelta + token "
                        "decode)": round(t_exact, 2),
                        "sa_encode_keys, once per cache (host-timed, one call)": round(t_enc, 1)},
         "kept_block_fraction": round(kept / (B * Hkv * nb), 4),
+        "margin_0": {"us_per_pass": round(t_fused0, 2),
+                     "kept_block_fraction": round(kept0 / (B * Hkv * nb), 4),
+                     "note": "the same fused pass with the filter at tau itself (margin 0)"},
         "scan_bytes_per_token": D // 4 + 2 * D * 4 / blk,
         "roofline": {"bound": "hbm", "kernel": "k_thumb_scan (2-bit codes + block ranges; the "
                      "call also runs the window decode, pseudo-max, list and refine kernels)",

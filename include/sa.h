@@ -97,7 +97,8 @@ enum {
   SA_OP_SELECT_TOPDELTA = 4,
   SA_OP_SELECT_PRUNED = 5,
   SA_OP_SELECT_LOWBIT = 6,
-  SA_OP_MASS_SELECT = 7
+  SA_OP_MASS_SELECT = 7,
+  SA_OP_DECODE_LOWBIT = 8
 };
 
 /*
@@ -339,6 +340,36 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes,
                                     int32_t* count, float* tau, float* bmax,
                                     void* khat, void* ws, size_t ws_bytes,
                                     void* stream);
+
+/*
+ * sa_decode_topdelta_lowbit -- [FFD]'s fused decode (Metodologia §3) in full:
+ * stages (1) and (2) of sa_select_topdelta_lowbit (the window's refined keys
+ * into khat, tau, the thumbnail filter and the kept-block list), then (3) the
+ * refinement and the attention in one pass: a block-mode split-K decode over
+ * the kept blocks whose key rows are rebuilt inside the kernel from their codes
+ * and residuals (the value sa_decode_keys writes) and whose values come from
+ * V.  Same idx, count, tau and bmax as sa_select_topdelta_lowbit, and bitwise
+ * the output of sa_select_topdelta_lowbit followed by sa_sparse_decode over
+ * khat on the same lists, except that only the window's rows of khat are
+ * written.
+ *
+ *   Q, codes, resid, meta, block, sink, local, delta, margin, scale, kcap,
+ *            idx, count, tau, bmax: as sa_select_topdelta_lowbit
+ *            (kcap <= 1920)
+ *   V        [B, Hkv, N, D] bf16 (N * D * 2 <= 0x7f000000)
+ *   khat     [B, Hkv, N, D] bf16 scratch: the window blocks' rows are written
+ *   O        [B, Hq, D] out_dtype;  lse [B, Hq] float32 (NULL to skip)
+ * ws: sa_workspace_bytes(SA_OP_DECODE_LOWBIT, B, Hq, Hkv, N, D, block, kcap).
+ */
+sa_status sa_decode_topdelta_lowbit(const void* Q, const uint8_t* codes,
+                                    const int8_t* resid, const float* meta,
+                                    const void* V, int B, int Hq, int Hkv, int N,
+                                    int D, int block, int sink, int local,
+                                    float delta, float margin, float scale,
+                                    int kcap, int32_t* idx, int32_t* count,
+                                    float* tau, float* bmax, void* khat, void* O,
+                                    int out_dtype, float* lse, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /*
  * sa_mass_select -- the attention-mass top-k oracle of [ORACLE] §2.1 on the

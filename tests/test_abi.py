@@ -62,7 +62,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
               "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
+              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit",
+              "sa_decode_topdelta_lowbit", "sa_mass_select",
               "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step",
               "sa_decode_step_noalloc", "sa_workspace_bytes",
               "sa_status_str",
@@ -376,6 +377,7 @@ def test_binding_binds_every_entry_point():
         assert hasattr(sa, "_" + n[len("sa_"):]), f"no ctypes signature for {n}"
     for n in ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
               "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
+              "sa_select_threshold_pruned", "sa_select_topdelta_lowbit",
+              "sa_decode_topdelta_lowbit", "sa_mass_select",
               "sa_sparse_decode", "sa_sparse_prefill", "sa_select_decode", "sa_decode_step"]:
         assert callable(getattr(sa, n)), n

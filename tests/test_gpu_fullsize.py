@@ -191,6 +191,12 @@ def test_full_lowbit_topdelta():
         Qd, codes, resid, meta, wl.block, wl.sink, wl.local, wl.delta, wl.margin, wl.cap,
         want_bmax=True)
     O32, lse = sa.sa_sparse_decode(Qd, khat, Vd, idx, cnt, block=wl.block, out_dtype=torch.float32)
+    # the fused decode: the same lists and bitwise the same attention
+    O2, lse2, idx2, cnt2, _, _ = sa.sa_decode_topdelta_lowbit(
+        Qd, codes, resid, meta, Vd, wl.block, wl.sink, wl.local, wl.delta, wl.margin, wl.cap,
+        out_dtype=torch.float32)
+    assert torch.equal(idx2, idx) and torch.equal(cnt2, cnt)
+    assert torch.equal(O2, O32) and torch.equal(lse2, lse)
     c_x, r_x, m_x = oracle.lowbit_encode(K, wl.block)
     assert np.array_equal(resid.cpu().numpy(), r_x)
     assert np.array_equal(meta.cpu().numpy().view(np.uint32), m_x.view(np.uint32))

@@ -718,6 +718,14 @@ def test_lowbit_topdelta_parity(name, over):
     err = max_abs(O32.cpu().numpy(), O_ref)
     assert err <= OUT_TOL["bf16"], err
     assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+    # the fused decode (keys rebuilt inside the attention kernel): the same
+    # selection, and bitwise the output of the two-pass path above
+    O2, lse2, idx2, cnt2, tau2, bmax2 = sa.sa_decode_topdelta_lowbit(
+        Qd, codes, resid, meta, Vd, blk, wl.sink, wl.local, wl.delta, wl.margin, wl.cap,
+        out_dtype=torch.float32, want_bmax=True)
+    assert torch.equal(idx2, idx) and torch.equal(cnt2, cnt)
+    assert torch.equal(tau2, tau) and torch.equal(bmax2, bmax)
+    assert torch.equal(O2, O32) and torch.equal(lse2, lse)
     print(f"{name} {over}: {cnt_h.mean() / nb:.1%} of blocks kept, {band} blocks in the bound's "
           f"band, max |bmax - oracle| {dev.max():.2e} (bound {delta.min():.2e}..{delta.max():.2e}), "
           f"max-abs O error {err:.2e}")

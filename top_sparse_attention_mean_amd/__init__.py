@@ -31,11 +31,13 @@ SA_F32, SA_BF16 = 0, 1
 SA_FORCE_SINK, SA_FORCE_LOCAL, SA_CAUSAL = 1, 2, 4
 SA_IDX_BLOCKS, SA_IDX_TOKENS = 0, 1
 (SA_OP_SELECT_TOPK, SA_OP_SELECT_THRESHOLD, SA_OP_SPARSE_DECODE, SA_OP_DECODE_STEP,
- SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED, SA_OP_SELECT_LOWBIT, SA_OP_MASS_SELECT) = range(8)
+ SA_OP_SELECT_TOPDELTA, SA_OP_SELECT_PRUNED, SA_OP_SELECT_LOWBIT, SA_OP_MASS_SELECT,
+ SA_OP_DECODE_LOWBIT) = range(9)
 
 EXPORTS = ["sa_build_sketch", "sa_build_radius", "sa_encode_keys", "sa_decode_keys",
            "sa_select_topk", "sa_select_threshold", "sa_select_topdelta",
-           "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_mass_select",
+           "sa_select_threshold_pruned", "sa_select_topdelta_lowbit", "sa_decode_topdelta_lowbit",
+           "sa_mass_select",
            "sa_sparse_decode",
            "sa_sparse_prefill", "sa_select_decode", "sa_decode_step", "sa_decode_step_noalloc",
            "sa_workspace_bytes",
@@ -69,6 +71,9 @@ _decode_keys = _sig("sa_decode_keys", _I, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P
                     _P)
 _select_topdelta_lowbit = _sig("sa_select_topdelta_lowbit", _I, _P, _P, _P, _P, _I, _I, _I, _I,
                                _I, _I, _I, _I, _F, _F, _F, _I, _P, _P, _P, _P, _P, _P, _Z, _P)
+_decode_topdelta_lowbit = _sig("sa_decode_topdelta_lowbit", _I, _P, _P, _P, _P, _P, _I, _I, _I,
+                               _I, _I, _I, _I, _I, _F, _F, _F, _I, _P, _P, _P, _P, _P, _P, _I,
+                               _P, _P, _Z, _P)
 _mass_select = _sig("sa_mass_select", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _P,
                     _P, _P, _P, _P, _Z, _P)
 _select_topdelta = _sig("sa_select_topdelta", _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -462,6 +467,58 @@ def sa_select_topdelta_lowbit(Q: torch.Tensor, codes: torch.Tensor, resid: torch
                                    _ptr(count), _ptr(tau), _ptr(bmax), _ptr(khat), _ptr(ws),
                                    ws.numel(), _stream(stream)), "sa_select_topdelta_lowbit")
     return idx, count, tau, bmax, khat
+
+
+def sa_decode_topdelta_lowbit(Q: torch.Tensor, codes: torch.Tensor, resid: torch.Tensor,
+                              meta: torch.Tensor, V: torch.Tensor, block: int, sink: int,
+                              local: int, delta: float, margin: float, kcap: int,
+                              scale: float = 0.0, out_dtype=None, khat=None, idx=None,
+                              count=None, tau=None, O=None, lse=None, want_bmax: bool = False,
+                              want_lse: bool = True, ws=None, stream=None):
+    """The whole low-bit top-delta decode: the thumbnail filter, then the
+    split-K attention over the kept blocks with their keys rebuilt from codes
+    and residuals inside the kernel.  Returns O [B, Hq, D], lse [B, Hq], idx,
+    count, tau and bmax (or None); khat holds only the window blocks' rows."""
+    _rank(Q, "Q", 3)
+    _rank(resid, "resid", 4)
+    B, Hq, D = Q.shape
+    _, Hkv, N, _ = resid.shape
+    nb = -(-N // block)
+    _need(Q, "Q", None, (torch.bfloat16,))
+    _need(resid, "resid", (B, Hkv, N, D), (torch.int8,))
+    _need(codes, "codes", (B, Hkv, N, D // 4), (torch.uint8,))
+    _need(meta, "meta", (B, Hkv, nb, 3, D), _F32)
+    _need(V, "V", (B, Hkv, N, D), (torch.bfloat16,))
+    _need(khat, "khat", (B, Hkv, N, D), (torch.bfloat16,))
+    _need(idx, "idx", (B, Hkv, kcap), _I32)
+    _need(count, "count", (B, Hkv), _I32)
+    _need(tau, "tau", (B, Hq), _F32)
+    _need(O, "O", (B, Hq, D), (out_dtype,) if out_dtype else _FP)
+    _need(lse, "lse", (B, Hq), _F32)
+    _dev(Q, codes, resid, meta, V, khat, idx, count, tau, O, lse)
+    dev = Q.device
+    if khat is None:
+        khat = torch.zeros(B, Hkv, N, D, dtype=torch.bfloat16, device=dev)
+    if idx is None:
+        idx = torch.empty(B, Hkv, kcap, dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(B, Hkv, dtype=torch.int32, device=dev)
+    if tau is None:
+        tau = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    if O is None:
+        O = torch.empty(B, Hq, D, dtype=out_dtype or Q.dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=dev)
+    bmax = torch.empty(B, Hq, nb, dtype=torch.float32, device=dev) if want_bmax else None
+    need = workspace_bytes(SA_OP_DECODE_LOWBIT, B, Hq, Hkv, N, D, block, kcap)
+    if ws is None:
+        ws = workspace(need, dev, ("decode_lowbit", B, Hq, Hkv, N, D, block, kcap))
+    _check(_decode_topdelta_lowbit(_ptr(Q), _ptr(codes), _ptr(resid), _ptr(meta), _ptr(V), B, Hq,
+                                   Hkv, N, D, block, sink, local, delta, margin, scale, kcap,
+                                   _ptr(idx), _ptr(count), _ptr(tau), _ptr(bmax), _ptr(khat),
+                                   _ptr(O), _dt(O), _ptr(lse), _ptr(ws), ws.numel(),
+                                   _stream(stream)), "sa_decode_topdelta_lowbit")
+    return O, lse, idx, count, tau, bmax
 
 
 def sa_mass_select(Q: torch.Tensor, K: torch.Tensor, k_free: int, block: int = 128,

@@ -55,6 +55,11 @@ struct DecodeArgs {
   int32_t* sel_idx;
   int32_t* sel_count;
   int32_t* sel_ent;   // [B*Hkv, kSelEntCap] kept block (or -1) per entry of a row
+  // keys rebuilt from thumbnails (k_decode_lowbit): codes [B*Hkv, N, D/4],
+  // residuals [B*Hkv, N, D], (lo, step, rstep) rows [B*Hkv, nb, 3, D]
+  const uint8_t* lb_codes;
+  const int8_t* lb_resid;
+  const float* lb_meta;
 };
 static_assert(kSelWords * 32 >= kMaxNbDecode, "one bitmap word per 32 blocks of a row");
 static_assert(2 + kCandCap <= kSelEntCap && kSelEntCap <= 3 * 256, "entries of a row: forced blocks and candidates");
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
   const __amdgpu_buffer_rsrc_t rV =
       make_rsrc(static_cast<const uint16_t*>(a.V) + size_t(bh) * N * D, uint32_t(N) * D * 2);
   const int nbk = (N + BLOCK - 1) / BLOCK;
-  run_tiles<D, G>(ta, qb, rK, rV, N, a.sl2, ntiles, [&](int t) {
+  run_tiles<D, G>(ta, qb, KRowsBf16<D>{rK}, rV, N, a.sl2, ntiles, [&](int t) {
     if (SEL && cmode) return wl[t];
     if ((g0 + t) / TPB < cnt) {
       const int blk = ib[(g0 + t) / TPB];
@@ -272,6 +277,75 @@ __global__ __launch_bounds__(256, 2) void k_decode_blocks_mfma(DecodeArgs a) {
     merge_tail<D>(a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S, a.S,
                   MergeDst{a.O, a.out_bf16, a.lse}, h0, G, s_w, s_lv);
   }
+}
+
+// ---------------------------------------------------------------- thumbnail keys
+// k_decode_lowbit (bf16): the block-mode split-K decode with every key row
+// rebuilt from its 2-bit code and 8-bit residual inside the tile pipeline
+// (KRowsLowbit), so the refinement of the kept blocks and the attention over
+// them are one pass over codes, residuals and values ("Faster Than Flash",
+// Metodologia §3).  Split s takes the tile slice of the block decode; the
+// (lo, step, rstep) rows of the slice's blocks (at most kLowbitMetaBlocks) are
+// staged in LDS first.
+template <int D, int G, int BLOCK>
+__global__ __launch_bounds__(256, 2) void k_decode_lowbit(DecodeArgs a) {
+  static_assert(2 * G <= 16, "g must be at most 8");
+  constexpr int TPB = BLOCK / 16;  // 16-token tiles per block
+  __shared__ CombineLds<D, G> s_cmb;
+  __shared__ __attribute__((aligned(16))) float s_w[G * kMaxSplits], s_lv[G * kMaxSplits];
+  __shared__ __attribute__((aligned(16))) float s_meta[kLowbitMetaBlocks][3 * D];
+  __shared__ int s_flag;
+
+  const int BH = a.B * a.Hkv, N = a.N;
+  const int bh = blockIdx.x % BH, s = blockIdx.x / BH;
+  const int b = bh / a.Hkv, kh = bh % a.Hkv;
+  const int tid = threadIdx.x;
+  const int tps = (a.idx_stride * TPB + a.S - 1) / a.S;
+  const int g0 = s * tps;
+  const int ntiles = max(min(g0 + tps, a.idx_stride * TPB) - g0, 0);
+  const int cnt = a.count ? min(max(a.count[bh], 0), a.idx_stride) : a.idx_stride;
+  const int32_t* ib = a.idx + size_t(bh) * a.idx_stride;
+  const int nbk = (N + BLOCK - 1) / BLOCK;
+  // the slice's list entries [e0, e0 + ne): their (lo, step, rstep) rows
+  const int e0 = g0 / TPB;
+  const int ne = ntiles > 0 ? min((g0 + ntiles - 1) / TPB - e0 + 1, kLowbitMetaBlocks) : 0;
+  for (int i = tid; i < ne * (3 * D / 4); i += 256) {
+    const int q = i / (3 * D / 4), c4 = i % (3 * D / 4);
+    const int e = e0 + q;
+    const int blk = e < cnt ? ib[e] : -1;
+    f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (blk >= 0 && blk < nbk)
+      v = *reinterpret_cast<const f32x4*>(a.lb_meta + (size_t(bh) * nbk + blk) * 3 * D + 4 * c4);
+    *reinterpret_cast<f32x4*>(&s_meta[q][4 * c4]) = v;
+  }
+  u32x4 qb[D / 32];
+  tile_q_operand<D, G>(static_cast<const uint16_t*>(a.Q) + (size_t(b) * a.Hq + kh * G) * D, qb);
+  TileAcc<D> ta;
+  tile_acc_init(ta);
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rC = make_rsrc(a.lb_codes + size_t(bh) * N * (D / 4), uint32_t(N) * (D / 4));
+  const __amdgpu_buffer_rsrc_t rR = make_rsrc(a.lb_resid + size_t(bh) * N * D, uint32_t(N) * D);
+  const __amdgpu_buffer_rsrc_t rV =
+      make_rsrc(static_cast<const uint16_t*>(a.V) + size_t(bh) * N * D, uint32_t(N) * D * 2);
+  auto meta_of = [&](int t) -> const float* { return &s_meta[(g0 + t) / TPB - e0][0]; };
+  const KRowsLowbit<D, decltype(meta_of)> ks{rC, rR, meta_of};
+  run_tiles<D, G>(ta, qb, ks, rV, N, a.sl2, ntiles, [&](int t) {
+    const int e = (g0 + t) / TPB;
+    if (e < cnt && e - e0 < kLowbitMetaBlocks) {
+      const int blk = ib[e];
+      if (blk >= 0 && blk < nbk) {
+        const int tok0 = blk * BLOCK + ((g0 + t) % TPB) * 16;
+        return tok0 < N ? tok0 : -1;
+      }
+    }
+    return -1;
+  });
+  const int h0 = b * a.Hq + kh * G;
+  store_partial<D, G>(ta, s_cmb, a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S,
+                      a.S, s, true);
+  if (!arrive_last(&a.counter[bh * kCounterStride], a.S, &s_flag)) return;
+  merge_tail<D>(a.pacc + size_t(h0) * a.S * D, a.pml + 2 * size_t(h0) * a.S, a.S,
+                MergeDst{a.O, a.out_bf16, a.lse}, h0, G, s_w, s_lv);
 }
 
 // ---------------------------------------------------------------- float32 VALU
@@ -623,6 +697,7 @@ static DecodeArgs make_args(const void* Q, const void* K, const void* V, int B, 
   a.sel_scores = nullptr; a.nb = 0; a.k = 0; a.flags = 0; a.sel_idx = nullptr;
   a.sel_count = nullptr;
   a.sel_ent = reinterpret_cast<int32_t*>(base + w.ent_off);
+  a.lb_codes = nullptr; a.lb_resid = nullptr; a.lb_meta = nullptr;
   return a;
 }
 
@@ -667,6 +742,37 @@ hipError_t launch_decode_blocks(const void* Q, const void* K, const void* V, int
   } else {
     if (D == 128) launch_valu_g<128>(a, Hq / Hkv, g, st);
     else          launch_valu_g<64>(a, Hq / Hkv, g, st);
+  }
+  return hipGetLastError();
+}
+
+template <int D, int BLOCK>
+static void launch_lowbit_g(const DecodeArgs& a, int G, dim3 g, hipStream_t st) {
+  switch (G) {
+    case 1: k_decode_lowbit<D, 1, BLOCK><<<g, 256, 0, st>>>(a); break;
+    case 2: k_decode_lowbit<D, 2, BLOCK><<<g, 256, 0, st>>>(a); break;
+    case 4: k_decode_lowbit<D, 4, BLOCK><<<g, 256, 0, st>>>(a); break;
+    default: k_decode_lowbit<D, 8, BLOCK><<<g, 256, 0, st>>>(a); break;
+  }
+}
+
+hipError_t launch_decode_lowbit(const void* Q, const uint8_t* codes, const int8_t* resid,
+                                const float* meta, const void* V, int B, int Hq, int Hkv, int N,
+                                int D, float scale, int block, const int32_t* idx,
+                                const int32_t* count, int idx_stride, const DecodeWs& w, void* ws,
+                                void* O, int out_dtype, float* lse, hipStream_t st) {
+  DecodeArgs a = make_args(Q, nullptr, V, B, Hq, Hkv, N, block, scale, idx, count, idx_stride,
+                           nullptr, w, ws, O, out_dtype, lse);
+  a.S = decode_lowbit_splits(idx_stride, block);   // within the partials decode_ws sizes
+  a.lb_codes = codes; a.lb_resid = resid; a.lb_meta = meta;
+  const dim3 g(static_cast<unsigned>(long(B) * Hkv * a.S));
+  const int G = Hq / Hkv;
+  if (D == 128) {
+    if (block == 64) launch_lowbit_g<128, 64>(a, G, g, st);
+    else             launch_lowbit_g<128, 128>(a, G, g, st);
+  } else {
+    if (block == 64) launch_lowbit_g<64, 64>(a, G, g, st);
+    else             launch_lowbit_g<64, 128>(a, G, g, st);
   }
   return hipGetLastError();
 }

@@ -529,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void k_decode_step(StepArgs a) {
   tile_acc_init(ta);
   const __amdgpu_buffer_rsrc_t rK = make_rsrc(a.K + size_t(bh) * N * D, uint32_t(N) * D * 2);
   const __amdgpu_buffer_rsrc_t rV = make_rsrc(a.V + size_t(bh) * N * D, uint32_t(N) * D * 2);
-  run_tiles<D, G>(ta, qb, rK, rV, N, a.sl2, g1 - g0, [&](int t) {
+  run_tiles<D, G>(ta, qb, KRowsBf16<D>{rK}, rV, N, a.sl2, g1 - g0, [&](int t) {
     const int u = g0 + t;
     const int tok0 = s_list[u / TPB] * BLOCK + (u % TPB) * 16;
     return tok0 < N ? tok0 : -1;

@@ -162,6 +162,77 @@ sa_status v_decode(const void* Q, const void* K, const void* V, int dtype, int B
 
 }  // namespace
 
+// Checks of the low-bit selection's arguments (nothing enqueued).
+static sa_status v_lowbit(const void* Q, const uint8_t* codes, const int8_t* resid,
+                          const float* meta, int B, int Hq, int Hkv, int N, int D, int block,
+                          int sink, int local, float delta, float margin, int kcap,
+                          int32_t* idx, int32_t* count, float* tau, float* bmax, void* khat,
+                          void* ws, size_t ws_bytes) {
+  PTR(Q);
+  PTR(codes);
+  PTR(resid);
+  PTR(meta);
+  PTR(idx);
+  PTR(count);
+  PTR(khat);
+  if (tau) PTR(tau);
+  if (bmax) PTR(bmax);
+  sa_status s = check_heads(B, Hq, Hkv);
+  if (s) return s;
+  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
+  SUP(block == 64 || block == 128, "block must be 64 or 128 (got %d)", block);
+  SUP(pow2_le8(Hq / Hkv), "the low-bit filter needs g in {1, 2, 4, 8}");
+  REQ(N >= 1 && kcap >= 1, "N and kcap must be >= 1");
+  REQ(sink >= 0 && local >= 0, "sink and local must be >= 0 (got %d, %d)", sink, local);
+  REQ(sink > 0 || local > 0, "the sink and local windows are both empty");
+  REQ(delta >= 0.f, "delta must be >= 0 (got %g)", double(delta));
+  REQ(margin >= 0.f, "margin must be >= 0 (got %g)", double(margin));
+  const int nb = cdiv(N, block);
+  REQ(long(B) * Hkv * cdiv(nb, 4) < (1L << 31), "grid too large");
+  const size_t need = lowbit_ws_bytes(B, Hq, Hkv, N, block);
+  if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+  PTR(ws);
+  return SA_OK;
+}
+
+// The low-bit selection's launches: the window's refined keys into khat, the
+// pseudo-maximum and tau, the thumbnail scan and the block list; then, when
+// refine_kept, the refined keys of the kept blocks into khat.
+static sa_status run_lowbit_select(const void* Q, const uint8_t* codes, const int8_t* resid,
+                                   const float* meta, int B, int Hq, int Hkv, int N, int D,
+                                   int block, int sink, int local, float delta, float margin,
+                                   float scale, int kcap, int32_t* idx, int32_t* count,
+                                   float* tau, float* bmax, void* khat, void* ws,
+                                   bool refine_kept, hipStream_t st, const char* what) {
+  const int nb = cdiv(N, block);
+  const float sc = eff_scale(scale, D);
+  char* base = static_cast<char*>(ws);
+  uint8_t* flag = reinterpret_cast<uint8_t*>(base);
+  float* t = tau ? tau : reinterpret_cast<float*>(base + align256(size_t(B) * Hkv * nb));
+  uint16_t* kh = static_cast<uint16_t*>(khat);
+  // the window's blocks: [0, f1) holds the sink tokens, [f2, nb) the local ones
+  const int ns = sink < N ? sink : N;
+  const int lt = N - (local < N ? local : N);
+  const int tw = lt > ns ? lt : ns;
+  const int f1 = cdiv(ns, block), f2 = tw < N ? tw / block : nb;
+  hipError_t e = launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, nullptr, nullptr, 0,
+                                    0, f1, kh, st);
+  if (e == hipSuccess)
+    e = launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, nullptr, nullptr, 0, f2, nb,
+                           kh, st);
+  if (e != hipSuccess) return hip_status(e, what);
+  e = launch_pseudo_max(Q, kh, SA_BF16, B, Hq, Hkv, N, D, sink, local, delta, sc, t, st);
+  if (e != hipSuccess) return hip_status(e, what);
+  e = launch_thumb_scan(static_cast<const uint16_t*>(Q), codes, meta, B, Hq, Hkv, N, D, block, sc,
+                        t, margin, 0, f1, f2, nb, bmax, flag, st);
+  if (e != hipSuccess) return hip_status(e, what);
+  e = launch_block_list(flag, B * Hkv, nb, kcap, idx, count, st);
+  if (e != hipSuccess || !refine_kept) return hip_status(e, what);
+  return hip_status(launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, idx, count, kcap,
+                                       0, 0, kh, st),
+                    what);
+}
+
 // Selection from a score row fused with the split-K decode where a fused
 // kernel exists (bf16, D = 128, k <= kMaxKFused); otherwise the selection
 // kernel followed by the block decode.
@@ -294,6 +365,10 @@ size_t sa_workspace_bytes(int op, int B, int Hq, int Hkv, int N, int D, int bloc
     case SA_OP_SELECT_LOWBIT:        // block = the block size
       if (block < 1) return SIZE_MAX;
       return lowbit_ws_bytes(B, Hq, Hkv, N, block);
+    case SA_OP_DECODE_LOWBIT:        // block = the block size, k = kcap
+      if (block < 1 || k < 1) return SIZE_MAX;
+      return lowbit_ws_bytes(B, Hq, Hkv, N, block) +
+             decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k).bytes;
     case SA_OP_SPARSE_DECODE:        // k = idx_stride; block = 0 for token mode
       if (k < 1) return SIZE_MAX;
       return decode_ws(B, Hq, Hkv, D, block > 0 ? SA_IDX_BLOCKS : SA_IDX_TOKENS, block, k).bytes;
@@ -520,57 +595,47 @@ sa_status sa_select_topdelta_lowbit(const void* Q, const uint8_t* codes, const i
                                     float scale, int kcap, int32_t* idx, int32_t* count,
                                     float* tau, float* bmax, void* khat, void* ws,
                                     size_t ws_bytes, void* stream) {
-  PTR(Q);
-  PTR(codes);
-  PTR(resid);
-  PTR(meta);
-  PTR(idx);
-  PTR(count);
-  PTR(khat);
-  if (tau) PTR(tau);
-  if (bmax) PTR(bmax);
-  sa_status s = check_heads(B, Hq, Hkv);
+  sa_status s = v_lowbit(Q, codes, resid, meta, B, Hq, Hkv, N, D, block, sink, local, delta,
+                         margin, kcap, idx, count, tau, bmax, khat, ws, ws_bytes);
   if (s) return s;
-  SUP(D == 64 || D == 128, "D must be 64 or 128 (got %d)", D);
-  SUP(block == 64 || block == 128, "block must be 64 or 128 (got %d)", block);
-  SUP(pow2_le8(Hq / Hkv), "the low-bit filter needs g in {1, 2, 4, 8}");
-  REQ(N >= 1 && kcap >= 1, "N and kcap must be >= 1");
-  REQ(sink >= 0 && local >= 0, "sink and local must be >= 0 (got %d, %d)", sink, local);
-  REQ(sink > 0 || local > 0, "the sink and local windows are both empty");
-  REQ(delta >= 0.f, "delta must be >= 0 (got %g)", double(delta));
-  REQ(margin >= 0.f, "margin must be >= 0 (got %g)", double(margin));
-  const int nb = cdiv(N, block);
-  REQ(long(B) * Hkv * cdiv(nb, 4) < (1L << 31), "grid too large");
-  const size_t need = lowbit_ws_bytes(B, Hq, Hkv, N, block);
-  if (ws_bytes < need) return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
-  PTR(ws);
+  return run_lowbit_select(Q, codes, resid, meta, B, Hq, Hkv, N, D, block, sink, local, delta,
+                           margin, scale, kcap, idx, count, tau, bmax, khat, ws, true,
+                           static_cast<hipStream_t>(stream), "sa_select_topdelta_lowbit");
+}
+
+sa_status sa_decode_topdelta_lowbit(const void* Q, const uint8_t* codes, const int8_t* resid,
+                                    const float* meta, const void* V, int B, int Hq, int Hkv,
+                                    int N, int D, int block, int sink, int local, float delta,
+                                    float margin, float scale, int kcap, int32_t* idx,
+                                    int32_t* count, float* tau, float* bmax, void* khat, void* O,
+                                    int out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                    void* stream) {
+  PTR(V);
+  PTR(O);
+  if (lse) PTR(lse);
+  REQ(dtype_ok(out_dtype), "unknown output dtype %d", out_dtype);
+  const size_t lws = lowbit_ws_bytes(B, Hq, Hkv, N, block);
+  sa_status s = v_lowbit(Q, codes, resid, meta, B, Hq, Hkv, N, D, block, sink, local, delta,
+                         margin, kcap, idx, count, tau, bmax, khat, ws, ws_bytes);
+  if (s) return s;
+  SUP(kcap <= kMaxSplits * (kLowbitMetaBlocks - 1),
+      "the thumbnail-key decode lists at most %d blocks (kcap = %d)",
+      kMaxSplits * (kLowbitMetaBlocks - 1), kcap);
+  SUP(long(N) * D * 2 <= 0x7f000000L, "the thumbnail-key decode reads one kv head through a "
+      "buffer resource of at most 0x7f000000 bytes (N * D * 2 = %ld)", long(N) * D * 2);
+  const DecodeWs dw = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, kcap);
+  if (ws_bytes < lws + dw.bytes)
+    return fail(SA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", lws + dw.bytes, ws_bytes);
+  REQ(long(B) * Hkv * decode_lowbit_splits(kcap, block) < (1L << 31), "grid too large");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float sc = eff_scale(scale, D);
-  char* base = static_cast<char*>(ws);
-  uint8_t* flag = reinterpret_cast<uint8_t*>(base);
-  float* t = tau ? tau : reinterpret_cast<float*>(base + align256(size_t(B) * Hkv * nb));
-  uint16_t* kh = static_cast<uint16_t*>(khat);
-  // the window's blocks: [0, f1) holds the sink tokens, [f2, nb) the local ones
-  const int ns = sink < N ? sink : N;
-  const int lt = N - (local < N ? local : N);
-  const int tw = lt > ns ? lt : ns;
-  const int f1 = cdiv(ns, block), f2 = tw < N ? tw / block : nb;
-  hipError_t e = launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, nullptr, nullptr, 0,
-                                    0, f1, kh, st);
-  if (e == hipSuccess)
-    e = launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, nullptr, nullptr, 0, f2, nb,
-                           kh, st);
-  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (window keys)");
-  e = launch_pseudo_max(Q, kh, SA_BF16, B, Hq, Hkv, N, D, sink, local, delta, sc, t, st);
-  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (pseudo-max)");
-  e = launch_thumb_scan(static_cast<const uint16_t*>(Q), codes, meta, B, Hq, Hkv, N, D, block, sc,
-                        t, margin, 0, f1, f2, nb, bmax, flag, st);
-  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (thumbnail scan)");
-  e = launch_block_list(flag, B * Hkv, nb, kcap, idx, count, st);
-  if (e != hipSuccess) return hip_status(e, "sa_select_topdelta_lowbit (block list)");
-  return hip_status(launch_decode_keys(codes, resid, meta, B, Hkv, N, D, block, idx, count, kcap,
-                                       0, 0, kh, st),
-                    "sa_select_topdelta_lowbit (refined keys)");
+  s = run_lowbit_select(Q, codes, resid, meta, B, Hq, Hkv, N, D, block, sink, local, delta,
+                        margin, scale, kcap, idx, count, tau, bmax, khat, ws, false, st,
+                        "sa_decode_topdelta_lowbit");
+  if (s) return s;
+  return hip_status(launch_decode_lowbit(Q, codes, resid, meta, V, B, Hq, Hkv, N, D,
+                                         eff_scale(scale, D), block, idx, count, kcap, dw,
+                                         static_cast<char*>(ws) + lws, O, out_dtype, lse, st),
+                    "sa_decode_topdelta_lowbit (decode)");
 }
 
 sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq, int Hkv, int L,

@@ -26,7 +26,7 @@
 
 namespace sa {
 
-constexpr int kTileBatch = 4;
+constexpr int kTileBatch = 4;   // tiles per wave whose loads are issued together
 
 // Running state of one wave: lane l keeps (m, l) of head l%16 (< g) in log2
 // units and accumulator rows 4*(l/16)+r (hi rows 0..g-1, lo rows g..2g-1).
@@ -59,50 +59,136 @@ __device__ __forceinline__ void tile_q_operand(const uint16_t* Qg, u32x4 (&qb)[D
   }
 }
 
+// Key sources of the tile pipeline.  issue() starts the loads of lane
+// (gq, nn)'s share of a tile's key rows (row tok0 + nn, channels
+// 8 gq + 32 st .. + 7 for st < D / 32) into a raw register set; finish()
+// turns them into the score MFMA's A operand once they are needed.
+//
+// KRowsBf16: bf16 key rows through a buffer resource over the head's K (rows
+// past N, and tok0 < 0, read as zeros).
+template <int D>
+struct KRowsBf16 {
+  __amdgpu_buffer_rsrc_t rK;
+  struct Raw {
+    u32x4 k[D / 32];
+  };
+  __device__ __forceinline__ void issue(int tok0, int /*t*/, Raw& r) const {
+    const int lane = threadIdx.x & 63, gq = lane >> 4, nn = lane & 15;
+    const int koff = tok0 >= 0 ? ((tok0 + nn) * D + 8 * gq) * 2 : kBufOOB;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) r.k[st] = bld16(rK, koff + 64 * st);
+  }
+  __device__ __forceinline__ void finish(const Raw& r, int /*t*/, u32x4 (&ka)[D / 32]) const {
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) ka[st] = r.k[st];
+  }
+};
+
+// KRowsLowbit: keys rebuilt from their 2-bit codes and 8-bit residuals
+// ("Faster Than Flash", Metodologia §3: the kept blocks are refined with the
+// residuals), k^ = fma(code, step, lo) + r8 * rstep rounded to bf16 (nearest,
+// ties to even) -- the same float32 operations, so the same value, as the
+// stand-alone key rebuild.  rC / rR: buffer resources over the head's codes
+// (D / 4 bytes per token: one word per 16 channels, channel 16 g + i at bit
+// 8 (i % 4) + 2 (i / 4)) and residuals (D bytes per token); meta_of(t): the
+// (lo, step, rstep) rows (3 x D floats, LDS) of tile t's block.
+template <int D, typename MetaOf>
+struct KRowsLowbit {
+  __amdgpu_buffer_rsrc_t rC, rR;
+  MetaOf meta_of;
+  struct Raw {
+    uint32_t c[D / 32];
+    u32x2 r[D / 32];
+  };
+  __device__ __forceinline__ void issue(int tok0, int /*t*/, Raw& w) const {
+    const int lane = threadIdx.x & 63, gq = lane >> 4, nn = lane & 15;
+    const int row = tok0 + nn;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const int c0 = 8 * gq + 32 * st;
+      w.c[st] = bld4(rC, tok0 >= 0 ? row * (D / 4) + (c0 / 16) * 4 : kBufOOB);
+      w.r[st] = bld8(rR, tok0 >= 0 ? row * D + c0 : kBufOOB);
+    }
+  }
+  __device__ __forceinline__ void finish(const Raw& w, int t, u32x4 (&ka)[D / 32]) const {
+    const int lane = threadIdx.x & 63, gq = lane >> 4;
+    const float* m = meta_of(t);
+    const int hw = gq & 1;                 // which half of its 16-channel word
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      const int c0 = 8 * gq + 32 * st;
+      const f32x4 lo0 = *reinterpret_cast<const f32x4*>(m + c0);
+      const f32x4 lo1 = *reinterpret_cast<const f32x4*>(m + c0 + 4);
+      const f32x4 sp0 = *reinterpret_cast<const f32x4*>(m + D + c0);
+      const f32x4 sp1 = *reinterpret_cast<const f32x4*>(m + D + c0 + 4);
+      const f32x4 rs0 = *reinterpret_cast<const f32x4*>(m + 2 * D + c0);
+      const f32x4 rs1 = *reinterpret_cast<const f32x4*>(m + 2 * D + c0 + 4);
+      float kh[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int code = int((w.c[st] >> (8 * (e & 3) + 2 * (2 * hw + (e >> 2)))) & 3u);
+        const int r8 = int(int8_t((w.r[st][e / 4] >> (8 * (e % 4))) & 0xffu));
+        const float lo = e < 4 ? lo0[e] : lo1[e - 4];
+        const float sp = e < 4 ? sp0[e] : sp1[e - 4];
+        const float rs = e < 4 ? rs0[e] : rs1[e - 4];
+        const float tb = fmaf(float(code), sp, lo);
+        kh[e] = tb + float(r8) * rs;
+      }
+      ka[st] = u32x4{pack_bf16x2(kh[0], kh[1]), pack_bf16x2(kh[2], kh[3]),
+                     pack_bf16x2(kh[4], kh[5]), pack_bf16x2(kh[6], kh[7])};
+    }
+  }
+};
+
 // Tiles t = wave, wave + 4, ... < ntiles of one (b, kv head); tok_of(t) gives a
-// tile's first token, or -1 to skip it (uniform across the wave).  rK / rV:
-// buffer resources over the head's K and V rows; sl2 = scale * log2(e).
-template <int D, int G, typename TokOf>
+// tile's first token, or -1 to skip it (uniform across the wave).  ks: the key
+// source; rV: a buffer resource over the head's V rows; sl2 = scale * log2(e).
+template <int D, int G, typename KSrc, typename TokOf>
 __device__ __forceinline__ void run_tiles(TileAcc<D>& ta, const u32x4 (&qb)[D / 32],
-                                          __amdgpu_buffer_rsrc_t rK, __amdgpu_buffer_rsrc_t rV,
+                                          const KSrc& ks, __amdgpu_buffer_rsrc_t rV,
                                           int N, float sl2, int ntiles, TokOf tok_of) {
   static_assert(2 * G <= 16, "g must be at most 8");
   constexpr int NST = D / 32;      // contraction steps of the score MFMA
   constexpr int EPL = D / 16;      // value columns per lane = PV MFMAs per tile
+  constexpr int TB = kTileBatch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gq = lane >> 4, nn = lane & 15;
-  for (int tb = wave; tb < ntiles; tb += 4 * kTileBatch) {
-    u32x4 ka[kTileBatch][NST];
-    uint32_t vw[kTileBatch][4][EPL / 2];
-    int tok0s[kTileBatch];
-    // issue every load of the batch first
+  // the raw loads of TB tiles (tiles tb, tb + 4, ... of this wave)
+  struct Batch {
+    typename KSrc::Raw kr[TB];
+    uint32_t vw[TB][4][EPL / 2];
+    int tok0[TB];
+  };
+  auto issue = [&](int tb, Batch& bt) {
 #pragma unroll
-    for (int u = 0; u < kTileBatch; ++u) {
+    for (int u = 0; u < TB; ++u) {
       const int t = tb + 4 * u;
       const int tok0 = t < ntiles ? tok_of(t) : -1;
-      tok0s[u] = tok0;
-      const int koff = tok0 >= 0 ? ((tok0 + nn) * D + 8 * gq) * 2 : kBufOOB;
+      bt.tok0[u] = tok0;
+      ks.issue(tok0, t, bt.kr[u]);
       const int voff = tok0 >= 0 ? ((tok0 + 4 * gq) * D + EPL * nn) * 2 : kBufOOB;
-#pragma unroll
-      for (int st = 0; st < NST; ++st) ka[u][st] = bld16(rK, koff + 64 * st);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (EPL == 8) {
           const u32x4 w = bld16(rV, voff + j * D * 2);
-          vw[u][j][0] = w[0]; vw[u][j][1] = w[1]; vw[u][j][2] = w[2]; vw[u][j][3] = w[3];
+          bt.vw[u][j][0] = w[0]; bt.vw[u][j][1] = w[1]; bt.vw[u][j][2] = w[2]; bt.vw[u][j][3] = w[3];
         } else {
           const u32x2 w = bld8(rV, voff + j * D * 2);
-          vw[u][j][0] = w[0]; vw[u][j][1] = w[1];
+          bt.vw[u][j][0] = w[0]; bt.vw[u][j][1] = w[1];
         }
       }
     }
+  };
+  auto compute = [&](int tb, const Batch& bt) {
 #pragma unroll
-    for (int u = 0; u < kTileBatch; ++u) {
-      const int tok0 = tok0s[u];
+    for (int u = 0; u < TB; ++u) {
+      const int tok0 = bt.tok0[u];
       if (tok0 < 0) continue;  // uniform across the wave
+      u32x4 ka[NST];
+      ks.finish(bt.kr[u], tb + 4 * u, ka);
       f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < NST; ++st) sc = mfma16x16x32(ka[u][st], qb[st], sc);
+      for (int st = 0; st < NST; ++st) sc = mfma16x16x32(ka[st], qb[st], sc);
       float sv[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[r] = tok0 + 4 * gq + r < N ? sc[r] * sl2 : -__builtin_inff();
@@ -141,11 +227,18 @@ __device__ __forceinline__ void run_tiles(TileAcc<D>& ta, const u32x4 (&qb)[D / 
       for (int e = 0; e < EPL; ++e) {
         const int c = e >> 1;
         u32x2 bv;
-        if (e & 1) bv = u32x2{pack_hi(vw[u][0][c], vw[u][1][c]), pack_hi(vw[u][2][c], vw[u][3][c])};
-        else       bv = u32x2{pack_lo(vw[u][0][c], vw[u][1][c]), pack_lo(vw[u][2][c], vw[u][3][c])};
+        if (e & 1) bv = u32x2{pack_hi(bt.vw[u][0][c], bt.vw[u][1][c]), pack_hi(bt.vw[u][2][c], bt.vw[u][3][c])};
+        else       bv = u32x2{pack_lo(bt.vw[u][0][c], bt.vw[u][1][c]), pack_lo(bt.vw[u][2][c], bt.vw[u][3][c])};
         ta.acc[e] = mfma16x16x16(pa, bv, ta.acc[e]);
       }
     }
+  };
+  // every load of a batch is issued before its first tile is computed (issuing
+  // the next batch's loads before this batch's arithmetic measured slower)
+  for (int tb = wave; tb < ntiles; tb += 4 * TB) {
+    Batch A;
+    issue(tb, A);
+    compute(tb, A);
   }
 }
 

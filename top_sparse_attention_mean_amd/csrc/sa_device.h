@@ -84,6 +84,9 @@ __device__ __forceinline__ u32x4 bld16(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ u32x2 bld8(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 // Plain buffer stores: they land in this XCD's L2, where sc1 loads from the
 // same XCD see them (but not loads from another XCD).
 __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {

@@ -46,6 +46,19 @@ inline int decode_valu_splits(int idx_stride, int block) {
   if (S < 1) S = 1;
   return S;
 }
+// Splits per (b, kv head) of the thumbnail-key decode (k_decode_lowbit): the
+// block decode's, raised so that a split's tiles touch at most
+// kLowbitMetaBlocks list entries (their block rows are staged in LDS).  Never
+// above decode_valu_splits, so decode_ws already sizes its partials.
+constexpr int kLowbitMetaBlocks = 16;
+inline int decode_lowbit_splits(int idx_stride, int block) {
+  int S = decode_block_splits(idx_stride, block);
+  const int smin = cdiv(idx_stride, kLowbitMetaBlocks - 1);
+  if (S < smin) S = smin;
+  if (S > idx_stride) S = idx_stride;
+  if (S > kMaxSplits) S = kMaxSplits;
+  return S;
+}
 // Splits per (b, query head) for token-mode decode.
 inline int decode_token_splits(int BHq, int idx_stride) {
   int S = cdiv(kTargetWGs, BHq);
@@ -270,6 +283,16 @@ sa_status decode_step(const void* Q, const void* K, const void* V, int dtype, in
                       StepPhase phase);
 // Records `what` as the calling thread's sa_last_error() message; returns s.
 sa_status report(sa_status s, const char* what);
+// The block-mode split-K decode over keys rebuilt from 2-bit codes and 8-bit
+// residuals (bf16 V; D 64 or 128; blocks of 64 or 128; g in {1, 2, 4, 8}).
+// Needs decode_lowbit_splits(idx_stride, block) <= kMaxSplits splits whose
+// tiles span at most kLowbitMetaBlocks entries (idx_stride <=
+// kMaxSplits * (kLowbitMetaBlocks - 1)).
+hipError_t launch_decode_lowbit(const void* Q, const uint8_t* codes, const int8_t* resid,
+                                const float* meta, const void* V, int B, int Hq, int Hkv, int N,
+                                int D, float scale, int block, const int32_t* idx,
+                                const int32_t* count, int idx_stride, const DecodeWs& w, void* ws,
+                                void* O, int out_dtype, float* lse, hipStream_t st);
 hipError_t launch_prefill_select(const float* qbar, const float* ksk, int BH,
                                  int M, int nb, int D, int k, unsigned flags,
                                  float scale, int32_t* idx, int32_t* count,
