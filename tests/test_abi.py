@@ -43,6 +43,8 @@ def lib():
     L.sa_sparse_prefill.argtypes = [P, P, P, I, I, I, I, I, I, F, I, P, P, I, P, I, P, P]
     L.sa_decode_step.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P, P, Z, P]
     L.sa_select_decode.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, U, F, P, P, P, I, P, P, Z, P]
+    L.sa_decode_topdelta_lowbit.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, I, F, F, F, I, P, P,
+                                            P, P, P, P, I, P, P, Z, P]
     L.sa_decode_step_noalloc.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, F, P, P, P, P, I, P,
                                          P]
     L.sa_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
@@ -259,6 +261,21 @@ def test_lowbit_validation(lib):
     a = list(sb)
     a[10], a[11] = 0, 0                           # empty window
     assert sel(*a) == INVALID
+    fused = lib.sa_decode_topdelta_lowbit
+    fb = [A, A, A, A, A, 1, 64, 8, 32768, 128, 64, 64, 64, 5.0, 1.0, 0.0, 512, A, A, None, None,
+          A, A, 1, None, A, 1 << 30, None]
+
+    def fcall(i, v):
+        a = list(fb)
+        a[i] = v
+        return fused(*a)
+
+    assert fcall(4, None) == INVALID              # V
+    assert fcall(22, None) == INVALID             # O
+    assert fcall(23, 7) == INVALID                # output dtype
+    assert fcall(16, 1921) == UNSUPPORTED         # more listed blocks than the splits can stage
+    assert fcall(10, 32) == UNSUPPORTED           # block
+    assert fcall(26, 4096) == WORKSPACE           # the selection's and the decode's workspace
 
 
 def test_mass_select_validation(lib):
