@@ -123,7 +123,9 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0) -> dict:
     from oracle.attention import widen
     threads = _blas_threads()
     q, K, V = (widen(x, wl.dtype) for x in (inp.Q, inp.K, inp.V))
-    sk = oracle.sketch(K, wl.block)                      # amortised at prefill, not timed
+    t_sk = time.perf_counter()
+    sk = oracle.sketch(K, wl.block)                      # amortised at prefill: timed apart
+    t_sk = time.perf_counter() - t_sk
     steps, t0 = 0, time.perf_counter()
     while True:
         j = wl.nb - 1                                    # newest block refreshed each step
@@ -138,7 +140,8 @@ def cpu_baseline(inp, wl, budget_s: float = 12.0) -> dict:
     return {"value": round(el / steps * 1e6, 1), "unit": "us/step", "cores": threads,
             "kind": "oracle", "cpu": _cpu_model(),
             "sample": f"{steps} full decode steps of {wl.name} (float64 NumPy, "
-                      f"BLAS threads={threads}); sketch build excluded (amortised at prefill)"}
+                      f"BLAS threads={threads}); sketch build excluded (amortised at prefill)",
+            "o1_sketch_build_us": round(t_sk * 1e6, 1)}
 
 
 # The sources the counted kernel (the selecting split-K decode of the step)
@@ -300,11 +303,28 @@ def bench_decode(args, name=None, calls=None, layers=None, extras=True) -> dict:
                      if bf else None,
                      "algorithmic_bytes": dom_bytes, "avg_us": round(t_dom, 3)},
     }
+    if res["roofline"]["traffic"]:
+        # counter bytes over the same live launch time (what the kernel actually moved)
+        res["roofline"]["traffic_GBps"] = round(res["roofline"]["traffic"] / (t_dom * 1e-6) / 1e9, 1)
     if not bf:
         res["roofline"]["note"] = ("latency-bound: one launch moves under 0.3 MB, so GB/s says "
                                    "little; the figure is the step time")
     if extras:
         res["eager_us_per_step"] = round(time_loop(step, min(args.steps, 500), st), 3)
+        # the same step without the newest block's sketch refresh
+        def step_norefresh(i):
+            r = i % R
+            sa.sa_decode_step(Qs[r], Ks[r], Vs[r], sks[r], wl.k, block=wl.block, update_block=-1,
+                              idx=idx, count=cnt, O=O, lse=lse, ws=ws)
+        t_nr, _, _ = graph_trials(step_norefresh, min(K, 10 * R), R, trials=args.trials)
+        res["us_per_step_without_sketch_update"] = round(t_nr, 3)
+        # achievable stream rate: a plain device copy of 1 GiB (2 GiB moved)
+        cx = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cy = torch.empty_like(cx)
+        cy.copy_(cx)
+        t_cp, _, _ = graph_trials(lambda i: cy.copy_(cx), 4, 1, trials=args.trials)
+        res["copy_achievable_GBps"] = round(2 * cx.numel() * 4 / (t_cp * 1e-6) / 1e9, 1)
+        del cx, cy
         # the one-launch form of the same step (k_step.hip), its own workspace
         os.environ["SA_STEP_MODE"] = "1"
         try:
