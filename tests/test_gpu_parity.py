@@ -804,6 +804,11 @@ PREFILL_CASES = [
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 1024 + 33, "D": 64, "block": 64, "needles": 4}),
     ("sparse_prefill_bf16", {"Hq": 4, "Hkv": 1, "N": 1024, "block": 64, "needles": 4}),
     ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 1536 + 5, "D": 64, "needles": 4}),
+    # shorter than one block; one token past a block edge; an odd group (one
+    # head per workgroup at D 128 with blocks of 128, two heads otherwise)
+    ("sparse_prefill_bf16", {"Hq": 8, "Hkv": 2, "N": 37, "needles": 0}),
+    ("sparse_prefill_bf16", {"Hq": 4, "Hkv": 2, "N": 129, "D": 64, "block": 64, "needles": 1}),
+    ("sparse_prefill_bf16", {"Hq": 6, "Hkv": 2, "N": 300, "needles": 1}),
 ]
 
 
