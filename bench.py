@@ -830,7 +830,9 @@ def bench_mass(args) -> dict:
                 rec.append(len(want & got) / len(want))
     tiles = B * Hkv * M * (M + 1) // 2 * (Hq // Hkv)
     passes = -(-M // 128)
-    flops = passes * tiles * 4.0 * blk * blk * D
+    # QK^T of every causal tile twice: the statistics pass and the mass passes
+    # (each chunk's pass scores only that chunk's blocks)
+    flops = 2 * tiles * 2.0 * blk * blk * D
     tflops = flops / (t_mass * 1e-6) / 1e12
     res = {
         "workload": wl.name, "us_per_call": round(t_mass, 1), "k_free": kf,
@@ -839,8 +841,9 @@ def bench_mass(args) -> dict:
         "recall_over": f"query blocks 9..{M - 1} of every kv head ({len(rec)} blocks)",
         "per_row_topk_held_by_block_shared_topk": round(float(np.mean(shared)), 4),
         "query_blocks": len(rec),
-        "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 over every earlier block, V = "
-                     "one-hot block indicators (the call also builds V, reduces and selects)",
+        "roofline": {"bound": "mfma", "kernel": "k_prefill_bf16 scores of every causal tile, "
+                     "twice (row statistics, then block masses; the call also reduces and "
+                     "selects)",
                      "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "traffic": None,
                      "flops_per_call": flops, "avg_us": round(t_mass, 1)},

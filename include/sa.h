@@ -378,9 +378,10 @@ sa_status sa_decode_topdelta_lowbit(const void* Q, const uint8_t* codes,
  * the group, each row's probability summed over every key block j, averaged
  * over the rows and heads -> mass[i][j]; the k_free blocks j in [1, i-1] with
  * the largest mass (ties to the lower j) are listed ascending.  A reference
- * for the recall of the sketch selector, not a fast path: it runs dense
- * causal attention, one pass per 128 key blocks (the prefill kernel with V
- * replaced by one-hot block indicators).
+ * for the recall of the sketch selector, not a fast path: it runs the dense
+ * causal scores twice, once for each row's softmax maximum and sum and once
+ * (per chunk of 128 key blocks) for its probability mass on each block,
+ * summed over the block's keys in float32.
  *
  *   Q [B, Hq, L, D], K [B, Hkv, L, D] bf16; D = 128, block = 128,
  *            L * D * 2 <= 0x7f000000 (else SA_ERR_UNSUPPORTED)
@@ -395,7 +396,7 @@ sa_status sa_decode_topdelta_lowbit(const void* Q, const uint8_t* codes,
  *            row_count [B, Hkv, L]
  *   k_free   1..64
  * ws: sa_workspace_bytes(SA_OP_MASS_SELECT, B, Hq, Hkv, L, D, block, k_free):
- *     about L * (Hkv * 256 + Hq * 512) bytes per batch row plus the lists.
+ *     about L * Hq * 520 bytes per batch row plus the lists.
  */
 sa_status sa_mass_select(const void* Q, const void* K, int dtype, int B, int Hq,
                          int Hkv, int L, int D, int block, int k_free,

@@ -8,17 +8,15 @@
 // the dense attention it is meant to avoid); here it makes the recall of the
 // sketch selector measurable over every query block.
 //
-// The dense pass reuses the block-sparse prefill kernel with every earlier
-// block listed: with V replaced by one-hot block indicators (row t of V has a
-// 1 in column j - 128 c when token t lies in key block j of chunk c), the
-// attention output of row t is its softmax mass per key block.  The kernel is
-// asked to take every probability as bf16 hi + lo (about 16 significant bits,
-// so a mass is off by at most 2^-17 of itself plus float32 rounding; the plain
-// bf16 P of the sparse prefill would allow 2^-9).  128 blocks
-// fit in the 128 columns of one pass; longer sequences take one pass per
-// chunk of 128 blocks.
+// The dense passes reuse the block-sparse prefill kernel's staging and score
+// tiles with every earlier block listed and no value product: one pass
+// writes each row's softmax statistics (its maximum m and sum l over all of
+// its keys); then, per chunk of 128 key blocks, a second pass recomputes the
+// scores of the chunk's blocks and writes each row's mass on each of them,
+// the sum over the block's keys of 2^(s log2e scale - m) / l, in float32.
+// Both passes compute each score the same way, so a row's masses over all
+// blocks sum to 1 up to float32 rounding.
 //
-//   k_onehot_v     V1 [B, Hkv, L, 128] bf16 for chunk c
 //   k_dense_list   idx [B, Hkv, M, M] = 0..i for query block i (dense causal)
 //   k_mass_reduce  one workgroup per (b, kv head, query block): the chunk's
 //                  columns summed over the block's rows and the group's heads
@@ -30,22 +28,6 @@
 #include "sa_internal.h"
 
 namespace sa {
-
-__global__ __launch_bounds__(256) void k_onehot_v(int L, int block, int c, long rows,
-                                                  uint16_t* __restrict__ v1) {
-  const long o = long(blockIdx.x) * 256 + threadIdx.x;   // (row, 8-column group)
-  if (o >= rows * 16) return;
-  const long row = o / 16;
-  const int g = int(o % 16);
-  const int t = int(row % L);
-  const int col = t / block - 128 * c;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if (col >= 8 * g && col < 8 * g + 8) {
-    const int e = col - 8 * g;
-    w[e / 2] = (e & 1) ? 0x3f800000u : 0x00003f80u;      // bf16(1.0)
-  }
-  *reinterpret_cast<u32x4*>(v1 + row * 128 + 8 * g) = u32x4{w[0], w[1], w[2], w[3]};
-}
 
 __global__ __launch_bounds__(256) void k_dense_list(int M, long rows, int32_t* __restrict__ idx,
                                                     int32_t* __restrict__ count) {
@@ -154,7 +136,7 @@ hipError_t launch_mass_select(const void* Q, const void* K, int B, int Hq, int H
                               int32_t* count, float* row_mass, int32_t* row_idx,
                               int32_t* row_count, const MassWs& w, void* ws, hipStream_t st) {
   char* base = static_cast<char*>(ws);
-  uint16_t* v1 = reinterpret_cast<uint16_t*>(base + w.v_off);
+  float* stats = reinterpret_cast<float*>(base + w.stats_off);
   float* O = reinterpret_cast<float*>(base + w.o_off);
   int32_t* lst = reinterpret_cast<int32_t*>(base + w.list_off);
   int32_t* lcnt = reinterpret_cast<int32_t*>(base + w.lcnt_off);
@@ -165,11 +147,11 @@ hipError_t launch_mass_select(const void* Q, const void* K, int B, int Hq, int H
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long vrows = long(B) * Hkv * L;
+  e = launch_prefill_mass(Q, K, B, Hq, Hkv, L, scale, lst, lcnt, M, O, stats, 0, true, st);
+  if (e != hipSuccess) return e;
   for (int c = 0; c * 128 < M; ++c) {
-    k_onehot_v<<<dim3(unsigned(cdiv(vrows * 16, 256))), 256, 0, st>>>(L, block, c, vrows, v1);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    e = launch_prefill(Q, K, v1, B, Hq, Hkv, L, D, scale, block, lst, lcnt, M, O, SA_F32,
-                       nullptr, st, true);
+    e = launch_prefill_mass(Q, K, B, Hq, Hkv, L, scale, lst, lcnt, M, O, stats, 128 * c, false,
+                            st);
     if (e != hipSuccess) return e;
     k_mass_reduce<<<dim3(unsigned(lrows)), 256, 0, st>>>(O, Hq, Hkv, L, block, M, c, ms);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -34,6 +34,7 @@
 namespace sa {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 struct f32x2_pair {
   float a, b;
 };
@@ -130,12 +131,20 @@ __device__ __forceinline__ void pv_tiles(const uint16_t* __restrict__ vt, const 
 //         bf16 hi + lo (its rows see at most BLK keys); MODE 1: every block
 //         with P as hi + lo.  Keeping the hi + lo path out of MODE 0 keeps that
 //         kernel within its registers (one inlined copy of the value product).
+// MODE 3 and 4 serve the attention-mass selector and stage no V: MODE 3
+//         writes each row's softmax statistics over its listed blocks, stats
+//         [b, h, row] = (m, l) (m the row maximum in log2 units, l the sum of
+//         2^(s log2e scale - m)); MODE 4 takes them and writes, for each
+//         listed block j in [c0, c0 + 128), the row's probability mass on
+//         block j, sum over its keys of 2^(s log2e scale - m) / l, to
+//         O [b, h, row, j - c0] (float32; other columns untouched).
 template <int MODE, int D, int BLK, int HPW>
 __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, int Hq, int Hkv, int L, int M, int units, float sl2,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int kmax,
-    void* __restrict__ O, int out_bf16, float* __restrict__ lse) {
+    void* __restrict__ O, int out_bf16, float* __restrict__ lse, float* __restrict__ stats,
+    int c0) {
   using Gm = PfGeom<D, BLK, HPW>;
   __shared__ __attribute__((aligned(16))) unsigned char kt_lds[Gm::NG * Gm::GB];
   __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * Gm::VS];
@@ -231,9 +240,14 @@ __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
       }
     }
   };
-  // listed blocks outside 0..i are skipped (uniform)
+  // listed blocks outside 0..i (in MODE 4 also outside [c0, c0 + 128)) are
+  // skipped (uniform)
   auto next_listed = [&](int e) {
-    while (e < cnt && (lst[e] < 0 || lst[e] > i)) ++e;
+    while (e < cnt) {
+      const int jb = lst[e];
+      if (jb >= 0 && jb <= i && (MODE != 4 || (jb >= c0 && jb < c0 + 128))) break;
+      ++e;
+    }
     return e;
   };
   // this lane's K read address for score tile 0: position col, bytes 16 half
@@ -249,13 +263,24 @@ __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
   // barrier.
   int e = next_listed(0);
   if (e < cnt) {
-    u32x4 wv[Gm::VP][4];
     load_k(lst[e]);
-    load_v(lst[e], wv);
-    store_v(wv);
+    if constexpr (MODE < 3) {
+      u32x4 wv[Gm::VP][4];
+      load_v(lst[e], wv);
+      store_v(wv);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+
+  // MODE 4: the row's statistics from MODE 3
+  float m_fin = 0.f, inv_l = 0.f;
+  if constexpr (MODE == 4) {
+    const int qr = min(qrow, L - 1);
+    const f32x2 st2 = *reinterpret_cast<const f32x2*>(stats + 2 * ((size_t(b) * Hq + h) * L + qr));
+    m_fin = st2[0];
+    inv_l = st2[1] > 0.f ? 1.f / st2[1] : 0.f;
+  }
 
   while (e < cnt) {
     const int jb = lst[e];
@@ -294,7 +319,7 @@ __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
     u32x4 wv[Gm::VP][4];
     if (more) {
       load_k(lst[en]);
-      load_v(lst[en], wv);
+      if constexpr (MODE < 3) load_v(lst[en], wv);
     }
     // one maximum, rescale and exponent base for the whole block
     float mraw = -__builtin_inff();
@@ -320,6 +345,25 @@ __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
 #pragma unroll
           for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, sall[sb][kk][r]);
     }
+    if constexpr (MODE == 4) {
+      // the block's probability mass for this row, with the row's final
+      // maximum and sum (masked keys give 2^-inf = 0)
+      float ps = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int kk = 0; kk < PF_KT; ++kk)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ps += exp2_fast(__builtin_fmaf(sall[sb][kk][r], sl2, -m_fin));
+      const f32x2_pair pp = pair32(ps);
+      if (qrow < L && half == 0)
+        static_cast<float*>(O)[((size_t(b) * Hq + h) * L + qrow) * 128 + (jb - c0)] =
+            (pp.a + pp.b) * inv_l;
+      __builtin_amdgcn_s_waitcnt(0);         // this wave's loads of the next block
+      __syncthreads();
+      e = en;
+      continue;
+    }
     {
       const f32x2_pair pr = pair32(mraw);
       mraw = fmaxf(pr.a, pr.b);
@@ -331,7 +375,7 @@ __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
     l *= alpha;
     m = m_new;
     // the accumulators change only where a row's maximum moved
-    if (__ballot(alpha != 1.f)) {
+    if (MODE < 3 && __ballot(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -351,12 +395,23 @@ __global__ __launch_bounds__(2 * BLK * HPW, 2 / HPW) void k_prefill_bf16(
         }
       }
       l += ls;
-      pv_tiles<MODE != 0, PF_KT, D, Gm::VS>(vt_lds, sfr, PF_KT * sb, acc, lane);
+      if constexpr (MODE < 3)
+        pv_tiles<MODE != 0, PF_KT, D, Gm::VS>(vt_lds, sfr, PF_KT * sb, acc, lane);
     }
     __builtin_amdgcn_s_waitcnt(0);           // this wave's loads of the next block
     __syncthreads();                         // every wave is done reading V^T
-    if (more) store_v(wv);
+    if constexpr (MODE < 3) {
+      if (more) store_v(wv);
+    }
     e = en;
+  }
+  if constexpr (MODE == 4) return;
+  if constexpr (MODE == 3) {
+    const f32x2_pair lp = pair32(l);
+    if (qrow < L && half == 0)
+      *reinterpret_cast<f32x2*>(stats + 2 * ((size_t(b) * Hq + h) * L + qrow)) =
+          f32x2{m, lp.a + lp.b};
+    return;
   }
 
   // ---- epilogue: lane holds O^T[d = 32 dt + 8 (r/4) + 4 half + r%4][qrow]
@@ -398,17 +453,17 @@ static hipError_t launch_prefill_db(const uint16_t* q, const uint16_t* k, const 
   if (split_p) {
     const long grid = long(cdiv(units, 8)) * 8 * GH;
     k_prefill_bf16<1, D, BLK, HPW><<<dim3(static_cast<unsigned>(grid)), blk, 0, st>>>(
-        q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
+        q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse, nullptr, 0);
     return hipGetLastError();
   }
   const long grid = long(cdiv(units, 8)) * 8 * GH;
   k_prefill_bf16<0, D, BLK, HPW><<<dim3(static_cast<unsigned>(grid)), blk, 0, st>>>(
-      q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse);
+      q, k, v, Hq, Hkv, L, M, units, sl2, idx, count, kmax, O, ob, lse, nullptr, 0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const long grid0 = long(cdiv(firsts, 8)) * 8 * GH;
   k_prefill_bf16<2, D, BLK, HPW><<<dim3(static_cast<unsigned>(grid0)), blk, 0, st>>>(
-      q, k, v, Hq, Hkv, L, M, firsts, sl2, idx, count, kmax, O, ob, lse);
+      q, k, v, Hq, Hkv, L, M, firsts, sl2, idx, count, kmax, O, ob, lse, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -435,6 +490,34 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B, in
                                          st, split_p);
   return launch_prefill_db<64, 64, 1>(q, k, v, B, Hq, Hkv, L, sl2, idx, count, kmax, O, ob, lse,
                                       st, split_p);
+}
+
+template <int MODE, int HPW>
+static hipError_t launch_mass_mode(const uint16_t* q, const uint16_t* k, int B, int Hq, int Hkv,
+                                   int L, float sl2, const int32_t* idx, const int32_t* count,
+                                   int kmax, float* O, float* stats, int c0, hipStream_t st) {
+  const int M = cdiv(L, 128);
+  const int GH = Hq / Hkv / HPW;
+  const int units = B * Hkv * M;
+  const long grid = long(cdiv(units, 8)) * 8 * GH;
+  k_prefill_bf16<MODE, 128, 128, HPW><<<dim3(static_cast<unsigned>(grid)), dim3(256 * HPW), 0,
+                                        st>>>(q, k, nullptr, Hq, Hkv, L, M, units, sl2, idx, count,
+                                              kmax, O, 0, nullptr, stats, c0);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_mass(const void* Q, const void* K, int B, int Hq, int Hkv, int L,
+                               float scale, const int32_t* idx, const int32_t* count, int kmax,
+                               float* O, float* stats, int c0, bool stats_pass, hipStream_t st) {
+  auto q = static_cast<const uint16_t*>(Q);
+  auto k = static_cast<const uint16_t*>(K);
+  const float sl2 = scale * kLog2e;
+  // one head per workgroup: with no value product a wave takes 144-152
+  // VGPRs, so three 4-wave workgroups share a compute unit (38.9 ms per call
+  // at L = 64K against 45.2 ms for two heads in one 8-wave workgroup)
+  if (stats_pass)
+    return launch_mass_mode<3, 1>(q, k, B, Hq, Hkv, L, sl2, idx, count, kmax, O, stats, c0, st);
+  return launch_mass_mode<4, 1>(q, k, B, Hq, Hkv, L, sl2, idx, count, kmax, O, stats, c0, st);
 }
 
 }  // namespace sa

@@ -218,17 +218,18 @@ inline size_t topdelta_ws_bytes(int B, int Hq, int N) {
 inline size_t lowbit_ws_bytes(int B, int Hq, int Hkv, int N, int block) {
   return align256(size_t(B) * Hkv * cdiv(N, block)) + align256(size_t(B) * Hq * sizeof(float));
 }
-// The attention-mass selector: one-hot V [B, Hkv, L, 128] bf16, the dense
-// pass's output [B, Hq, L, 128] f32, the dense causal block lists [B, Hkv, M, M]
-// and counts, and the masses [B, Hkv, M, M] f32 (unless the caller takes them).
+// The attention-mass selector: the rows' softmax statistics [B, Hq, L, 2] f32,
+// the mass pass's output [B, Hq, L, 128] f32, the dense causal block lists
+// [B, Hkv, M, M] and counts, and the masses [B, Hkv, M, M] f32 (unless the
+// caller takes them).
 struct MassWs {
-  size_t v_off, o_off, list_off, lcnt_off, mass_off, bytes;
+  size_t stats_off, o_off, list_off, lcnt_off, mass_off, bytes;
 };
 inline MassWs mass_ws(int B, int Hq, int Hkv, int L, int block) {
   MassWs w{};
   const size_t M = size_t(cdiv(L, block));
-  w.v_off = 0;
-  w.o_off = align256(size_t(B) * Hkv * L * 128 * 2);
+  w.stats_off = 0;
+  w.o_off = align256(size_t(B) * Hq * L * 2 * 4);
   w.list_off = w.o_off + align256(size_t(B) * Hq * L * 128 * 4);
   w.lcnt_off = w.list_off + align256(size_t(B) * Hkv * M * M * 4);
   w.mass_off = w.lcnt_off + align256(size_t(B) * Hkv * M * 4);
@@ -350,5 +351,12 @@ hipError_t launch_prefill(const void* Q, const void* K, const void* V, int B,
                           const int32_t* idx, const int32_t* count, int kmax,
                           void* O, int out_dtype, float* lse, hipStream_t st,
                           bool split_p = false);
+// The attention-mass selector's dense passes (D = 128, blocks of 128): the
+// rows' softmax statistics stats [B, Hq, L, 2] over their listed blocks
+// (stats_pass), or each row's probability mass on its listed blocks in
+// [c0, c0 + 128), written to O [B, Hq, L, 128] float32.
+hipError_t launch_prefill_mass(const void* Q, const void* K, int B, int Hq, int Hkv, int L,
+                               float scale, const int32_t* idx, const int32_t* count, int kmax,
+                               float* O, float* stats, int c0, bool stats_pass, hipStream_t st);
 
 }  // namespace sa
