@@ -753,9 +753,9 @@ def test_mass_select_parity(name, over, qblocks):
     for (b, kh, i), (m_x, sel_x) in res.items():
         m_g = mass_h[b, kh, i]
         worst = max(worst, float(np.abs(m_g[:M] - m_x).max()))
-        # the dense pass takes each probability into the PV product as bf16
-        # hi + lo (about 16 significant bits): <= 2^-17 of each mass, plus
-        # float32 rounding of the scores and sums
+        # the masses are float32 sums of float32 probabilities: the rounding of
+        # the float32 scores (128-term dot products), of their exponents and of
+        # the sums, far inside the bar
         assert np.abs(m_g - m_x).max() <= MASS_TOL, (b, kh, i)
         n = int(cnt_h[b, kh, i])
         assert n == min(kf, max(i - 1, 0))
