@@ -121,6 +121,48 @@ def test_decode_step_equals_separate_calls():
     assert torch.equal(O, O3) and torch.equal(lse, lse3)          # bitwise repeatable
 
 
+F32_STEP_CASES = [
+    {},
+    {"N": 4096 - 23},                                  # ragged last block
+    {"k": 64},                                         # k = nb: every block
+    {"N": 50, "k": 8},                                 # nb = 1
+    {"Hq": 8, "Hkv": 2, "D": 128, "N": 3000},          # g = 4, D = 128
+    {"Hq": 6, "Hkv": 2, "N": 2500, "k": 11},           # g = 3
+    {"N": 64 * 600, "k": 12},                          # nb = 600: the list from k_select_rows
+]
+
+
+@pytest.mark.parametrize("over", F32_STEP_CASES)
+def test_decode_step_f32_equals_separate_calls(over):
+    """The float32 step (its decode kernel selecting its own blocks up to 512
+    blocks per row) against the separate selection and decode: the same lists
+    and, the split of the blocks being the same, the same outputs bit for bit;
+    sa_select_decode on the step's scores likewise."""
+    wl, inp, q, K, V = _decode_case("tiny_decode_f32", over)
+    Qd, Kd, Vd = to_dev(inp.Q, "f32"), to_dev(inp.K, "f32"), to_dev(inp.V, "f32")
+    sk_full = sa.sa_build_sketch(Kd, wl.block)
+    sk = sk_full.clone()
+    sk[:, :, -1] = 0                                   # stale newest block, refreshed in the step
+    score = torch.empty(wl.B, wl.Hkv, wl.nb, dtype=torch.float32, device="cuda")
+    O, lse, idx, cnt = sa.sa_decode_step(Qd, Kd, Vd, sk, wl.k, block=wl.block,
+                                         update_block=wl.nb - 1, score=score,
+                                         out_dtype=torch.float32)
+    assert torch.equal(sk, sk_full)
+    idx2, cnt2, _ = sa.sa_select_topk(Qd, sk_full, wl.k)
+    O2, lse2 = sa.sa_sparse_decode(Qd, Kd, Vd, idx2, cnt2, block=wl.block, out_dtype=torch.float32)
+    assert torch.equal(idx, idx2) and torch.equal(cnt, cnt2)
+    assert torch.equal(O, O2) and torch.equal(lse, lse2)
+    O3, lse3, idx3, cnt3 = sa.sa_select_decode(Qd, Kd, Vd, score, wl.k, block=wl.block,
+                                               out_dtype=torch.float32)
+    assert torch.equal(idx3, idx) and torch.equal(cnt3, cnt)
+    assert torch.equal(O3, O) and torch.equal(lse3, lse)
+    # and against the oracle on the lists
+    O_ref, lse_ref = oracle.attend_blocks(q, K, V, idx.cpu().numpy(), wl.block,
+                                          count=cnt.cpu().numpy())
+    assert max_abs(O.cpu().numpy(), O_ref) <= OUT_TOL["f32"]
+    assert max_abs(lse.cpu().numpy(), lse_ref) <= 1e-4
+
+
 @pytest.mark.parametrize("D,upd", [(128, 5), (128, -1), (64, 7)])
 def test_decode_step_scores_and_paths(D, upd):
     """The decode step's scores equal the standalone selection's bit for bit

@@ -349,8 +349,12 @@ __global__ __launch_bounds__(256, 2) void k_decode_lowbit(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------- float32 VALU
-template <int D, int G>
+template <int D, int G, int SELKPT>
 __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
+  // SELKPT > 0: the selecting variant (rows of nb <= 256 SELKPT blocks): every
+  // split takes the top-k of its kv head's score row itself (the selection of
+  // k_select_rows) instead of reading a list, and split 0 writes the list out
+  static_assert(SELKPT >= 0, "keys per thread of the selection");
   constexpr int CH = 256;                // tokens per round: 64 per wave
   constexpr int OPT = (G * D + 255) / 256;   // (head, column) outputs per thread
   constexpr int LPR = D / 4;             // lanes per K/V row (16-byte segments)
@@ -375,9 +379,29 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
   const int blk0 = s * bps;
   const int blk1 = min(blk0 + bps, a.idx_stride);
   const int ntok = max(blk1 - blk0, 0) * block;
-  const int cnt = a.count ? min(max(a.count[bh], 0), a.idx_stride) : a.idx_stride;
+  int cnt;
+  const int32_t* ib;
+  if constexpr (SELKPT > 0) {
+    // the selection's LDS state lives in the value tile, unused until the
+    // first round
+    __shared__ int s_list[kValuSelMaxK];
+    static_assert(sizeof(SelectLdsT<256, SELKPT>) <= sizeof(sv), "selection state in sv");
+    auto& S = *reinterpret_cast<SelectLdsT<256, SELKPT>*>(sv);
+    uint32_t kr[SELKPT];
+    load_keys_reg<256, SELKPT>(a.sel_scores + size_t(bh) * a.nb, a.nb, kr);
+    cnt = select_decode_row<256, SELKPT>(kr, a.nb, a.k, a.flags, s_list, S);
+    __syncthreads();
+    if (s == 0) {
+      int32_t* orow = a.sel_idx + size_t(bh) * a.k;
+      for (int j = tid; j < a.k; j += 256) orow[j] = j < cnt ? s_list[j] : -1;
+      if (tid == 0) a.sel_count[bh] = cnt;
+    }
+    ib = s_list;
+  } else {
+    cnt = a.count ? min(max(a.count[bh], 0), a.idx_stride) : a.idx_stride;
+    ib = a.idx + size_t(bh) * a.idx_stride;
+  }
   const int nbk = (N + block - 1) / block;
-  const int32_t* ib = a.idx + size_t(bh) * a.idx_stride;
   const float* Kb = static_cast<const float*>(a.K) + size_t(bh) * N * D;
   const float* Vb = static_cast<const float*>(a.V) + size_t(bh) * N * D;
   const float* Q = static_cast<const float*>(a.Q);
@@ -711,17 +735,17 @@ static void launch_mfma_g(const DecodeArgs& a, dim3 g, size_t lds, hipStream_t s
   }
 }
 
-template <int D>
+template <int D, int SELKPT = 0>
 static void launch_valu_g(const DecodeArgs& a, int G, dim3 g, hipStream_t st) {
   switch (G) {
-    case 1: k_decode_blocks_valu<D, 1><<<g, 256, 0, st>>>(a); break;
-    case 2: k_decode_blocks_valu<D, 2><<<g, 256, 0, st>>>(a); break;
-    case 3: k_decode_blocks_valu<D, 3><<<g, 256, 0, st>>>(a); break;
-    case 4: k_decode_blocks_valu<D, 4><<<g, 256, 0, st>>>(a); break;
-    case 5: k_decode_blocks_valu<D, 5><<<g, 256, 0, st>>>(a); break;
-    case 6: k_decode_blocks_valu<D, 6><<<g, 256, 0, st>>>(a); break;
-    case 7: k_decode_blocks_valu<D, 7><<<g, 256, 0, st>>>(a); break;
-    default: k_decode_blocks_valu<D, 8><<<g, 256, 0, st>>>(a); break;
+    case 1: k_decode_blocks_valu<D, 1, SELKPT><<<g, 256, 0, st>>>(a); break;
+    case 2: k_decode_blocks_valu<D, 2, SELKPT><<<g, 256, 0, st>>>(a); break;
+    case 3: k_decode_blocks_valu<D, 3, SELKPT><<<g, 256, 0, st>>>(a); break;
+    case 4: k_decode_blocks_valu<D, 4, SELKPT><<<g, 256, 0, st>>>(a); break;
+    case 5: k_decode_blocks_valu<D, 5, SELKPT><<<g, 256, 0, st>>>(a); break;
+    case 6: k_decode_blocks_valu<D, 6, SELKPT><<<g, 256, 0, st>>>(a); break;
+    case 7: k_decode_blocks_valu<D, 7, SELKPT><<<g, 256, 0, st>>>(a); break;
+    default: k_decode_blocks_valu<D, 8, SELKPT><<<g, 256, 0, st>>>(a); break;
   }
 }
 
@@ -796,6 +820,21 @@ hipError_t launch_decode_select_blocks(const void* Q, const void* K, const void*
     if (small) launch_mfma_g<128, 128, 16>(a, g, lds, st);
     else       launch_mfma_g<128, 128, 32>(a, g, lds, st);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_select_valu(const void* Q, const void* K, const void* V, int B, int Hq,
+                                     int Hkv, int N, int D, float scale, int block,
+                                     const float* scores, int nb, int k, unsigned flags,
+                                     int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
+                                     void* O, int out_dtype, float* lse, hipStream_t st) {
+  DecodeArgs a = make_args(Q, K, V, B, Hq, Hkv, N, block, scale, nullptr, nullptr, k, nullptr, w,
+                           ws, O, out_dtype, lse);
+  a.S = decode_valu_splits(k, block);   // sized for by decode_ws
+  a.sel_scores = scores; a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
+  const dim3 g(static_cast<unsigned>(long(B) * Hkv * a.S));
+  if (D == 128) launch_valu_g<128, kValuSelKpt>(a, Hq / Hkv, g, st);
+  else          launch_valu_g<64, kValuSelKpt>(a, Hq / Hkv, g, st);
   return hipGetLastError();
 }
 

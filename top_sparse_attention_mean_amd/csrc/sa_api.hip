@@ -250,6 +250,11 @@ static sa_status run_select_decode(const void* Q, const void* K, const void* V, 
                       what);
   }
   const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
+  if (dtype == SA_F32 && nb <= 256 * kValuSelKpt && k <= kValuSelMaxK)
+    return hip_status(launch_decode_select_valu(Q, K, V, B, Hq, Hkv, N, D, sc, block, scores, nb,
+                                                k, flags, idx, count, w, dws, O, out_dtype, lse,
+                                                st),
+                      what);
   const hipError_t e = launch_select_rows(scores, B * Hkv, nb, k, flags, idx, count, st);
   if (e != hipSuccess) return hip_status(e, what);
   return hip_status(launch_decode_blocks(Q, K, V, dtype, B, Hq, Hkv, N, D, sc, block, idx, count,

@@ -21,6 +21,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 constexpr int kMaxSplits = 128;       // partials merged by one workgroup
 constexpr int kMaxKFused = 1024;      // k of the decode step that selects inside the decode kernel
+// The float32 decode selects its own blocks for rows of up to 256 kValuSelKpt
+// blocks and k up to kValuSelMaxK; longer rows go through k_select_rows.
+constexpr int kValuSelKpt = 2;
+constexpr int kValuSelMaxK = 512;
 constexpr int kTokensPerSplit = 256;  // block-mode split target: 16 tiles of 16 tokens
 constexpr int kCounterStride = 64;    // arrival counters 256 B apart (own cache lines)
 constexpr int kScoreRows = 32;        // sketch rows per scoring workgroup
@@ -265,6 +269,13 @@ hipError_t launch_decode_select_blocks(const void* Q, const void* K, const void*
                                        const float* scores, int nb, int k, unsigned flags,
                                        int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
                                        void* O, int out_dtype, float* lse, hipStream_t st);
+// The same for float32 (k_decode_blocks_valu selecting its own blocks): rows of
+// nb <= 256 kValuSelKpt blocks, k <= kValuSelMaxK.
+hipError_t launch_decode_select_valu(const void* Q, const void* K, const void* V, int B, int Hq,
+                                     int Hkv, int N, int D, float scale, int block,
+                                     const float* scores, int nb, int k, unsigned flags,
+                                     int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
+                                     void* O, int out_dtype, float* lse, hipStream_t st);
 // The one-launch decode step (bf16; step_fusable shapes).  coh_mode: 0 plain
 // stores inside an XCD team, 1 device-coherent stores throughout, 2 every
 // workgroup acts as if it ran off its team's XCD (both for tests).
