@@ -27,6 +27,7 @@
 #include "sa_decode_core.h"
 #include "sa_device.h"
 #include "sa_internal.h"
+#include "sa_score_core.h"
 #include "sa_select_core.h"
 
 namespace sa {
@@ -55,6 +56,11 @@ struct DecodeArgs {
   int32_t* sel_idx;
   int32_t* sel_count;
   int32_t* sel_ent;   // [B*Hkv, kSelEntCap] kept block (or -1) per entry of a row
+  // in-kernel scoring (float32 step, k_decode_blocks_valu): the sketch
+  // [B*Hkv, nb, D] (row upd rebuilt from K first, upd = -1: none) scored
+  // against the group-mean query; sel_scores then receives the scores
+  float* sk;
+  int upd;
   // keys rebuilt from thumbnails (k_decode_lowbit): codes [B*Hkv, N, D/4],
   // residuals [B*Hkv, N, D], (lo, step, rstep) rows [B*Hkv, nb, 3, D]
   const uint8_t* lb_codes;
@@ -388,7 +394,57 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
     static_assert(sizeof(SelectLdsT<256, SELKPT>) <= sizeof(sv), "selection state in sv");
     auto& S = *reinterpret_cast<SelectLdsT<256, SELKPT>*>(sv);
     uint32_t kr[SELKPT];
-    load_keys_reg<256, SELKPT>(a.sel_scores + size_t(bh) * a.nb, a.nb, kr);
+    if (a.sk) {
+      // The whole decode step in one launch: every split scores its kv head's
+      // row itself with the scoring kernel's arithmetic (the same functions,
+      // so the same scores bit for bit), the newest block's sketch rebuilt
+      // from K; split 0 stores that sketch row and the scores.
+      constexpr int SOFF = (sizeof(SelectLdsT<256, SELKPT>) + 255) / 256 * 64;   // floats
+      float* srow = sv + SOFF;                                 // nb <= 256 SELKPT
+      float* dummy = srow + 256 * SELKPT;                      // D floats
+      auto& U = *reinterpret_cast<ScoreUpdLds<D>*>(dummy + D);
+      static_assert(SOFF + 256 * SELKPT + D + sizeof(ScoreUpdLds<D>) / 4 <= CH * D,
+                    "scoring state in sv");
+      const int nbr = a.nb, upd = a.upd;
+      const float* Qg = static_cast<const float*>(a.Q) + (size_t(b) * a.Hq + kh * G) * D;
+      {
+        constexpr int SLPR = D / 4, SRPI = 64 / SLPR, SB = 8;   // rows of a load batch: SB SRPI
+        const int ssub = lane / SLPR, slc = lane % SLPR;
+        QCol<float> qv[8];
+        score_q_issue<float, D>(Qg, G, slc, qv);
+        float q[4];
+        score_q_finish<float, D>(Qg, G, slc, a.scale, qv, q);
+        const float* base = a.sk + size_t(bh) * nbr * D;
+        for (int r0 = wave * SB * SRPI; r0 < nbr; r0 += 4 * SB * SRPI) {
+          u32x4 w[SB];
+#pragma unroll
+          for (int u = 0; u < SB; ++u)
+            w[u] = ld16(base + size_t(min(r0 + u * SRPI + ssub, nbr - 1)) * D + slc * 4);
+#pragma unroll
+          for (int u = 0; u < SB; ++u) {
+            const int r = r0 + u * SRPI + ssub;
+            const float pr = score_row<D>(q, w[u]);
+            if (r < nbr && r != upd && slc == SLPR - 1) srow[r] = pr;
+          }
+        }
+      }
+      if (upd >= 0) {
+        const int t0 = upd * block, nj = min(block, N - t0);
+        const float pu = score_update_block<float, D>(
+            static_cast<const float*>(a.K) + (size_t(bh) * N + t0) * D, nj, Qg, G, a.scale,
+            s == 0 ? a.sk + (size_t(bh) * nbr + upd) * D : dummy, U);
+        if (tid == 0) srow[upd] = pu;
+      }
+      __syncthreads();
+      if (s == 0 && a.sel_scores) {
+        float* so = const_cast<float*>(a.sel_scores) + size_t(bh) * nbr;
+        for (int j = tid; j < nbr; j += 256) so[j] = srow[j];
+      }
+      load_keys_reg<256, SELKPT>(srow, nbr, kr);
+      __syncthreads();                         // srow read before the selection's state is set
+    } else {
+      load_keys_reg<256, SELKPT>(a.sel_scores + size_t(bh) * a.nb, a.nb, kr);
+    }
     cnt = select_decode_row<256, SELKPT>(kr, a.nb, a.k, a.flags, s_list, S);
     __syncthreads();
     if (s == 0) {
@@ -721,6 +777,7 @@ static DecodeArgs make_args(const void* Q, const void* K, const void* V, int B, 
   a.sel_scores = nullptr; a.nb = 0; a.k = 0; a.flags = 0; a.sel_idx = nullptr;
   a.sel_count = nullptr;
   a.sel_ent = reinterpret_cast<int32_t*>(base + w.ent_off);
+  a.sk = nullptr; a.upd = -1;
   a.lb_codes = nullptr; a.lb_resid = nullptr; a.lb_meta = nullptr;
   return a;
 }
@@ -832,6 +889,22 @@ hipError_t launch_decode_select_valu(const void* Q, const void* K, const void* V
                            ws, O, out_dtype, lse);
   a.S = decode_valu_splits(k, block);   // sized for by decode_ws
   a.sel_scores = scores; a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
+  const dim3 g(static_cast<unsigned>(long(B) * Hkv * a.S));
+  if (D == 128) launch_valu_g<128, kValuSelKpt>(a, Hq / Hkv, g, st);
+  else          launch_valu_g<64, kValuSelKpt>(a, Hq / Hkv, g, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step_valu(const void* Q, const void* K, const void* V, int B, int Hq,
+                                   int Hkv, int N, int D, float scale, int block, float* sketch,
+                                   int update_block, float* scores, int nb, int k, unsigned flags,
+                                   int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
+                                   void* O, int out_dtype, float* lse, hipStream_t st) {
+  DecodeArgs a = make_args(Q, K, V, B, Hq, Hkv, N, block, scale, nullptr, nullptr, k, nullptr, w,
+                           ws, O, out_dtype, lse);
+  a.S = decode_valu_splits(k, block);   // sized for by decode_ws
+  a.sel_scores = scores; a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
+  a.sk = sketch; a.upd = update_block;
   const dim3 g(static_cast<unsigned>(long(B) * Hkv * a.S));
   if (D == 128) launch_valu_g<128, kValuSelKpt>(a, Hq / Hkv, g, st);
   else          launch_valu_g<64, kValuSelKpt>(a, Hq / Hkv, g, st);

@@ -325,6 +325,15 @@ sa_status decode_step(const void* Q, const void* K, const void* V, int dtype, in
                       "sa_decode_step");
   const SelectWs sw = select_ws(B, Hkv, 1, D, 1, nb);
   float* scores = score ? score : reinterpret_cast<float*>(static_cast<char*>(ws) + sw.score_off);
+  if (dtype == SA_F32 && nb <= 256 * kValuSelKpt && k <= kValuSelMaxK) {
+    // float32 rows of up to 512 blocks: the whole step in the decode kernel
+    const DecodeWs w = decode_ws(B, Hq, Hkv, D, SA_IDX_BLOCKS, block, k);
+    return hip_status(launch_decode_step_valu(Q, K, V, B, Hq, Hkv, N, D, sc, block, ksketch,
+                                              update_block, scores, nb, k,
+                                              SA_FORCE_SINK | SA_FORCE_LOCAL, idx, count, w, dws,
+                                              O, out_dtype, lse, st),
+                      "sa_decode_step (one-launch float32 step)");
+  }
   hipError_t e = launch_score(Q, dtype, B, Hq, Hkv, D, ksketch, nb, K, N, block, update_block, sc,
                               scores, st);
   if (e != hipSuccess) return hip_status(e, "sa_decode_step (score)");

@@ -276,6 +276,14 @@ hipError_t launch_decode_select_valu(const void* Q, const void* K, const void* V
                                      const float* scores, int nb, int k, unsigned flags,
                                      int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
                                      void* O, int out_dtype, float* lse, hipStream_t st);
+// The whole float32 decode step in one launch (the same shapes): every split
+// scores its kv head's sketch row itself (row update_block rebuilt from K
+// first; -1: none), split 0 storing that sketch row and the scores.
+hipError_t launch_decode_step_valu(const void* Q, const void* K, const void* V, int B, int Hq,
+                                   int Hkv, int N, int D, float scale, int block, float* sketch,
+                                   int update_block, float* scores, int nb, int k, unsigned flags,
+                                   int32_t* idx, int32_t* count, const DecodeWs& w, void* ws,
+                                   void* O, int out_dtype, float* lse, hipStream_t st);
 // The one-launch decode step (bf16; step_fusable shapes).  coh_mode: 0 plain
 // stores inside an XCD team, 1 device-coherent stores throughout, 2 every
 // workgroup acts as if it ran off its team's XCD (both for tests).
