@@ -58,9 +58,10 @@ struct DecodeArgs {
   int32_t* sel_ent;   // [B*Hkv, kSelEntCap] kept block (or -1) per entry of a row
   // in-kernel scoring (float32 step, k_decode_blocks_valu): the sketch
   // [B*Hkv, nb, D] (row upd rebuilt from K first, upd = -1: none) scored
-  // against the group-mean query; sel_scores then receives the scores
+  // against the group-mean query, the scores written to sc_out [B*Hkv, nb]
   float* sk;
   int upd;
+  float* sc_out;
   // keys rebuilt from thumbnails (k_decode_lowbit): codes [B*Hkv, N, D/4],
   // residuals [B*Hkv, N, D], (lo, step, rstep) rows [B*Hkv, nb, 3, D]
   const uint8_t* lb_codes;
@@ -436,8 +437,8 @@ __global__ __launch_bounds__(256) void k_decode_blocks_valu(DecodeArgs a) {
         if (tid == 0) srow[upd] = pu;
       }
       __syncthreads();
-      if (s == 0 && a.sel_scores) {
-        float* so = const_cast<float*>(a.sel_scores) + size_t(bh) * nbr;
+      if (s == 0) {
+        float* so = a.sc_out + size_t(bh) * nbr;
         for (int j = tid; j < nbr; j += 256) so[j] = srow[j];
       }
       load_keys_reg<256, SELKPT>(srow, nbr, kr);
@@ -777,7 +778,7 @@ static DecodeArgs make_args(const void* Q, const void* K, const void* V, int B, 
   a.sel_scores = nullptr; a.nb = 0; a.k = 0; a.flags = 0; a.sel_idx = nullptr;
   a.sel_count = nullptr;
   a.sel_ent = reinterpret_cast<int32_t*>(base + w.ent_off);
-  a.sk = nullptr; a.upd = -1;
+  a.sk = nullptr; a.upd = -1; a.sc_out = nullptr;
   a.lb_codes = nullptr; a.lb_resid = nullptr; a.lb_meta = nullptr;
   return a;
 }
@@ -903,8 +904,8 @@ hipError_t launch_decode_step_valu(const void* Q, const void* K, const void* V, 
   DecodeArgs a = make_args(Q, K, V, B, Hq, Hkv, N, block, scale, nullptr, nullptr, k, nullptr, w,
                            ws, O, out_dtype, lse);
   a.S = decode_valu_splits(k, block);   // sized for by decode_ws
-  a.sel_scores = scores; a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
-  a.sk = sketch; a.upd = update_block;
+  a.nb = nb; a.k = k; a.flags = flags; a.sel_idx = idx; a.sel_count = count;
+  a.sk = sketch; a.upd = update_block; a.sc_out = scores;
   const dim3 g(static_cast<unsigned>(long(B) * Hkv * a.S));
   if (D == 128) launch_valu_g<128, kValuSelKpt>(a, Hq / Hkv, g, st);
   else          launch_valu_g<64, kValuSelKpt>(a, Hq / Hkv, g, st);
