@@ -20,8 +20,13 @@
 //   (ranking only those candidates) or, when the list does not suit slices,
 //   from the fully ranked selection.  Workgroup id % (B*Hkv) selects the
 //   (b, kv head): all splits of one kv head share an XCD and its L2.
-// k_decode_blocks_valu (float32): per-thread dot products, LDS softmax over
-//   1024-token chunks, (head, column)-parallel value pass; float32 throughout.
+// k_decode_blocks_valu (float32): one split per 64-token block; K and V rows
+//   loaded by D/4 lanes each (scores summed over the row's lanes), an LDS
+//   softmax per round of 256 tokens, a (head, column)-parallel value pass;
+//   float32 throughout.  Its selecting variant (rows of up to 512 blocks)
+//   takes the top-k of the score row in every split; for the decode step it
+//   also scores the row itself, with the scoring kernel's functions, so the
+//   whole step is one launch.
 // k_decode_tokens: per (b, query head, split) over an explicit token list
 //   (threshold selection), reusing the selector's scores when given.
 #include "sa_decode_core.h"
